@@ -1,0 +1,224 @@
+"""Float64 CPU oracle of the modal-SSM Hyena operator (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The product library never does, and
+this package imports nothing from it.
+
+Contents
+--------
+build()                 compile ``modal_oracle.c`` with gcc (OpenMP, no fast-math,
+                        no FP contraction) into ``liboracle.so``.
+filter_taps()           h[g][t], t < L, from the closed form of the modal filter.
+modal_scan()            the recurrence (prefill with a zero state, or decode steps
+                        from a given state), float64.
+rms_inv(), dense()      the projected stack's per-token inverse RMS and a float64
+                        matrix product (numpy's matmul as the library primitive).
+stack_layer()           one layer of the projected stack, teacher-forced on a given
+                        input sequence (see ``stack_layer``'s docstring).
+
+The operator, its readings and its pins are described at the top of
+``modal_oracle.c``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "modal_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+DT_F32, DT_BF16, DT_F64 = 0, 1, 2
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc.  Returns the library path."""
+    if not force and os.path.exists(_LIB_PATH) and \
+            os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + f".tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_filter.argtypes = [i64, i64, p, p, p, i64, p]
+    lib.oracle_filter.restype = ctypes.c_int
+    lib.oracle_modal_scan.argtypes = [i64, i64, i64, i64, p, p, p, i64, ctypes.c_int,
+                                      p, p, p, i64, i64, i64, p, p, p]
+    lib.oracle_modal_scan.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _tables(params):
+    poles = np.ascontiguousarray(params.poles, dtype=np.float64)
+    res = np.ascontiguousarray(params.residues, dtype=np.float64)
+    skip = np.ascontiguousarray(params.skip, dtype=np.float64)
+    return poles, res, skip
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return DT_F32
+    if a.dtype == np.uint16:
+        return DT_BF16
+    if a.dtype == np.float64:
+        return DT_F64
+    raise TypeError(f"unsupported activation dtype {a.dtype}")
+
+
+def filter_taps(params, L: int, _lib_handle=None) -> np.ndarray:
+    """h [H][L] float64: h[g,0] = D_g, h[g,t] = Re sum_n R_gn lambda_gn^(t-1)."""
+    lib = _lib_handle or _load()
+    poles, res, skip = _tables(params)
+    H, d = poles.shape[0], poles.shape[1]
+    h = np.empty((H, L), dtype=np.float64)
+    rc = lib.oracle_filter(H, d, _ptr(poles), _ptr(res), _ptr(skip), L, _ptr(h))
+    if rc:
+        raise ValueError("oracle_filter rejected its arguments")
+    return h
+
+
+def modal_scan(params, q, k, v, state=None, channels=None, batch_axis=0, time_axis=1,
+               _lib_handle=None):
+    """Run the recurrence over every time step of q, k, v.
+
+    q, k, v: 3-D arrays (float32, bfloat16 bit patterns as uint16, or float64) of
+    identical shape and dtype, C-contiguous, with the channel axis last.  The
+    batch and time axes are given by ``batch_axis``/``time_axis`` (0/1 for
+    [B][T][D] prompts, 1/0 for [S][B][D] generated steps).
+    state: [B][n_sel][d][2] float64 initial state (None: zero).
+    channels: optional channel indices to compute (default: all).
+    Returns (y [B][T][n_sel] float64, final state [B][n_sel][d][2] float64).
+    """
+    lib = _lib_handle or _load()
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    if not (q.shape == k.shape == v.shape) or q.ndim != 3:
+        raise ValueError("q, k, v must share one 3-D shape")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share one dtype")
+    poles, res, skip = _tables(params)
+    H, d = poles.shape[0], poles.shape[1]
+    D = q.shape[2]
+    B, T = q.shape[batch_axis], q.shape[time_axis]
+    strides = [q.strides[i] // q.itemsize for i in range(3)]
+    sb, st = strides[batch_axis], strides[time_axis]
+    if channels is None:
+        n_sel, sel_ptr, sel = D, None, None
+    else:
+        sel = np.ascontiguousarray(channels, dtype=np.int64)
+        if sel.size and (sel.min() < 0 or sel.max() >= D):
+            raise ValueError("channel index out of range")
+        n_sel, sel_ptr = sel.size, _ptr(sel)
+    y = np.empty((B, T, n_sel), dtype=np.float64)
+    if state is None:
+        state = np.zeros((B, n_sel, d, 2), dtype=np.float64)
+    else:
+        state = np.array(state, dtype=np.float64, order="C", copy=True)
+        if state.shape != (B, n_sel, d, 2):
+            raise ValueError(f"state shape {state.shape} != {(B, n_sel, d, 2)}")
+    rc = lib.oracle_modal_scan(B, D, H, d, _ptr(poles), _ptr(res), _ptr(skip), T,
+                               _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), sb, st,
+                               n_sel, sel_ptr, _ptr(y), _ptr(state))
+    if rc:
+        raise ValueError("oracle_modal_scan rejected its arguments")
+    return y, state
+
+
+# ------------------------------------------------------------ projected stack
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def rms_inv(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """1 / sqrt(mean(x^2) + eps) over the last axis, float64."""
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / np.sqrt(np.mean(x * x, axis=-1) + eps)
+
+
+def dense(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """x @ w^T in float64 (w stored [out][in])."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
+def stack_layer(params, w_in, w_out, x_prompt, x_steps=None, eps: float = 1e-6):
+    """One layer of the projected stack in float64, teacher-forced.
+
+    Layer input x (per token, width D) -> s = 1/rms(x) -> [q|k|v] = (x W_in^T) s
+    (contiguous thirds) -> y = q * (h conv (k v)) through the modal recurrence ->
+    layer output y W_out^T.  No bias, no residual.
+
+    x_prompt: [B][L][D] layer input over the prompt; x_steps: optional
+    [S][B][D] layer inputs of the generated steps (each one the actual input the
+    layer received at that step).  Returns (out_prompt [B][L][D],
+    out_steps [S][B][D] or None, state after the prompt, final state).
+    """
+    D = x_prompt.shape[-1]
+    w_in = bf16_to_f64(w_in) if w_in.dtype == np.uint16 else np.asarray(w_in, np.float64)
+    w_out = bf16_to_f64(w_out) if w_out.dtype == np.uint16 else np.asarray(w_out, np.float64)
+
+    def project(x):
+        x = bf16_to_f64(x) if x.dtype == np.uint16 else np.asarray(x, np.float64)
+        qkv = dense(x, w_in) * rms_inv(x, eps)[..., None]
+        return (np.ascontiguousarray(qkv[..., :D]), np.ascontiguousarray(qkv[..., D:2 * D]),
+                np.ascontiguousarray(qkv[..., 2 * D:]))
+
+    q, k, v = project(x_prompt)
+    y, st_prompt = modal_scan(params, q, k, v)
+    out_prompt = dense(y, w_out)
+    out_steps, st = None, st_prompt
+    if x_steps is not None:
+        q, k, v = project(x_steps)
+        ys, st = modal_scan(params, q, k, v, state=st_prompt, batch_axis=1, time_axis=0)
+        # ys is [B][S][D]; return step-major like the inputs
+        out_steps = dense(np.ascontiguousarray(ys.transpose(1, 0, 2)), w_out)
+    return out_prompt, out_steps, st_prompt, st
+
+
+class Bound:
+    """The oracle's functions bound to another build of ``modal_oracle.c``.
+
+    Used by the tests that plant mistakes in a copy of the oracle source to show
+    that the pins catch them.
+    """
+
+    def __init__(self, lib_path: str):
+        self._h = _bind(lib_path)
+
+    def filter_taps(self, params, L):
+        return filter_taps(params, L, _lib_handle=self._h)
+
+    def modal_scan(self, *a, **kw):
+        return modal_scan(*a, _lib_handle=self._h, **kw)
+
+    def stack_layer(self, *a, **kw):
+        raise NotImplementedError

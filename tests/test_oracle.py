@@ -1,0 +1,307 @@
+"""Pins of the float64 oracle against facts fixed outside the oracle.
+
+Each test checks the oracle against something it does not compute itself:
+hand-derived worked examples, the direct (brute-force) causal convolution with
+the closed-form filter, the one-mode geometric-series closed form, Horner
+evaluation (numpy.polyval), FFT convolution (numpy.fft), and structural facts
+(impulse response, composition, linearity, time shift, semiseparable rank,
+stability bound).  Mistakes these catch include: a flipped sign of the
+imaginary part in Re(R x), conjugated poles, update-before-read ordering
+(h shifted by one tap), a dropped skip term D, a wrong channel-to-head map,
+wrong strides, a wrong state layout or exponent in the final state.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+from workloads import get_config, modal_params, prompt_inputs, decode_inputs
+from workloads.generate import ModalParams
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples_d1.txt")
+
+
+def _random_params(rng, H, d, r_lo=0.5, r_hi=0.99):
+    r = rng.uniform(r_lo, r_hi, (H, d))
+    th = rng.uniform(0, np.pi, (H, d))
+    poles = np.stack([r * np.cos(th), r * np.sin(th)], -1).astype(np.float32)
+    res = (rng.standard_normal((H, d, 2)) / np.sqrt(2 * d)).astype(np.float32)
+    skip = rng.standard_normal(H).astype(np.float32)
+    return ModalParams(poles, res, skip)
+
+
+def _closed_form_h(params, T):
+    """h[g][t] via numpy complex powers (np.power), independent of the oracle."""
+    lam = params.poles[..., 0].astype(np.float64) + 1j * params.poles[..., 1]
+    R = params.residues[..., 0].astype(np.float64) + 1j * params.residues[..., 1]
+    t = np.arange(T - 1)
+    pw = np.power(lam[:, :, None], t[None, None, :])          # [H][d][T-1]
+    h = np.empty((params.H, T))
+    h[:, 0] = params.skip
+    h[:, 1:] = np.real(np.sum(R[:, :, None] * pw, axis=1))
+    return h
+
+
+def _direct_conv(params, q, k, v):
+    """y = diag(q) T_h diag(k) v per channel with an explicit causal Toeplitz T_h."""
+    B, T, D = q.shape
+    P = D // params.H
+    h = _closed_form_h(params, T)
+    y = np.zeros((B, T, D))
+    idx = np.arange(T)[:, None] - np.arange(T)[None, :]
+    for g in range(params.H):
+        Th = np.where(idx >= 0, h[g][np.clip(idx, 0, None)], 0.0)
+        for c in range(g * P, (g + 1) * P):
+            for b in range(B):
+                u = k[b, :, c].astype(np.float64) * v[b, :, c]
+                y[b, :, c] = q[b, :, c] * (Th @ u)
+    return y
+
+
+def _read_golden():
+    blocks, cur = [], None
+    for line in open(GOLDEN, encoding="utf-8"):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        key, *vals = line.split()
+        if key == "name":
+            cur = {"name": vals[0]}
+            blocks.append(cur)
+        elif key == "lambda":
+            cur["lambda"] = (float(vals[0]), float(vals[1]))
+            cur["R"] = (float(vals[3]), float(vals[4]))
+            cur["D"] = float(vals[6])
+        else:
+            cur[key] = np.array([float(x) for x in vals])
+    return blocks
+
+
+# ------------------------------------------------------------------ worked examples
+
+
+@pytest.mark.parametrize("ex", _read_golden(), ids=lambda e: e["name"])
+def test_hand_worked_examples(oracle_lib, ex):
+    params = ModalParams(np.array([[ex["lambda"]]], np.float32), np.array([[ex["R"]]], np.float32),
+                         np.array([ex["D"]], np.float32))
+    T = ex["q"].size
+    q, k, v = (ex[n].astype(np.float32).reshape(1, T, 1) for n in ("q", "k", "v"))
+    y, st = oracle_lib.modal_scan(params, q, k, v)
+    assert np.array_equal(y.ravel(), ex["y"])
+    assert np.array_equal(st.ravel(), ex["x"])
+    h = oracle_lib.filter_taps(params, T)
+    assert np.array_equal(h.ravel(), ex["h"])
+
+
+# ------------------------------------------------------------------ brute force
+
+
+@pytest.mark.parametrize("d", [1, 3, 8])
+def test_recurrence_equals_direct_convolution(oracle_lib, d):
+    rng = np.random.default_rng(7 + d)
+    B, D, H, T = 2, 8, 2, 160
+    params = _random_params(rng, H, d)
+    q, k, v = (rng.standard_normal((B, T, D)).astype(np.float32) for _ in range(3))
+    y, _ = oracle_lib.modal_scan(params, q, k, v)
+    ref = _direct_conv(params, q, k, v)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_bf16_inputs_and_strided_layout(oracle_lib):
+    """bf16 bit patterns and a [S][B][D] (time-major) layout give the same numbers."""
+    from workloads import bf16_bits_to_f32, round_to_bf16_bits
+    rng = np.random.default_rng(3)
+    B, D, H, T, d = 3, 12, 3, 40, 4
+    params = _random_params(rng, H, d)
+    raw = [round_to_bf16_bits(rng.standard_normal((B, T, D))) for _ in range(3)]
+    f32 = [bf16_bits_to_f32(a) for a in raw]
+    y_bits, st_bits = oracle_lib.modal_scan(params, *raw)
+    ref = _direct_conv(params, *f32)
+    assert np.max(np.abs(y_bits - ref)) <= 1e-12 * np.max(np.abs(ref))
+    tm = [np.ascontiguousarray(a.transpose(1, 0, 2)) for a in raw]
+    y_tm, st_tm = oracle_lib.modal_scan(params, *tm, batch_axis=1, time_axis=0)
+    assert np.array_equal(y_tm, y_bits) and np.array_equal(st_tm, st_bits)
+
+
+def test_channel_subset_matches_full(oracle_lib):
+    rng = np.random.default_rng(11)
+    B, D, H, T, d = 2, 16, 4, 50, 3
+    params = _random_params(rng, H, d)
+    q, k, v = (rng.standard_normal((B, T, D)).astype(np.float32) for _ in range(3))
+    y, st = oracle_lib.modal_scan(params, q, k, v)
+    sel = np.array([15, 0, 7, 8])
+    ys, sts = oracle_lib.modal_scan(params, q, k, v, channels=sel)
+    assert np.array_equal(ys, y[:, :, sel]) and np.array_equal(sts, st[:, sel])
+
+
+# ------------------------------------------------------------------ closed forms
+
+
+def test_one_mode_geometric_series(oracle_lib):
+    """d = 1, q = 1, u = 1: x_t = (1 - lam^t)/(1 - lam), y_t = D + Re(R x_t)."""
+    lam = np.float32(0.93) * np.exp(1j * 0.7)
+    params = ModalParams(np.array([[[lam.real, lam.imag]]], np.float32),
+                         np.array([[[0.6, -1.3]]], np.float32), np.array([0.25], np.float32))
+    T = 300
+    ones = np.ones((1, T, 1), np.float32)
+    y, st = oracle_lib.modal_scan(params, ones, ones, ones)
+    lam64 = complex(float(params.poles[0, 0, 0]), float(params.poles[0, 0, 1]))
+    R = complex(float(params.residues[0, 0, 0]), float(params.residues[0, 0, 1]))
+    t = np.arange(T)
+    xt = (1 - lam64 ** t) / (1 - lam64)                 # state read at step t
+    expect = 0.25 + np.real(R * xt)
+    assert np.max(np.abs(y.ravel() - expect)) < 1e-12
+    xT = (1 - lam64 ** T) / (1 - lam64)
+    assert abs(complex(st[0, 0, 0, 0], st[0, 0, 0, 1]) - xT) < 1e-12
+
+
+def test_final_state_is_horner_polynomial(oracle_lib):
+    """x_L,n = sum_t lam_n^(L-1-t) u_t = polyval(u, lam_n)."""
+    rng = np.random.default_rng(5)
+    B, D, H, T, d = 2, 6, 2, 120, 5
+    params = _random_params(rng, H, d)
+    q, k, v = (rng.standard_normal((B, T, D)).astype(np.float32) for _ in range(3))
+    _, st = oracle_lib.modal_scan(params, q, k, v)
+    P = D // H
+    for b in range(B):
+        for c in range(D):
+            u = k[b, :, c].astype(np.float64) * v[b, :, c]
+            for n in range(d):
+                lam = complex(*params.poles[c // P, n].astype(np.float64))
+                want = np.polyval(u, lam)
+                got = complex(*st[b, c, n])
+                assert abs(got - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_fft_convolution_mid_size(oracle_lib):
+    """L = 4096: the recurrence equals an FFT convolution with the materialised h."""
+    cfg = get_config(2)
+    params = modal_params(cfg)
+    rng = np.random.default_rng(9)
+    L, D = 4096, cfg.D
+    chans = np.array([0, 130, 700, 2047])
+    q = np.zeros((1, L, D), np.float32)
+    k = np.zeros((1, L, D), np.float32)
+    v = np.zeros((1, L, D), np.float32)
+    for a in (q, k, v):
+        a[0][:, chans] = rng.standard_normal((L, chans.size))
+    y, _ = oracle_lib.modal_scan(params, q, k, v, channels=chans)
+    h = oracle_lib.filter_taps(params, L)
+    for i, c in enumerate(chans):
+        u = k[0, :, c].astype(np.float64) * v[0, :, c]
+        conv = np.fft.irfft(np.fft.rfft(h[c // cfg.P], 2 * L) * np.fft.rfft(u, 2 * L), 2 * L)[:L]
+        ref = q[0, :, c] * conv
+        assert np.max(np.abs(y[0, :, i] - ref)) <= 1e-10 * np.max(np.abs(ref))
+
+
+# ------------------------------------------------------------------ structure
+
+
+def test_impulse_response_is_filter(oracle_lib):
+    rng = np.random.default_rng(2)
+    H, d, T = 3, 6, 500
+    params = _random_params(rng, H, d, 0.8, 0.999)
+    D = H * 2
+    q = np.ones((1, T, D), np.float32)
+    k = np.zeros((1, T, D), np.float32)
+    k[0, 0, :] = 1
+    y, _ = oracle_lib.modal_scan(params, q, k, q)
+    h = oracle_lib.filter_taps(params, T)
+    for c in range(D):
+        assert np.max(np.abs(y[0, :, c] - h[c // 2])) <= 1e-13 * np.max(np.abs(h))
+    ref = _closed_form_h(params, T)
+    assert np.max(np.abs(h - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_prefill_then_decode_equals_one_pass(oracle_lib):
+    rng = np.random.default_rng(4)
+    B, D, H, L, S, d = 2, 8, 2, 90, 30, 4
+    params = _random_params(rng, H, d)
+    q, k, v = (rng.standard_normal((B, L + S, D)).astype(np.float32) for _ in range(3))
+    y_all, st_all = oracle_lib.modal_scan(params, q, k, v)
+    y_p, st_p = oracle_lib.modal_scan(params, q[:, :L], k[:, :L], v[:, :L])
+    st = st_p
+    for s in range(S):
+        sl = slice(L + s, L + s + 1)
+        y_s, st = oracle_lib.modal_scan(params, q[:, sl], k[:, sl], v[:, sl], state=st)
+        assert np.array_equal(y_s[:, 0], y_all[:, L + s])
+    assert np.array_equal(y_p, y_all[:, :L])
+    assert np.array_equal(st, st_all)
+
+
+def test_linearity_and_time_shift(oracle_lib):
+    rng = np.random.default_rng(6)
+    B, D, H, T, d, sh = 1, 4, 2, 80, 3, 17
+    params = _random_params(rng, H, d)
+    q, k, v1, v2 = (rng.standard_normal((B, T, D)) for _ in range(4))
+    ya, _ = oracle_lib.modal_scan(params, q, k, v1)
+    yb, _ = oracle_lib.modal_scan(params, q, k, v2)
+    yab, _ = oracle_lib.modal_scan(params, q, k, v1 + v2)
+    assert np.max(np.abs(yab - ya - yb)) <= 1e-12 * np.max(np.abs(yab))
+    pad = lambda a: np.concatenate([np.zeros((B, sh, D)), a[:, :T - sh]], axis=1)
+    ys, _ = oracle_lib.modal_scan(params, pad(q), pad(k), pad(v1))
+    assert np.all(ys[:, :sh] == 0)
+    assert np.max(np.abs(ys[:, sh:] - ya[:, :T - sh])) <= 1e-12 * np.max(np.abs(ya))
+
+
+def test_toeplitz_offdiagonal_rank(oracle_lib):
+    """Off-diagonal blocks of the causal Toeplitz T_h have rank <= 2d (semiseparable)."""
+    rng = np.random.default_rng(8)
+    H, d, T = 1, 5, 200
+    params = _random_params(rng, H, d, 0.7, 0.95)
+    h = oracle_lib.filter_taps(params, T)[0]
+    m = 100
+    blk = np.array([[h[t - s] for s in range(m)] for t in range(m, T)])
+    sv = np.linalg.svd(blk, compute_uv=False)
+    assert np.sum(sv > 1e-10 * sv[0]) <= 2 * d
+    assert sv[2 * d - 1] > 1e-10 * sv[0]  # the bound is reached with distinct poles
+
+
+def test_stability_bounds(oracle_lib):
+    for i in (1, 2, 3, 4):
+        cfg = get_config(i)
+        p = modal_params(cfg)
+        mag = np.hypot(p.poles[..., 0].astype(np.float64), p.poles[..., 1])
+        assert np.all(mag < 1.0) and np.all(mag >= cfg.r_lo * (1 - 1e-6))
+    cfg = get_config(1)
+    p = modal_params(cfg)
+    inp = prompt_inputs(cfg)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    _, st = oracle_lib.modal_scan(p, q, k, v)
+    umax = np.max(np.abs(k.astype(np.float64) * v), axis=1)   # [B][D]
+    mag = np.hypot(p.poles[..., 0].astype(np.float64), p.poles[..., 1])
+    for c in range(cfg.D):
+        bound = umax[:, c, None] / (1 - mag[c // cfg.P])[None, :]
+        got = np.hypot(st[:, c, :, 0], st[:, c, :, 1])
+        assert np.all(got <= bound * (1 + 1e-12))
+    h = oracle_lib.filter_taps(p, 4000)
+    assert np.max(np.abs(h[:, -100:])) < 1e-6 * np.max(np.abs(h[:, 1:10]))
+
+
+def test_workload1_full_run_is_finite(oracle_lib):
+    cfg = get_config(1)
+    p = modal_params(cfg)
+    inp = prompt_inputs(cfg)
+    dec = decode_inputs(cfg)
+    y, st = oracle_lib.modal_scan(p, inp["q"], inp["k"], inp["v"])
+    yd, st2 = oracle_lib.modal_scan(p, dec["q"], dec["k"], dec["v"], state=st,
+                                    batch_axis=1, time_axis=0)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(yd)) and np.all(np.isfinite(st2))
+    assert yd.shape == (cfg.B, cfg.S, cfg.D)
+
+
+def test_stack_layer_matches_unrolled_definition(oracle_lib):
+    """The projected layer equals rms -> in_proj -> brute-force Hyena -> out_proj."""
+    rng = np.random.default_rng(12)
+    D, H, d, B, L = 8, 2, 3, 2, 24
+    params = _random_params(rng, H, d)
+    w_in = rng.standard_normal((3 * D, D)) * 0.3
+    w_out = rng.standard_normal((D, D)) * 0.3
+    x = rng.standard_normal((B, L, D))
+    out, _, _, _ = oracle_lib.stack_layer(params, w_in, w_out, x)
+    s = 1 / np.sqrt((x ** 2).mean(-1, keepdims=True) + 1e-6)
+    qkv = np.einsum("btk,nk->btn", x, w_in) * s
+    y = _direct_conv(params, qkv[..., :D], qkv[..., D:2 * D], qkv[..., 2 * D:])
+    ref = np.einsum("btk,nk->btn", y, w_out)
+    assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
