@@ -1,0 +1,256 @@
+"""ctypes binding of ``libhyena_modal.so`` (the C ABI in include/hyena_modal.h).
+
+Argument marshalling only: every computation runs in the library's HIP kernels.
+Pointer arguments accept an ``int`` device address, ``None`` (NULL) or any
+object with ``data_ptr()`` (a torch tensor); ``stream`` accepts an ``int``
+hipStream_t, ``None`` (the current torch stream when torch is loaded, else the
+default stream) or a torch stream.
+
+The library must have been built in-tree (``distilled_modal_ssm_amd/build.py``);
+if it is missing, loading raises :class:`LibraryMissing` -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhyena_modal.so")
+
+HM_ABI_VERSION = 1
+HM_MAX_MODES = 64
+HM_F32, HM_BF16 = 0, 1
+HM_OK, HM_ERR_INVALID_ARG, HM_ERR_UNSUPPORTED, HM_ERR_WORKSPACE, HM_ERR_HIP = range(5)
+
+EXPORTS = (
+    "hm_abi_version",
+    "hm_status_string",
+    "hyena_modal_prefill_workspace",
+    "hyena_modal_prefill_workspace_chunked",
+    "hyena_modal_prefill",
+    "hyena_modal_prefill_chunked",
+    "hyena_modal_decode_step",
+    "hyena_filter_materialize",
+)
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class HMError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+class hm_desc(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int64),
+        ("channels", ctypes.c_int64),
+        ("heads", ctypes.c_int64),
+        ("modes", ctypes.c_int64),
+        ("poles", ctypes.c_void_p),
+        ("residues", ctypes.c_void_p),
+        ("skip", ctypes.c_void_p),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once (raises LibraryMissing if it was not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise LibraryMissing(
+                f"{path} not found: build it with `python -m distilled_modal_ssm_amd.build` "
+                "(or __graft_entry__.build()); there is no CPU fallback")
+        lib = ctypes.CDLL(path)
+        i64, p, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        D = ctypes.POINTER(hm_desc)
+        sig = {
+            "hm_abi_version": ([], ctypes.c_int),
+            "hm_status_string": ([ctypes.c_int], ctypes.c_char_p),
+            "hyena_modal_prefill_workspace": ([D, i64, ctypes.POINTER(sz)], ctypes.c_int),
+            "hyena_modal_prefill_workspace_chunked": ([D, i64, i64, ctypes.POINTER(sz)], ctypes.c_int),
+            "hyena_modal_prefill": ([D, i64, p, p, p, i64, p, i64, p, p, p, sz, p], ctypes.c_int),
+            "hyena_modal_prefill_chunked": ([D, i64, p, p, p, i64, p, i64, p, p, p, sz, i64, p],
+                                            ctypes.c_int),
+            "hyena_modal_decode_step": ([D, p, p, p, i64, p, i64, p, p], ctypes.c_int),
+            "hyena_filter_materialize": ([D, i64, p, p], ctypes.c_int),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        if lib.hm_abi_version() != HM_ABI_VERSION:
+            raise LibraryMissing("libhyena_modal.so has a different ABI version")
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().hm_status_string(status).decode()
+    except LibraryMissing:
+        return f"status {status}"
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(s):
+    if s is None:
+        import sys
+        torch = sys.modules.get("torch")
+        if torch is not None and torch.cuda.is_initialized():
+            return int(torch.cuda.current_stream().cuda_stream)
+        return None
+    if isinstance(s, int):
+        return s
+    return int(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != HM_OK:
+        raise HMError(status, where)
+
+
+def make_desc(batch, channels, heads, modes, act_dtype, poles, residues, skip) -> hm_desc:
+    return hm_desc(HM_ABI_VERSION, act_dtype, batch, channels, heads, modes,
+                   _ptr(poles), _ptr(residues), _ptr(skip))
+
+
+# ----------------------------------------------------------------- raw entry points
+
+
+def hm_abi_version() -> int:
+    return load().hm_abi_version()
+
+
+def hyena_modal_prefill_workspace(desc: hm_desc, L: int, chunk: int = 0) -> int:
+    n = ctypes.c_size_t(0)
+    if chunk:
+        st = load().hyena_modal_prefill_workspace_chunked(ctypes.byref(desc), L, chunk, ctypes.byref(n))
+    else:
+        st = load().hyena_modal_prefill_workspace(ctypes.byref(desc), L, ctypes.byref(n))
+    _check(st, "hyena_modal_prefill_workspace")
+    return n.value
+
+
+def hyena_modal_prefill(desc: hm_desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out,
+                        workspace, ws_bytes, stream=None, chunk: int = 0) -> None:
+    lib = load()
+    args = (ctypes.byref(desc), L, _ptr(q), _ptr(k), _ptr(v), ld_in, _ptr(y), ld_y,
+            _ptr(state_in), _ptr(state_out), _ptr(workspace), ws_bytes)
+    if chunk:
+        st = lib.hyena_modal_prefill_chunked(*args, chunk, _stream(stream))
+    else:
+        st = lib.hyena_modal_prefill(*args, _stream(stream))
+    _check(st, "hyena_modal_prefill")
+
+
+def hyena_modal_decode_step(desc: hm_desc, q, k, v, ld_in, y, ld_y, state, stream=None) -> None:
+    st = load().hyena_modal_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), ld_in,
+                                        _ptr(y), ld_y, _ptr(state), _stream(stream))
+    _check(st, "hyena_modal_decode_step")
+
+
+def hyena_filter_materialize(desc: hm_desc, L, h_out, stream=None) -> None:
+    st = load().hyena_filter_materialize(ctypes.byref(desc), L, _ptr(h_out), _stream(stream))
+    _check(st, "hyena_filter_materialize")
+
+
+# ----------------------------------------------------------------- tensor helpers
+
+
+def _row_stride(t, same):
+    """Row stride ld of a [B][L][D] view laid out as (b*L + t)*ld + c; checks peers."""
+    if t.dim() != 3 or (t.shape[2] > 1 and t.stride(2) != 1):
+        raise ValueError("activations must be [B][L][D] views with unit channel stride")
+    B, L = t.shape[0], t.shape[1]
+    ld = t.stride(1) if L > 1 else (t.stride(0) if B > 1 else t.shape[2])
+    if B > 1 and L > 0 and t.stride(0) != L * ld:
+        raise ValueError("batch rows must be contiguous runs of L rows (stride(0) == L*stride(1))")
+    for o in same:
+        if o.shape != t.shape or (L > 1 and o.stride(1) != ld) or (B > 1 and L > 0 and o.stride(0) != t.stride(0)):
+            raise ValueError("q, k, v must share shape and strides")
+    return ld
+
+
+class ModalHyena:
+    """Device tables of one operator plus calls on torch tensors.
+
+    poles, residues: [H][d][2] float32; skip: [H] float32 (host arrays or
+    tensors; copied to ``device``).  Activations are torch tensors of dtype
+    float32 or bfloat16 on the same device; outputs are allocated with torch
+    (device memory is torch's job, the arithmetic is the library's).
+    """
+
+    def __init__(self, poles, residues, skip, batch: int, channels: int, act: str, device="cuda"):
+        import torch
+        self.torch = torch
+        self.device = torch.device(device)
+        t = lambda a: torch.as_tensor(a, dtype=torch.float32).contiguous().to(self.device)
+        self.poles, self.residues, self.skip = t(poles), t(residues), t(skip)
+        self.H, self.d = int(self.poles.shape[0]), int(self.poles.shape[1])
+        self.B, self.D = int(batch), int(channels)
+        self.P = self.D // self.H
+        self.act = act
+        self.tdtype = torch.bfloat16 if act == "bf16" else torch.float32
+        self.desc = make_desc(self.B, self.D, self.H, self.d, HM_BF16 if act == "bf16" else HM_F32,
+                              self.poles, self.residues, self.skip)
+        self._ws = None
+
+    def new_state(self):
+        return self.torch.zeros((self.B, self.H, self.d, self.P, 2), dtype=self.torch.float32,
+                                device=self.device)
+
+    def workspace(self, L: int, chunk: int = 0):
+        n = hyena_modal_prefill_workspace(self.desc, L, chunk)
+        if self._ws is None or self._ws.numel() < n:
+            self._ws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device=self.device)
+        return self._ws, n
+
+    def prefill(self, q, k, v, y=None, state_in=None, state_out=None, chunk: int = 0, stream=None):
+        """q, k, v: [B][L][ld] views with unit channel stride.  Returns (y, state)."""
+        B, L = q.shape[0], q.shape[1]
+        if y is None:
+            y = self.torch.empty((B, L, self.D), dtype=self.tdtype, device=self.device)
+        if state_out is None:
+            state_out = self.new_state()
+        ld_in = _row_stride(q, (k, v))
+        ld_y = _row_stride(y, ())
+        ws, n = self.workspace(L, chunk)
+        hyena_modal_prefill(self.desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out, ws, n,
+                            stream, chunk)
+        return y, state_out
+
+    def decode_step(self, q, k, v, state, y=None, stream=None):
+        """q, k, v: [B][ld] rows.  Updates state in place; returns y [B][D]."""
+        if y is None:
+            y = self.torch.empty((self.B, self.D), dtype=self.tdtype, device=self.device)
+        for t in (q, k, v, y):
+            if t.dim() != 2 or t.stride(1) != 1 or (t.shape[0] > 1 and t.stride(0) != q.stride(0) and t is not y):
+                raise ValueError("decode_step needs [B][D] rows with unit channel stride and one row stride for q, k, v")
+        hyena_modal_decode_step(self.desc, q, k, v, q.stride(0), y, y.stride(0), state, stream)
+        return y
+
+    def filter(self, L: int, stream=None):
+        h = self.torch.empty((self.H, L), dtype=self.torch.float32, device=self.device)
+        hyena_filter_materialize(self.desc, L, h, stream)
+        return h

@@ -1,0 +1,198 @@
+// hm_api.cpp -- the C ABI declared in include/hyena_modal.h.
+//
+// Every entry point validates its arguments on the host first (sizes, pointers,
+// alignment, workspace) and returns a status without touching the GPU when they
+// are wrong.  Valid calls build an argument block and enqueue kernels on the
+// caller's stream; nothing here allocates, frees or synchronises.
+#include "hyena_modal.h"
+
+#include <hip/hip_runtime.h>
+
+#include "hm_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 46;  // guard against int64 overflow in offsets
+
+bool aligned(const void *p, uintptr_t m) { return (reinterpret_cast<uintptr_t>(p) % m) == 0; }
+
+hm_status check_desc(const hm_desc *desc) {
+    if (!desc) return HM_ERR_INVALID_ARG;
+    if (desc->abi_version != HM_ABI_VERSION) return HM_ERR_INVALID_ARG;
+    if (desc->act_dtype != HM_F32 && desc->act_dtype != HM_BF16) return HM_ERR_UNSUPPORTED;
+    if (desc->batch < 0 || desc->channels < 1 || desc->heads < 1 || desc->modes < 1)
+        return HM_ERR_INVALID_ARG;
+    if (desc->channels % desc->heads != 0) return HM_ERR_INVALID_ARG;
+    if (desc->modes > HM_MAX_MODES) return HM_ERR_UNSUPPORTED;
+    if (!desc->poles || !desc->residues || !desc->skip) return HM_ERR_INVALID_ARG;
+    if (!aligned(desc->poles, 8) || !aligned(desc->residues, 8) || !aligned(desc->skip, 4))
+        return HM_ERR_UNSUPPORTED;
+    if (desc->batch > kMaxElems / desc->channels) return HM_ERR_INVALID_ARG;
+    if (desc->batch * desc->channels > kMaxElems / desc->modes) return HM_ERR_INVALID_ARG;
+    return HM_OK;
+}
+
+hm::OpShape shape_of(const hm_desc *desc) {
+    hm::OpShape s;
+    s.B = desc->batch;
+    s.D = desc->channels;
+    s.H = desc->heads;
+    s.d = desc->modes;
+    s.P = desc->channels / desc->heads;
+    s.act = desc->act_dtype == HM_BF16 ? hm::kBF16 : hm::kF32;
+    s.poles = reinterpret_cast<const float2 *>(desc->poles);
+    s.residues = reinterpret_cast<const float2 *>(desc->residues);
+    s.skip = desc->skip;
+    return s;
+}
+
+int elem_bytes(const hm_desc *desc) { return desc->act_dtype == HM_BF16 ? 2 : 4; }
+
+hm_status check_act(const hm_desc *desc, const void *p) {
+    if (!p) return HM_ERR_INVALID_ARG;
+    if (!aligned(p, (uintptr_t)elem_bytes(desc))) return HM_ERR_UNSUPPORTED;
+    return HM_OK;
+}
+
+hm_status check_chunk(int64_t chunk) {
+    if (chunk < 0) return HM_ERR_INVALID_ARG;
+    if (chunk > 0 && chunk % 64 != 0) return HM_ERR_UNSUPPORTED;
+    return HM_OK;
+}
+
+hm_status prefill_impl(const hm_desc *desc, int64_t L, const void *q, const void *k, const void *v,
+                       int64_t ld_in, void *y, int64_t ld_y, const float *state_in, float *state_out,
+                       void *workspace, size_t ws_bytes, void *stream, int64_t chunk) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if ((st = check_chunk(chunk)) != HM_OK) return st;
+    if (L < 0 || L > kMaxElems) return HM_ERR_INVALID_ARG;
+    const hm::OpShape s = shape_of(desc);
+    if (s.B > 0 && L > 0) {
+        if ((st = check_act(desc, q)) != HM_OK || (st = check_act(desc, k)) != HM_OK ||
+            (st = check_act(desc, v)) != HM_OK || (st = check_act(desc, y)) != HM_OK)
+            return st;
+        if (ld_in < s.D || ld_y < s.D) return HM_ERR_INVALID_ARG;
+        if (s.B * L > kMaxElems / ld_in || s.B * L > kMaxElems / ld_y) return HM_ERR_INVALID_ARG;
+    }
+    if (s.B > 0) {
+        if (!state_out) return HM_ERR_INVALID_ARG;
+        if (!aligned(state_out, 8) || (state_in && !aligned(state_in, 8))) return HM_ERR_UNSUPPORTED;
+    }
+    const hm::PrefillPlan plan = hm::make_prefill_plan(s, L, chunk);
+    // grid limits: batch rows and chunks map to the y/z launch dimensions
+    if (s.B > 65535 || plan.NC > 65535) return HM_ERR_UNSUPPORTED;
+    if (s.B > 0 && plan.bytes > 0) {
+        if (!workspace || ws_bytes < plan.bytes) return HM_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return HM_ERR_UNSUPPORTED;
+    }
+    if (s.B == 0) return HM_OK;
+    hm::PrefillArgs a;
+    a.s = s;
+    a.plan = plan;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.ld_in = ld_in;
+    a.y = y;
+    a.ld_y = ld_y;
+    a.state_in = reinterpret_cast<const float2 *>(state_in);
+    a.state_out = reinterpret_cast<float2 *>(state_out);
+    a.ws = static_cast<unsigned char *>(workspace);
+    const hipError_t err = hm::launch_prefill(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+hm_status workspace_impl(const hm_desc *desc, int64_t L, int64_t chunk, size_t *bytes) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if ((st = check_chunk(chunk)) != HM_OK) return st;
+    if (!bytes || L < 0 || L > kMaxElems) return HM_ERR_INVALID_ARG;
+    *bytes = desc->batch > 0 ? hm::make_prefill_plan(shape_of(desc), L, chunk).bytes : 0;
+    return HM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hm_abi_version(void) { return HM_ABI_VERSION; }
+
+const char *hm_status_string(hm_status status) {
+    switch (status) {
+        case HM_OK: return "HM_OK";
+        case HM_ERR_INVALID_ARG: return "HM_ERR_INVALID_ARG: invalid argument";
+        case HM_ERR_UNSUPPORTED: return "HM_ERR_UNSUPPORTED: unsupported dtype, size or alignment";
+        case HM_ERR_WORKSPACE: return "HM_ERR_WORKSPACE: workspace missing or too small";
+        case HM_ERR_HIP: return "HM_ERR_HIP: kernel launch failed";
+    }
+    return "unknown hm_status";
+}
+
+hm_status hyena_modal_prefill_workspace(const hm_desc *desc, int64_t L, size_t *bytes) {
+    return workspace_impl(desc, L, 0, bytes);
+}
+
+hm_status hyena_modal_prefill_workspace_chunked(const hm_desc *desc, int64_t L, int64_t chunk,
+                                                size_t *bytes) {
+    return workspace_impl(desc, L, chunk, bytes);
+}
+
+hm_status hyena_modal_prefill(const hm_desc *desc, int64_t L, const void *q, const void *k,
+                              const void *v, int64_t ld_in, void *y, int64_t ld_y,
+                              const float *state_in, float *state_out, void *workspace,
+                              size_t ws_bytes, void *stream) {
+    return prefill_impl(desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out, workspace, ws_bytes,
+                        stream, 0);
+}
+
+hm_status hyena_modal_prefill_chunked(const hm_desc *desc, int64_t L, const void *q, const void *k,
+                                      const void *v, int64_t ld_in, void *y, int64_t ld_y,
+                                      const float *state_in, float *state_out, void *workspace,
+                                      size_t ws_bytes, int64_t chunk, void *stream) {
+    return prefill_impl(desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out, workspace, ws_bytes,
+                        stream, chunk);
+}
+
+hm_status hyena_modal_decode_step(const hm_desc *desc, const void *q, const void *k, const void *v,
+                                  int64_t ld_in, void *y, int64_t ld_y, float *state, void *stream) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    const hm::OpShape s = shape_of(desc);
+    if (s.B == 0) return HM_OK;
+    if ((st = check_act(desc, q)) != HM_OK || (st = check_act(desc, k)) != HM_OK ||
+        (st = check_act(desc, v)) != HM_OK || (st = check_act(desc, y)) != HM_OK)
+        return st;
+    if (!state) return HM_ERR_INVALID_ARG;
+    if (!aligned(state, 8)) return HM_ERR_UNSUPPORTED;
+    if (ld_in < s.D || ld_y < s.D) return HM_ERR_INVALID_ARG;
+    if (s.B > kMaxElems / ld_in || s.B > kMaxElems / ld_y) return HM_ERR_INVALID_ARG;
+    hm::DecodeArgs a;
+    a.s = s;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.ld_in = ld_in;
+    a.y = y;
+    a.ld_y = ld_y;
+    a.state = reinterpret_cast<float2 *>(state);
+    const hipError_t err = hm::launch_decode_step(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+hm_status hyena_filter_materialize(const hm_desc *desc, int64_t L, float *h_out, void *stream) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if (L < 0 || L > kMaxElems / desc->heads) return HM_ERR_INVALID_ARG;
+    if (L == 0) return HM_OK;
+    if (!h_out) return HM_ERR_INVALID_ARG;
+    if (!aligned(h_out, 4)) return HM_ERR_UNSUPPORTED;
+    hm::FilterArgs a;
+    a.s = shape_of(desc);
+    a.L = L;
+    a.h = h_out;
+    const hipError_t err = hm::launch_filter(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+}  // extern "C"

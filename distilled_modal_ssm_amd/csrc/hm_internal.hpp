@@ -1,0 +1,112 @@
+// Internal declarations of the gfx950 modal-SSM Hyena library: argument blocks
+// passed to the kernel launchers, and device helpers shared by the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hm {
+
+constexpr int kWave = 64;
+constexpr int kMaxModes = 64;  // largest supported number of modes d
+
+enum ActType : int { kF32 = 0, kBF16 = 1 };
+
+// ---------------------------------------------------------------- bfloat16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Activation element access for float32 (ACT = kF32) or bfloat16 bit patterns.
+template <int ACT> struct Act;
+
+template <> struct Act<kF32> {
+    using T = float;
+    static constexpr int kBytes = 4;
+    __device__ static float ld(const T *p) { return *p; }
+    __device__ static float2 ld2(const T *p) { return *reinterpret_cast<const float2 *>(p); }
+    __device__ static void st(T *p, float x) { *p = x; }
+    __device__ static void st2(T *p, float a, float b) {
+        *reinterpret_cast<float2 *>(p) = make_float2(a, b);
+    }
+};
+
+template <> struct Act<kBF16> {
+    using T = uint16_t;
+    static constexpr int kBytes = 2;
+    __device__ static float ld(const T *p) { return __uint_as_float((uint32_t)*p << 16); }
+    __device__ static float2 ld2(const T *p) {
+        uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+        return make_float2(bf16_lo(w), bf16_hi(w));
+    }
+    __device__ static void st(T *p, float x) { *p = (uint16_t)f32_to_bf16(x); }
+    __device__ static void st2(T *p, float a, float b) {
+        *reinterpret_cast<uint32_t *>(p) = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+    }
+};
+
+// ---------------------------------------------------------------- argument blocks
+
+struct OpShape {
+    int64_t B, D, H, d, P;
+    int act;
+    const float2 *poles;    // [H][d]
+    const float2 *residues; // [H][d]
+    const float *skip;      // [H]
+};
+
+struct DecodeArgs {
+    OpShape s;
+    const void *q, *k, *v;
+    int64_t ld_in;
+    void *y;
+    int64_t ld_y;
+    float2 *state; // [B][H][d][P]
+};
+
+struct FilterArgs {
+    OpShape s;
+    int64_t L;
+    float *h; // [H][L]
+};
+
+// Chunked prefill plan: NC chunks of T steps (the last one may be shorter).
+struct PrefillPlan {
+    int64_t L, T, NC;
+    int64_t mtiles;      // 16-row tiles of the 2d Vandermonde rows
+    size_t off_vand_hi;  // bf16 A-operand fragments, [H][mtiles][T/32][64 lanes][8]
+    size_t off_vand_lo;
+    size_t off_lamT;     // float2 [H][d]: lambda^T
+    size_t off_carry;    // float2 [NC][B][H][d][P]: state entering each chunk
+    size_t bytes;        // total workspace
+};
+
+struct PrefillArgs {
+    OpShape s;
+    PrefillPlan plan;
+    const void *q, *k, *v;
+    int64_t ld_in;
+    void *y;
+    int64_t ld_y;
+    const float2 *state_in; // nullable
+    float2 *state_out;
+    unsigned char *ws;
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; none synchronises.
+
+hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_filter(const FilterArgs &a, hipStream_t stream);
+PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace hm

@@ -1,0 +1,160 @@
+/*
+ * hyena_modal.h -- C ABI of the MI355X (gfx950) modal-SSM Hyena library.
+ *
+ * The operator is the order-2 Hyena operator y = q * (h conv (k * v)): a causal
+ * long convolution between two element-wise gates (StripedHyena article,
+ * sections "Hyena塊" and "Hyena層次結構", which also give its matrix form
+ * diag(q) T_h diag(k) v with T_h causal Toeplitz).  Each head's long filter,
+ * shared by the head's channels (weight tying, Laughing Hyena Distillery review,
+ * ABSTRACT and "提出的方法"), is a distilled low-dimensional linear SSM
+ * (same review, ABSTRACT), taken here in diagonal (modal) form:
+ *
+ *     h[0] = D_h,   h[t] = Re( sum_n R_n * lambda_n^(t-1) )   for t >= 1,
+ *
+ * with d complex poles lambda_n, residues R_n and a real skip D_h per head.
+ * Generation then costs O(d) memory and O(d) time per token (same review,
+ * "主要发现"):  u = k v;  y = q (D_h u + Re(sum_n R_n x_n));  x_n <- lambda_n x_n + u.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All data pointers are DEVICE pointers (memory of the current HIP device),
+ *    owned by the caller.  The library never allocates or frees memory, keeps no
+ *    pointer after returning, and never synchronises: work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream) and completes
+ *    asynchronously.  The library holds no mutable global state.
+ *  - Channel c (0 <= c < D) belongs to head g = c / (D / H).
+ *  - Activations (q, k, v, y) are row-major: element (b, t, c) of a
+ *    [B][T][width] tensor sits at element offset (b*T + t)*ld + c, where ld >= D
+ *    is the row stride in elements.  Their type is hm_desc.act_dtype (float32 or
+ *    bfloat16); arithmetic is float32 and y is rounded to the activation type
+ *    (round to nearest even).
+ *  - Modal state: float32 complex, interleaved (re, im), laid out
+ *    [B][H][d][D/H]: the value of mode n of channel c = g*(D/H) + p in batch row b
+ *    is at float2 index ((b*H + g)*d + n)*(D/H) + p.
+ *  - Tables: poles and residues are [H][d] float32 complex interleaved (re, im);
+ *    skip is [H] float32.  Precondition (not checked): |lambda| < 1, all inputs
+ *    finite.
+ *  - Errors are returned as hm_status, never thrown.  Arguments are validated on
+ *    the host before any HIP call; on a validation error nothing is enqueued.
+ *    HM_ERR_HIP reports a failed kernel launch (hipGetLastError after launch).
+ *  - Alignment: every pointer must be aligned to its element (2 bytes for
+ *    bfloat16, 4 for float32, 8 for the complex state); otherwise
+ *    HM_ERR_UNSUPPORTED.  Wider vector paths are chosen automatically when
+ *    pointers are 16-byte aligned and strides even.
+ */
+#ifndef HYENA_MODAL_H
+#define HYENA_MODAL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HM_ABI_VERSION 1
+#define HM_MAX_MODES 64 /* largest supported d */
+
+typedef enum hm_status {
+    HM_OK = 0,
+    HM_ERR_INVALID_ARG = 1, /* null pointer, negative size, D % H != 0, ld < D, bad version */
+    HM_ERR_UNSUPPORTED = 2, /* d > HM_MAX_MODES, unknown dtype, misaligned pointer/stride */
+    HM_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the queried size */
+    HM_ERR_HIP = 4          /* a kernel launch failed */
+} hm_status;
+
+typedef enum hm_dtype { HM_F32 = 0, HM_BF16 = 1 } hm_dtype;
+
+/* Operator descriptor.  Sizes: batch B >= 0, channels D >= 1, heads H >= 1 with
+ * D % H == 0, modes 1 <= d <= HM_MAX_MODES.  Table pointers are device pointers
+ * (see conventions above). */
+typedef struct hm_desc {
+    int32_t abi_version; /* must be HM_ABI_VERSION */
+    int32_t act_dtype;   /* hm_dtype of q, k, v, y */
+    int64_t batch;       /* B */
+    int64_t channels;    /* D */
+    int64_t heads;       /* H */
+    int64_t modes;       /* d */
+    const float *poles;    /* [H][d][2] */
+    const float *residues; /* [H][d][2] */
+    const float *skip;     /* [H] */
+} hm_desc;
+
+/* ABI version compiled into the library (HM_ABI_VERSION). */
+int hm_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *hm_status_string(hm_status status);
+
+/*
+ * Workspace bytes hyena_modal_prefill needs for this descriptor and prompt
+ * length L >= 0.  Writes the size to *bytes (0 is possible).  Pure host
+ * computation.
+ */
+hm_status hyena_modal_prefill_workspace(const hm_desc *desc, int64_t L, size_t *bytes);
+
+/*
+ * Prefill: the causal long convolution over a prompt of L tokens plus the
+ * end-of-prompt modal state (the Vandermonde contraction
+ * x_n = lambda_n^L x0_n + sum_t lambda_n^(L-1-t) u_t).
+ *   q, k, v   [B][L][ld_in] activations (may alias one fused [B][L][3D] buffer
+ *             with k = q + D, v = q + 2D and ld_in = 3D).
+ *   y         [B][L][ld_y] output activations.
+ *   state_in  initial state x0 in the state layout, or NULL for zero (a fresh
+ *             prompt).  A non-NULL state_in continues a previous prompt.
+ *   state_out end-of-prompt state (may equal state_in).
+ *   workspace device scratch of at least hyena_modal_prefill_workspace() bytes;
+ *             its contents on entry do not matter.
+ * The hot path splits the prompt into chunks: a chunk-local Vandermonde
+ * contraction on the matrix cores, a carry scan over chunks, and an in-chunk
+ * modal scan that produces y (the Hyena evaluation without materialising T_h,
+ * StripedHyena article, "Hyena層次結構").
+ */
+hm_status hyena_modal_prefill(const hm_desc *desc, int64_t L,
+                              const void *q, const void *k, const void *v, int64_t ld_in,
+                              void *y, int64_t ld_y,
+                              const float *state_in, float *state_out,
+                              void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The same prefill with an explicit chunk length (a positive multiple of 64;
+ * 0 = automatic, as hyena_modal_prefill).  The chunk length changes how the
+ * prompt is split across the GPU, never the result beyond float32 rounding.
+ * Workspace size for it: hyena_modal_prefill_workspace_chunked.
+ */
+hm_status hyena_modal_prefill_chunked(const hm_desc *desc, int64_t L,
+                                      const void *q, const void *k, const void *v, int64_t ld_in,
+                                      void *y, int64_t ld_y,
+                                      const float *state_in, float *state_out,
+                                      void *workspace, size_t ws_bytes, int64_t chunk,
+                                      void *stream);
+
+hm_status hyena_modal_prefill_workspace_chunked(const hm_desc *desc, int64_t L, int64_t chunk,
+                                                size_t *bytes);
+
+/*
+ * One generation step for every batch row: reads the state before updating it,
+ *   y = q (D_h u + Re(sum_n R_n x_n)),  x_n <- lambda_n x_n + u,  u = k v,
+ * which is the convolution with h continued past the prompt (Laughing Hyena
+ * Distillery review, "主要发现": O(d) memory and time per token).
+ *   q, k, v  [B][ld_in] one token per batch row;  y [B][ld_y];
+ *   state    [B][H][d][D/H] complex, updated in place.
+ */
+hm_status hyena_modal_decode_step(const hm_desc *desc,
+                                  const void *q, const void *k, const void *v, int64_t ld_in,
+                                  void *y, int64_t ld_y, float *state, void *stream);
+
+/*
+ * The first L taps of every head's filter, h_out [H][L] float32:
+ *   h[g][0] = D_g,  h[g][t] = Re(sum_n R_gn lambda_gn^(t-1)).
+ * Powers are formed in float64 and each tap is rounded once to float32.
+ * (The distillation objective compares filters, Laughing Hyena Distillery
+ * review, "提出的方法"; this exports them.)
+ */
+hm_status hyena_filter_materialize(const hm_desc *desc, int64_t L, float *h_out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYENA_MODAL_H */

@@ -1,0 +1,153 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from distilled_modal_ssm_amd import binding as hb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hyena_modal.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hb.LIB_PATH):
+        from distilled_modal_ssm_amd import build
+        build.build()
+    return hb.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"\b(hm_\w+|hyena_\w+)\s*\(", src))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == set(hb.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_strings(lib):
+    assert hb.hm_abi_version() == hb.HM_ABI_VERSION
+    for s in range(5):
+        assert lib.hm_status_string(s).decode().startswith("HM_")
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _desc(**kw):
+    base = dict(batch=2, channels=64, heads=4, modes=8, act_dtype=hb.HM_F32, poles=FAKE,
+                residues=FAKE, skip=FAKE)
+    base.update(kw)
+    d = hb.make_desc(base["batch"], base["channels"], base["heads"], base["modes"], base["act_dtype"],
+                     base["poles"], base["residues"], base["skip"])
+    if "abi_version" in kw:
+        d.abi_version = kw["abi_version"]
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(abi_version=99), hb.HM_ERR_INVALID_ARG),
+    (dict(act_dtype=7), hb.HM_ERR_UNSUPPORTED),
+    (dict(channels=60, heads=8), hb.HM_ERR_INVALID_ARG),     # D % H != 0
+    (dict(modes=0), hb.HM_ERR_INVALID_ARG),
+    (dict(modes=65), hb.HM_ERR_UNSUPPORTED),
+    (dict(batch=-1), hb.HM_ERR_INVALID_ARG),
+    (dict(heads=0), hb.HM_ERR_INVALID_ARG),
+    (dict(poles=0), hb.HM_ERR_INVALID_ARG),
+    (dict(skip=0x10002), hb.HM_ERR_UNSUPPORTED),            # misaligned table
+])
+def test_descriptor_validation(lib, kw, status):
+    d = _desc(**kw)
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_filter_materialize(d, 16, FAKE, stream=0)
+    assert e.value.status == status
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_modal_decode_step(d, FAKE, FAKE, FAKE, 64, FAKE, 64, FAKE, stream=0)
+    assert e.value.status == status
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_modal_prefill_workspace(d, 128)
+    assert e.value.status == status
+
+
+def test_prefill_argument_errors(lib):
+    d = _desc()
+    ws = hb.hyena_modal_prefill_workspace(d, 4096)
+    assert ws > 0
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, ld_in=64, y=FAKE, ld_y=64, state_in=None, state_out=FAKE,
+              workspace=FAKE, ws_bytes=ws)
+
+    def call(L=4096, chunk=0, **kw):
+        a = dict(ok)
+        a.update(kw)
+        hb.hyena_modal_prefill(d, L, a["q"], a["k"], a["v"], a["ld_in"], a["y"], a["ld_y"],
+                               a["state_in"], a["state_out"], a["workspace"], a["ws_bytes"], stream=0,
+                               chunk=chunk)
+
+    cases = [
+        (dict(L=-1), hb.HM_ERR_INVALID_ARG),
+        (dict(q=None), hb.HM_ERR_INVALID_ARG),
+        (dict(y=None), hb.HM_ERR_INVALID_ARG),
+        (dict(state_out=None), hb.HM_ERR_INVALID_ARG),
+        (dict(ld_in=63), hb.HM_ERR_INVALID_ARG),
+        (dict(ld_y=10), hb.HM_ERR_INVALID_ARG),
+        (dict(k=FAKE + 2), hb.HM_ERR_UNSUPPORTED),            # misaligned f32 pointer
+        (dict(workspace=None), hb.HM_ERR_WORKSPACE),
+        (dict(ws_bytes=ws - 1), hb.HM_ERR_WORKSPACE),
+        (dict(workspace=FAKE + 16), hb.HM_ERR_UNSUPPORTED),    # workspace must be 256-B aligned
+        (dict(chunk=100), hb.HM_ERR_UNSUPPORTED),              # chunk not a multiple of 64
+        (dict(chunk=-64), hb.HM_ERR_INVALID_ARG),
+    ]
+    for kw, status in cases:
+        with pytest.raises(hb.HMError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+
+
+def test_no_work_calls_succeed_without_gpu(lib):
+    """B = 0 and empty filters enqueue nothing, so they return OK even here."""
+    d = _desc(batch=0)
+    hb.hyena_modal_prefill(d, 128, None, None, None, 64, None, 64, None, None, None, 0, stream=0)
+    hb.hyena_modal_decode_step(d, None, None, None, 64, None, 64, None, stream=0)
+    assert hb.hyena_modal_prefill_workspace(d, 128) == 0
+    hb.hyena_filter_materialize(_desc(), 0, None, stream=0)
+
+
+def test_workspace_sizes_follow_the_chunk_plan(lib):
+    d = _desc(batch=4, channels=4096, heads=32, modes=32)
+    # a single chunk needs no workspace
+    assert hb.hyena_modal_prefill_workspace(d, 4096, chunk=4096) == 0
+    big = hb.hyena_modal_prefill_workspace(d, 65536, chunk=2048)
+    # 32 chunk-state slots of B*D*d complex64 dominate
+    assert big >= 32 * 4 * 4096 * 32 * 8
+    assert hb.hyena_modal_prefill_workspace(d, 65536, chunk=4096) < big
+
+
+def test_decode_state_validation(lib):
+    d = _desc()
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_modal_decode_step(d, FAKE, FAKE, FAKE, 64, FAKE, 64, None, stream=0)
+    assert e.value.status == hb.HM_ERR_INVALID_ARG
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_modal_decode_step(d, FAKE, FAKE, FAKE, 64, FAKE, 64, FAKE + 4, stream=0)
+    assert e.value.status == hb.HM_ERR_UNSUPPORTED
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = hb._lib
+    hb._lib = None
+    try:
+        with pytest.raises(hb.LibraryMissing):
+            hb.load(str(tmp_path / "nope.so"))
+    finally:
+        hb._lib = saved

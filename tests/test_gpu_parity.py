@@ -1,0 +1,305 @@
+"""GPU parity of the HIP path against the float64 oracle (through the C ABI).
+
+Tolerances (max |err| over the compared tensor, relative to its max |oracle|):
+1e-4 for float32 activations, 2e-2 for bfloat16 activations; the same rule is
+applied to the modal states and, at 1e-4, to the materialised filter.
+Large workloads run at full size on the GPU, in the launch configuration the
+benchmark uses (automatic chunking); the oracle then recomputes a seeded sample
+of channels (channels are independent, so each sampled channel is exact).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from _gpu_common import (TOL, act_to_f64, log, rel_err, require_gpu, state_for_channels,
+                         state_to_gpu_layout, to_dev, to_np64)
+from distilled_modal_ssm_amd import ModalHyena
+from distilled_modal_ssm_amd import binding as hb
+from workloads import decode_inputs, get_config, modal_params, prompt_inputs
+from workloads.generate import ModalParams
+
+pytestmark = pytest.mark.gpu
+
+
+def _op(params, B, D, act):
+    return ModalHyena(params.poles, params.residues, params.skip, B, D, act)
+
+
+def _sample_channels(cfg, n_random, seed):
+    rng = np.random.default_rng(seed)
+    P = cfg.P
+    fixed = [0, P - 1, P, cfg.D - 1]
+    extra = rng.choice(cfg.D, size=n_random, replace=False)
+    return np.unique(np.concatenate([fixed, extra])).astype(np.int64)
+
+
+def _rand_params(rng, H, d, r_lo=0.5, r_hi=0.99):
+    r = rng.uniform(r_lo, r_hi, (H, d))
+    th = rng.uniform(0, np.pi, (H, d))
+    poles = np.stack([r * np.cos(th), r * np.sin(th)], -1).astype(np.float32)
+    res = (rng.standard_normal((H, d, 2)) / np.sqrt(2 * d)).astype(np.float32)
+    return ModalParams(poles, res, rng.standard_normal(H).astype(np.float32))
+
+
+def _rand_act(rng, shape, act):
+    from workloads import round_to_bf16_bits
+    x = rng.standard_normal(shape)
+    return round_to_bf16_bits(x) if act == "bf16" else x.astype(np.float32)
+
+
+# ------------------------------------------------------------------ filter
+
+
+@pytest.mark.parametrize("ci", [1, 2, 3, 4, 5])
+def test_filter_materialize(ci):
+    torch = require_gpu()
+    cfg = get_config(ci)
+    params = modal_params(cfg)
+    log(f"filter workload {ci} H={cfg.H} d={cfg.d} L={cfg.L}")
+    h = to_np64(_op(params, cfg.B, cfg.D, cfg.act).filter(cfg.L))
+    torch.cuda.synchronize()
+    ref = oracle.filter_taps(params, cfg.L)
+    err = rel_err(h, ref)
+    print(f"filter workload {ci}: rel err {err:.3e}")
+    assert err <= 1e-4
+    assert np.array_equal(h[:, 0], params.skip.astype(np.float64))
+
+
+# ------------------------------------------------------------------ tiny workload, full oracle
+
+
+@pytest.mark.parametrize("chunk", [0, 64, 128, 192])
+def test_workload1_prefill_and_decode(chunk):
+    torch = require_gpu()
+    cfg = get_config(1)
+    params = modal_params(cfg)
+    inp = prompt_inputs(cfg)
+    dec = decode_inputs(cfg)
+    op = _op(params, cfg.B, cfg.D, cfg.act)
+    q, k, v = (to_dev(inp[n], cfg.act) for n in "qkv")
+    log(f"workload 1 prefill chunk={chunk}")
+    y, st = op.prefill(q, k, v, chunk=chunk)
+    torch.cuda.synchronize()
+    y_or, st_or = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"])
+    assert rel_err(to_np64(y), y_or) <= TOL["f32"]
+    all_ch = np.arange(cfg.D)
+    assert rel_err(state_for_channels(st, all_ch, cfg.P), st_or) <= TOL["f32"]
+
+    dq, dk, dv = (to_dev(dec[n], cfg.act) for n in "qkv")
+    ys = torch.empty((cfg.S, cfg.B, cfg.D), dtype=torch.float32, device="cuda")
+    log("workload 1 decode")
+    for s in range(cfg.S):
+        op.decode_step(dq[s], dk[s], dv[s], st, y=ys[s])
+    torch.cuda.synchronize()
+    yd_or, st2_or = oracle.modal_scan(params, dec["q"], dec["k"], dec["v"], state=st_or,
+                                      batch_axis=1, time_axis=0)
+    assert rel_err(to_np64(ys).transpose(1, 0, 2), yd_or) <= TOL["f32"]
+    assert rel_err(state_for_channels(st, all_ch, cfg.P), st2_or) <= TOL["f32"]
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+
+
+@pytest.mark.parametrize("ci", [2, 3, 4])
+def test_workload_full_size_sampled(ci):
+    torch = require_gpu()
+    cfg = get_config(ci)
+    params = modal_params(cfg)
+    tol = TOL[cfg.act]
+    inp = prompt_inputs(cfg)
+    op = _op(params, cfg.B, cfg.D, cfg.act)
+    q, k, v = (to_dev(inp[n], cfg.act) for n in "qkv")
+    log(f"workload {ci} prefill {cfg.describe()}")
+    y, st = op.prefill(q, k, v)
+    torch.cuda.synchronize()
+    del q, k, v
+    chans = _sample_channels(cfg, 28, 100 + ci)
+    batches = np.arange(cfg.B) if cfg.B <= 16 else np.sort(
+        np.random.default_rng(200 + ci).choice(cfg.B, 8, replace=False))
+    sub = lambda a: a if len(batches) == cfg.B else np.ascontiguousarray(a[batches])
+    y_or, st_or = oracle.modal_scan(params, sub(inp["q"]), sub(inp["k"]), sub(inp["v"]), channels=chans)
+    del inp
+    bt, ct = torch.as_tensor(batches, device="cuda"), torch.as_tensor(chans, device="cuda")
+    y_gpu = to_np64(y.index_select(2, ct).index_select(0, bt))
+    e_y = rel_err(y_gpu, y_or)
+    st_gpu = state_for_channels(st, chans, cfg.P)[batches]
+    e_s = rel_err(st_gpu, st_or)
+    print(f"workload {ci} prefill: y rel err {e_y:.3e}, state rel err {e_s:.3e}")
+    assert e_y <= tol and e_s <= tol
+    del y
+
+    dec = decode_inputs(cfg)
+    dq, dk, dv = (to_dev(dec[n], cfg.act) for n in "qkv")
+    ys = torch.empty((cfg.S, cfg.B, cfg.D), dtype=op.tdtype, device="cuda")
+    log(f"workload {ci} decode S={cfg.S}")
+    for s in range(cfg.S):
+        op.decode_step(dq[s], dk[s], dv[s], st, y=ys[s])
+    torch.cuda.synchronize()
+    yd_or, st2_or = oracle.modal_scan(params, np.ascontiguousarray(dec["q"][:, batches]),
+                                      np.ascontiguousarray(dec["k"][:, batches]),
+                                      np.ascontiguousarray(dec["v"][:, batches]), state=st_or,
+                                      channels=chans, batch_axis=1, time_axis=0)
+    yd_gpu = to_np64(ys.index_select(2, ct).index_select(1, bt))
+    e_yd = rel_err(yd_gpu.transpose(1, 0, 2), yd_or)
+    e_s2 = rel_err(state_for_channels(st, chans, cfg.P)[batches], st2_or)
+    print(f"workload {ci} decode: y rel err {e_yd:.3e}, state rel err {e_s2:.3e}")
+    assert e_yd <= tol and e_s2 <= tol
+
+
+# ------------------------------------------------------------------ structure and edge cases
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [
+    # (B, D, H, d, L, chunk)
+    (3, 36, 3, 5, 200, 64),      # odd head dim 12, generic mode count, ragged last chunk
+    (2, 16, 2, 1, 130, 64),      # one mode
+    (2, 128, 2, 64, 256, 128),   # largest mode count
+    (1, 64, 1, 8, 10, 0),        # prompt shorter than one chunk
+    (2, 256, 2, 16, 700, 64),    # many chunks, ragged
+    (1, 192, 3, 32, 320, 128),   # three heads of 64 (wave-uniform heads), d = 32
+])
+def test_shapes_and_chunking(act, shape):
+    torch = require_gpu()
+    B, D, H, d, L, chunk = shape
+    rng = np.random.default_rng(hash(shape) % 2**32)
+    params = _rand_params(rng, H, d)
+    q_, k_, v_ = (_rand_act(rng, (B, L, D), act) for _ in range(3))
+    op = _op(params, B, D, act)
+    log(f"shape {shape} act {act}")
+    y, st = op.prefill(to_dev(q_, act), to_dev(k_, act), to_dev(v_, act), chunk=chunk)
+    torch.cuda.synchronize()
+    y_or, st_or = oracle.modal_scan(params, q_, k_, v_)
+    assert rel_err(to_np64(y), y_or) <= TOL[act]
+    assert rel_err(state_for_channels(st, np.arange(D), D // H), st_or) <= TOL[act]
+    # a few decode steps on top
+    qd, kd, vd = (_rand_act(rng, (4, B, D), act) for _ in range(3))
+    ys = [op.decode_step(to_dev(qd[s], act), to_dev(kd[s], act), to_dev(vd[s], act), st) for s in range(4)]
+    torch.cuda.synchronize()
+    yd_or, _ = oracle.modal_scan(params, qd, kd, vd, state=st_or, batch_axis=1, time_axis=0)
+    assert rel_err(np.stack([to_np64(t) for t in ys], 1), yd_or) <= TOL[act]
+
+
+def test_empty_prompt_and_empty_batch():
+    torch = require_gpu()
+    rng = np.random.default_rng(1)
+    params = _rand_params(rng, 2, 8)
+    op = _op(params, 2, 32, "f32")
+    x0 = torch.randn((2, 2, 8, 16, 2), device="cuda")
+    out = torch.full_like(x0, 7.0)
+    empty = torch.empty((2, 0, 32), device="cuda")
+    log("empty prompt with state_in")
+    op.prefill(empty, empty, empty, state_in=x0, state_out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, x0)
+    log("empty prompt without state_in")
+    op.prefill(empty, empty, empty, state_out=out)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
+    op0 = _op(params, 0, 32, "f32")
+    y0, _ = op0.prefill(torch.empty((0, 5, 32), device="cuda"), torch.empty((0, 5, 32), device="cuda"),
+                        torch.empty((0, 5, 32), device="cuda"))
+    assert y0.shape == (0, 5, 32)
+
+
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_prompt_continuation_with_state_in(chunk):
+    """prefill(a) then prefill(b, state_in) equals prefill(a + b); also in place."""
+    torch = require_gpu()
+    cfg = get_config(1)
+    params = modal_params(cfg)
+    inp = prompt_inputs(cfg)
+    op = _op(params, cfg.B, cfg.D, "f32")
+    q, k, v = (to_dev(inp[n], "f32") for n in "qkv")
+    cut = 100
+    log(f"continuation chunk={chunk}")
+    y_all, st_all = op.prefill(q, k, v, chunk=chunk)
+    y1, st1 = op.prefill(q[:, :cut], k[:, :cut], v[:, :cut], chunk=chunk)
+    y2, _ = op.prefill(q[:, cut:], k[:, cut:], v[:, cut:], state_in=st1, state_out=st1, chunk=chunk)
+    torch.cuda.synchronize()
+    y_or, st_or = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"])
+    assert rel_err(np.concatenate([to_np64(y1), to_np64(y2)], 1), y_or) <= TOL["f32"]
+    assert rel_err(state_for_channels(st1, np.arange(cfg.D), cfg.P), st_or) <= TOL["f32"]
+    # a non-zero state_in from the oracle continues exactly as the oracle does
+    st_in = torch.from_numpy(state_to_gpu_layout(st_or, cfg.H, cfg.P)).cuda()
+    y3, st3 = op.prefill(q[:, :60], k[:, :60], v[:, :60], state_in=st_in, chunk=chunk)
+    torch.cuda.synchronize()
+    y3_or, st3_or = oracle.modal_scan(params, inp["q"][:, :60], inp["k"][:, :60], inp["v"][:, :60],
+                                      state=st_or)
+    assert rel_err(to_np64(y3), y3_or) <= TOL["f32"]
+    assert rel_err(state_for_channels(st3, np.arange(cfg.D), cfg.P), st3_or) <= TOL["f32"]
+
+
+def test_fused_qkv_buffer_and_strided_output():
+    """q, k, v as thirds of one [B][L][3D] buffer; y written into a wider buffer."""
+    torch = require_gpu()
+    rng = np.random.default_rng(5)
+    B, D, H, d, L = 2, 256, 2, 16, 300
+    params = _rand_params(rng, H, d, 0.8, 0.999)
+    qkv_np = _rand_act(rng, (B, L, 3 * D), "bf16")
+    qkv = to_dev(qkv_np, "bf16")
+    op = _op(params, B, D, "bf16")
+    ybuf = torch.full((B, L, D + 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    log("fused qkv")
+    op.prefill(qkv[:, :, :D], qkv[:, :, D:2 * D], qkv[:, :, 2 * D:], y=ybuf[:, :, :D], chunk=64)
+    torch.cuda.synchronize()
+    y_or, _ = oracle.modal_scan(params, np.ascontiguousarray(qkv_np[:, :, :D]),
+                                np.ascontiguousarray(qkv_np[:, :, D:2 * D]),
+                                np.ascontiguousarray(qkv_np[:, :, 2 * D:]))
+    assert rel_err(to_np64(ybuf[:, :, :D]), y_or) <= TOL["bf16"]
+    assert torch.all(ybuf[:, :, D:] == 3.0).item()
+
+
+def test_odd_row_stride_scalar_paths():
+    """An odd row stride forces the scalar (unvectorised) load paths."""
+    torch = require_gpu()
+    rng = np.random.default_rng(6)
+    B, D, H, d, L = 2, 128, 2, 8, 200
+    params = _rand_params(rng, H, d)
+    ld = D + 1
+    big = [_rand_act(rng, (B, L, ld), "f32") for _ in range(3)]
+    dev = [to_dev(a, "f32") for a in big]
+    op = _op(params, B, D, "f32")
+    log("odd stride")
+    y, st = op.prefill(*(t[:, :, :D] for t in dev), chunk=64)
+    torch.cuda.synchronize()
+    y_or, _ = oracle.modal_scan(params, *(np.ascontiguousarray(a[:, :, :D]) for a in big))
+    assert rel_err(to_np64(y), y_or) <= TOL["f32"]
+
+
+def test_impulse_response_matches_filter():
+    torch = require_gpu()
+    cfg = get_config(2)
+    params = modal_params(cfg)
+    B, D, L = 1, cfg.D, 1000
+    q = torch.ones((B, L, D), dtype=torch.float32, device="cuda")
+    k = torch.zeros_like(q)
+    k[:, 0, :] = 1
+    op = _op(params, B, D, "f32")
+    log("impulse response")
+    y, _ = op.prefill(q, k, q, chunk=128)
+    h = op.filter(L)
+    torch.cuda.synchronize()
+    hy = to_np64(y[0]).T.reshape(cfg.H, cfg.P, L)
+    ref = oracle.filter_taps(params, L)
+    assert rel_err(hy, np.broadcast_to(ref[:, None, :], hy.shape)) <= 1e-4
+    assert rel_err(to_np64(h), ref) <= 1e-4
+
+
+def test_bitwise_determinism():
+    torch = require_gpu()
+    cfg = get_config(2)
+    params = modal_params(cfg)
+    inp = prompt_inputs(cfg, batches=[0, 1, 2, 3])
+    op = _op(params, 4, cfg.D, cfg.act)
+    q, k, v = (to_dev(inp[n], cfg.act) for n in "qkv")
+    log("determinism")
+    y1, s1 = op.prefill(q, k, v)
+    y2, s2 = op.prefill(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(s1, s2)
+    a1 = op.decode_step(q[:, 0], k[:, 0], v[:, 0], s1)
+    a2 = op.decode_step(q[:, 0], k[:, 0], v[:, 0], s2)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2) and torch.equal(s1, s2)
