@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the modal-SSM Hyena hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  1. materialise the first L filter taps of every head,
+  2. prefill over the L-token prompt (chunk-local Vandermonde contraction on
+     the matrix cores, carry scan, in-chunk modal scan -> y and the modal state),
+  3. S generation steps (one decode launch per token, captured once in a HIP
+     graph and replayed), consuming the prefill state.
+Inputs are resident in HBM before the timed region starts.
+
+Printed: one JSON line (last line of stdout).  value = whole-step tokens/s,
+B*(L+S) / step time; prefill and decode rates are reported beside it.
+The roofline object covers the kernel that dominates the step, measured live
+with HIP events on the stream the kernels run on; cpu_baseline times the float64
+oracle on this host's cores over the same workload (rank 0, N = 1 only).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+VALU_F32_PEAK_TFLOPS = 78.6    # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, unpacked float32
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=2, help="workload index (1-4)")
+    ap.add_argument("--decode-mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, params, inp, dec):
+    """The float64 oracle (as it stands) on this host over the same workload."""
+    import oracle
+    budget = 6e9  # mode-steps, ~10 s on 8 cores
+    per_channel = cfg.B * (cfg.L + cfg.S) * cfg.d
+    n_sel = int(min(cfg.D, max(1, budget // per_channel)))
+    reps = int(max(1, min(3, budget // (per_channel * n_sel))))
+    chans = np.linspace(0, cfg.D - 1, n_sel).round().astype(np.int64) if n_sel < cfg.D else None
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.filter_taps(params, cfg.L)
+        _, st = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"], channels=chans)
+        oracle.modal_scan(params, dec["q"], dec["k"], dec["v"], state=st, channels=chans,
+                          batch_axis=1, time_axis=0)
+    dt = time.perf_counter() - t0
+    tokens = cfg.B * (cfg.L + cfg.S) * (n_sel / cfg.D) * reps
+    sample = (f"full step (filter, prefill L={cfg.L}, {cfg.S} decode steps) for "
+              f"{'all' if n_sel == cfg.D else n_sel} of {cfg.D} channels x {cfg.B} rows, {reps} repetition(s), "
+              f"{dt:.1f} s; tokens scaled by the channel fraction")
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": sample}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path shards by batch rows and heads with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from distilled_modal_ssm_amd import ModalHyena
+    from workloads import decode_inputs, get_config, modal_params, prompt_inputs
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    cfg = get_config(args.config)
+    if cfg.layers:
+        log("the projected stack is measured by its own driver")
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {cfg.index} {cfg.describe()}")
+
+    params = modal_params(cfg)
+    inp = prompt_inputs(cfg)
+    dec = decode_inputs(cfg)
+
+    def to_dev(a):
+        if cfg.act == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = (to_dev(inp[n]) for n in "qkv")
+    dq, dk, dv = (to_dev(dec[n]) for n in "qkv")
+    op = ModalHyena(params.poles, params.residues, params.skip, cfg.B, cfg.D, cfg.act, device=dev)
+    tdt = op.tdtype
+    y = torch.empty((cfg.B, cfg.L, cfg.D), dtype=tdt, device=dev)
+    ys = torch.empty((cfg.S, cfg.B, cfg.D), dtype=tdt, device=dev)
+    state = op.new_state()
+    h = torch.empty((cfg.H, cfg.L), dtype=torch.float32, device=dev)
+    op.workspace(cfg.L)  # allocate once, outside the timed region
+
+    from distilled_modal_ssm_amd import binding as hb
+
+    def filter_call():
+        hb.hyena_filter_materialize(op.desc, cfg.L, h)
+
+    def prefill_call():
+        op.prefill(q, k, v, y=y, state_out=state)
+
+    def decode_eager():
+        for s in range(cfg.S):
+            op.decode_step(dq[s], dk[s], dv[s], state, y=ys[s])
+
+    stream = torch.cuda.current_stream()
+    if args.decode_mode == "graph":
+        prefill_call()
+        decode_eager()  # warm the launch path before capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decode_eager()
+        torch.cuda.synchronize()
+        decode_call = graph.replay
+    else:
+        decode_call = decode_eager
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        filter_call()
+        if ev:
+            ev[1].record(stream)
+        prefill_call()
+        if ev:
+            ev[2].record(stream)
+        decode_call()
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    ph = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
+    ms_filter, ms_prefill, ms_decode = (float(np.median(ph[:, i])) for i in range(3))
+    ms_decode_launch = ms_decode / cfg.S
+
+    E = cfg.B * cfg.L * cfg.D
+    sb = cfg.act_bytes
+    decode_bytes = cfg.B * cfg.D * (16 * cfg.d + 4 * sb)
+    prefill_flops = (12 * cfg.d + 5) * E
+    prefill_bytes = 4 * sb * E + 8 * cfg.B * cfg.D * cfg.d
+    kernels = {
+        "decode_step": dict(bound="hbm", unit="GB/s", per_launch=decode_bytes, ms=ms_decode_launch,
+                            total_ms=ms_decode, peak=HBM_PEAK_GBS),
+        "prefill": dict(bound="alu", unit="TFLOP/s", per_launch=prefill_flops, ms=ms_prefill,
+                        total_ms=ms_prefill, peak=VALU_F32_PEAK_TFLOPS),
+    }
+    dom_name = max(kernels, key=lambda n: kernels[n]["total_ms"])
+    dom = kernels[dom_name]
+    scale = 1e-6 if dom["unit"] == "GB/s" else 1e-9  # bytes/ms -> GB/s ; flops/ms -> TFLOP/s
+    achieved = dom["per_launch"] / dom["ms"] * scale
+    roofline = {"bound": dom["bound"], "achieved": round(achieved, 3), "peak": dom["peak"],
+                "unit": dom["unit"], "frac": round(achieved / dom["peak"], 4), "traffic": None,
+                "kernel": dom_name, "launch_ms": round(dom["ms"], 6)}
+
+    tokens = cfg.B * (cfg.L + cfg.S)
+    res = {
+        "metric": "decode tokens/sec and prefill tokens/sec at 1 GPU; % of HBM roofline",
+        "value": tokens / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.describe()}", "B": cfg.B, "D": cfg.D, "H": cfg.H,
+                   "d": cfg.d, "L": cfg.L, "S": cfg.S, "act_dtype": cfg.act,
+                   "decode_mode": args.decode_mode},
+        "prefill_tokens_per_s": cfg.B * cfg.L / (ms_prefill / 1e3),
+        "decode_tokens_per_s": cfg.B / (ms_decode_launch / 1e3),
+        "phase_ms": {"filter": ms_filter, "prefill": ms_prefill, "decode_total": ms_decode,
+                     "decode_per_step": ms_decode_launch},
+        "prefill_rates": {"alu_TFLOPs": prefill_flops / ms_prefill * 1e-9,
+                          "alu_frac": prefill_flops / ms_prefill * 1e-9 / VALU_F32_PEAK_TFLOPS,
+                          "hbm_GBs": prefill_bytes / ms_prefill * 1e-6,
+                          "hbm_frac": prefill_bytes / ms_prefill * 1e-6 / HBM_PEAK_GBS},
+        "decode_rates": {"hbm_GBs": decode_bytes / ms_decode_launch * 1e-6,
+                         "hbm_frac": decode_bytes / ms_decode_launch * 1e-6 / HBM_PEAK_GBS},
+        "wall_s_timed": t_wall,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (float64 oracle)")
+        res["cpu_baseline"] = cpu_baseline(cfg, params, inp, dec)
+    line = json.dumps(res)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
+if __name__ == "__main__":
+    main()

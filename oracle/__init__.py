@@ -59,6 +59,8 @@ def _bind(path: str):
     lib.oracle_modal_scan.argtypes = [i64, i64, i64, i64, p, p, p, i64, ctypes.c_int,
                                       p, p, p, i64, i64, i64, p, p, p]
     lib.oracle_modal_scan.restype = ctypes.c_int
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ctypes.c_int
     return lib
 
 
@@ -69,6 +71,11 @@ def _load():
             build(force=False)
             _lib = _bind(_LIB_PATH)
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses on this host."""
+    return int(_load().oracle_threads())
 
 
 def _ptr(a: np.ndarray):

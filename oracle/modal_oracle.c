@@ -48,6 +48,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
@@ -75,6 +78,16 @@ static cplx table_at(const double *tab, int64_t i)
 }
 
 int oracle_abi(void) { return 1; }
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* h[g*L + t], t < L.  poles/residues: [H][d][2] (re, im); skip: [H]. */
 int oracle_filter(int64_t H, int64_t d, const double *poles, const double *residues,
