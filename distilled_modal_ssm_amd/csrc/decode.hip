@@ -8,42 +8,61 @@
 // the causal convolution with h[0] = D_g, h[t] = Re(sum_n R_gn lambda_gn^(t-1)).
 //
 // The step is a pure stream over the state (16 d bytes per channel read and
-// written) plus four activations, so it is bound by HBM bandwidth.  Layout and
+// written) plus four activations, so it is bound by HBM bandwidth (or, for
+// small batches whose state stays in L2, by launch latency).  Layout and
 // mapping:
-//   - a thread owns CPT adjacent channels (2 when aligned) of one batch row and
-//     all their modes in registers;
-//   - the state is [B][H][d][P] complex float32, so for a fixed mode the
-//     threads of a wave touch consecutive 16-byte pairs: every state access of a
-//     wave is one contiguous 1 KiB segment;
-//   - when a wave stays inside one head (P a multiple of 64*CPT) the head
-//     index is made wave-uniform, and the pole/residue tables are fetched with
-//     scalar loads into SGPRs, once per wave.
+//   - the state is [B][H][d][P] complex float32, so for a fixed mode the lanes
+//     of a wave touch consecutive channels: each state access of a wave is one
+//     contiguous segment (1 KiB with two channels per lane);
+//   - large batches: a lane owns two adjacent channels and all their modes
+//     (16-byte state accesses); when a wave stays inside one head the head index
+//     is made wave-uniform and the pole/residue tables come through the scalar
+//     cache into SGPRs;
+//   - small batches (fewer than 64 K channels) or many modes: SPLIT adjacent
+//     lanes share a channel, DL modes each, so more waves carry the step; their
+//     partial readouts are summed with DPP.
 #include "hm_internal.hpp"
 
 namespace hm {
 namespace {
 
-template <int DP, int ACT, int CPT, bool UNIFORM>
+// Sum over the SPLIT adjacent lanes of a channel (DPP quad permutations).
+template <int SPLIT>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    if constexpr (SPLIT >= 2)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    if constexpr (SPLIT >= 4)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    return v;
+}
+
+// Grid: x = lane blocks over the channels of one batch row, y = batch row.
+// A lane owns CPT adjacent channels (CPT = 2 only with SPLIT = 1) and DL of
+// their modes; SPLIT lanes share a channel when the batch is too small to fill
+// the GPU otherwise, and their partial outputs are summed with DPP.
+template <int DL, int SPLIT, int CPT, int ACT, bool UNIFORM>
 __global__ __launch_bounds__(256) void decode_step_fixed(DecodeArgs a) {
     using A = Act<ACT>;
     using T = typename A::T;
-    const int64_t D = a.s.D, P = a.s.P, H = a.s.H;
-    const int64_t per_row = D / CPT;
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (tid >= a.s.B * per_row) return;
-    const int64_t b = tid / per_row;
-    const int64_t c = (tid - b * per_row) * CPT;
-    int g = (int)(c / P);
+    constexpr int DP = DL * SPLIT;
+    const int64_t P = a.s.P, H = a.s.H;
+    const int lane_id = (int)(blockIdx.x * blockDim.x + threadIdx.x);  // within the batch row
+    const int part = lane_id % SPLIT;
+    const int c = (lane_id / SPLIT) * CPT;
+    if (c >= a.s.D) return;
+    const int64_t b = blockIdx.y;
+    int g = c / (int)P;
     if (UNIFORM) g = __builtin_amdgcn_readfirstlane(g);
     const int64_t p = c - (int64_t)g * P;
+    const int n0 = part * DL;
 
     const T *qp = static_cast<const T *>(a.q) + b * a.ld_in + c;
     const T *kp = static_cast<const T *>(a.k) + b * a.ld_in + c;
     const T *vp = static_cast<const T *>(a.v) + b * a.ld_in + c;
     T *yp = static_cast<T *>(a.y) + b * a.ld_y + c;
-    const float2 *lam = a.s.poles + (int64_t)g * DP;
-    const float2 *res = a.s.residues + (int64_t)g * DP;
-    float2 *st = a.state + ((b * H + g) * DP) * P + p;
+    const float2 *lam = a.s.poles + (int64_t)g * DP + n0;
+    const float2 *res = a.s.residues + (int64_t)g * DP + n0;
+    float2 *st = a.state + ((b * H + g) * DP + n0) * P + p;
 
     float u[CPT], qv[CPT], acc[CPT];
     if constexpr (CPT == 2) {
@@ -57,10 +76,10 @@ __global__ __launch_bounds__(256) void decode_step_fixed(DecodeArgs a) {
         qv[0] = A::ld(qp);
     }
 
-    // All state loads first: DP independent 8*CPT-byte loads in flight per thread.
-    float2 x[DP][CPT];
+    // All state loads first: DL independent 8*CPT-byte loads in flight per lane.
+    float2 x[DL][CPT];
 #pragma unroll
-    for (int n = 0; n < DP; ++n) {
+    for (int n = 0; n < DL; ++n) {
         if constexpr (CPT == 2) {
             const float4 t = *reinterpret_cast<const float4 *>(st + n * P);
             x[n][0] = make_float2(t.x, t.y);
@@ -72,22 +91,20 @@ __global__ __launch_bounds__(256) void decode_step_fixed(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < CPT; ++j) acc[j] = 0.f;
 #pragma unroll
-    for (int n = 0; n < DP; ++n) {
+    for (int n = 0; n < DL; ++n) {
         const float2 l = lam[n], r = res[n];
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
             const float2 xo = x[n][j];
             acc[j] = fmaf(r.x, xo.x, acc[j]);
             acc[j] = fmaf(-r.y, xo.y, acc[j]);
-            x[n][j] = make_float2(fmaf(l.x, xo.x, fmaf(-l.y, xo.y, u[j])),
-                                  fmaf(l.x, xo.y, l.y * xo.x));
+            x[n][j] = make_float2(fmaf(l.x, xo.x, fmaf(-l.y, xo.y, u[j])), fmaf(l.x, xo.y, l.y * xo.x));
         }
     }
 #pragma unroll
-    for (int n = 0; n < DP; ++n) {
+    for (int n = 0; n < DL; ++n) {
         if constexpr (CPT == 2) {
-            *reinterpret_cast<float4 *>(st + n * P) =
-                make_float4(x[n][0].x, x[n][0].y, x[n][1].x, x[n][1].y);
+            *reinterpret_cast<float4 *>(st + n * P) = make_float4(x[n][0].x, x[n][0].y, x[n][1].x, x[n][1].y);
         } else {
             st[n * P] = x[n][0];
         }
@@ -96,7 +113,8 @@ __global__ __launch_bounds__(256) void decode_step_fixed(DecodeArgs a) {
     if constexpr (CPT == 2) {
         A::st2(yp, qv[0] * fmaf(Dg, u[0], acc[0]), qv[1] * fmaf(Dg, u[1], acc[1]));
     } else {
-        A::st(yp, qv[0] * fmaf(Dg, u[0], acc[0]));
+        // every lane of the group holds the same sum and stores it
+        A::st(yp, qv[0] * fmaf(Dg, u[0], lane_group_sum<SPLIT>(acc[0])));
     }
 }
 
@@ -126,21 +144,17 @@ __global__ __launch_bounds__(256) void decode_step_generic(DecodeArgs a) {
     A::st(static_cast<T *>(a.y) + b * a.ld_y + c, qv * fmaf(a.s.skip[g], u, acc));
 }
 
-template <int DP, int ACT>
-hipError_t launch_fixed(const DecodeArgs &a, bool pair, bool uniform, hipStream_t stream) {
-    const int64_t threads = a.s.B * a.s.D / (pair ? 2 : 1);
-    const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-    if (pair) {
-        if (uniform)
-            decode_step_fixed<DP, ACT, 2, true><<<grid, block, 0, stream>>>(a);
-        else
-            decode_step_fixed<DP, ACT, 2, false><<<grid, block, 0, stream>>>(a);
-    } else {
-        if (uniform)
-            decode_step_fixed<DP, ACT, 1, true><<<grid, block, 0, stream>>>(a);
-        else
-            decode_step_fixed<DP, ACT, 1, false><<<grid, block, 0, stream>>>(a);
-    }
+template <int DL, int SPLIT, int CPT, int ACT>
+hipError_t launch_fixed(const DecodeArgs &a, hipStream_t stream) {
+    const int64_t lanes = a.s.D / CPT * SPLIT;  // per batch row
+    // small launches: one-wave workgroups spread the work over more CUs
+    const int bs = (lanes * a.s.B >= 256 * 1024) ? 256 : 64;
+    const dim3 grid((unsigned)((lanes + bs - 1) / bs), (unsigned)a.s.B), block(bs);
+    const bool uniform = SPLIT == 1 && (a.s.P % (kWave * CPT) == 0);
+    if (uniform)
+        decode_step_fixed<DL, SPLIT, CPT, ACT, (SPLIT == 1)><<<grid, block, 0, stream>>>(a);
+    else
+        decode_step_fixed<DL, SPLIT, CPT, ACT, false><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -152,12 +166,20 @@ hipError_t launch_act(const DecodeArgs &a, hipStream_t stream) {
     const bool pair = (P % 2 == 0) && (a.ld_in % 2 == 0) && (a.ld_y % 2 == 0) &&
                       aligned(a.q, 2 * esz) && aligned(a.k, 2 * esz) && aligned(a.v, 2 * esz) &&
                       aligned(a.y, 2 * esz) && aligned(a.state, 16);
-    const bool uniform = (P % (kWave * (pair ? 2 : 1)) == 0);
+    // fewer than ~64 K channels in the batch: split modes over lanes for parallelism
+    const bool small = a.s.B * a.s.D < 65536;
     switch (d) {
-        case 8: return launch_fixed<8, ACT>(a, pair, uniform, stream);
-        case 16: return launch_fixed<16, ACT>(a, pair, uniform, stream);
-        case 32: return launch_fixed<32, ACT>(a, pair, uniform, stream);
-        default: break;
+        case 8:
+            return pair ? launch_fixed<8, 1, 2, ACT>(a, stream) : launch_fixed<8, 1, 1, ACT>(a, stream);
+        case 16:
+            if (small) return launch_fixed<8, 2, 1, ACT>(a, stream);
+            return pair ? launch_fixed<16, 1, 2, ACT>(a, stream) : launch_fixed<16, 1, 1, ACT>(a, stream);
+        case 32:
+            return small ? launch_fixed<8, 4, 1, ACT>(a, stream) : launch_fixed<16, 2, 1, ACT>(a, stream);
+        case 64:
+            return launch_fixed<16, 4, 1, ACT>(a, stream);
+        default:
+            break;
     }
     const int64_t threads = a.s.B * a.s.D;
     decode_step_generic<ACT><<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(a);

@@ -167,6 +167,7 @@ hm_status hyena_modal_decode_step(const hm_desc *desc, const void *q, const void
     if (!aligned(state, 8)) return HM_ERR_UNSUPPORTED;
     if (ld_in < s.D || ld_y < s.D) return HM_ERR_INVALID_ARG;
     if (s.B > kMaxElems / ld_in || s.B > kMaxElems / ld_y) return HM_ERR_INVALID_ARG;
+    if (s.B > 65535 || s.D * 4 > INT32_MAX) return HM_ERR_UNSUPPORTED;  // grid limits
     hm::DecodeArgs a;
     a.s = s;
     a.q = q;

@@ -18,11 +18,9 @@ enum ActType : int { kF32 = 0, kBF16 = 1 };
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float32 -> bfloat16 bits, round to nearest even (NaN stays NaN).
+// float32 -> bfloat16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Activation element access for float32 (ACT = kF32) or bfloat16 bit patterns.
@@ -50,6 +48,35 @@ template <> struct Act<kBF16> {
     __device__ static void st(T *p, float x) { *p = (uint16_t)f32_to_bf16(x); }
     __device__ static void st2(T *p, float a, float b) {
         *reinterpret_cast<uint32_t *>(p) = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+    }
+};
+
+// Raw-buffer access to activations: a wave-uniform descriptor over one region,
+// a per-lane 32-bit byte offset and a wave-uniform (scalar) byte offset, so the
+// address arithmetic stays off the vector ALUs.  Every access must lie inside
+// the region given to make_region.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_region(const void *base, uint32_t bytes) {
+    // dword 3 = 0x00020000: 32-bit data format, the value the gfx9 family expects
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int ACT> struct BufAct;
+
+template <> struct BufAct<kF32> {
+    __device__ static float ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    }
+    __device__ static void st(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float x) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, voff, soff, 0);
+    }
+};
+
+template <> struct BufAct<kBF16> {
+    __device__ static float ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+        return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0) << 16);
+    }
+    __device__ static void st(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float x) {
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)f32_to_bf16(x), r, voff, soff, 0);
     }
 };
 

@@ -280,86 +280,117 @@ __global__ __launch_bounds__(256) void carry_scan_kernel(PrefillArgs a) {
 
 // ------------------------------------------------------------- phase 3
 
-// One lane per (batch row, chunk, channel); 256 channels per workgroup.  The
-// lane keeps the DP complex modes of its channel in registers and runs the
-// recurrence over its chunk.  q, k, v are prefetched U steps ahead.  When a
-// wave lies inside one head the pole/residue tables are wave-uniform (scalar
-// registers).
-template <int DP, int ACT, bool UNIFORM, int U>
+// Sum of v over the SPLIT adjacent lanes of one channel (SPLIT = 1, 2 or 4),
+// with DPP quad permutations: one VALU op per halving.
+template <int SPLIT>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    if constexpr (SPLIT >= 2)  // swap lanes 0<->1, 2<->3
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+    if constexpr (SPLIT >= 4)  // swap pairs 01<->23
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+    return v;
+}
+
+// In-chunk modal scan.  A channel's d = DL*SPLIT modes are held by SPLIT
+// adjacent lanes (DL each), so one lane never holds more than 16 modes: the
+// complex state (2 DL floats) and, with SPLIT = 1 and a wave inside one head,
+// the pole/residue tables fit in registers (scalar registers when wave-uniform,
+// vector registers otherwise).  Each lane group runs the recurrence over its
+// chunk U steps at a time with q, k, v of the next U steps already in flight;
+// the output sums the lane group with DPP.  Activations go through raw-buffer
+// accesses whose per-step offset is a scalar (no vector address arithmetic).
+// Workgroup: 256 lanes = 256 / SPLIT channels of one batch row and chunk.
+template <int DL, int SPLIT, int ACT, bool UNIFORM, int U>
 __global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillArgs a, const float2 *carry0) {
-    using A = Act<ACT>;
-    using T = typename A::T;
+    using T = typename Act<ACT>::T;
+    using BA = BufAct<ACT>;
+    constexpr uint32_t esz = Act<ACT>::kBytes;
+    constexpr int DP = DL * SPLIT;  // modes per channel
+    constexpr int CPB = 256 / SPLIT;  // channels per workgroup
     const OpShape &s = a.s;
-    const int64_t D = s.D, P = s.P, H = s.H, L = a.plan.L, Tc = a.plan.T;
-    const int64_t ch = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t P = s.P, H = s.H, L = a.plan.L, Tc = a.plan.T;
+    const int part = (int)(threadIdx.x % SPLIT);
+    const int ch = (int)(blockIdx.x * CPB + threadIdx.x / SPLIT);
     const int64_t c = blockIdx.y, b = blockIdx.z;
-    if (ch >= D) return;
-    int g = (int)(ch / P);
+    if (ch >= s.D) return;
+    int g = ch / (int)P;
     if (UNIFORM) g = __builtin_amdgcn_readfirstlane(g);
     const int64_t p = ch - (int64_t)g * P;
+    const int n0 = part * DL;  // first mode of this lane
 
-    float2 lam[DP], res[DP];
+    float lr[DL], li[DL], rr[DL], ri[DL];
 #pragma unroll
-    for (int n = 0; n < DP; ++n) {
-        lam[n] = s.poles[(int64_t)g * DP + n];
-        res[n] = s.residues[(int64_t)g * DP + n];
+    for (int n = 0; n < DL; ++n) {
+        const float2 l = s.poles[(int64_t)g * DP + n0 + n], r = s.residues[(int64_t)g * DP + n0 + n];
+        lr[n] = l.x;
+        li[n] = l.y;
+        rr[n] = r.x;
+        ri[n] = r.y;
     }
-    const float Dg = s.skip[g];
+    const float Dg = (part == 0) ? s.skip[g] : 0.f;  // the skip term is added once per channel
 
-    const int64_t sidx = ((b * H + g) * DP) * P + p;  // mode 0 of this channel in a state slot
-    float2 x[DP];
-    const float2 *src = nullptr;
-    if (c == 0) {
-        src = carry0 ? carry0 + sidx : nullptr;
-    } else {
-        src = reinterpret_cast<const float2 *>(a.ws + a.plan.off_carry) + c * (s.B * H * DP * P) + sidx;
-    }
+    const int64_t sidx = ((b * H + g) * DP + n0) * P + p;  // mode n0 of this channel in a state slot
+    const float2 *src = (c == 0) ? (carry0 ? carry0 + sidx : nullptr)
+                                 : reinterpret_cast<const float2 *>(a.ws + a.plan.off_carry) +
+                                       c * (s.B * H * DP * P) + sidx;
+    float xr[DL], xi[DL];
 #pragma unroll
-    for (int n = 0; n < DP; ++n) x[n] = src ? src[n * P] : make_float2(0.f, 0.f);
+    for (int n = 0; n < DL; ++n) {
+        const float2 v = src ? src[n * P] : make_float2(0.f, 0.f);
+        xr[n] = v.x;
+        xi[n] = v.y;
+    }
 
+    // Regions of this (batch row, chunk): nsteps rows of ld elements each; the
+    // host guarantees they fit 31-bit byte offsets.
     const int64_t t0 = c * Tc;
-    const int64_t nsteps = ((L - t0) < Tc) ? (L - t0) : Tc;
-    const T *qp = static_cast<const T *>(a.q) + (b * L + t0) * a.ld_in + ch;
-    const T *kp = static_cast<const T *>(a.k) + (b * L + t0) * a.ld_in + ch;
-    const T *vp = static_cast<const T *>(a.v) + (b * L + t0) * a.ld_in + ch;
-    T *yp = static_cast<T *>(a.y) + (b * L + t0) * a.ld_y + ch;
-    const int64_t ldi = a.ld_in, ldo = a.ld_y;
+    const int nsteps = (int)(((L - t0) < Tc) ? (L - t0) : Tc);
+    const uint32_t ldi = (uint32_t)(a.ld_in * esz), ldo = (uint32_t)(a.ld_y * esz);
+    const uint32_t in_bytes = (uint32_t)(nsteps - 1) * ldi + (uint32_t)s.D * esz;
+    const uint32_t out_bytes = (uint32_t)(nsteps - 1) * ldo + (uint32_t)s.D * esz;
+    const auto rq = make_region(static_cast<const T *>(a.q) + (b * L + t0) * a.ld_in, in_bytes);
+    const auto rk = make_region(static_cast<const T *>(a.k) + (b * L + t0) * a.ld_in, in_bytes);
+    const auto rv = make_region(static_cast<const T *>(a.v) + (b * L + t0) * a.ld_in, in_bytes);
+    const auto ry = make_region(static_cast<T *>(a.y) + (b * L + t0) * a.ld_y, out_bytes);
+    const uint32_t lane_off = (uint32_t)ch * esz;
+
+    auto step = [&](float qv, float kv, float vv) -> float {
+        const float u = kv * vv;
+        float z0 = Dg * u, z1 = 0.f;
+#pragma unroll
+        for (int n = 0; n < DL; ++n) {
+            z0 = fmaf(rr[n], xr[n], z0);
+            z1 = fmaf(-ri[n], xi[n], z1);
+            const float cross = li[n] * xr[n];
+            xr[n] = fmaf(lr[n], xr[n], fmaf(-li[n], xi[n], u));
+            xi[n] = fmaf(lr[n], xi[n], cross);
+        }
+        return qv * lane_group_sum<SPLIT>(z0 + z1);
+    };
+    // every lane of a group holds the same y and stores it: one instruction, no branch
+    auto store = [&](int t, float yv) { BA::st(ry, lane_off, (uint32_t)t * ldo, yv); };
 
     float cq[U], ck[U], cv[U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-        if (i < nsteps) {
-            cq[i] = A::ld(qp + i * ldi);
-            ck[i] = A::ld(kp + i * ldi);
-            cv[i] = A::ld(vp + i * ldi);
-        }
+        const uint32_t o = (uint32_t)(i < nsteps ? i : nsteps - 1) * ldi;
+        cq[i] = BA::ld(rq, lane_off, o);
+        ck[i] = BA::ld(rk, lane_off, o);
+        cv[i] = BA::ld(rv, lane_off, o);
     }
-    for (int64_t t = 0; t < nsteps; t += U) {
+    const int nfull = nsteps - nsteps % U;
+    for (int t = 0; t < nfull; t += U) {
         float nq[U], nk[U], nv[U];
 #pragma unroll
-        for (int i = 0; i < U; ++i) {
-            if (t + U + i < nsteps) {
-                nq[i] = A::ld(qp + (t + U + i) * ldi);
-                nk[i] = A::ld(kp + (t + U + i) * ldi);
-                nv[i] = A::ld(vp + (t + U + i) * ldi);
-            }
+        for (int i = 0; i < U; ++i) {  // next U steps, clamped into the chunk
+            const int tt = (t + U + i < nsteps) ? t + U + i : nsteps - 1;
+            const uint32_t o = (uint32_t)tt * ldi;
+            nq[i] = BA::ld(rq, lane_off, o);
+            nk[i] = BA::ld(rk, lane_off, o);
+            nv[i] = BA::ld(rv, lane_off, o);
         }
 #pragma unroll
-        for (int i = 0; i < U; ++i) {
-            if (t + i < nsteps) {
-                const float u = ck[i] * cv[i];
-                float z0 = Dg * u, z1 = 0.f;
-#pragma unroll
-                for (int n = 0; n < DP; ++n) {
-                    const float2 xo = x[n];
-                    z0 = fmaf(res[n].x, xo.x, z0);
-                    z1 = fmaf(-res[n].y, xo.y, z1);
-                    x[n] = make_float2(fmaf(lam[n].x, xo.x, fmaf(-lam[n].y, xo.y, u)),
-                                       fmaf(lam[n].x, xo.y, lam[n].y * xo.x));
-                }
-                A::st(yp + (t + i) * ldo, cq[i] * (z0 + z1));
-            }
-        }
+        for (int i = 0; i < U; ++i) store(t + i, step(cq[i], ck[i], cv[i]));
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             cq[i] = nq[i];
@@ -367,10 +398,14 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(PrefillArgs a, const fl
             cv[i] = nv[i];
         }
     }
+#pragma unroll
+    for (int i = 0; i < U; ++i)  // ragged tail: fewer than U steps, already loaded
+        if (nfull + i < nsteps) store(nfull + i, step(cq[i], ck[i], cv[i]));
+
     if (c == a.plan.NC - 1) {
         float2 *dst = a.state_out + sidx;
 #pragma unroll
-        for (int n = 0; n < DP; ++n) dst[n * P] = x[n];
+        for (int n = 0; n < DL; ++n) dst[n * P] = make_float2(xr[n], xi[n]);
     }
 }
 
@@ -439,22 +474,30 @@ hipError_t launch_chunk_state(const PrefillArgs &a, bool vec, hipStream_t stream
     }
 }
 
-template <int DP, int ACT, int U>
+template <int DL, int SPLIT, int ACT, int U>
 hipError_t launch_scan_dp(const PrefillArgs &a, const float2 *carry0, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.s.D + 255) / 256), (unsigned)a.plan.NC, (unsigned)a.s.B);
-    if (a.s.P % kWave == 0)
-        chunk_scan_kernel<DP, ACT, true, U><<<grid, dim3(256), 0, stream>>>(a, carry0);
-    else
-        chunk_scan_kernel<DP, ACT, false, U><<<grid, dim3(256), 0, stream>>>(a, carry0);
+    constexpr int cpb = 256 / SPLIT;
+    const dim3 grid((unsigned)((a.s.D + cpb - 1) / cpb), (unsigned)a.plan.NC, (unsigned)a.s.B);
+    if constexpr (SPLIT == 1) {
+        if (a.s.P % kWave == 0) {
+            chunk_scan_kernel<DL, SPLIT, ACT, true, U><<<grid, dim3(256), 0, stream>>>(a, carry0);
+            return hipGetLastError();
+        }
+    }
+    chunk_scan_kernel<DL, SPLIT, ACT, false, U><<<grid, dim3(256), 0, stream>>>(a, carry0);
     return hipGetLastError();
 }
 
 template <int ACT>
 hipError_t launch_scan(const PrefillArgs &a, const float2 *carry0, hipStream_t stream) {
-    switch (a.s.d) {
-        case 8: return launch_scan_dp<8, ACT, 8>(a, carry0, stream);
-        case 16: return launch_scan_dp<16, ACT, 8>(a, carry0, stream);
-        case 32: return launch_scan_dp<32, ACT, 4>(a, carry0, stream);
+    const int64_t esz = Act<ACT>::kBytes;
+    const int64_t ld = a.ld_in > a.ld_y ? a.ld_in : a.ld_y;
+    const bool fits = a.plan.T * ld * esz < (int64_t(1) << 31);
+    switch (fits ? a.s.d : 0) {
+        case 8: return launch_scan_dp<8, 1, ACT, 8>(a, carry0, stream);
+        case 16: return launch_scan_dp<16, 1, ACT, 8>(a, carry0, stream);
+        case 32: return launch_scan_dp<16, 2, ACT, 8>(a, carry0, stream);
+        case 64: return launch_scan_dp<16, 4, ACT, 8>(a, carry0, stream);
         default: break;
     }
     const dim3 grid((unsigned)((a.s.D + 255) / 256), (unsigned)a.plan.NC, (unsigned)a.s.B);
