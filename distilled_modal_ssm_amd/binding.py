@@ -33,6 +33,8 @@ EXPORTS = (
     "hyena_modal_prefill_chunked",
     "hyena_modal_decode_step",
     "hyena_filter_materialize",
+    "hyena_row_rms",
+    "hyena_dense_bf16",
 )
 
 
@@ -87,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                             ctypes.c_int),
             "hyena_modal_decode_step": ([D, p, p, p, i64, p, i64, p, p], ctypes.c_int),
             "hyena_filter_materialize": ([D, i64, p, p], ctypes.c_int),
+            "hyena_row_rms": ([p, i64, i64, i64, ctypes.c_float, p, p], ctypes.c_int),
+            "hyena_dense_bf16": ([i64, i64, i64, p, i64, p, i64, p, p, i64, p], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -173,6 +177,17 @@ def hyena_modal_decode_step(desc: hm_desc, q, k, v, ld_in, y, ld_y, state, strea
 def hyena_filter_materialize(desc: hm_desc, L, h_out, stream=None) -> None:
     st = load().hyena_filter_materialize(ctypes.byref(desc), L, _ptr(h_out), _stream(stream))
     _check(st, "hyena_filter_materialize")
+
+
+def hyena_row_rms(x, M, D, ld, eps, inv_rms, stream=None) -> None:
+    st = load().hyena_row_rms(_ptr(x), M, D, ld, eps, _ptr(inv_rms), _stream(stream))
+    _check(st, "hyena_row_rms")
+
+
+def hyena_dense_bf16(M, N, K, A, lda, W, ldw, row_scale, C, ldc, stream=None) -> None:
+    st = load().hyena_dense_bf16(M, N, K, _ptr(A), lda, _ptr(W), ldw, _ptr(row_scale), _ptr(C), ldc,
+                                 _stream(stream))
+    _check(st, "hyena_dense_bf16")
 
 
 # ----------------------------------------------------------------- tensor helpers

@@ -196,4 +196,50 @@ hm_status hyena_filter_materialize(const hm_desc *desc, int64_t L, float *h_out,
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
 }
 
+hm_status hyena_row_rms(const void *x, int64_t M, int64_t D, int64_t ld, float eps, float *inv_rms,
+                        void *stream) {
+    if (M < 0 || D < 1 || ld < D || M > kMaxElems / ld || !(eps >= 0.0f)) return HM_ERR_INVALID_ARG;
+    if (M == 0) return HM_OK;
+    if (!x || !inv_rms) return HM_ERR_INVALID_ARG;
+    if (!aligned(x, 2) || !aligned(inv_rms, 4)) return HM_ERR_UNSUPPORTED;
+    if (M > int64_t(UINT32_MAX) * 4) return HM_ERR_UNSUPPORTED;
+    hm::RmsArgs a;
+    a.x = x;
+    a.M = M;
+    a.D = D;
+    a.ld = ld;
+    a.eps = eps;
+    a.inv_rms = inv_rms;
+    a.vec = aligned(x, 16) && D % 8 == 0 && ld % 8 == 0;
+    const hipError_t err = hm::launch_row_rms(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+hm_status hyena_dense_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *W,
+                           int64_t ldw, const float *row_scale, void *C, int64_t ldc, void *stream) {
+    if (M < 0 || N < 0 || K < 1) return HM_ERR_INVALID_ARG;
+    if (lda < K || ldw < K || ldc < N) return HM_ERR_INVALID_ARG;
+    if (M > kMaxElems / lda || N > kMaxElems / ldw || M > kMaxElems / (ldc > 0 ? ldc : 1))
+        return HM_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return HM_OK;
+    if (!A || !W || !C) return HM_ERR_INVALID_ARG;
+    if (K % 64 != 0 || lda % 8 != 0 || ldw % 8 != 0) return HM_ERR_UNSUPPORTED;
+    if (!aligned(A, 16) || !aligned(W, 16) || !aligned(C, 2) || (row_scale && !aligned(row_scale, 4)))
+        return HM_ERR_UNSUPPORTED;
+    if (((M + 127) / 128) * ((N + 255) / 256) > INT32_MAX) return HM_ERR_UNSUPPORTED;
+    hm::GemmArgs g;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.A = A;
+    g.lda = lda;
+    g.W = W;
+    g.ldw = ldw;
+    g.row_scale = row_scale;
+    g.C = C;
+    g.ldc = ldc;
+    const hipError_t err = hm::launch_gemm(g, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
 }  // extern "C"

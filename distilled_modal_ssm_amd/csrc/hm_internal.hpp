@@ -128,6 +128,25 @@ struct PrefillArgs {
     unsigned char *ws;
 };
 
+struct RmsArgs {
+    const void *x;  // bf16 [M][ld]
+    int64_t M, D, ld;
+    float eps;
+    float *inv_rms;  // [M]
+    bool vec;        // rows 16-byte aligned and D % 8 == 0
+};
+
+struct GemmArgs {
+    int64_t M, N, K;
+    const void *A;  // bf16 [M][lda]
+    int64_t lda;
+    const void *W;  // bf16 [N][ldw]
+    int64_t ldw;
+    const float *row_scale;  // [M] or null
+    void *C;                 // bf16 [M][ldc]
+    int64_t ldc;
+};
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; none synchronises.
 
@@ -135,5 +154,7 @@ hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_filter(const FilterArgs &a, hipStream_t stream);
 PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_row_rms(const RmsArgs &a, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
 
 }  // namespace hm

@@ -153,6 +153,35 @@ hm_status hyena_modal_decode_step(const hm_desc *desc,
  */
 hm_status hyena_filter_materialize(const hm_desc *desc, int64_t L, float *h_out, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Projections of a projected Hyena stack (a model built from the operator:
+ * per-token input normalisation, in_proj D -> 3D, the operator, out_proj D -> D;
+ * the 1.3B generation comparisons of the Laughing Hyena Distillery review,
+ * "主要发现", are measured on such a model).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * inv_rms[m] = 1 / sqrt(mean_k x[m][k]^2 + eps) for every row m < M of a bf16
+ * matrix x [M][ld] (D columns used), computed in float32.  Writes M floats.
+ * Errors: M < 0, D < 1, ld < D or eps < 0 -> HM_ERR_INVALID_ARG.
+ */
+hm_status hyena_row_rms(const void *x, int64_t M, int64_t D, int64_t ld, float eps, float *inv_rms,
+                        void *stream);
+
+/*
+ * C[m][n] = bf16( row_scale[m] * sum_k A[m][k] * W[n][k] ),  m < M, n < N, k < K.
+ *   A [M][lda] bf16 (activations), W [N][ldw] bf16 (weights, output-major, as a
+ *   torch Linear stores them), C [M][ldc] bf16, row_scale [M] float32 or NULL
+ *   (= 1).  Products accumulate in float32 on the matrix cores; C is rounded
+ *   once (nearest even).  C must not overlap A or W.
+ * Requirements: K a positive multiple of 64; lda, ldw multiples of 8; A and W
+ * 16-byte aligned (else HM_ERR_UNSUPPORTED).  M <= 64 takes a weight-streaming
+ * path (the generation step), larger M an LDS-tiled path.
+ */
+hm_status hyena_dense_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                           const void *W, int64_t ldw, const float *row_scale, void *C,
+                           int64_t ldc, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -151,3 +151,35 @@ def test_missing_library_fails_loudly(tmp_path):
             hb.load(str(tmp_path / "nope.so"))
     finally:
         hb._lib = saved
+
+
+def test_dense_and_rms_validation(lib):
+    def dense(**kw):
+        a = dict(M=64, N=128, K=256, A=FAKE, lda=256, W=FAKE, ldw=256, S=None, C=FAKE, ldc=128)
+        a.update(kw)
+        hb.hyena_dense_bf16(a["M"], a["N"], a["K"], a["A"], a["lda"], a["W"], a["ldw"], a["S"], a["C"],
+                            a["ldc"], stream=0)
+
+    cases = [
+        (dict(K=0), hb.HM_ERR_INVALID_ARG),
+        (dict(M=-1), hb.HM_ERR_INVALID_ARG),
+        (dict(lda=100), hb.HM_ERR_INVALID_ARG),
+        (dict(ldc=64), hb.HM_ERR_INVALID_ARG),
+        (dict(A=None), hb.HM_ERR_INVALID_ARG),
+        (dict(K=96, lda=96, ldw=96), hb.HM_ERR_UNSUPPORTED),   # K not a multiple of 64
+        (dict(lda=260), hb.HM_ERR_UNSUPPORTED),                # row stride not a multiple of 8
+        (dict(W=FAKE + 8), hb.HM_ERR_UNSUPPORTED),             # W not 16-byte aligned
+        (dict(S=FAKE + 2), hb.HM_ERR_UNSUPPORTED),             # misaligned row scale
+    ]
+    for kw, status in cases:
+        with pytest.raises(hb.HMError) as e:
+            dense(**kw)
+        assert e.value.status == status, kw
+    dense(M=0)  # empty: no launch
+    for kw, status in [(dict(D=0), hb.HM_ERR_INVALID_ARG), (dict(ld=10), hb.HM_ERR_INVALID_ARG),
+                       (dict(eps=-1.0), hb.HM_ERR_INVALID_ARG), (dict(x=FAKE + 1), hb.HM_ERR_UNSUPPORTED)]:
+        a = dict(x=FAKE, M=4, D=64, ld=64, eps=1e-6, out=FAKE)
+        a.update(kw)
+        with pytest.raises(hb.HMError) as e:
+            hb.hyena_row_rms(a["x"], a["M"], a["D"], a["ld"], a["eps"], a["out"], stream=0)
+        assert e.value.status == status, kw
