@@ -14,10 +14,13 @@
 //     16-lane fragment reads hit distinct banks), 4 waves each owning a WM x WN
 //     sub-tile of 16x16x32 MFMAs.  Tiles are ordered so each XCD walks a
 //     contiguous range, grouped GM m-tiles at a time, to keep A and W in L2.
-//   * gemm_skinny (M <= 64, the generation step): a workgroup owns BN columns
-//     and all rows; its KW waves split K, stream W and A fragments straight from
-//     memory (no LDS staging), and reduce their partial tiles through LDS.  The
-//     step is bound by streaming W from HBM.
+//   * gemm_stream / gemm_skinny (M <= 64, the generation step): a workgroup
+//     owns 16-32 columns and all rows.  gemm_stream (wide outputs, K = 2048)
+//     streams A and W fragments through a register ring with its K loop
+//     unrolled; gemm_skinny stages contiguous A and W slabs through
+//     double-buffered LDS.  Both sum their K parts through LDS.  Every
+//     workgroup re-reads all of A (64 x K), so these are bound by L1->L2
+//     request throughput, not by the W stream alone.
 #include "hm_internal.hpp"
 
 namespace hm {
@@ -173,69 +176,192 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
 
 // ------------------------------------------------------------------ skinny GEMM
 
-// Workgroup: KW waves, all M (<= 64) rows x BN columns.  Wave w accumulates the
-// K range [w*K/KW, (w+1)*K/KW) with fragments loaded straight from memory, then
-// the partial tiles are summed through LDS.
-template <int BN, int KW>
-__global__ __launch_bounds__(KW * 64) void gemm_skinny_kernel(GemmArgs g) {
-    constexpr int NT = BN / 16;
-    constexpr int UK = 4;  // 32-wide k steps per unrolled batch of loads
-    __shared__ float part[KW][64 * BN];
-    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+// Workgroup = 4 waves on all M <= 64 rows x BN columns.  K advances in slabs of
+// kSkCK: the A slab [64][kSkCK] and the W slab [BN][kSkCK] are read with
+// contiguous 16-byte pieces (whole 512-byte row runs, which HBM streams
+// efficiently) into registers one slab ahead, then written to double-buffered
+// LDS.  Wave w owns column tile w % NTB and K half-range w / NTB of the slab
+// (NTB = BN / 16 column tiles, 4 / NTB K parts); the K parts are summed
+// through LDS at the end.
+constexpr int kSkCK = 256;            // K per slab
+constexpr int kSkLd = kSkCK + 8;      // padded LDS row (bf16), 528 B
+
+template <int BN>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
+    constexpr int NTB = BN / 16;          // column tiles
+    constexpr int KP = 4 / NTB;           // K parts per slab
+    constexpr int KPS = kSkCK / KP / 32;  // 32-wide k steps per wave per slab
+    constexpr int A_P = 64 * (kSkCK / 8) / 256;  // 16-byte pieces per thread
+    constexpr int W_P = BN * (kSkCK / 8) / 256;
+    static_assert(NTB * KP == 4 && A_P * 256 == 64 * (kSkCK / 8) && W_P * 256 == BN * (kSkCK / 8), "shape");
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][64 * kSkLd];
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][BN * kSkLd];
+
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int nt = w % NTB, kp = w / NTB;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int64_t kspan = g.K / KW, kbeg = (int64_t)w * kspan;
+    const uint16_t *A = static_cast<const uint16_t *>(g.A);
+    const uint16_t *W = static_cast<const uint16_t *>(g.W);
+
+    uint4 ra[A_P], rw[W_P];
+    auto load = [&](int64_t k0) {
+#pragma unroll
+        for (int i = 0; i < A_P; ++i) {
+            const int p = tid + i * 256, r = p / (kSkCK / 8), kk = (p % (kSkCK / 8)) * 8;
+            ra[i] = r < g.M ? *reinterpret_cast<const uint4 *>(A + r * g.lda + k0 + kk) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < W_P; ++i) {
+            const int p = tid + i * 256, r = p / (kSkCK / 8), kk = (p % (kSkCK / 8)) * 8;
+            const int64_t row = n0 + r;
+            rw[i] = row < g.N ? *reinterpret_cast<const uint4 *>(W + row * g.ldw + k0 + kk) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < A_P; ++i) {
+            const int p = tid + i * 256;
+            *reinterpret_cast<uint4 *>(&As[buf][(p / (kSkCK / 8)) * kSkLd + (p % (kSkCK / 8)) * 8]) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < W_P; ++i) {
+            const int p = tid + i * 256;
+            *reinterpret_cast<uint4 *>(&Ws[buf][(p / (kSkCK / 8)) * kSkLd + (p % (kSkCK / 8)) * 8]) = rw[i];
+        }
+    };
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int ns = (int)(g.K / kSkCK);
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int sl = 0; sl < ns; ++sl) {
+        const int buf = sl & 1;
+        if (sl + 1 < ns) load((int64_t)(sl + 1) * kSkCK);
+#pragma unroll
+        for (int st = 0; st < KPS; ++st) {
+            const int ko = (kp * KPS + st) * 32 + 8 * (lane / 16);
+            const uint4 bf = *reinterpret_cast<const uint4 *>(&Ws[buf][(nt * 16 + lane % 16) * kSkLd + ko]);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint4 af = *reinterpret_cast<const uint4 *>(&As[buf][(m * 16 + lane % 16) * kSkLd + ko]);
+                acc[m] = mfma16(af, bf, acc[m]);
+            }
+        }
+        if (sl + 1 < ns) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    // sum the K parts: C-tile lane l holds rows 16m + 4*(l/16) + r, column l%16
+    float *red = reinterpret_cast<float *>(&As[0][0]);  // [KP][64][BN] floats fit in one A buffer
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[(kp * 64 + m * 16 + 4 * (lane / 16) + r) * BN + nt * 16 + lane % 16] = acc[m][r];
+    __syncthreads();
+    uint16_t *C = static_cast<uint16_t *>(g.C);
+    for (int e = tid; e < 64 * BN; e += 256) {
+        const int row = e / BN, c = e % BN;
+        const int64_t col = n0 + c;
+        if (row >= g.M || col >= g.N) continue;
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < KP; ++q) sum += red[(q * 64 + row) * BN + c];
+        const float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+        C[row * g.ldc + col] = (uint16_t)f32_to_bf16(sum * sc);
+    }
+}
+
+// Weight-streaming GEMM for a fixed K (fully unrolled).  Workgroup = 4 waves on
+// all M <= 64 rows x 16*NTW columns; wave w takes K quarter w (NSTEPS 32-wide
+// steps).  Each wave streams its A and W fragments straight from memory
+// through an R-deep register ring: the loads for step s+R are issued before
+// step s is multiplied.  The K loop is unrolled at compile time so that every
+// wait names exactly the load it needs (a rolled loop makes the compiler drain
+// all loads at the loop head, which serialises the HBM latency).  The four
+// quarters are summed through LDS.
+template <int NTW, int R, int NSTEPS>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
+    constexpr int BN = 16 * NTW;
+    __shared__ float red[4 * 64 * BN];
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    // Every workgroup reads all of A.  Rotating the K order by the workgroup
+    // index (quarter and step) spreads the simultaneous A requests of all CUs
+    // over the L2 channels instead of hammering the same lines.
+    const int quarter = (w + (int)blockIdx.x) % 4, rot = (int)(blockIdx.x / 4) % NSTEPS;
+    const int64_t kbeg = (int64_t)quarter * NSTEPS * 32;
+    auto kstep = [&](int st) { return (st + rot) % NSTEPS; };
     const uint16_t *A = static_cast<const uint16_t *>(g.A);
     const uint16_t *W = static_cast<const uint16_t *>(g.W);
     const int ko = 8 * (lane / 16);
-
-    f32x4 acc[4][NT];
+    const uint16_t *arow[4];
+    const uint16_t *wrow[NTW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int64_t k = kbeg; k < kbeg + kspan; k += 32 * UK) {
-        uint4 af[UK][4], bf[UK][NT];
-#pragma unroll
-        for (int u = 0; u < UK; ++u) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = i * 16 + lane % 16;
-                af[u][i] = row < g.M ? *reinterpret_cast<const uint4 *>(A + row * g.lda + k + 32 * u + ko)
-                                     : make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int64_t col = n0 + j * 16 + lane % 16;
-                bf[u][j] = col < g.N ? *reinterpret_cast<const uint4 *>(W + col * g.ldw + k + 32 * u + ko)
-                                     : make_uint4(0, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < UK; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < NT; ++j) acc[i][j] = mfma16(af[u][i], bf[u][j], acc[i][j]);
+    for (int m = 0; m < 4; ++m) {
+        const int r = m * 16 + lane % 16;
+        arow[m] = A + (int64_t)(r < g.M ? r : 0) * g.lda + kbeg + ko;  // clamped rows are masked at the end
     }
-    // partial tile of this wave -> LDS [row][col]
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < NTW; ++j) {
+        const int64_t c = n0 + j * 16 + lane % 16;
+        wrow[j] = W + (c < g.N ? c : 0) * g.ldw + kbeg + ko;
+    }
+    uint4 ra[R][4], rw[R][NTW];
 #pragma unroll
-        for (int j = 0; j < NT; ++j)
+    for (int i = 0; i < R; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                part[w][(i * 16 + 4 * (lane / 16) + r) * BN + j * 16 + lane % 16] = acc[i][j][r];
+        for (int m = 0; m < 4; ++m) ra[i][m] = *reinterpret_cast<const uint4 *>(arow[m] + 32 * kstep(i));
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) rw[i][j] = *reinterpret_cast<const uint4 *>(wrow[j] + 32 * kstep(i));
+    }
+    // keep the scheduler from sinking the ring loads towards their uses
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[4][NTW];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < NSTEPS; ++st) {
+        const int i = st % R;
+        uint4 a[4], b[NTW];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) a[m] = ra[i][m];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) b[j] = rw[i][j];
+        if (st + R < NSTEPS) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) ra[i][m] = *reinterpret_cast<const uint4 *>(arow[m] + 32 * kstep(st + R));
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) rw[i][j] = *reinterpret_cast<const uint4 *>(wrow[j] + 32 * kstep(st + R));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[m][j] = mfma16(a[m], b[j], acc[m][j]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[(w * 64 + m * 16 + 4 * (lane / 16) + r) * BN + j * 16 + lane % 16] = acc[m][j][r];
     __syncthreads();
     uint16_t *C = static_cast<uint16_t *>(g.C);
-    for (int e = threadIdx.x; e < 64 * BN; e += KW * 64) {
-        const int row = e / BN, col = e % BN;
-        if (row >= g.M || n0 + col >= g.N) continue;
-        float s = 0.f;
-#pragma unroll
-        for (int q = 0; q < KW; ++q) s += part[q][e];
+    for (int e = tid; e < 64 * BN; e += 256) {
+        const int row = e / BN, c = e % BN;
+        const int64_t col = n0 + c;
+        if (row >= g.M || col >= g.N) continue;
+        const float sum = red[(0 * 64 + row) * BN + c] + red[(1 * 64 + row) * BN + c] +
+                          red[(2 * 64 + row) * BN + c] + red[(3 * 64 + row) * BN + c];
         const float sc = g.row_scale ? g.row_scale[row] : 1.0f;
-        C[row * g.ldc + n0 + col] = (uint16_t)f32_to_bf16(s * sc);
+        C[row * g.ldc + col] = (uint16_t)f32_to_bf16(sum * sc);
     }
 }
 
@@ -256,15 +382,16 @@ hipError_t launch_row_rms(const RmsArgs &a, hipStream_t stream) {
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream) {
     if (g.M == 0 || g.N == 0) return hipSuccess;
-    if (g.M <= 64 && g.K % (8 * 32 * 4) == 0) {
-        const int64_t bn = (g.N >= 4096) ? 32 : 16;
-        if (bn == 32)
-            gemm_skinny_kernel<32, 8><<<dim3((unsigned)((g.N + 31) / 32)), dim3(512), 0, stream>>>(g);
+    if (g.M <= 64 && g.K % kSkCK == 0) {
+        // Measured on MI355X at M = 64, K = 2048: the unrolled streaming kernel
+        // is fastest for wide outputs, the LDS-staged one for narrow outputs.
+        if (g.K == 2048 && g.N >= 4096)
+            gemm_stream_kernel<2, 4, 16><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
         else
-            gemm_skinny_kernel<16, 8><<<dim3((unsigned)((g.N + 15) / 16)), dim3(512), 0, stream>>>(g);
+            gemm_skinny_kernel<16><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
         return hipGetLastError();
     }
-    return launch_tiled<128, 256, 64, 128, 4>(g, stream);
+    return launch_tiled<256, 256, 128, 128, 4>(g, stream);
 }
 
 }  // namespace hm
