@@ -35,6 +35,7 @@ EXPORTS = (
     "hyena_filter_materialize",
     "hyena_row_rms",
     "hyena_dense_bf16",
+    "hyena_dense_rms_bf16",
 )
 
 
@@ -91,6 +92,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "hyena_filter_materialize": ([D, i64, p, p], ctypes.c_int),
             "hyena_row_rms": ([p, i64, i64, i64, ctypes.c_float, p, p], ctypes.c_int),
             "hyena_dense_bf16": ([i64, i64, i64, p, i64, p, i64, p, p, i64, p], ctypes.c_int),
+            "hyena_dense_rms_bf16": ([i64, i64, i64, p, i64, p, i64, ctypes.c_float, p, i64, p], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -188,6 +190,11 @@ def hyena_dense_bf16(M, N, K, A, lda, W, ldw, row_scale, C, ldc, stream=None) ->
     st = load().hyena_dense_bf16(M, N, K, _ptr(A), lda, _ptr(W), ldw, _ptr(row_scale), _ptr(C), ldc,
                                  _stream(stream))
     _check(st, "hyena_dense_bf16")
+
+
+def hyena_dense_rms_bf16(M, N, K, A, lda, W, ldw, eps, C, ldc, stream=None) -> None:
+    st = load().hyena_dense_rms_bf16(M, N, K, _ptr(A), lda, _ptr(W), ldw, eps, _ptr(C), ldc, _stream(stream))
+    _check(st, "hyena_dense_rms_bf16")
 
 
 # ----------------------------------------------------------------- tensor helpers

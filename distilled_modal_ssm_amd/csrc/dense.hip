@@ -34,6 +34,21 @@ __device__ __forceinline__ f32x4 mfma16(const uint4 a, const uint4 b, f32x4 c) {
                                                     c, 0, 0, 0);
 }
 
+// Row sums of squares come from one extra MFMA per A fragment: the diagonal of
+// A_tile A_tile^T is sum_k a[row][k]^2.  In a 16x16 C tile lane l holds rows
+// 4*(l/16)..+3 of column l%16, so diagonal entry q sits in lane 16*(q/4) + q,
+// register q % 4.  diag_of returns it for the lanes that hold one (others: 0)
+// together with its row q.
+__device__ __forceinline__ float diag_of(const f32x4 c, int lane, int &q) {
+    q = lane % 16;
+    const int r = q - 4 * (lane / 16);
+    return (r >= 0 && r < 4) ? c[r] : 0.f;
+}
+
+__device__ __forceinline__ float rms_scale(float sumsq, int64_t K, float eps) {
+    return 1.0f / sqrtf(sumsq / (float)K + eps);
+}
+
 // ------------------------------------------------------------------ RMS
 
 // One wave per row; lanes stride over the row in 16-byte (8 x bf16) pieces.
@@ -70,7 +85,7 @@ __global__ __launch_bounds__(256) void row_rms_kernel(RmsArgs a) {
 constexpr int kBK = 64;            // K per LDS stage
 constexpr int kLdsK = kBK + 8;     // padded LDS row, bf16 elements (144 B)
 
-template <int BM, int BN, int WM, int WN, int GM>
+template <int BM, int BN, int WM, int WN, int GM, bool RMS>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
     static_assert((BM / WM) * (BN / WN) == 4, "four waves per workgroup");
     constexpr int MT = WM / 16, NT = WN / 16;
@@ -129,9 +144,27 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // row sums of squares from the A pieces this thread stages (row p/8 of piece i)
+    float ssq[RMS ? A_LOADS : 1];
+#pragma unroll
+    for (int i = 0; i < (RMS ? A_LOADS : 1); ++i) ssq[i] = 0.f;
+    auto accumulate_squares = [&]() {
+        if constexpr (RMS) {
+#pragma unroll
+            for (int i = 0; i < A_LOADS; ++i) {
+                const uint32_t wv[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = bf16_lo(wv[e]), hi = bf16_hi(wv[e]);
+                    ssq[i] = fmaf(lo, lo, fmaf(hi, hi, ssq[i]));
+                }
+            }
+        }
+    };
 
     const int nk = (int)(g.K / kBK);
     load_stage(0);
+    accumulate_squares();
     store_stage(0);
     __syncthreads();
     for (int kb = 0; kb < nk; ++kb) {
@@ -152,7 +185,23 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
 #pragma unroll
                 for (int j = 0; j < NT; ++j) acc[i][j] = mfma16(af[i], bf[j], acc[i][j]);
         }
-        if (kb + 1 < nk) store_stage(buf ^ 1);
+        if (kb + 1 < nk) {
+            accumulate_squares();
+            store_stage(buf ^ 1);
+        }
+        __syncthreads();
+    }
+    // per-row scale: the 8 consecutive lanes that staged a row sum their parts
+    __shared__ float rs[RMS ? BM : 1];
+    if constexpr (RMS) {
+#pragma unroll
+        for (int i = 0; i < A_LOADS; ++i) {
+            float v = ssq[i];
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            v += __shfl_xor(v, 4);
+            if ((tid & 7) == 0) rs[(tid + i * 256) / 8] = rms_scale(v, g.K, g.rms_eps);
+        }
         __syncthreads();
     }
 
@@ -164,7 +213,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
         for (int r = 0; r < 4; ++r) {
             const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane / 16) + r;
             if (row >= g.M) continue;
-            const float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+            float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+            if constexpr (RMS) sc *= rs[wm * WM + i * 16 + 4 * (lane / 16) + r];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const int64_t col = n0 + wn * WN + j * 16 + lane % 16;
@@ -186,7 +236,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmArgs g) {
 constexpr int kSkCK = 256;            // K per slab
 constexpr int kSkLd = kSkCK + 8;      // padded LDS row (bf16), 528 B
 
-template <int BN>
+template <int BN, bool RMS>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     constexpr int NTB = BN / 16;          // column tiles
     constexpr int KP = 4 / NTB;           // K parts per slab
@@ -230,9 +280,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
         }
     };
 
-    f32x4 acc[4];
+    f32x4 acc[4], ss[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) acc[i] = ss[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int ns = (int)(g.K / kSkCK);
     load(0);
@@ -249,6 +299,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
             for (int m = 0; m < 4; ++m) {
                 const uint4 af = *reinterpret_cast<const uint4 *>(&As[buf][(m * 16 + lane % 16) * kSkLd + ko]);
                 acc[m] = mfma16(af, bf, acc[m]);
+                if constexpr (RMS) {
+                    if (nt == 0) ss[m] = mfma16(af, af, ss[m]);  // one column tile per K part is enough
+                }
             }
         }
         if (sl + 1 < ns) store(buf ^ 1);
@@ -257,10 +310,21 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 
     // sum the K parts: C-tile lane l holds rows 16m + 4*(l/16) + r, column l%16
     float *red = reinterpret_cast<float *>(&As[0][0]);  // [KP][64][BN] floats fit in one A buffer
+    float *red_ss = reinterpret_cast<float *>(&Ws[0][0]);  // [KP][64]
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) red[(kp * 64 + m * 16 + 4 * (lane / 16) + r) * BN + nt * 16 + lane % 16] = acc[m][r];
+    if constexpr (RMS) {
+        if (nt == 0) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                int q;
+                const float dg = diag_of(ss[m], lane, q);
+                if (4 * (lane / 16) <= q && q < 4 * (lane / 16) + 4) red_ss[kp * 64 + m * 16 + q] = dg;
+            }
+        }
+    }
     __syncthreads();
     uint16_t *C = static_cast<uint16_t *>(g.C);
     for (int e = tid; e < 64 * BN; e += 256) {
@@ -270,7 +334,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
         float sum = 0.f;
 #pragma unroll
         for (int q = 0; q < KP; ++q) sum += red[(q * 64 + row) * BN + c];
-        const float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+        float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+        if constexpr (RMS) {
+            float s2 = 0.f;
+#pragma unroll
+            for (int q = 0; q < KP; ++q) s2 += red_ss[q * 64 + row];
+            sc *= rms_scale(s2, g.K, g.rms_eps);
+        }
         C[row * g.ldc + col] = (uint16_t)f32_to_bf16(sum * sc);
     }
 }
@@ -283,10 +353,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // wait names exactly the load it needs (a rolled loop makes the compiler drain
 // all loads at the loop head, which serialises the HBM latency).  The four
 // quarters are summed through LDS.
-template <int NTW, int R, int NSTEPS>
+template <int NTW, int R, int NSTEPS, bool RMS>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
     constexpr int BN = 16 * NTW;
     __shared__ float red[4 * 64 * BN];
+    __shared__ float red_ss[RMS ? 4 * 64 : 1];
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
     // Every workgroup reads all of A.  Rotating the K order by the workgroup
@@ -320,11 +391,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
     }
     // keep the scheduler from sinking the ring loads towards their uses
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc[4][NTW];
+    f32x4 acc[4][NTW], ss[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 4; ++m) {
+        ss[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 #pragma unroll
     for (int st = 0; st < NSTEPS; ++st) {
         const int i = st % R;
@@ -344,7 +417,19 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
         for (int m = 0; m < 4; ++m)
 #pragma unroll
             for (int j = 0; j < NTW; ++j) acc[m][j] = mfma16(a[m], b[j], acc[m][j]);
+        if constexpr (RMS) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) ss[m] = mfma16(a[m], a[m], ss[m]);
+        }
         __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (RMS) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            int q;
+            const float dg = diag_of(ss[m], lane, q);
+            if (4 * (lane / 16) <= q && q < 4 * (lane / 16) + 4) red_ss[w * 64 + m * 16 + q] = dg;
+        }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -360,15 +445,27 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
         if (row >= g.M || col >= g.N) continue;
         const float sum = red[(0 * 64 + row) * BN + c] + red[(1 * 64 + row) * BN + c] +
                           red[(2 * 64 + row) * BN + c] + red[(3 * 64 + row) * BN + c];
-        const float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+        float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+        if constexpr (RMS)
+            sc *= rms_scale(red_ss[row] + red_ss[64 + row] + red_ss[128 + row] + red_ss[192 + row], g.K, g.rms_eps);
         C[row * g.ldc + col] = (uint16_t)f32_to_bf16(sum * sc);
     }
 }
 
-template <int BM, int BN, int WM, int WN, int GM>
-hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
+template <bool RMS>
+hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
+    if (g.M <= 64 && g.K % kSkCK == 0) {
+        // Measured on MI355X at M = 64, K = 2048: the unrolled streaming kernel
+        // is fastest for wide outputs, the LDS-staged one for narrow outputs.
+        if (g.K == 2048 && g.N >= 4096)
+            gemm_stream_kernel<2, 4, 16, RMS><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
+        else
+            gemm_skinny_kernel<16, RMS><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
+        return hipGetLastError();
+    }
+    constexpr int BM = 256, BN = 256;
     const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-    gemm_tiled_kernel<BM, BN, WM, WN, GM><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(g);
+    gemm_tiled_kernel<BM, BN, 128, 128, 4, RMS><<<dim3((unsigned)tiles), dim3(256), 0, stream>>>(g);
     return hipGetLastError();
 }
 
@@ -382,16 +479,7 @@ hipError_t launch_row_rms(const RmsArgs &a, hipStream_t stream) {
 
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream) {
     if (g.M == 0 || g.N == 0) return hipSuccess;
-    if (g.M <= 64 && g.K % kSkCK == 0) {
-        // Measured on MI355X at M = 64, K = 2048: the unrolled streaming kernel
-        // is fastest for wide outputs, the LDS-staged one for narrow outputs.
-        if (g.K == 2048 && g.N >= 4096)
-            gemm_stream_kernel<2, 4, 16><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
-        else
-            gemm_skinny_kernel<16><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
-        return hipGetLastError();
-    }
-    return launch_tiled<256, 256, 128, 128, 4>(g, stream);
+    return g.rms ? launch_gemm_t<true>(g, stream) : launch_gemm_t<false>(g, stream);
 }
 
 }  // namespace hm

@@ -215,8 +215,8 @@ hm_status hyena_row_rms(const void *x, int64_t M, int64_t D, int64_t ld, float e
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
 }
 
-hm_status hyena_dense_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *W,
-                           int64_t ldw, const float *row_scale, void *C, int64_t ldc, void *stream) {
+static hm_status dense_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *W, int64_t ldw,
+                     const float *row_scale, bool rms, float eps, void *C, int64_t ldc, void *stream) {
     if (M < 0 || N < 0 || K < 1) return HM_ERR_INVALID_ARG;
     if (lda < K || ldw < K || ldc < N) return HM_ERR_INVALID_ARG;
     if (M > kMaxElems / lda || N > kMaxElems / ldw || M > kMaxElems / (ldc > 0 ? ldc : 1))
@@ -238,8 +238,21 @@ hm_status hyena_dense_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64
     g.row_scale = row_scale;
     g.C = C;
     g.ldc = ldc;
+    g.rms = rms;
+    g.rms_eps = eps;
     const hipError_t err = hm::launch_gemm(g, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+hm_status hyena_dense_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *W,
+                           int64_t ldw, const float *row_scale, void *C, int64_t ldc, void *stream) {
+    return dense_impl(M, N, K, A, lda, W, ldw, row_scale, false, 0.0f, C, ldc, stream);
+}
+
+hm_status hyena_dense_rms_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *W,
+                               int64_t ldw, float eps, void *C, int64_t ldc, void *stream) {
+    if (!(eps >= 0.0f)) return HM_ERR_INVALID_ARG;
+    return dense_impl(M, N, K, A, lda, W, ldw, nullptr, true, eps, C, ldc, stream);
 }
 
 }  // extern "C"

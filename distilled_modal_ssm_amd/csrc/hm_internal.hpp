@@ -145,6 +145,8 @@ struct GemmArgs {
     const float *row_scale;  // [M] or null
     void *C;                 // bf16 [M][ldc]
     int64_t ldc;
+    bool rms;                // also scale row m by 1/sqrt(mean_k A[m][k]^2 + rms_eps)
+    float rms_eps;
 };
 
 // ---------------------------------------------------------------- launchers

@@ -1,8 +1,9 @@
 """A projected Hyena stack over the C ABI (argument marshalling only).
 
-Each layer: per-token inverse RMS of the layer input -> in_proj (D -> 3D, row
-scaled by the inverse RMS) -> the modal Hyena operator on [q|k|v] (contiguous
-thirds of the in_proj output) -> out_proj (D -> D).  No bias, no residual.
+Each layer: in_proj (D -> 3D) of the layer input with each token's row scaled
+by its inverse RMS (fused into the projection) -> the modal Hyena operator on
+[q|k|v] (contiguous thirds of the in_proj output) -> out_proj (D -> D).  No
+bias, no residual.
 The stack's output at the last prompt position is the first generation input;
 each later generation input is the previous step's output.  Every computation
 is a library call; torch only provides device memory, views and streams.
@@ -45,13 +46,11 @@ class HyenaStack:
         self.x = [torch.empty((M, D), dtype=bf, **e), torch.empty((M, D), dtype=bf, **e)]
         self.qkv = torch.empty((M, 3 * D), dtype=bf, **e)
         self.y = torch.empty((M, D), dtype=bf, **e)
-        self.s = torch.empty((M,), dtype=torch.float32, **e)
         # generation buffers
         self.xd = torch.empty((B, D), dtype=bf, **e)      # step input (and, fed back, output)
         self.xd_mid = [torch.empty((B, D), dtype=bf, **e), torch.empty((B, D), dtype=bf, **e)]
         self.qkvd = torch.empty((B, 3 * D), dtype=bf, **e)
         self.yd = torch.empty((B, D), dtype=bf, **e)
-        self.sd = torch.empty((B,), dtype=torch.float32, **e)
         self.states = [op.new_state() for op in self.ops]
 
     def _bf16(self, w):
@@ -63,10 +62,9 @@ class HyenaStack:
 
     # ------------------------------------------------------------ one layer
 
-    def _layer(self, l, x, out, M, qkv, y, s, rows_time, prefill: bool):
+    def _layer(self, l, x, out, M, qkv, y, rows_time, prefill: bool):
         D = self.D
-        hb.hyena_row_rms(x, M, D, D, RMS_EPS, s)
-        hb.hyena_dense_bf16(M, 3 * D, D, x, D, self.w_in[l], D, s, qkv, 3 * D)
+        hb.hyena_dense_rms_bf16(M, 3 * D, D, x, D, self.w_in[l], D, RMS_EPS, qkv, 3 * D)
         if prefill:
             B, L = rows_time
             q3 = qkv.view(B, L, 3 * D)
@@ -87,7 +85,7 @@ class HyenaStack:
             if record is not None:
                 record(l, src)
             dst = self.x[l % 2]
-            self._layer(l, src, dst, M, self.qkv, self.y, self.s, (self.B, self.L), True)
+            self._layer(l, src, dst, M, self.qkv, self.y, (self.B, self.L), True)
             src = dst
         return src
 
@@ -102,6 +100,6 @@ class HyenaStack:
             if record is not None:
                 record(l, src)
             dst = self.xd if l == self.nl - 1 else self.xd_mid[l % 2]
-            self._layer(l, src, dst, self.B, self.qkvd, self.yd, self.sd, None, False)
+            self._layer(l, src, dst, self.B, self.qkvd, self.yd, None, False)
             src = dst
         return self.xd

@@ -182,6 +182,16 @@ hm_status hyena_dense_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64
                            const void *W, int64_t ldw, const float *row_scale, void *C,
                            int64_t ldc, void *stream);
 
+/*
+ * The in_proj of a projected layer with its input normalisation fused:
+ *   C[m][n] = bf16( sum_k A[m][k] W[n][k] / sqrt(mean_k A[m][k]^2 + eps) ),
+ * the mean over the K columns of row m, in float32.  Same layouts and
+ * requirements as hyena_dense_bf16; eps < 0 -> HM_ERR_INVALID_ARG.
+ */
+hm_status hyena_dense_rms_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                               const void *W, int64_t ldw, float eps, void *C, int64_t ldc,
+                               void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -176,6 +176,12 @@ def test_dense_and_rms_validation(lib):
             dense(**kw)
         assert e.value.status == status, kw
     dense(M=0)  # empty: no launch
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_dense_rms_bf16(64, 128, 256, FAKE, 256, FAKE, 256, -1.0, FAKE, 128, stream=0)
+    assert e.value.status == hb.HM_ERR_INVALID_ARG
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_dense_rms_bf16(64, 128, 96, FAKE, 96, FAKE, 96, 1e-6, FAKE, 128, stream=0)
+    assert e.value.status == hb.HM_ERR_UNSUPPORTED
     for kw, status in [(dict(D=0), hb.HM_ERR_INVALID_ARG), (dict(ld=10), hb.HM_ERR_INVALID_ARG),
                        (dict(eps=-1.0), hb.HM_ERR_INVALID_ARG), (dict(x=FAKE + 1), hb.HM_ERR_UNSUPPORTED)]:
         a = dict(x=FAKE, M=4, D=64, ld=64, eps=1e-6, out=FAKE)

@@ -54,6 +54,26 @@ def test_dense_bf16(M, N, K, scaled):
     assert err <= 8e-3
 
 
+@pytest.mark.parametrize("M,N,K", [(64, 6144, 2048), (64, 2048, 2048), (50, 100, 512), (700, 300, 256),
+                                   (2048, 6144, 2048)])
+def test_dense_rms_fused(M, N, K):
+    """in_proj with the inverse-RMS row scale computed inside the GEMM."""
+    torch = require_gpu()
+    rng = np.random.default_rng(M + 3 * N + K)
+    a = _bits(rng, (M, K), 2.5)
+    w = _bits(rng, (N, K), 0.02)
+    A, W = to_dev(a, "bf16"), to_dev(w, "bf16")
+    C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    log(f"dense_rms M={M} N={N} K={K}")
+    hb.hyena_dense_rms_bf16(M, N, K, A, K, W, K, 1e-6, C, N)
+    torch.cuda.synchronize()
+    a64 = oracle.bf16_to_f64(a)
+    ref = oracle.dense(a64, oracle.bf16_to_f64(w)) * oracle.rms_inv(a64, 1e-6)[:, None]
+    err = rel_err(to_np64(C), ref)
+    print(f"dense_rms {M}x{N}x{K}: rel err {err:.2e}")
+    assert err <= 8e-3
+
+
 def test_dense_strided_operands():
     """Row strides larger than K / N (a column block of a wider matrix)."""
     torch = require_gpu()
