@@ -23,14 +23,17 @@ HM_ABI_VERSION = 1
 HM_MAX_MODES = 64
 HM_F32, HM_BF16 = 0, 1
 HM_OK, HM_ERR_INVALID_ARG, HM_ERR_UNSUPPORTED, HM_ERR_WORKSPACE, HM_ERR_HIP = range(5)
+HM_PREFILL_AUTO, HM_PREFILL_SCAN, HM_PREFILL_MFMA = 0, 1, 2
+ALGOS = {"auto": HM_PREFILL_AUTO, "scan": HM_PREFILL_SCAN, "mfma": HM_PREFILL_MFMA}
 
 EXPORTS = (
     "hm_abi_version",
     "hm_status_string",
     "hyena_modal_prefill_workspace",
-    "hyena_modal_prefill_workspace_chunked",
+    "hyena_modal_prefill_workspace_ex",
+    "hyena_modal_prefill_plan",
     "hyena_modal_prefill",
-    "hyena_modal_prefill_chunked",
+    "hyena_modal_prefill_ex",
     "hyena_modal_decode_step",
     "hyena_filter_materialize",
     "hyena_row_rms",
@@ -63,6 +66,15 @@ class hm_desc(ctypes.Structure):
     ]
 
 
+class hm_prefill_opts(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int64), ("algo", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class hm_prefill_info(ctypes.Structure):
+    _fields_ = [("algo", ctypes.c_int32), ("reserved", ctypes.c_int32), ("chunk", ctypes.c_int64),
+                ("n_chunks", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -84,10 +96,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "hm_abi_version": ([], ctypes.c_int),
             "hm_status_string": ([ctypes.c_int], ctypes.c_char_p),
             "hyena_modal_prefill_workspace": ([D, i64, ctypes.POINTER(sz)], ctypes.c_int),
-            "hyena_modal_prefill_workspace_chunked": ([D, i64, i64, ctypes.POINTER(sz)], ctypes.c_int),
+            "hyena_modal_prefill_workspace_ex": ([D, i64, ctypes.POINTER(hm_prefill_opts), ctypes.POINTER(sz)],
+                                                 ctypes.c_int),
+            "hyena_modal_prefill_plan": ([D, i64, ctypes.POINTER(hm_prefill_opts), ctypes.POINTER(hm_prefill_info)],
+                                         ctypes.c_int),
             "hyena_modal_prefill": ([D, i64, p, p, p, i64, p, i64, p, p, p, sz, p], ctypes.c_int),
-            "hyena_modal_prefill_chunked": ([D, i64, p, p, p, i64, p, i64, p, p, p, sz, i64, p],
-                                            ctypes.c_int),
+            "hyena_modal_prefill_ex": ([D, i64, p, p, p, i64, p, i64, p, p, p, sz,
+                                        ctypes.POINTER(hm_prefill_opts), p], ctypes.c_int),
             "hyena_modal_decode_step": ([D, p, p, p, i64, p, i64, p, p], ctypes.c_int),
             "hyena_filter_materialize": ([D, i64, p, p], ctypes.c_int),
             "hyena_row_rms": ([p, i64, i64, i64, ctypes.c_float, p, p], ctypes.c_int),
@@ -148,23 +163,41 @@ def hm_abi_version() -> int:
     return load().hm_abi_version()
 
 
-def hyena_modal_prefill_workspace(desc: hm_desc, L: int, chunk: int = 0) -> int:
+def _opts(chunk, algo):
+    a = ALGOS[algo] if isinstance(algo, str) else int(algo)
+    return hm_prefill_opts(int(chunk), a, 0)
+
+
+def hyena_modal_prefill_workspace(desc: hm_desc, L: int, chunk: int = 0, algo="auto") -> int:
     n = ctypes.c_size_t(0)
-    if chunk:
-        st = load().hyena_modal_prefill_workspace_chunked(ctypes.byref(desc), L, chunk, ctypes.byref(n))
+    if chunk or algo not in ("auto", HM_PREFILL_AUTO):
+        o = _opts(chunk, algo)
+        st = load().hyena_modal_prefill_workspace_ex(ctypes.byref(desc), L, ctypes.byref(o), ctypes.byref(n))
     else:
         st = load().hyena_modal_prefill_workspace(ctypes.byref(desc), L, ctypes.byref(n))
     _check(st, "hyena_modal_prefill_workspace")
     return n.value
 
 
+def hyena_modal_prefill_plan(desc: hm_desc, L: int, chunk: int = 0, algo="auto") -> dict:
+    """What a prefill would run: {"algo": "scan"|"mfma", "chunk", "n_chunks", "workspace_bytes"}."""
+    o = _opts(chunk, algo)
+    info = hm_prefill_info()
+    _check(load().hyena_modal_prefill_plan(ctypes.byref(desc), L, ctypes.byref(o), ctypes.byref(info)),
+           "hyena_modal_prefill_plan")
+    names = {HM_PREFILL_SCAN: "scan", HM_PREFILL_MFMA: "mfma"}
+    return {"algo": names[info.algo], "chunk": info.chunk, "n_chunks": info.n_chunks,
+            "workspace_bytes": info.workspace_bytes}
+
+
 def hyena_modal_prefill(desc: hm_desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out,
-                        workspace, ws_bytes, stream=None, chunk: int = 0) -> None:
+                        workspace, ws_bytes, stream=None, chunk: int = 0, algo="auto") -> None:
     lib = load()
     args = (ctypes.byref(desc), L, _ptr(q), _ptr(k), _ptr(v), ld_in, _ptr(y), ld_y,
             _ptr(state_in), _ptr(state_out), _ptr(workspace), ws_bytes)
-    if chunk:
-        st = lib.hyena_modal_prefill_chunked(*args, chunk, _stream(stream))
+    if chunk or algo not in ("auto", HM_PREFILL_AUTO):
+        o = _opts(chunk, algo)
+        st = lib.hyena_modal_prefill_ex(*args, ctypes.byref(o), _stream(stream))
     else:
         st = lib.hyena_modal_prefill(*args, _stream(stream))
     _check(st, "hyena_modal_prefill")
@@ -242,14 +275,21 @@ class ModalHyena:
         return self.torch.zeros((self.B, self.H, self.d, self.P, 2), dtype=self.torch.float32,
                                 device=self.device)
 
-    def workspace(self, L: int, chunk: int = 0):
-        n = hyena_modal_prefill_workspace(self.desc, L, chunk)
+    def workspace(self, L: int, chunk: int = 0, algo="auto"):
+        n = hyena_modal_prefill_workspace(self.desc, L, chunk, algo)
         if self._ws is None or self._ws.numel() < n:
             self._ws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device=self.device)
         return self._ws, n
 
-    def prefill(self, q, k, v, y=None, state_in=None, state_out=None, chunk: int = 0, stream=None):
-        """q, k, v: [B][L][ld] views with unit channel stride.  Returns (y, state)."""
+    def plan(self, L: int, chunk: int = 0, algo="auto") -> dict:
+        return hyena_modal_prefill_plan(self.desc, L, chunk, algo)
+
+    def prefill(self, q, k, v, y=None, state_in=None, state_out=None, chunk: int = 0, algo="auto",
+                stream=None):
+        """q, k, v: [B][L][ld] views with unit channel stride.  Returns (y, state).
+
+        algo: "auto", "scan" (vector-ALU modal scan) or "mfma" (matrix-core sub-blocks).
+        """
         B, L = q.shape[0], q.shape[1]
         if y is None:
             y = self.torch.empty((B, L, self.D), dtype=self.tdtype, device=self.device)
@@ -257,9 +297,9 @@ class ModalHyena:
             state_out = self.new_state()
         ld_in = _row_stride(q, (k, v))
         ld_y = _row_stride(y, ())
-        ws, n = self.workspace(L, chunk)
+        ws, n = self.workspace(L, chunk, algo)
         hyena_modal_prefill(self.desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out, ws, n,
-                            stream, chunk)
+                            stream, chunk, algo)
         return y, state_out
 
     def decode_step(self, q, k, v, state, y=None, stream=None):

@@ -60,12 +60,28 @@ hm_status check_chunk(int64_t chunk) {
     return HM_OK;
 }
 
+hm_status check_opts(const hm_prefill_opts *opts, int64_t *chunk, int *algo) {
+    *chunk = 0;
+    *algo = hm::kAlgoAuto;
+    if (!opts) return HM_OK;
+    hm_status st = check_chunk(opts->chunk);
+    if (st != HM_OK) return st;
+    if (opts->algo != HM_PREFILL_AUTO && opts->algo != HM_PREFILL_SCAN && opts->algo != HM_PREFILL_MFMA)
+        return HM_ERR_INVALID_ARG;
+    *chunk = opts->chunk;
+    *algo = opts->algo == HM_PREFILL_SCAN ? hm::kAlgoScan : opts->algo == HM_PREFILL_MFMA ? hm::kAlgoMfma
+                                                                                              : hm::kAlgoAuto;
+    return HM_OK;
+}
+
 hm_status prefill_impl(const hm_desc *desc, int64_t L, const void *q, const void *k, const void *v,
                        int64_t ld_in, void *y, int64_t ld_y, const float *state_in, float *state_out,
-                       void *workspace, size_t ws_bytes, void *stream, int64_t chunk) {
+                       void *workspace, size_t ws_bytes, void *stream, const hm_prefill_opts *opts) {
     hm_status st = check_desc(desc);
     if (st != HM_OK) return st;
-    if ((st = check_chunk(chunk)) != HM_OK) return st;
+    int64_t chunk;
+    int algo;
+    if ((st = check_opts(opts, &chunk, &algo)) != HM_OK) return st;
     if (L < 0 || L > kMaxElems) return HM_ERR_INVALID_ARG;
     const hm::OpShape s = shape_of(desc);
     if (s.B > 0 && L > 0) {
@@ -79,9 +95,16 @@ hm_status prefill_impl(const hm_desc *desc, int64_t L, const void *q, const void
         if (!state_out) return HM_ERR_INVALID_ARG;
         if (!aligned(state_out, 8) || (state_in && !aligned(state_in, 8))) return HM_ERR_UNSUPPORTED;
     }
-    const hm::PrefillPlan plan = hm::make_prefill_plan(s, L, chunk);
+    const hm::PrefillPlan plan = hm::make_prefill_plan(s, L, chunk, algo);
     // grid limits: batch rows and chunks map to the y/z launch dimensions
     if (s.B > 65535 || plan.NC > 65535) return HM_ERR_UNSUPPORTED;
+    if (algo == hm::kAlgoMfma && s.B > 0 && L > 0) {
+        // the matrix-core path was asked for explicitly: shape and alignment must allow it
+        const int esz = elem_bytes(desc);
+        if (plan.algo != hm::kAlgoMfma || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+            !aligned(y, 16) || (ld_in * esz) % 16 != 0 || (ld_y * esz) % 16 != 0)
+            return HM_ERR_UNSUPPORTED;
+    }
     if (s.B > 0 && plan.bytes > 0) {
         if (!workspace || ws_bytes < plan.bytes) return HM_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return HM_ERR_UNSUPPORTED;
@@ -103,12 +126,31 @@ hm_status prefill_impl(const hm_desc *desc, int64_t L, const void *q, const void
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
 }
 
-hm_status workspace_impl(const hm_desc *desc, int64_t L, int64_t chunk, size_t *bytes) {
+hm_status workspace_impl(const hm_desc *desc, int64_t L, const hm_prefill_opts *opts, size_t *bytes) {
     hm_status st = check_desc(desc);
     if (st != HM_OK) return st;
-    if ((st = check_chunk(chunk)) != HM_OK) return st;
+    int64_t chunk;
+    int algo;
+    if ((st = check_opts(opts, &chunk, &algo)) != HM_OK) return st;
     if (!bytes || L < 0 || L > kMaxElems) return HM_ERR_INVALID_ARG;
-    *bytes = desc->batch > 0 ? hm::make_prefill_plan(shape_of(desc), L, chunk).bytes : 0;
+    *bytes = desc->batch > 0 ? hm::make_prefill_plan(shape_of(desc), L, chunk, algo).bytes : 0;
+    return HM_OK;
+}
+
+hm_status plan_impl(const hm_desc *desc, int64_t L, const hm_prefill_opts *opts, hm_prefill_info *info) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    int64_t chunk;
+    int algo;
+    if ((st = check_opts(opts, &chunk, &algo)) != HM_OK) return st;
+    if (!info || L < 0 || L > kMaxElems) return HM_ERR_INVALID_ARG;
+    const hm::PrefillPlan plan = hm::make_prefill_plan(shape_of(desc), L, chunk, algo);
+    if (algo == hm::kAlgoMfma && plan.algo != hm::kAlgoMfma) return HM_ERR_UNSUPPORTED;
+    info->algo = plan.algo == hm::kAlgoMfma ? HM_PREFILL_MFMA : HM_PREFILL_SCAN;
+    info->reserved = 0;
+    info->chunk = plan.T;
+    info->n_chunks = plan.NC;
+    info->workspace_bytes = desc->batch > 0 ? plan.bytes : 0;
     return HM_OK;
 }
 
@@ -130,12 +172,17 @@ const char *hm_status_string(hm_status status) {
 }
 
 hm_status hyena_modal_prefill_workspace(const hm_desc *desc, int64_t L, size_t *bytes) {
-    return workspace_impl(desc, L, 0, bytes);
+    return workspace_impl(desc, L, nullptr, bytes);
 }
 
-hm_status hyena_modal_prefill_workspace_chunked(const hm_desc *desc, int64_t L, int64_t chunk,
-                                                size_t *bytes) {
-    return workspace_impl(desc, L, chunk, bytes);
+hm_status hyena_modal_prefill_workspace_ex(const hm_desc *desc, int64_t L, const hm_prefill_opts *opts,
+                                           size_t *bytes) {
+    return workspace_impl(desc, L, opts, bytes);
+}
+
+hm_status hyena_modal_prefill_plan(const hm_desc *desc, int64_t L, const hm_prefill_opts *opts,
+                                   hm_prefill_info *info) {
+    return plan_impl(desc, L, opts, info);
 }
 
 hm_status hyena_modal_prefill(const hm_desc *desc, int64_t L, const void *q, const void *k,
@@ -143,15 +190,15 @@ hm_status hyena_modal_prefill(const hm_desc *desc, int64_t L, const void *q, con
                               const float *state_in, float *state_out, void *workspace,
                               size_t ws_bytes, void *stream) {
     return prefill_impl(desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out, workspace, ws_bytes,
-                        stream, 0);
+                        stream, nullptr);
 }
 
-hm_status hyena_modal_prefill_chunked(const hm_desc *desc, int64_t L, const void *q, const void *k,
-                                      const void *v, int64_t ld_in, void *y, int64_t ld_y,
-                                      const float *state_in, float *state_out, void *workspace,
-                                      size_t ws_bytes, int64_t chunk, void *stream) {
+hm_status hyena_modal_prefill_ex(const hm_desc *desc, int64_t L, const void *q, const void *k,
+                                 const void *v, int64_t ld_in, void *y, int64_t ld_y,
+                                 const float *state_in, float *state_out, void *workspace,
+                                 size_t ws_bytes, const hm_prefill_opts *opts, void *stream) {
     return prefill_impl(desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out, workspace, ws_bytes,
-                        stream, chunk);
+                        stream, opts);
 }
 
 hm_status hyena_modal_decode_step(const hm_desc *desc, const void *q, const void *k, const void *v,

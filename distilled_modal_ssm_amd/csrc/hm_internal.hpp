@@ -105,15 +105,31 @@ struct FilterArgs {
     float *h; // [H][L]
 };
 
+// In-chunk algorithms of prefill.
+enum PrefillAlgo : int { kAlgoAuto = 0, kAlgoScan = 1, kAlgoMfma = 2 };
+
 // Chunked prefill plan: NC chunks of T steps (the last one may be shorter).
 struct PrefillPlan {
     int64_t L, T, NC;
-    int64_t mtiles;      // 16-row tiles of the 2d Vandermonde rows
+    int algo;            // kAlgoScan or kAlgoMfma (resolved)
+    int64_t mtiles;      // 16-row tiles of the 2d Vandermonde rows (chunk states)
     size_t off_vand_hi;  // bf16 A-operand fragments, [H][mtiles][T/32][64 lanes][8]
     size_t off_vand_lo;
     size_t off_lamT;     // float2 [H][d]: lambda^T
     size_t off_carry;    // float2 [NC][B][H][d][P]: state entering each chunk
+    size_t off_mfma_tab; // sub-block tables (matrix-core path)
+    size_t off_mfma_lam; // float2 [H][D2/2]: lambda^64
     size_t bytes;        // total workspace
+};
+
+// Geometry of the matrix-core prefill for d modes: D2 = mode rows (Re/Im of
+// each mode, padded to at least 32), fragment counts of the per-head tables.
+constexpr int kSubBlock = 64;  // steps per sub-block
+template <int DD> struct MfmaGeom {
+    static constexpr int D2 = (2 * DD < 32) ? 32 : 2 * DD;
+    static constexpr int KC = D2 / 32;   // 32-wide k steps of C X
+    static constexpr int MTS = D2 / 16;  // 16-row tiles of V U
+    static constexpr int NFRAG = 8 + 4 * KC + 2 * MTS;  // T + C + V fragments
 };
 
 struct PrefillArgs {
@@ -154,8 +170,14 @@ struct GemmArgs {
 
 hipError_t launch_decode_step(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_filter(const FilterArgs &a, hipStream_t stream);
-PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk);
+PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk, int algo);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+// matrix-core prefill (prefill_mfma.hip)
+int mfma_channel_tile(int64_t d, int64_t P);  // channels per workgroup, 0 = not eligible
+size_t mfma_table_bytes(int64_t H, int64_t d);
+size_t mfma_lam_bytes(int64_t H, int64_t d);
+hipError_t launch_mfma_tables(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_chunk_mfma(const PrefillArgs &a, const float2 *carry0, hipStream_t stream);
 hipError_t launch_row_rms(const RmsArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
 

@@ -507,9 +507,11 @@ hipError_t launch_scan(const PrefillArgs &a, const float2 *carry0, hipStream_t s
 
 }  // namespace
 
-PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk) {
+PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk, int algo) {
     PrefillPlan p{};
     p.L = L;
+    const int pt = mfma_channel_tile(s.d, s.P);
+    p.algo = (algo == kAlgoScan || pt == 0) ? kAlgoScan : kAlgoMfma;
     if (L <= 0) {
         p.T = 0;
         p.NC = 0;
@@ -519,10 +521,17 @@ PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk) {
     if (chunk > 0) {
         T = chunk;
     } else {
-        // Enough independent (b, chunk, channel) lanes for ~32 waves per CU.
-        const int64_t waves_per_chunk = (s.B * s.D + kWave - 1) / kWave;
-        const int64_t target = 8192;
-        int64_t nc = (target + waves_per_chunk - 1) / (waves_per_chunk > 0 ? waves_per_chunk : 1);
+        int64_t nc;
+        if (p.algo == kAlgoMfma) {
+            // one workgroup (batch row, head, channel tile) per CU: chunk the
+            // prompt only when there are fewer such tiles than CUs
+            const int64_t tiles = s.B * s.H * (s.P / pt);
+            nc = (256 + tiles - 1) / (tiles > 0 ? tiles : 1);
+        } else {
+            // enough independent (b, chunk, channel) lanes for ~32 waves per CU
+            const int64_t waves_per_chunk = (s.B * s.D + kWave - 1) / kWave;
+            nc = (8192 + waves_per_chunk - 1) / (waves_per_chunk > 0 ? waves_per_chunk : 1);
+        }
         const int64_t ncmax = (L + kKB - 1) / kKB;
         if (nc < 1) nc = 1;
         if (nc > ncmax) nc = ncmax;
@@ -546,8 +555,23 @@ PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk) {
         p.off_carry = off;
         off = align256(off + (size_t)p.NC * s.B * s.D * s.d * 8);
     }
+    if (p.algo == kAlgoMfma) {
+        p.off_mfma_tab = off;
+        off = align256(off + mfma_table_bytes(s.H, s.d));
+        p.off_mfma_lam = off;
+        off = align256(off + mfma_lam_bytes(s.H, s.d));
+    }
     p.bytes = off;
     return p;
+}
+
+// The matrix-core path streams 16-byte pieces of 8 channels: it needs aligned
+// activation rows.
+static bool mfma_aligned(const PrefillArgs &a) {
+    const int esz = a.s.act == kBF16 ? 2 : 4;
+    auto al16 = [](const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) % 16) == 0; };
+    return al16(a.q) && al16(a.k) && al16(a.v) && al16(a.y) && (a.ld_in * esz) % 16 == 0 &&
+           (a.ld_y * esz) % 16 == 0;
 }
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
@@ -576,6 +600,10 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
         carry_scan_kernel<<<dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         carry0 = a.state_in ? reinterpret_cast<const float2 *>(a.ws + a.plan.off_carry) : nullptr;
+    }
+    if (a.plan.algo == kAlgoMfma && mfma_aligned(a)) {
+        if ((err = launch_mfma_tables(a, stream)) != hipSuccess) return err;
+        return launch_chunk_mfma(a, carry0, stream);
     }
     return s.act == kBF16 ? launch_scan<kBF16>(a, carry0, stream) : launch_scan<kF32>(a, carry0, stream);
 }

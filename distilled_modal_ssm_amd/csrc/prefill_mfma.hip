@@ -1,0 +1,494 @@
+// prefill_mfma.hip -- prompt processing of the modal Hyena operator on the
+// matrix cores (gfx950 MFMA), in sub-blocks of 64 steps.
+//
+// For a sub-block of 64 steps entering with state X (complex, d modes per
+// channel), with u_j = k_j v_j:
+//     y_i = q_i ( sum_{j<=i} h[i-j] u_j + Re sum_n R_n lambda_n^i X_n )      i < 64
+//     X'  = lambda^64 X + sum_j lambda^(63-j) u_j
+// (h[0] = D, h[m] = Re sum_n R_n lambda_n^(m-1)).  This is the causal long
+// convolution y = q (h conv (k v)) of the StripedHyena article ("Hyena層次結構")
+// cut at sub-block boundaries: the part inside the sub-block is a 64x64 causal
+// Toeplitz product, the part from before it reaches the sub-block through the
+// modal state.  Per head, all three matrices -- T (64x64 Toeplitz of h), C
+// (64 x 2d readout rows Re/-Im of R lambda^i) and V (2d x 64 Vandermonde rows
+// Re/Im of lambda^(63-j)) -- are shared by every channel and batch row (weight
+// tying, Laughing Hyena Distillery review, "提出的方法"), so
+//     Y = T U + C X,      S = V U,      X' = lambda^64 (.) X + S
+// are dense GEMMs with N = channels.  They run as bf16 16x16x32 MFMAs with every
+// operand split into a high and a low bfloat16 part (hi*hi + hi*lo + lo*hi,
+// float32 accumulation, ~16 significant bits per product).  The state stays in
+// float32 registers from sub-block to sub-block.
+//
+// Work per element: 2*(64 + 4*D2) flops on the matrix cores (x3 for the split);
+// the kernel is bound by streaming q, k, v and y through HBM.
+//
+// Workgroup: one (batch row, head, tile of PT channels, chunk), 4 waves of PT/4
+// channels each.  Per sub-block: q, k, v for 64 steps x PT channels are loaded
+// one sub-block ahead (contiguous 16-byte pieces), u = k v is split and
+// transposed into LDS ([channel][step], the MFMA B operand), q goes to an LDS
+// tile that becomes the y tile after gating, and y is written back as whole
+// row pieces.  Per-head table fragments (in A-operand lane order) sit in LDS.
+#include "hm_internal.hpp"
+
+namespace hm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma(const uint4 a, const uint4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                    c, 0, 0, 0);
+}
+
+// hi*hi + hi*lo + lo*hi
+__device__ __forceinline__ f32x4 mfma3(const uint4 ah, const uint4 al, const uint4 bh, const uint4 bl, f32x4 c) {
+    c = mfma(ah, bh, c);
+    c = mfma(ah, bl, c);
+    return mfma(al, bh, c);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return f32_to_bf16(x); }
+__device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
+
+// lambda^e in float64 from the polar form
+__device__ inline void polar_pow(double lr, double li, double e, double &re, double &im) {
+    if (e == 0.0) {
+        re = 1.0;
+        im = 0.0;
+        return;
+    }
+    const double mag = exp(e * log(hypot(lr, li)));
+    double s, c;
+    sincos(e * atan2(li, lr), &s, &c);
+    re = mag * c;
+    im = mag * s;
+}
+
+// ------------------------------------------------------------------ tables
+
+// One workgroup per head.  Fragment f of the head, lane l, holds the eight
+// A-operand values of that lane (row l%16 of the tile, k 8*(l/16)..+7):
+//   f in [0, 8)            T tile (mt = f/2, kk = f%2): T[i][j] = h[i-j], j <= i
+//   f in [8, 8+4KC)        C tile (mt, kc): C[i][2n] = Re(R_n lam_n^i), C[i][2n+1] = -Im(R_n lam_n^i)
+//   f in [8+4KC, NFRAG)    V tile (ms, kk): V[2n][j] = Re lam_n^(63-j), V[2n+1][j] = Im lam_n^(63-j)
+// stored as [head][f][hi, lo][lane] uint4; also lam64[head][D2/2] = lambda^64.
+template <int DD>
+__global__ __launch_bounds__(256) void mfma_tables_kernel(OpShape s, uint4 *frag, float2 *lam64) {
+    using G = MfmaGeom<DD>;
+    constexpr int D2 = G::D2, KC = G::KC, NFRAG = G::NFRAG;
+    __shared__ double pr[65 * DD], pi[65 * DD];  // lambda_n^i, i <= 64
+    __shared__ double hh[kSubBlock];
+    const int g = blockIdx.x, tid = threadIdx.x;
+    for (int idx = tid; idx < 65 * DD; idx += 256) {
+        const int i = idx / DD, n = idx % DD;
+        const float2 l = s.poles[(int64_t)g * DD + n];
+        polar_pow(l.x, l.y, (double)i, pr[idx], pi[idx]);
+    }
+    __syncthreads();
+    for (int m = tid; m < kSubBlock; m += 256) {
+        double acc = 0.0;
+        if (m == 0) {
+            acc = s.skip[g];
+        } else {
+            for (int n = 0; n < DD; ++n) {
+                const float2 r = s.residues[(int64_t)g * DD + n];
+                acc += (double)r.x * pr[(m - 1) * DD + n] - (double)r.y * pi[(m - 1) * DD + n];
+            }
+        }
+        hh[m] = acc;
+    }
+    if (tid < D2 / 2)
+        lam64[g * (D2 / 2) + tid] =
+            tid < DD ? make_float2((float)pr[64 * DD + tid], (float)pi[64 * DD + tid]) : make_float2(0.f, 0.f);
+    __syncthreads();
+    for (int idx = tid; idx < NFRAG * kWave; idx += 256) {
+        const int f = idx / kWave, l = idx % kWave;
+        const int r16 = l % 16, k8 = 8 * (l / 16);
+        uint32_t hi[8], lo[8];
+        for (int e = 0; e < 8; ++e) {
+            double v = 0.0;
+            if (f < 8) {
+                const int i = 16 * (f / 2) + r16, j = 32 * (f % 2) + k8 + e;
+                v = (j <= i) ? hh[i - j] : 0.0;
+            } else if (f < 8 + 4 * KC) {
+                const int f2 = f - 8, i = 16 * (f2 / KC) + r16, k = 32 * (f2 % KC) + k8 + e, n = k / 2;
+                if (n < DD) {
+                    const float2 r = s.residues[(int64_t)g * DD + n];
+                    const double a = pr[i * DD + n], b = pi[i * DD + n];
+                    v = (k % 2 == 0) ? ((double)r.x * a - (double)r.y * b) : -((double)r.x * b + (double)r.y * a);
+                }
+            } else {
+                const int f3 = f - 8 - 4 * KC, row = 16 * (f3 / 2) + r16, j = 32 * (f3 % 2) + k8 + e, n = row / 2;
+                if (n < DD) v = (row % 2 == 0) ? pr[(63 - j) * DD + n] : pi[(63 - j) * DD + n];
+            }
+            const float vf = (float)v;
+            hi[e] = bf16_bits(vf);
+            lo[e] = bf16_bits(vf - bf16_val(hi[e]));
+        }
+        uint4 *o = frag + ((int64_t)(g * NFRAG + f) * 2) * kWave + l;
+        o[0] = make_uint4(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16, hi[6] | hi[7] << 16);
+        o[kWave] = make_uint4(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16, lo[6] | lo[7] << 16);
+    }
+}
+
+// ------------------------------------------------------------------ sub-block kernel
+
+template <int ACT> struct Piece;  // 8 consecutive channels of one row
+template <> struct Piece<kBF16> {
+    uint4 w;
+    __device__ void load(const void *p) { w = *reinterpret_cast<const uint4 *>(p); }
+    __device__ float get(int e) const {
+        const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+        return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
+    }
+};
+template <> struct Piece<kF32> {
+    float4 a, b;
+    __device__ void load(const void *p) {
+        a = reinterpret_cast<const float4 *>(p)[0];
+        b = reinterpret_cast<const float4 *>(p)[1];
+    }
+    __device__ float get(int e) const {
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        return v[e];
+    }
+};
+
+__device__ __forceinline__ void store8(uint16_t *p, const float *v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = bf16_bits(v[2 * e]) | (bf16_bits(v[2 * e + 1]) << 16);
+    *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+__device__ __forceinline__ void store8(float *p, const float *v) {
+    reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+template <int DD, int PT, int ACT>
+__global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const float2 *carry0) {
+    using G = MfmaGeom<DD>;
+    using T = typename Act<ACT>::T;
+    constexpr int D2 = G::D2, KC = G::KC, MTS = G::MTS, NFRAG = G::NFRAG;
+    constexpr int CW = PT / 4, NTW = CW / 16;  // channels and 16-wide tiles per wave
+    constexpr int RG = PT / 32;                // staging rows per thread
+    constexpr int CG = PT / 8;                 // 8-channel groups per row
+    constexpr int LU = kSubBlock + 8;          // LDS row of u (bf16), per channel
+    constexpr int LX = D2 + 8;                 // LDS row of x (bf16), per channel
+    constexpr int LQ = PT + 4;                 // LDS row of q / y (float), per step
+    static_assert((64 / RG) * CG == 256, "one staging piece group per thread");
+
+    __shared__ uint4 tab[NFRAG * 2 * kWave];
+    __shared__ __attribute__((aligned(16))) uint16_t uhi[PT * LU];
+    __shared__ __attribute__((aligned(16))) uint16_t ulo[PT * LU];
+    __shared__ __attribute__((aligned(16))) uint16_t xhi[PT * LX];
+    __shared__ __attribute__((aligned(16))) uint16_t xlo[PT * LX];
+    __shared__ __attribute__((aligned(16))) float qy[kSubBlock * LQ];
+    __shared__ float2 lamT[D2 / 2];
+
+    const OpShape &s = a.s;
+    const int64_t P = s.P, H = s.H, L = a.plan.L, Tc = a.plan.T;
+    const int ntile = (int)(P / PT);
+    const int g = blockIdx.x / ntile, ct = blockIdx.x % ntile;
+    const int64_t c = blockIdx.y, b = blockIdx.z;
+    const int64_t p0 = (int64_t)ct * PT;
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int cw = w * CW;  // first local channel of this wave
+
+    // per-head tables -> LDS
+    {
+        const uint4 *gt = reinterpret_cast<const uint4 *>(a.ws + a.plan.off_mfma_tab) + (int64_t)g * NFRAG * 2 * kWave;
+        for (int i = tid; i < NFRAG * 2 * kWave; i += 256) tab[i] = gt[i];
+        if (tid < D2 / 2)
+            lamT[tid] = reinterpret_cast<const float2 *>(a.ws + a.plan.off_mfma_lam)[(int64_t)g * (D2 / 2) + tid];
+    }
+
+    // entering state in C-tile layout: Xr[ms][j] holds mode rows 16ms + 4(l/16) + 0..3
+    // (modes 8ms + 2(l/16) and +1, Re/Im interleaved) of channel cw + 16j + l%16
+    f32x4 Xr[MTS][NTW];
+    {
+        const float2 *src = (c == 0) ? carry0
+                                     : reinterpret_cast<const float2 *>(a.ws + a.plan.off_carry) +
+                                           c * (s.B * H * DD * P);
+#pragma unroll
+        for (int ms = 0; ms < MTS; ++ms)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int64_t p = p0 + cw + 16 * j + lane % 16;
+                const int n0 = 8 * ms + 2 * (lane / 16);
+                float2 x0 = make_float2(0.f, 0.f), x1 = make_float2(0.f, 0.f);
+                if (src && n0 < DD) x0 = src[((b * H + g) * DD + n0) * P + p];
+                if (src && n0 + 1 < DD) x1 = src[((b * H + g) * DD + n0 + 1) * P + p];
+                Xr[ms][j] = f32x4{x0.x, x0.y, x1.x, x1.y};
+            }
+    }
+    auto write_x = [&]() {
+#pragma unroll
+        for (int ms = 0; ms < MTS; ++ms)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                uint32_t h[4], lo[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    h[r] = bf16_bits(Xr[ms][j][r]);
+                    lo[r] = bf16_bits(Xr[ms][j][r] - bf16_val(h[r]));
+                }
+                const int o = (cw + 16 * j + lane % 16) * LX + 16 * ms + 4 * (lane / 16);
+                *reinterpret_cast<uint2 *>(&xhi[o]) = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
+                *reinterpret_cast<uint2 *>(&xlo[o]) = make_uint2(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16);
+            }
+    };
+    write_x();
+
+    // staging role: RG rows x 8 channels
+    const int cg = tid % CG, rg = tid / CG;
+    const int64_t ch0 = (int64_t)g * P + p0 + 8 * cg;  // global channel of the piece
+    const int64_t t_begin = c * Tc;
+    const int nsteps = (int)(((L - t_begin) < Tc) ? (L - t_begin) : Tc);
+    const int nsb = (nsteps + kSubBlock - 1) / kSubBlock;
+    const T *qb = static_cast<const T *>(a.q) + (b * L + t_begin) * a.ld_in + ch0;
+    const T *kb = static_cast<const T *>(a.k) + (b * L + t_begin) * a.ld_in + ch0;
+    const T *vb = static_cast<const T *>(a.v) + (b * L + t_begin) * a.ld_in + ch0;
+    T *yb = static_cast<T *>(a.y) + (b * L + t_begin) * a.ld_y + ch0;
+
+    Piece<ACT> pq[RG], pk[RG], pv[RG];
+    auto load = [&](int sb) {
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            int row = sb * kSubBlock + rg * RG + r;
+            row = row < nsteps ? row : nsteps - 1;  // clamped; rows past the prompt are masked in staging
+            const int64_t o = (int64_t)row * a.ld_in;
+            pq[r].load(qb + o);
+            pk[r].load(kb + o);
+            pv[r].load(vb + o);
+        }
+    };
+
+    load(0);
+    for (int sb = 0; sb < nsb; ++sb) {
+        const int nv = (nsteps - sb * kSubBlock < kSubBlock) ? nsteps - sb * kSubBlock : kSubBlock;
+        __syncthreads();  // previous sub-block's LDS tiles fully consumed
+        // ---- stage: u = k v split into hi/lo, transposed to [channel][step]; q to [step][channel]
+        {
+            float uu[RG][8];
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                const int row = rg * RG + r;
+                const bool valid = row < nv;
+                float qv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uu[r][e] = valid ? pk[r].get(e) * pv[r].get(e) : 0.f;
+                    qv[e] = valid ? pq[r].get(e) : 0.f;
+                }
+                store8(&qy[row * LQ + 8 * cg], qv);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                uint32_t h[RG], lo[RG];
+#pragma unroll
+                for (int r = 0; r < RG; ++r) {
+                    h[r] = bf16_bits(uu[r][e]);
+                    lo[r] = bf16_bits(uu[r][e] - bf16_val(h[r]));
+                }
+                const int o = (8 * cg + e) * LU + rg * RG;
+                if constexpr (RG == 4) {
+                    *reinterpret_cast<uint2 *>(&uhi[o]) = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
+                    *reinterpret_cast<uint2 *>(&ulo[o]) = make_uint2(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16);
+                } else {
+                    *reinterpret_cast<uint32_t *>(&uhi[o]) = h[0] | h[1] << 16;
+                    *reinterpret_cast<uint32_t *>(&ulo[o]) = lo[0] | lo[1] << 16;
+                }
+            }
+        }
+        if (sb + 1 < nsb) load(sb + 1);  // next sub-block in flight during the products
+        __syncthreads();
+
+        // ---- products
+        f32x4 Y[4][NTW], S[MTS][NTW];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) Y[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < MTS; ++i)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) S[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            uint4 bh[NTW], bl[NTW];
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int o = (cw + 16 * j + lane % 16) * LU + 32 * kk + 8 * (lane / 16);
+                bh[j] = *reinterpret_cast<const uint4 *>(&uhi[o]);
+                bl[j] = *reinterpret_cast<const uint4 *>(&ulo[o]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int f = mt * 2 + kk;
+                const uint4 ah = tab[(f * 2) * kWave + lane], al = tab[(f * 2 + 1) * kWave + lane];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) Y[mt][j] = mfma3(ah, al, bh[j], bl[j], Y[mt][j]);
+            }
+#pragma unroll
+            for (int ms = 0; ms < MTS; ++ms) {
+                const int f = 8 + 4 * KC + ms * 2 + kk;
+                const uint4 ah = tab[(f * 2) * kWave + lane], al = tab[(f * 2 + 1) * kWave + lane];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) S[ms][j] = mfma3(ah, al, bh[j], bl[j], S[ms][j]);
+            }
+        }
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            uint4 xh[NTW], xl[NTW];
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int o = (cw + 16 * j + lane % 16) * LX + 32 * kc + 8 * (lane / 16);
+                xh[j] = *reinterpret_cast<const uint4 *>(&xhi[o]);
+                xl[j] = *reinterpret_cast<const uint4 *>(&xlo[o]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                const int f = 8 + mt * KC + kc;
+                const uint4 ah = tab[(f * 2) * kWave + lane], al = tab[(f * 2 + 1) * kWave + lane];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) Y[mt][j] = mfma3(ah, al, xh[j], xl[j], Y[mt][j]);
+            }
+        }
+
+        // ---- gate: y = q * Y in place of q (each element read and written by one lane)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int o = (16 * mt + 4 * (lane / 16) + r) * LQ + cw + 16 * j + lane % 16;
+                    qy[o] = qy[o] * Y[mt][j][r];
+                }
+
+        // ---- state hand-off
+        if (nv == kSubBlock) {
+#pragma unroll
+            for (int ms = 0; ms < MTS; ++ms)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; ++q2) {
+                        const float2 lt = lamT[8 * ms + 2 * (lane / 16) + q2];
+                        const float xr = Xr[ms][j][2 * q2], xi = Xr[ms][j][2 * q2 + 1];
+                        Xr[ms][j][2 * q2] = fmaf(lt.x, xr, fmaf(-lt.y, xi, S[ms][j][2 * q2]));
+                        Xr[ms][j][2 * q2 + 1] = fmaf(lt.x, xi, fmaf(lt.y, xr, S[ms][j][2 * q2 + 1]));
+                    }
+            write_x();
+        } else {
+            // ragged final sub-block (end of the prompt): step the recurrence
+            // over its nv steps on the vector ALUs, from u = hi + lo in LDS
+#pragma unroll
+            for (int ms = 0; ms < MTS; ++ms)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                    for (int q2 = 0; q2 < 2; ++q2) {
+                        const int n = 8 * ms + 2 * (lane / 16) + q2;
+                        if (n >= DD) continue;
+                        const float2 l = s.poles[(int64_t)g * DD + n];
+                        float xr = Xr[ms][j][2 * q2], xi = Xr[ms][j][2 * q2 + 1];
+                        const int ub = (cw + 16 * j + lane % 16) * LU;
+                        for (int t = 0; t < nv; ++t) {
+                            const float u = bf16_val(uhi[ub + t]) + bf16_val(ulo[ub + t]);
+                            const float nr = fmaf(l.x, xr, fmaf(-l.y, xi, u));
+                            xi = fmaf(l.x, xi, l.y * xr);
+                            xr = nr;
+                        }
+                        Xr[ms][j][2 * q2] = xr;
+                        Xr[ms][j][2 * q2 + 1] = xi;
+                    }
+        }
+        __syncthreads();
+
+        // ---- y tile -> memory, whole 8-channel pieces of valid rows
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+            const int row = rg * RG + r;
+            if (row < nv) {
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = qy[row * LQ + 8 * cg + e];
+                store8(reinterpret_cast<T *>(yb + (int64_t)(sb * kSubBlock + row) * a.ld_y), v);
+            }
+        }
+    }
+
+    if (c == a.plan.NC - 1) {
+#pragma unroll
+        for (int ms = 0; ms < MTS; ++ms)
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const int64_t p = p0 + cw + 16 * j + lane % 16;
+                const int n0 = 8 * ms + 2 * (lane / 16);
+                float2 *dst = a.state_out + ((b * H + g) * DD) * P + p;
+                if (n0 < DD) dst[(int64_t)n0 * P] = make_float2(Xr[ms][j][0], Xr[ms][j][1]);
+                if (n0 + 1 < DD) dst[(int64_t)(n0 + 1) * P] = make_float2(Xr[ms][j][2], Xr[ms][j][3]);
+            }
+    }
+}
+
+template <int DD, int PT>
+hipError_t launch_dd(const PrefillArgs &a, const float2 *carry0, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.s.H * (a.s.P / PT)), (unsigned)a.plan.NC, (unsigned)a.s.B);
+    if (a.s.act == kBF16)
+        chunk_mfma_kernel<DD, PT, kBF16><<<grid, dim3(256), 0, stream>>>(a, carry0);
+    else
+        chunk_mfma_kernel<DD, PT, kF32><<<grid, dim3(256), 0, stream>>>(a, carry0);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// 64-channel tiles: on MI355X two 64-channel workgroups per CU (d <= 16) stream
+// faster than one 128-channel workgroup.
+int mfma_channel_tile(int64_t d, int64_t P) {
+    if (d != 8 && d != 16 && d != 32) return 0;
+    return (P % 64 == 0) ? 64 : 0;
+}
+
+size_t mfma_table_bytes(int64_t H, int64_t d) {
+    switch (d) {
+        case 8: return (size_t)H * MfmaGeom<8>::NFRAG * 2 * kWave * 16;
+        case 16: return (size_t)H * MfmaGeom<16>::NFRAG * 2 * kWave * 16;
+        case 32: return (size_t)H * MfmaGeom<32>::NFRAG * 2 * kWave * 16;
+        default: return 0;
+    }
+}
+
+size_t mfma_lam_bytes(int64_t H, int64_t d) {
+    const int64_t d2 = (2 * d < 32) ? 32 : 2 * d;
+    return (size_t)H * (d2 / 2) * sizeof(float2);
+}
+
+hipError_t launch_mfma_tables(const PrefillArgs &a, hipStream_t stream) {
+    uint4 *frag = reinterpret_cast<uint4 *>(a.ws + a.plan.off_mfma_tab);
+    float2 *lam = reinterpret_cast<float2 *>(a.ws + a.plan.off_mfma_lam);
+    const dim3 grid((unsigned)a.s.H), block(256);
+    switch (a.s.d) {
+        case 8: mfma_tables_kernel<8><<<grid, block, 0, stream>>>(a.s, frag, lam); break;
+        case 16: mfma_tables_kernel<16><<<grid, block, 0, stream>>>(a.s, frag, lam); break;
+        case 32: mfma_tables_kernel<32><<<grid, block, 0, stream>>>(a.s, frag, lam); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_mfma(const PrefillArgs &a, const float2 *carry0, hipStream_t stream) {
+    if (mfma_channel_tile(a.s.d, a.s.P) != 64) return hipErrorInvalidValue;
+    switch (a.s.d) {
+        case 8: return launch_dd<8, 64>(a, carry0, stream);
+        case 16: return launch_dd<16, 64>(a, carry0, stream);
+        case 32: return launch_dd<32, 64>(a, carry0, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace hm

@@ -116,21 +116,64 @@ hm_status hyena_modal_prefill(const hm_desc *desc, int64_t L,
                               const float *state_in, float *state_out,
                               void *workspace, size_t ws_bytes, void *stream);
 
-/*
- * The same prefill with an explicit chunk length (a positive multiple of 64;
- * 0 = automatic, as hyena_modal_prefill).  The chunk length changes how the
- * prompt is split across the GPU, never the result beyond float32 rounding.
- * Workspace size for it: hyena_modal_prefill_workspace_chunked.
- */
-hm_status hyena_modal_prefill_chunked(const hm_desc *desc, int64_t L,
-                                      const void *q, const void *k, const void *v, int64_t ld_in,
-                                      void *y, int64_t ld_y,
-                                      const float *state_in, float *state_out,
-                                      void *workspace, size_t ws_bytes, int64_t chunk,
-                                      void *stream);
+/* Prefill options.  Zero-initialised options (or a NULL pointer) mean automatic. */
+typedef enum hm_prefill_algo {
+    HM_PREFILL_AUTO = 0, /* matrix-core sub-blocks when eligible, else the vector scan */
+    HM_PREFILL_SCAN = 1, /* per-lane modal scan on the vector ALUs, any shape */
+    HM_PREFILL_MFMA = 2  /* 64-step sub-blocks on the matrix cores: d in {8,16,32},
+                            D/H a multiple of 64, 16-byte aligned activation rows;
+                            otherwise HM_ERR_UNSUPPORTED */
+} hm_prefill_algo;
 
-hm_status hyena_modal_prefill_workspace_chunked(const hm_desc *desc, int64_t L, int64_t chunk,
-                                                size_t *bytes);
+typedef struct hm_prefill_opts {
+    int64_t chunk; /* prompt chunk length: a positive multiple of 64, or 0 = automatic */
+    int32_t algo;  /* hm_prefill_algo */
+    int32_t reserved;
+} hm_prefill_opts;
+
+/*
+ * The same prefill with options: the chunk length (how the prompt is split
+ * across the GPU) and the in-chunk algorithm.  Neither changes the result
+ * beyond float32 rounding.  Workspace size: hyena_modal_prefill_workspace_ex
+ * with the same options.
+ *
+ * In-chunk algorithms.  HM_PREFILL_SCAN runs the recurrence lane by lane.
+ * HM_PREFILL_MFMA cuts each chunk into 64-step sub-blocks; inside one, the
+ * convolution is a 64x64 causal Toeplitz product with the filter taps, the
+ * history enters through the modal state (readout rows Re(R lambda^i)), and the
+ * state moves on with a 64-column Vandermonde product -- all three per-head
+ * matrices shared by the head's channels (weight tying, Laughing Hyena
+ * Distillery review, "提出的方法"), so they run on the matrix cores.
+ */
+hm_status hyena_modal_prefill_ex(const hm_desc *desc, int64_t L,
+                                 const void *q, const void *k, const void *v, int64_t ld_in,
+                                 void *y, int64_t ld_y,
+                                 const float *state_in, float *state_out,
+                                 void *workspace, size_t ws_bytes,
+                                 const hm_prefill_opts *opts, void *stream);
+
+hm_status hyena_modal_prefill_workspace_ex(const hm_desc *desc, int64_t L,
+                                           const hm_prefill_opts *opts, size_t *bytes);
+
+/*
+ * What a prefill with these options would run, computed on the host only (no
+ * GPU call): the in-chunk algorithm (HM_PREFILL_SCAN or HM_PREFILL_MFMA, never
+ * AUTO), the chunk length, the number of chunks the prompt is cut into, and the
+ * workspace size.  The answer assumes 16-byte aligned activation rows; with
+ * unaligned rows an AUTO prefill falls back to the scan.  opts may be NULL
+ * (defaults).  HM_ERR_UNSUPPORTED when HM_PREFILL_MFMA is asked for a shape it
+ * does not cover; other errors as for the workspace query.
+ */
+typedef struct hm_prefill_info {
+    int32_t algo;           /* hm_prefill_algo that runs */
+    int32_t reserved;       /* 0 */
+    int64_t chunk;          /* chunk length in steps (L when the prompt is one chunk; 0 when L = 0) */
+    int64_t n_chunks;       /* number of chunks (0 when L = 0) */
+    size_t workspace_bytes; /* as hyena_modal_prefill_workspace_ex */
+} hm_prefill_info;
+
+hm_status hyena_modal_prefill_plan(const hm_desc *desc, int64_t L, const hm_prefill_opts *opts,
+                                   hm_prefill_info *info);
 
 /*
  * One generation step for every batch row: reads the state before updating it,

@@ -87,12 +87,12 @@ def test_prefill_argument_errors(lib):
     ok = dict(q=FAKE, k=FAKE, v=FAKE, ld_in=64, y=FAKE, ld_y=64, state_in=None, state_out=FAKE,
               workspace=FAKE, ws_bytes=ws)
 
-    def call(L=4096, chunk=0, **kw):
+    def call(L=4096, chunk=0, algo="auto", **kw):
         a = dict(ok)
         a.update(kw)
         hb.hyena_modal_prefill(d, L, a["q"], a["k"], a["v"], a["ld_in"], a["y"], a["ld_y"],
                                a["state_in"], a["state_out"], a["workspace"], a["ws_bytes"], stream=0,
-                               chunk=chunk)
+                               chunk=chunk, algo=algo)
 
     cases = [
         (dict(L=-1), hb.HM_ERR_INVALID_ARG),
@@ -107,6 +107,8 @@ def test_prefill_argument_errors(lib):
         (dict(workspace=FAKE + 16), hb.HM_ERR_UNSUPPORTED),    # workspace must be 256-B aligned
         (dict(chunk=100), hb.HM_ERR_UNSUPPORTED),              # chunk not a multiple of 64
         (dict(chunk=-64), hb.HM_ERR_INVALID_ARG),
+        (dict(algo=7), hb.HM_ERR_INVALID_ARG),                 # unknown algorithm
+        (dict(algo="mfma"), hb.HM_ERR_UNSUPPORTED),            # head dim 16: no matrix-core path
     ]
     for kw, status in cases:
         with pytest.raises(hb.HMError) as e:
@@ -125,12 +127,44 @@ def test_no_work_calls_succeed_without_gpu(lib):
 
 def test_workspace_sizes_follow_the_chunk_plan(lib):
     d = _desc(batch=4, channels=4096, heads=32, modes=32)
-    # a single chunk needs no workspace
-    assert hb.hyena_modal_prefill_workspace(d, 4096, chunk=4096) == 0
-    big = hb.hyena_modal_prefill_workspace(d, 65536, chunk=2048)
+    # a single chunk needs no workspace on the vector scan, only tables on the matrix cores
+    assert hb.hyena_modal_prefill_workspace(d, 4096, chunk=4096, algo="scan") == 0
+    tab = hb.hyena_modal_prefill_workspace(d, 4096, chunk=4096, algo="mfma")
+    assert 0 < tab < 4 << 20
+    big = hb.hyena_modal_prefill_workspace(d, 65536, chunk=2048, algo="scan")
     # 32 chunk-state slots of B*D*d complex64 dominate
     assert big >= 32 * 4 * 4096 * 32 * 8
-    assert hb.hyena_modal_prefill_workspace(d, 65536, chunk=4096) < big
+    assert hb.hyena_modal_prefill_workspace(d, 65536, chunk=4096, algo="scan") < big
+
+
+def test_prefill_plan_choices(lib):
+    """The host-side plan: matrix cores for d in {8,16,32} with 64-channel heads,
+    one chunk when batch x heads x tiles cover the CUs, the scan otherwise."""
+    w2 = _desc(batch=16, channels=2048, heads=16, modes=16, act_dtype=hb.HM_BF16)
+    p = hb.hyena_modal_prefill_plan(w2, 2048)
+    assert p["algo"] == "mfma" and p["n_chunks"] == 1 and p["chunk"] == 2048
+    assert p["workspace_bytes"] == hb.hyena_modal_prefill_workspace(w2, 2048)
+    # a single batch row over 4 heads: the prompt is cut into 64-step multiples
+    few = _desc(batch=1, channels=256, heads=4, modes=8)
+    p = hb.hyena_modal_prefill_plan(few, 4096)
+    assert p["algo"] == "mfma" and p["n_chunks"] > 1 and p["chunk"] % 64 == 0
+    assert p["chunk"] * (p["n_chunks"] - 1) < 4096 <= p["chunk"] * p["n_chunks"]
+    # shapes outside the matrix-core path run the scan; asking for mfma is refused
+    for kw in (dict(modes=12), dict(modes=64), dict(channels=96, heads=4)):
+        d = _desc(**kw)
+        assert hb.hyena_modal_prefill_plan(d, 512)["algo"] == "scan"
+        with pytest.raises(hb.HMError) as e:
+            hb.hyena_modal_prefill_plan(d, 512, algo="mfma")
+        assert e.value.status == hb.HM_ERR_UNSUPPORTED
+    assert hb.hyena_modal_prefill_plan(w2, 2048, algo="scan")["algo"] == "scan"
+    p = hb.hyena_modal_prefill_plan(w2, 2048, chunk=256)
+    assert p["chunk"] == 256 and p["n_chunks"] == 8
+    p = hb.hyena_modal_prefill_plan(w2, 0)
+    assert p["chunk"] == 0 and p["n_chunks"] == 0
+    with pytest.raises(hb.HMError):
+        hb.hyena_modal_prefill_plan(w2, -1)
+    with pytest.raises(hb.HMError):
+        hb.hyena_modal_prefill_plan(w2, 2048, chunk=100)
 
 
 def test_decode_state_validation(lib):

@@ -101,8 +101,10 @@ def test_workload1_prefill_and_decode(chunk):
 # ------------------------------------------------------------------ full-size workloads, sampled
 
 
+@pytest.mark.parametrize("algo", ["auto", "scan"])
 @pytest.mark.parametrize("ci", [2, 3, 4])
-def test_workload_full_size_sampled(ci):
+def test_workload_full_size_sampled(ci, algo):
+    """Automatic (matrix-core sub-blocks for these shapes) and vector-scan prefill."""
     torch = require_gpu()
     cfg = get_config(ci)
     params = modal_params(cfg)
@@ -110,8 +112,11 @@ def test_workload_full_size_sampled(ci):
     inp = prompt_inputs(cfg)
     op = _op(params, cfg.B, cfg.D, cfg.act)
     q, k, v = (to_dev(inp[n], cfg.act) for n in "qkv")
-    log(f"workload {ci} prefill {cfg.describe()}")
-    y, st = op.prefill(q, k, v)
+    plan = op.plan(cfg.L, algo=algo)
+    # the automatic plan at these sizes is the matrix-core path the benchmark times
+    assert plan["algo"] == ("mfma" if algo == "auto" else "scan")
+    log(f"workload {ci} prefill {cfg.describe()} algo={algo} plan={plan}")
+    y, st = op.prefill(q, k, v, algo=algo)
     torch.cuda.synchronize()
     del q, k, v
     chans = _sample_channels(cfg, 28, 100 + ci)
@@ -125,7 +130,7 @@ def test_workload_full_size_sampled(ci):
     e_y = rel_err(y_gpu, y_or)
     st_gpu = state_for_channels(st, chans, cfg.P)[batches]
     e_s = rel_err(st_gpu, st_or)
-    print(f"workload {ci} prefill: y rel err {e_y:.3e}, state rel err {e_s:.3e}")
+    print(f"workload {ci} prefill ({algo}): y rel err {e_y:.3e}, state rel err {e_s:.3e}")
     assert e_y <= tol and e_s <= tol
     del y
 
@@ -152,23 +157,30 @@ def test_workload_full_size_sampled(ci):
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [
-    # (B, D, H, d, L, chunk)
-    (3, 36, 3, 5, 200, 64),      # odd head dim 12, generic mode count, ragged last chunk
-    (2, 16, 2, 1, 130, 64),      # one mode
-    (2, 128, 2, 64, 256, 128),   # largest mode count
-    (1, 64, 1, 8, 10, 0),        # prompt shorter than one chunk
-    (2, 256, 2, 16, 700, 64),    # many chunks, ragged
-    (1, 192, 3, 32, 320, 128),   # three heads of 64 (wave-uniform heads), d = 32
+    # (B, D, H, d, L, chunk, algo)
+    (3, 36, 3, 5, 200, 64, "auto"),      # odd head dim 12, generic mode count, ragged last chunk
+    (2, 16, 2, 1, 130, 64, "auto"),      # one mode
+    (2, 128, 2, 64, 256, 128, "auto"),   # largest mode count
+    (1, 64, 1, 8, 10, 0, "scan"),        # prompt shorter than one chunk
+    (2, 256, 2, 16, 700, 64, "scan"),    # many chunks, ragged
+    (1, 192, 3, 32, 320, 128, "scan"),   # three heads of 64 (wave-uniform heads), d = 32
+    (2, 256, 2, 16, 700, 64, "mfma"),    # matrix-core sub-blocks, many chunks, ragged last sub-block
+    (1, 192, 3, 32, 320, 128, "mfma"),   # 64-channel tiles, d = 32
+    (2, 256, 2, 8, 300, 0, "mfma"),      # d = 8 (mode rows padded to 32), one chunk, ragged
+    (1, 256, 4, 16, 130, 0, "mfma"),     # head dim 64 with d = 16 (64-channel tiles)
+    (3, 128, 1, 16, 10, 0, "mfma"),      # prompt shorter than one sub-block
+    (1, 128, 1, 32, 64, 0, "mfma"),      # exactly one sub-block
+    (2, 512, 4, 16, 1000, 256, "mfma"),  # several chunks of several sub-blocks
 ])
 def test_shapes_and_chunking(act, shape):
     torch = require_gpu()
-    B, D, H, d, L, chunk = shape
+    B, D, H, d, L, chunk, algo = shape
     rng = np.random.default_rng(hash(shape) % 2**32)
     params = _rand_params(rng, H, d)
     q_, k_, v_ = (_rand_act(rng, (B, L, D), act) for _ in range(3))
     op = _op(params, B, D, act)
     log(f"shape {shape} act {act}")
-    y, st = op.prefill(to_dev(q_, act), to_dev(k_, act), to_dev(v_, act), chunk=chunk)
+    y, st = op.prefill(to_dev(q_, act), to_dev(k_, act), to_dev(v_, act), chunk=chunk, algo=algo)
     torch.cuda.synchronize()
     y_or, st_or = oracle.modal_scan(params, q_, k_, v_)
     assert rel_err(to_np64(y), y_or) <= TOL[act]
@@ -203,6 +215,28 @@ def test_empty_prompt_and_empty_batch():
     assert y0.shape == (0, 5, 32)
 
 
+@pytest.mark.parametrize("algo", ["scan", "mfma"])
+@pytest.mark.parametrize("chunk", [0, 64])
+def test_prompt_continuation_matrix_core(chunk, algo):
+    """Continuation with a non-zero state_in on both in-chunk algorithms (head dim 128)."""
+    torch = require_gpu()
+    rng = np.random.default_rng(21 + chunk)
+    B, D, H, d, L, cut = 2, 256, 2, 16, 330, 137
+    params = _rand_params(rng, H, d, 0.8, 0.999)
+    q_, k_, v_ = (_rand_act(rng, (B, L, D), "f32") for _ in range(3))
+    q, k, v = (to_dev(a, "f32") for a in (q_, k_, v_))
+    op = _op(params, B, D, "f32")
+    log(f"continuation mfma/scan algo={algo} chunk={chunk}")
+    head = [t[:, :cut].contiguous() for t in (q, k, v)]
+    tail = [t[:, cut:].contiguous() for t in (q, k, v)]
+    y1, st1 = op.prefill(*head, chunk=chunk, algo=algo)
+    y2, st2 = op.prefill(*tail, state_in=st1, chunk=chunk, algo=algo)
+    torch.cuda.synchronize()
+    y_or, st_or = oracle.modal_scan(params, q_, k_, v_)
+    assert rel_err(np.concatenate([to_np64(y1), to_np64(y2)], 1), y_or) <= TOL["f32"]
+    assert rel_err(state_for_channels(st2, np.arange(D), D // H), st_or) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("chunk", [0, 64])
 def test_prompt_continuation_with_state_in(chunk):
     """prefill(a) then prefill(b, state_in) equals prefill(a + b); also in place."""
@@ -231,7 +265,8 @@ def test_prompt_continuation_with_state_in(chunk):
     assert rel_err(state_for_channels(st3, np.arange(cfg.D), cfg.P), st3_or) <= TOL["f32"]
 
 
-def test_fused_qkv_buffer_and_strided_output():
+@pytest.mark.parametrize("algo", ["scan", "mfma"])
+def test_fused_qkv_buffer_and_strided_output(algo):
     """q, k, v as thirds of one [B][L][3D] buffer; y written into a wider buffer."""
     torch = require_gpu()
     rng = np.random.default_rng(5)
@@ -242,7 +277,7 @@ def test_fused_qkv_buffer_and_strided_output():
     op = _op(params, B, D, "bf16")
     ybuf = torch.full((B, L, D + 64), 3.0, dtype=torch.bfloat16, device="cuda")
     log("fused qkv")
-    op.prefill(qkv[:, :, :D], qkv[:, :, D:2 * D], qkv[:, :, 2 * D:], y=ybuf[:, :, :D], chunk=64)
+    op.prefill(qkv[:, :, :D], qkv[:, :, D:2 * D], qkv[:, :, 2 * D:], y=ybuf[:, :, :D], chunk=64, algo=algo)
     torch.cuda.synchronize()
     y_or, _ = oracle.modal_scan(params, np.ascontiguousarray(qkv_np[:, :, :D]),
                                 np.ascontiguousarray(qkv_np[:, :, D:2 * D]),
@@ -297,8 +332,11 @@ def test_bitwise_determinism():
     log("determinism")
     y1, s1 = op.prefill(q, k, v)
     y2, s2 = op.prefill(q, k, v)
+    y3, s3 = op.prefill(q, k, v, algo="scan")
+    y4, s4 = op.prefill(q, k, v, algo="scan")
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(s1, s2)
+    assert torch.equal(y3, y4) and torch.equal(s3, s4)
     a1 = op.decode_step(q[:, 0], k[:, 0], v[:, 0], s1)
     a2 = op.decode_step(q[:, 0], k[:, 0], v[:, 0], s2)
     torch.cuda.synchronize()
