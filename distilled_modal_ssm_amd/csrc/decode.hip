@@ -8,9 +8,9 @@
 // the causal convolution with h[0] = D_g, h[t] = Re(sum_n R_gn lambda_gn^(t-1)).
 //
 // The step is a pure stream over the state (16 d bytes per channel read and
-// written) plus four activations, so it is bound by HBM bandwidth (or, for
-// small batches whose state stays in L2, by launch latency).  Layout and
-// mapping:
+// written) plus four activations, so it is bound by HBM bandwidth -- or, for
+// small batches, by the fixed cost of a dispatch (about 1.6 us per launch on
+// MI355X, graph-replayed) plus one memory round trip.  Layout and mapping:
 //   - the state is [B][H][d][P] complex float32, so for a fixed mode the lanes
 //     of a wave touch consecutive channels: each state access of a wave is one
 //     contiguous segment (1 KiB with two channels per lane);
@@ -18,9 +18,11 @@
 //     (16-byte state accesses); when a wave stays inside one head the head index
 //     is made wave-uniform and the pole/residue tables come through the scalar
 //     cache into SGPRs;
-//   - small batches (fewer than 64 K channels) or many modes: SPLIT adjacent
-//     lanes share a channel, DL modes each, so more waves carry the step; their
-//     partial readouts are summed with DPP.
+//   - d = 32: one lane per channel and all 32 modes when the batch holds fewer
+//     than 64 K channels (fewer, longer lanes finish sooner than split ones:
+//     measured on MI355X, B = 4, D = 4096), else SPLIT = 2 adjacent lanes share
+//     a channel with 16 modes each; d = 64: four lanes of 16 modes.  Partial
+//     readouts of a channel are summed with DPP.
 #include "hm_internal.hpp"
 
 namespace hm {
@@ -166,16 +168,14 @@ hipError_t launch_act(const DecodeArgs &a, hipStream_t stream) {
     const bool pair = (P % 2 == 0) && (a.ld_in % 2 == 0) && (a.ld_y % 2 == 0) &&
                       aligned(a.q, 2 * esz) && aligned(a.k, 2 * esz) && aligned(a.v, 2 * esz) &&
                       aligned(a.y, 2 * esz) && aligned(a.state, 16);
-    // fewer than ~64 K channels in the batch: split modes over lanes for parallelism
     const bool small = a.s.B * a.s.D < 65536;
     switch (d) {
         case 8:
             return pair ? launch_fixed<8, 1, 2, ACT>(a, stream) : launch_fixed<8, 1, 1, ACT>(a, stream);
         case 16:
-            if (small) return launch_fixed<8, 2, 1, ACT>(a, stream);
             return pair ? launch_fixed<16, 1, 2, ACT>(a, stream) : launch_fixed<16, 1, 1, ACT>(a, stream);
         case 32:
-            return small ? launch_fixed<8, 4, 1, ACT>(a, stream) : launch_fixed<16, 2, 1, ACT>(a, stream);
+            return small ? launch_fixed<32, 1, 1, ACT>(a, stream) : launch_fixed<16, 2, 1, ACT>(a, stream);
         case 64:
             return launch_fixed<16, 4, 1, ACT>(a, stream);
         default:

@@ -23,6 +23,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Two float32 -> a packed bfloat16 pair (a in the low half), round to nearest
+// even, in one v_cvt_pk_bf16_f32.
+typedef __bf16 hm_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float hm_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(hm_f32x2{a, b}, hm_bf16x2));
+}
+
 // Activation element access for float32 (ACT = kF32) or bfloat16 bit patterns.
 template <int ACT> struct Act;
 
@@ -47,7 +55,7 @@ template <> struct Act<kBF16> {
     }
     __device__ static void st(T *p, float x) { *p = (uint16_t)f32_to_bf16(x); }
     __device__ static void st2(T *p, float a, float b) {
-        *reinterpret_cast<uint32_t *>(p) = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+        *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(a, b);
     }
 };
 

@@ -25,9 +25,10 @@
 // Workgroup: one (batch row, head, tile of PT channels, chunk), 4 waves of PT/4
 // channels each.  Per sub-block: q, k, v for 64 steps x PT channels are loaded
 // one sub-block ahead (contiguous 16-byte pieces), u = k v is split and
-// transposed into LDS ([channel][step], the MFMA B operand), q goes to an LDS
-// tile that becomes the y tile after gating, and y is written back as whole
-// row pieces.  Per-head table fragments (in A-operand lane order) sit in LDS.
+// transposed into LDS ([channel][step], the MFMA B operand), q stays in the
+// loading thread's registers, the Y accumulators go to an LDS tile that the
+// loading threads read back to gate (y = q Y) and write out as whole row
+// pieces.  Per-head table fragments (in A-operand lane order) sit in LDS.
 #include "hm_internal.hpp"
 
 namespace hm {
@@ -80,10 +81,21 @@ __global__ __launch_bounds__(256) void mfma_tables_kernel(OpShape s, uint4 *frag
     __shared__ double pr[65 * DD], pi[65 * DD];  // lambda_n^i, i <= 64
     __shared__ double hh[kSubBlock];
     const int g = blockIdx.x, tid = threadIdx.x;
-    for (int idx = tid; idx < 65 * DD; idx += 256) {
-        const int i = idx / DD, n = idx % DD;
+    // lambda^i for i = 4 seg .. 4 seg + 3: the first from the polar form, the
+    // rest by float64 complex products (relative error ~1e-16 per product)
+    for (int idx = tid; idx < 17 * DD; idx += 256) {
+        const int seg = idx / DD, n = idx % DD;
         const float2 l = s.poles[(int64_t)g * DD + n];
-        polar_pow(l.x, l.y, (double)i, pr[idx], pi[idx]);
+        const double lr = l.x, li = l.y;
+        double re, im;
+        polar_pow(lr, li, (double)(4 * seg), re, im);
+        for (int k = 0; k < 4 && 4 * seg + k <= 64; ++k) {
+            pr[(4 * seg + k) * DD + n] = re;
+            pi[(4 * seg + k) * DD + n] = im;
+            const double nr = re * lr - im * li;
+            im = re * li + im * lr;
+            re = nr;
+        }
     }
     __syncthreads();
     for (int m = tid; m < kSubBlock; m += 256) {
@@ -158,13 +170,28 @@ template <> struct Piece<kF32> {
 __device__ __forceinline__ void store8(uint16_t *p, const float *v) {
     uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = bf16_bits(v[2 * e]) | (bf16_bits(v[2 * e + 1]) << 16);
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
     *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 __device__ __forceinline__ void store8(float *p, const float *v) {
     reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
     reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
+
+// LDS row of u for one channel: 64 steps in 16-byte units of 8 steps, the unit
+// order XOR-permuted by (ch ^ ch/8) mod 8.  With it neither the transposing
+// stores (8 channel groups x 8 step pairs per instruction) nor the MFMA operand
+// reads (16 consecutive channels per instruction) meet a bank conflict on the
+// 32 four-byte LDS banks.
+constexpr int kLU = kSubBlock;
+__device__ __forceinline__ int u_index(int ch, int t) {
+    return ch * kLU + ((((t >> 3) ^ ((ch ^ (ch >> 3)) & 7))) << 3) + (t & 7);
+}
+
+// Y tile [step][channel] (float, row stride PT + 4): channels 32..63 of a row
+// swap the halves of each 8-channel group, so the gating phase's 16-byte reads
+// (8 channel groups of one row per 8 lanes) fall on disjoint banks.
+__device__ __forceinline__ int yt_index(int row, int col, int ld) { return row * ld + (col ^ (((col >> 5) & 1) << 2)); }
 
 template <int DD, int PT, int ACT>
 __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const float2 *carry0) {
@@ -174,17 +201,17 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
     constexpr int CW = PT / 4, NTW = CW / 16;  // channels and 16-wide tiles per wave
     constexpr int RG = PT / 32;                // staging rows per thread
     constexpr int CG = PT / 8;                 // 8-channel groups per row
-    constexpr int LU = kSubBlock + 8;          // LDS row of u (bf16), per channel
     constexpr int LX = D2 + 8;                 // LDS row of x (bf16), per channel
-    constexpr int LQ = PT + 4;                 // LDS row of q / y (float), per step
+    constexpr int LQ = PT + 4;                 // LDS row of the Y tile (float), per step
+    static_assert(PT == 64, "staging writes two steps per 32-bit word");
     static_assert((64 / RG) * CG == 256, "one staging piece group per thread");
 
     __shared__ uint4 tab[NFRAG * 2 * kWave];
-    __shared__ __attribute__((aligned(16))) uint16_t uhi[PT * LU];
-    __shared__ __attribute__((aligned(16))) uint16_t ulo[PT * LU];
+    __shared__ __attribute__((aligned(16))) uint16_t uhi[PT * kLU];
+    __shared__ __attribute__((aligned(16))) uint16_t ulo[PT * kLU];
     __shared__ __attribute__((aligned(16))) uint16_t xhi[PT * LX];
     __shared__ __attribute__((aligned(16))) uint16_t xlo[PT * LX];
-    __shared__ __attribute__((aligned(16))) float qy[kSubBlock * LQ];
+    __shared__ __attribute__((aligned(16))) float yt[kSubBlock * LQ];
     __shared__ float2 lamT[D2 / 2];
 
     const OpShape &s = a.s;
@@ -228,15 +255,13 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
         for (int ms = 0; ms < MTS; ++ms)
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
-                uint32_t h[4], lo[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    h[r] = bf16_bits(Xr[ms][j][r]);
-                    lo[r] = bf16_bits(Xr[ms][j][r] - bf16_val(h[r]));
-                }
+                const f32x4 x = Xr[ms][j];
+                const uint32_t h01 = pack_bf16x2(x[0], x[1]), h23 = pack_bf16x2(x[2], x[3]);
+                const uint32_t l01 = pack_bf16x2(x[0] - bf16_lo(h01), x[1] - bf16_hi(h01));
+                const uint32_t l23 = pack_bf16x2(x[2] - bf16_lo(h23), x[3] - bf16_hi(h23));
                 const int o = (cw + 16 * j + lane % 16) * LX + 16 * ms + 4 * (lane / 16);
-                *reinterpret_cast<uint2 *>(&xhi[o]) = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
-                *reinterpret_cast<uint2 *>(&xlo[o]) = make_uint2(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16);
+                *reinterpret_cast<uint2 *>(&xhi[o]) = make_uint2(h01, h23);
+                *reinterpret_cast<uint2 *>(&xlo[o]) = make_uint2(l01, l23);
             }
     };
     write_x();
@@ -265,41 +290,32 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
         }
     };
 
+    // Two barriers per sub-block.  Between the second barrier of one sub-block
+    // and the first of the next, threads read the Y tile (written before the
+    // second) and write the u tiles (last read before the second), so the two
+    // phases touch disjoint LDS.
     load(0);
     for (int sb = 0; sb < nsb; ++sb) {
         const int nv = (nsteps - sb * kSubBlock < kSubBlock) ? nsteps - sb * kSubBlock : kSubBlock;
-        __syncthreads();  // previous sub-block's LDS tiles fully consumed
-        // ---- stage: u = k v split into hi/lo, transposed to [channel][step]; q to [step][channel]
+        // ---- stage: u = k v split into hi/lo, transposed to [channel][step]; q stays in registers
+        Piece<ACT> cq[RG];
+#pragma unroll
+        for (int r = 0; r < RG; ++r) cq[r] = pq[r];
         {
             float uu[RG][8];
 #pragma unroll
             for (int r = 0; r < RG; ++r) {
-                const int row = rg * RG + r;
-                const bool valid = row < nv;
-                float qv[8];
+                const bool valid = rg * RG + r < nv;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    uu[r][e] = valid ? pk[r].get(e) * pv[r].get(e) : 0.f;
-                    qv[e] = valid ? pq[r].get(e) : 0.f;
-                }
-                store8(&qy[row * LQ + 8 * cg], qv);
+                for (int e = 0; e < 8; ++e) uu[r][e] = valid ? pk[r].get(e) * pv[r].get(e) : 0.f;
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                uint32_t h[RG], lo[RG];
-#pragma unroll
-                for (int r = 0; r < RG; ++r) {
-                    h[r] = bf16_bits(uu[r][e]);
-                    lo[r] = bf16_bits(uu[r][e] - bf16_val(h[r]));
-                }
-                const int o = (8 * cg + e) * LU + rg * RG;
-                if constexpr (RG == 4) {
-                    *reinterpret_cast<uint2 *>(&uhi[o]) = make_uint2(h[0] | h[1] << 16, h[2] | h[3] << 16);
-                    *reinterpret_cast<uint2 *>(&ulo[o]) = make_uint2(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16);
-                } else {
-                    *reinterpret_cast<uint32_t *>(&uhi[o]) = h[0] | h[1] << 16;
-                    *reinterpret_cast<uint32_t *>(&ulo[o]) = lo[0] | lo[1] << 16;
-                }
+                const uint32_t h = pack_bf16x2(uu[0][e], uu[1][e]);
+                const uint32_t lo = pack_bf16x2(uu[0][e] - bf16_lo(h), uu[1][e] - bf16_hi(h));
+                const int o = u_index(8 * cg + e, rg * RG);
+                *reinterpret_cast<uint32_t *>(&uhi[o]) = h;
+                *reinterpret_cast<uint32_t *>(&ulo[o]) = lo;
             }
         }
         if (sb + 1 < nsb) load(sb + 1);  // next sub-block in flight during the products
@@ -320,7 +336,7 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
             uint4 bh[NTW], bl[NTW];
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
-                const int o = (cw + 16 * j + lane % 16) * LU + 32 * kk + 8 * (lane / 16);
+                const int o = u_index(cw + 16 * j + lane % 16, 32 * kk + 8 * (lane / 16));
                 bh[j] = *reinterpret_cast<const uint4 *>(&uhi[o]);
                 bl[j] = *reinterpret_cast<const uint4 *>(&ulo[o]);
             }
@@ -357,16 +373,14 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
             }
         }
 
-        // ---- gate: y = q * Y in place of q (each element read and written by one lane)
+        // ---- Y tile -> LDS ([step][channel])
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int o = (16 * mt + 4 * (lane / 16) + r) * LQ + cw + 16 * j + lane % 16;
-                    qy[o] = qy[o] * Y[mt][j][r];
-                }
+                for (int r = 0; r < 4; ++r)
+                    yt[yt_index(16 * mt + 4 * (lane / 16) + r, cw + 16 * j + lane % 16, LQ)] = Y[mt][j][r];
 
         // ---- state hand-off
         if (nv == kSubBlock) {
@@ -395,9 +409,10 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
                         if (n >= DD) continue;
                         const float2 l = s.poles[(int64_t)g * DD + n];
                         float xr = Xr[ms][j][2 * q2], xi = Xr[ms][j][2 * q2 + 1];
-                        const int ub = (cw + 16 * j + lane % 16) * LU;
+                        const int ch = cw + 16 * j + lane % 16;
                         for (int t = 0; t < nv; ++t) {
-                            const float u = bf16_val(uhi[ub + t]) + bf16_val(ulo[ub + t]);
+                            const int o = u_index(ch, t);
+                            const float u = bf16_val(uhi[o]) + bf16_val(ulo[o]);
                             const float nr = fmaf(l.x, xr, fmaf(-l.y, xi, u));
                             xi = fmaf(l.x, xi, l.y * xr);
                             xr = nr;
@@ -408,14 +423,17 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
         }
         __syncthreads();
 
-        // ---- y tile -> memory, whole 8-channel pieces of valid rows
+        // ---- gate y = q Y and store whole 8-channel pieces of valid rows
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
             const int row = rg * RG + r;
             if (row < nv) {
+                const float4 y0 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, 8 * cg, LQ)]);
+                const float4 y1 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, 8 * cg + 4, LQ)]);
+                const float yy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
                 float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = qy[row * LQ + 8 * cg + e];
+                for (int e = 0; e < 8; ++e) v[e] = cq[r].get(e) * yy[e];
                 store8(reinterpret_cast<T *>(yb + (int64_t)(sb * kSubBlock + row) * a.ld_y), v);
             }
         }
