@@ -22,6 +22,9 @@ oracle on this host's cores over the same workload (rank 0, N = 1 only).
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +38,125 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 VALU_F32_PEAK_TFLOPS = 78.6    # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, unpacked float32
+
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "distilled_modal_ssm_amd", "csrc")
+# Sources whose change invalidates a hardware-counter measurement of a kernel.
+KERNEL_SOURCES = {
+    "decode_step_fixed": ["decode.hip", "hm_internal.hpp", "hm_api.cpp"],
+    "chunk_mfma_kernel": ["prefill_mfma.hip", "prefill.hip", "hm_internal.hpp", "hm_api.cpp"],
+    "chunk_scan_kernel": ["prefill.hip", "hm_internal.hpp", "hm_api.cpp"],
+}
+COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read, 1 GiB written
+
+
+def kernel_fingerprint(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(kernel: str, workload: str) -> str:
+    return os.path.join(PROFILES, f"{kernel}.{workload}.traffic.txt")
+
+
+def read_traffic(kernel: str, workload: str):
+    """Counter-measured HBM bytes per launch of `kernel` on `workload`, from the
+    committed summary, or None when there is none or the kernel's sources have
+    changed since the counters were taken."""
+    p = traffic_path(kernel, workload)
+    if kernel not in KERNEL_SOURCES or not os.path.exists(p):
+        return None
+    kv = {}
+    with open(p) as fh:
+        for line in fh:
+            if ":" in line and not line[0].isspace() and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("fingerprint") != kernel_fingerprint(kernel):
+        return None
+    return int(kv["traffic_bytes_per_launch"])
+
+
+def calibration_copy():
+    """One plain device copy of COPY_BYTES (three times), run only for counter
+    collection: its FETCH_SIZE / WRITE_SIZE readings scale the kernel's."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _counter_rows(directory: str, counter: str):
+    rows = []
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {directory}")
+    return rows
+
+
+def write_traffic(args):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    of this benchmark with --calibrate-copy into the per-launch traffic summary."""
+    from workloads import get_config
+    cfg = get_config(args.config)
+    kernel = args.traffic_kernel
+    fetch_dir, write_dir = args.traffic_from
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, name)
+        k = np.array([float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]])
+        copies = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        if len(k) == 0 or not copies:
+            raise SystemExit(f"{name}: no dispatches of {kernel} or of the calibration copy in {d}")
+        cal = max(copies)  # the 1 GiB copy is by far the largest copy dispatch
+        factor = COPY_BYTES / (cal * 1024.0)
+        out[name] = dict(n=len(k), mean=k.mean(), lo=k.min(), hi=k.max(), copy_kib=cal, factor=factor,
+                         bytes=k.mean() * 1024.0 * factor)
+    sb = cfg.act_bytes
+    if kernel.startswith("decode"):
+        alg = cfg.B * cfg.D * (16 * cfg.d + 4 * sb)
+    else:
+        alg = 4 * sb * cfg.B * cfg.L * cfg.D + 8 * cfg.B * cfg.D * cfg.d
+    total = int(round(out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]))
+    cmd = args.traffic_cmd or "(commands not recorded)"
+    lines = [
+        f"# HBM traffic per launch of {kernel}, workload {cfg.name} ({cfg.describe()})",
+        "#",
+        "# Commands (repository root, one MI355X):",
+    ] + [f"#     {c}" for c in cmd.split(" ;; ")] + [
+        "#",
+        "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by",
+        f"# {COPY_BYTES} bytes / (what the same counter reads for a plain {COPY_BYTES >> 30} GiB device copy).",
+        "#",
+    ]
+    for name in ("FETCH_SIZE", "WRITE_SIZE"):
+        o = out[name]
+        lines.append(f"# {name}: {o['n']} dispatches, mean {o['mean']:.1f} KiB (min {o['lo']:.1f}, max {o['hi']:.1f}); "
+                     f"copy reads {o['copy_kib']:.1f} KiB -> factor {o['factor']:.4f} -> {o['bytes'] / 1e6:.3f} MB")
+    lines += [
+        "#",
+        f"kernel: {kernel}",
+        f"workload: {cfg.name}",
+        f"fingerprint: {kernel_fingerprint(kernel)}",
+        f"fetch_factor: {out['FETCH_SIZE']['factor']:.6f}",
+        f"write_factor: {out['WRITE_SIZE']['factor']:.6f}",
+        f"traffic_bytes_per_launch: {total}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_over_algorithmic: {total / alg:.4f}",
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    path = traffic_path(kernel, cfg.name)
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(open(path).read())
 
 
 def log(*a):
@@ -50,6 +172,12 @@ def parse():
     ap.add_argument("--decode-mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="no GPU: write the traffic summary of --traffic-kernel from two rocprofv3 --pmc runs")
+    ap.add_argument("--traffic-kernel", default="decode_step_fixed")
+    ap.add_argument("--traffic-cmd", default=None, help="the profiling commands, ' ;; '-separated, for the summary")
     return ap.parse_args()
 
 
@@ -199,6 +327,8 @@ def bench_stack(args, cfg, dev):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        return write_traffic(args)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
               "(the path shards by batch rows and heads with no communication; see the design notes)",
@@ -318,9 +448,13 @@ def main():
     dom = kernels[dom_name]
     scale = 1e-6 if dom["unit"] == "GB/s" else 1e-9  # bytes/ms -> GB/s ; flops/ms -> TFLOP/s
     achieved = dom["per_launch"] / dom["ms"] * scale
+    kname = "decode_step_fixed" if dom_name == "decode_step" else (
+        "chunk_mfma_kernel" if plan["algo"] == "mfma" else "chunk_scan_kernel")
     roofline = {"bound": dom["bound"], "achieved": round(achieved, 3), "peak": dom["peak"],
-                "unit": dom["unit"], "frac": round(achieved / dom["peak"], 4), "traffic": None,
-                "kernel": dom_name, "launch_ms": round(dom["ms"], 6)}
+                "unit": dom["unit"], "frac": round(achieved / dom["peak"], 4),
+                "traffic": read_traffic(kname, cfg.name),
+                "kernel": kname, "launch_ms": round(dom["ms"], 6),
+                "algorithmic_bytes_per_launch": decode_bytes if dom_name == "decode_step" else prefill_bytes}
 
     tokens = cfg.B * (cfg.L + cfg.S)
     res = {
@@ -353,6 +487,8 @@ def main():
         "wall_s_timed": t_wall,
         "roofline": roofline,
     }
+    if args.calibrate_copy:
+        calibration_copy()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (float64 oracle)")
         res["cpu_baseline"] = cpu_baseline(cfg, params, inp, dec)

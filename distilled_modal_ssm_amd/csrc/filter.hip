@@ -7,14 +7,16 @@
 // distillation objective is stated on filters, same review, "提出的方法").
 //
 // Accuracy: a pole radius can be 0.9999 and t reaches 64k, so powers are never
-// formed by a long float32 product.  Each thread owns a run of kRun consecutive
-// taps of one head; per mode it evaluates lambda^(t0-1) once from the polar form
-// in float64 (|lambda|^e = exp(e log|lambda|), angle e*arg(lambda)), then walks
-// the run by float64 complex multiplication and accumulates in float64.  Every
-// tap is rounded once to float32.
+// formed by a long float32 product.  One thread owns one mode of one run of
+// kRun consecutive taps of a head: it forms lambda^(t0-1) for the run's first
+// tap by binary powering in float64 (at most 2 log2(L) complex products,
+// relative error ~1e-15), walks the run by float64 complex multiplication, and
+// leaves Re(R lambda^(t-1)) per tap in LDS; the workgroup then sums the modes
+// of each tap in float64 and rounds it once to float32.
 //
-// Work is O(H L d) float64 FMAs (about 6 per tap and mode) and the output is
-// H*L*4 bytes; the kernel is small next to prefill.
+// Mapping: a workgroup is one head and 256/DPAD runs, DPAD = d rounded up to a
+// power of two (lanes n >= d idle), so H * L * DPAD / kRun threads carry the
+// O(H L d) float64 work (about 6 FMAs per tap and mode plus the powering).
 #include "hm_internal.hpp"
 
 namespace hm {
@@ -22,33 +24,44 @@ namespace {
 
 constexpr int kRun = 32;
 
+template <int DPAD>
 __global__ __launch_bounds__(256) void filter_kernel(FilterArgs a) {
+    constexpr int RPB = 256 / DPAD;  // runs per workgroup
+    constexpr int TPB = RPB * kRun;  // taps per workgroup
+    constexpr int LP = kRun + 1;     // LDS row (one run and mode), padded
+    __shared__ double part[RPB * DPAD * LP];
     const int64_t L = a.L, d = a.s.d;
-    const int64_t runs = (L + kRun - 1) / kRun;
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (tid >= a.s.H * runs) return;
-    const int64_t g = tid / runs;
-    const int64_t t0 = (tid - g * runs) * kRun;
+    const int64_t tiles = (L + TPB - 1) / TPB;
+    const int64_t g = blockIdx.x / tiles, tile = blockIdx.x - g * tiles;
+    const int n = threadIdx.x % DPAD, rl = threadIdx.x / DPAD;
+    const int64_t t0 = tile * TPB + (int64_t)rl * kRun;  // first tap of this thread's run
 
     double acc[kRun];
 #pragma unroll
     for (int j = 0; j < kRun; ++j) acc[j] = 0.0;
-
-    // Tap t uses lambda^(t-1); the run starts at exponent e0 = t0 - 1 (t0 >= 1)
-    // or covers t = 0 (the skip) and then exponents 0, 1, ... .
-    const int64_t first = (t0 == 0) ? 1 : 0;  // index in the run of the first tap >= 1
-    const double e0 = (t0 == 0) ? 0.0 : (double)(t0 - 1);
-    for (int64_t n = 0; n < d; ++n) {
+    if (n < d && t0 < L) {
         const float2 lf = a.s.poles[g * d + n], rf = a.s.residues[g * d + n];
         const double lr = lf.x, li = lf.y, rr = rf.x, ri = rf.y;
-        const double mag = (e0 == 0.0) ? 1.0 : exp(e0 * log(hypot(lr, li)));
-        double s, c;
-        sincos(e0 * atan2(li, lr), &s, &c);
-        double pr = mag * c, pi = mag * s;
+        // tap t uses lambda^(t-1): the run starts at exponent t0 - 1, or at
+        // tap 0 (the skip term, added below) followed by exponents 0, 1, ...
+        int64_t e = (t0 == 0) ? 0 : t0 - 1;
+        double pr = 1.0, pi = 0.0, br = lr, bi = li;
+        while (e != 0) {
+            if (e & 1) {
+                const double nr = pr * br - pi * bi;
+                pi = pr * bi + pi * br;
+                pr = nr;
+            }
+            const double nb = br * br - bi * bi;
+            bi = 2.0 * br * bi;
+            br = nb;
+            e >>= 1;
+        }
+        const int first = (t0 == 0) ? 1 : 0;
 #pragma unroll
         for (int j = 0; j < kRun; ++j) {
             if (j >= first) {
-                acc[j] = fma(rr, pr, fma(-ri, pi, acc[j]));
+                acc[j] = fma(rr, pr, -ri * pi);
                 const double nr = fma(lr, pr, -li * pi);
                 const double ni = fma(lr, pi, li * pr);
                 pr = nr;
@@ -56,21 +69,41 @@ __global__ __launch_bounds__(256) void filter_kernel(FilterArgs a) {
             }
         }
     }
-    float *out = a.h + g * L + t0;
-    const int64_t cnt = (L - t0 < kRun) ? (L - t0) : kRun;
+    double *row = part + (rl * DPAD + n) * LP;
 #pragma unroll
-    for (int j = 0; j < kRun; ++j) {
-        if (j < cnt) out[j] = (t0 + j == 0) ? a.s.skip[g] : (float)acc[j];
+    for (int j = 0; j < kRun; ++j) row[j] = acc[j];
+    __syncthreads();
+
+    for (int tau = threadIdx.x; tau < TPB; tau += 256) {
+        const int64_t t = tile * TPB + tau;
+        if (t >= L) break;
+        const int run = tau / kRun, j = tau % kRun;
+        double sum = 0.0;
+        for (int m = 0; m < d; ++m) sum += part[(run * DPAD + m) * LP + j];
+        a.h[g * L + t] = (t == 0) ? a.s.skip[g] : (float)sum;
     }
+}
+
+template <int DPAD>
+hipError_t launch_dpad(const FilterArgs &a, hipStream_t stream) {
+    constexpr int TPB = (256 / DPAD) * kRun;
+    const int64_t blocks = a.s.H * ((a.L + TPB - 1) / TPB);
+    filter_kernel<DPAD><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_filter(const FilterArgs &a, hipStream_t stream) {
     if (a.L == 0) return hipSuccess;
-    const int64_t threads = a.s.H * ((a.L + kRun - 1) / kRun);
-    filter_kernel<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(a);
-    return hipGetLastError();
+    const int64_t d = a.s.d;
+    if (d <= 1) return launch_dpad<1>(a, stream);
+    if (d <= 2) return launch_dpad<2>(a, stream);
+    if (d <= 4) return launch_dpad<4>(a, stream);
+    if (d <= 8) return launch_dpad<8>(a, stream);
+    if (d <= 16) return launch_dpad<16>(a, stream);
+    if (d <= 32) return launch_dpad<32>(a, stream);
+    return launch_dpad<64>(a, stream);
 }
 
 }  // namespace hm

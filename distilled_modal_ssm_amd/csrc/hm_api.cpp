@@ -233,6 +233,8 @@ hm_status hyena_filter_materialize(const hm_desc *desc, int64_t L, float *h_out,
     if (st != HM_OK) return st;
     if (L < 0 || L > kMaxElems / desc->heads) return HM_ERR_INVALID_ARG;
     if (L == 0) return HM_OK;
+    // grid limit: one workgroup per head and (at least) 128 taps
+    if ((L + 127) / 128 > (int64_t)INT32_MAX / desc->heads) return HM_ERR_UNSUPPORTED;
     if (!h_out) return HM_ERR_INVALID_ARG;
     if (!aligned(h_out, 4)) return HM_ERR_UNSUPPORTED;
     hm::FilterArgs a;

@@ -191,6 +191,7 @@ hm_status hyena_modal_decode_step(const hm_desc *desc,
  * The first L taps of every head's filter, h_out [H][L] float32:
  *   h[g][0] = D_g,  h[g][t] = Re(sum_n R_gn lambda_gn^(t-1)).
  * Powers are formed in float64 and each tap is rounded once to float32.
+ * HM_ERR_UNSUPPORTED when H * L / 128 exceeds 2^31 - 1 (launch grid limit).
  * (The distillation objective compares filters, Laughing Hyena Distillery
  * review, "提出的方法"; this exports them.)
  */

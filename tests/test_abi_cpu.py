@@ -167,6 +167,16 @@ def test_prefill_plan_choices(lib):
         hb.hyena_modal_prefill_plan(w2, 2048, chunk=100)
 
 
+def test_filter_validation(lib):
+    d = _desc()
+    for L, h, status in [(-1, FAKE, hb.HM_ERR_INVALID_ARG), (16, None, hb.HM_ERR_INVALID_ARG),
+                         (16, FAKE + 2, hb.HM_ERR_UNSUPPORTED),
+                         (1 << 40, FAKE, hb.HM_ERR_UNSUPPORTED)]:  # beyond the launch grid
+        with pytest.raises(hb.HMError) as e:
+            hb.hyena_filter_materialize(d, L, h, stream=0)
+        assert e.value.status == status, (L, h)
+
+
 def test_decode_state_validation(lib):
     d = _desc()
     with pytest.raises(hb.HMError) as e:

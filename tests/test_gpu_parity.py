@@ -66,6 +66,22 @@ def test_filter_materialize(ci):
     assert np.array_equal(h[:, 0], params.skip.astype(np.float64))
 
 
+@pytest.mark.parametrize("H,d,L", [(3, 1, 1), (2, 5, 31), (2, 12, 33), (1, 33, 1000), (2, 64, 700),
+                                   (5, 16, 4097)])
+def test_filter_mode_counts_and_ragged_lengths(H, d, L):
+    """Every mode-count padding (d -> next power of two) and ragged tap tiles,
+    with poles close to the unit circle."""
+    torch = require_gpu()
+    rng = np.random.default_rng(H * 1000 + d * 10 + L)
+    params = _rand_params(rng, H, d, 0.9, 0.9999)
+    log(f"filter H={H} d={d} L={L}")
+    h = to_np64(_op(params, 1, 64 * H, "f32").filter(L))
+    torch.cuda.synchronize()
+    ref = oracle.filter_taps(params, L)
+    assert rel_err(h, ref) <= 1e-4
+    assert np.array_equal(h[:, 0], params.skip.astype(np.float64))
+
+
 # ------------------------------------------------------------------ tiny workload, full oracle
 
 
