@@ -305,3 +305,29 @@ def test_stack_layer_matches_unrolled_definition(oracle_lib):
     y = _direct_conv(params, qkv[..., :D], qkv[..., D:2 * D], qkv[..., 2 * D:])
     ref = np.einsum("btk,nk->btn", y, w_out)
     assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_rms_and_dense_special_cases():
+    """Pins of the projected stack's two helpers against closed forms, not their
+    own formulas: a constant row has RMS |c|; a one-hot row of width n has RMS
+    |v|/sqrt(n); RMS scales with |a|; x W^T with W = identity returns x, with a
+    permutation permutes columns, and a unit row e_i picks column i of W (a
+    transposed W fails)."""
+    import oracle
+    c = np.full((1, 64), -3.0)
+    assert oracle.rms_inv(c, 0.0)[0] == 1.0 / 3.0
+    assert abs(oracle.rms_inv(c, 1e-6)[0] - 1.0 / np.sqrt(9.0 + 1e-6)) <= 1e-15
+    onehot = np.zeros((1, 100))
+    onehot[0, 17] = 5.0
+    assert abs(oracle.rms_inv(onehot, 0.0)[0] - np.sqrt(100.0) / 5.0) <= 1e-14
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 40))
+    assert np.allclose(oracle.rms_inv(-4.0 * x, 0.0), oracle.rms_inv(x, 0.0) / 4.0, rtol=1e-14, atol=0)
+    w = rng.standard_normal((7, 40))
+    assert np.array_equal(oracle.dense(x, np.eye(40)), x)
+    perm = rng.permutation(40)
+    assert np.array_equal(oracle.dense(x, np.eye(40)[perm]), x[:, perm])
+    e = np.zeros((1, 40))
+    e[0, 11] = 1.0
+    assert np.array_equal(oracle.dense(e, w)[0], w[:, 11])
+    assert oracle.dense(x, w).shape == (3, 7)
