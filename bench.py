@@ -426,6 +426,25 @@ def main():
     ms_filter, ms_prefill, ms_decode = (float(np.median(ph[:, i])) for i in range(3))
     ms_decode_launch = ms_decode / cfg.S
 
+    # outside the timed region: 20 prefill calls alone, and 10 replays of the
+    # S-step decode graph (per-launch spread of the decode kernel: see the
+    # rocprofv3 kernel-trace summaries, which time every dispatch)
+    torch.cuda.synchronize()
+    pf_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+    for e in pf_ev:
+        e[0].record(stream)
+        prefill_call()
+        e[1].record(stream)
+    dg_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+    for e in dg_ev:
+        e[0].record(stream)
+        decode_call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    pf_ms = np.array([a.elapsed_time(b) for a, b in pf_ev])
+    dec_us = np.array([a.elapsed_time(b) * 1e3 / cfg.S for a, b in dg_ev])
+    pct = lambda x: {"p10": float(np.percentile(x, 10)), "p50": float(np.median(x)), "p90": float(np.percentile(x, 90))}
+
     E = cfg.B * cfg.L * cfg.D
     sb = cfg.act_bytes
     decode_bytes = cfg.B * cfg.D * (16 * cfg.d + 4 * sb)
@@ -478,6 +497,8 @@ def main():
         "decode_tokens_per_s": cfg.B / (ms_decode_launch / 1e3),
         "phase_ms": {"filter": ms_filter, "prefill": ms_prefill, "decode_total": ms_decode,
                      "decode_per_step": ms_decode_launch},
+        "decode_step_us_per_replay": pct(dec_us),
+        "prefill_ms_20_calls": pct(pf_ms),
         "prefill_rates": {"alu_TFLOPs": prefill_flops / ms_prefill * 1e-9,
                           "alu_frac": prefill_flops / ms_prefill * 1e-9 / VALU_F32_PEAK_TFLOPS,
                           "hbm_GBs": prefill_bytes / ms_prefill * 1e-6,

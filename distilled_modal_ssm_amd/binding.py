@@ -39,6 +39,9 @@ EXPORTS = (
     "hyena_row_rms",
     "hyena_dense_bf16",
     "hyena_dense_rms_bf16",
+    "hyena_dense_workspace",
+    "hyena_dense_bf16_ex",
+    "hyena_dense_rms_bf16_ex",
 )
 
 
@@ -108,6 +111,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "hyena_row_rms": ([p, i64, i64, i64, ctypes.c_float, p, p], ctypes.c_int),
             "hyena_dense_bf16": ([i64, i64, i64, p, i64, p, i64, p, p, i64, p], ctypes.c_int),
             "hyena_dense_rms_bf16": ([i64, i64, i64, p, i64, p, i64, ctypes.c_float, p, i64, p], ctypes.c_int),
+            "hyena_dense_workspace": ([i64, i64, i64, ctypes.POINTER(sz)], ctypes.c_int),
+            "hyena_dense_bf16_ex": ([i64, i64, i64, p, i64, p, i64, p, p, i64, p, sz, p], ctypes.c_int),
+            "hyena_dense_rms_bf16_ex": ([i64, i64, i64, p, i64, p, i64, ctypes.c_float, p, i64, p, sz, p],
+                                        ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -219,15 +226,39 @@ def hyena_row_rms(x, M, D, ld, eps, inv_rms, stream=None) -> None:
     _check(st, "hyena_row_rms")
 
 
-def hyena_dense_bf16(M, N, K, A, lda, W, ldw, row_scale, C, ldc, stream=None) -> None:
-    st = load().hyena_dense_bf16(M, N, K, _ptr(A), lda, _ptr(W), ldw, _ptr(row_scale), _ptr(C), ldc,
-                                 _stream(stream))
+def _ws_bytes(workspace, ws_bytes):
+    if ws_bytes is not None:
+        return int(ws_bytes)
+    return workspace.numel() * workspace.element_size() if workspace is not None else 0
+
+
+def hyena_dense_bf16(M, N, K, A, lda, W, ldw, row_scale, C, ldc, stream=None, workspace=None,
+                     ws_bytes=None) -> None:
+    """C = row_scale * A W^T; with a workspace, small M takes the split-K path."""
+    if workspace is None:
+        st = load().hyena_dense_bf16(M, N, K, _ptr(A), lda, _ptr(W), ldw, _ptr(row_scale), _ptr(C), ldc,
+                                     _stream(stream))
+    else:
+        st = load().hyena_dense_bf16_ex(M, N, K, _ptr(A), lda, _ptr(W), ldw, _ptr(row_scale), _ptr(C), ldc,
+                                        _ptr(workspace), _ws_bytes(workspace, ws_bytes), _stream(stream))
     _check(st, "hyena_dense_bf16")
 
 
-def hyena_dense_rms_bf16(M, N, K, A, lda, W, ldw, eps, C, ldc, stream=None) -> None:
-    st = load().hyena_dense_rms_bf16(M, N, K, _ptr(A), lda, _ptr(W), ldw, eps, _ptr(C), ldc, _stream(stream))
+def hyena_dense_rms_bf16(M, N, K, A, lda, W, ldw, eps, C, ldc, stream=None, workspace=None,
+                         ws_bytes=None) -> None:
+    if workspace is None:
+        st = load().hyena_dense_rms_bf16(M, N, K, _ptr(A), lda, _ptr(W), ldw, eps, _ptr(C), ldc,
+                                         _stream(stream))
+    else:
+        st = load().hyena_dense_rms_bf16_ex(M, N, K, _ptr(A), lda, _ptr(W), ldw, eps, _ptr(C), ldc,
+                                            _ptr(workspace), _ws_bytes(workspace, ws_bytes), _stream(stream))
     _check(st, "hyena_dense_rms_bf16")
+
+
+def hyena_dense_workspace(M, N, K) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().hyena_dense_workspace(M, N, K, ctypes.byref(n)), "hyena_dense_workspace")
+    return n.value
 
 
 # ----------------------------------------------------------------- tensor helpers

@@ -453,6 +453,147 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
     }
 }
 
+// ------------------------------------------------------------------ split-K GEMM (M <= 64)
+
+// Pass 1.  Workgroup = (64-column tile nt, 256-wide K slice sl), 4 waves; wave
+// w covers k in [sl*256 + 64w, +64) for all 64 rows and 64 columns: its A and
+// W fragments (16 x 16 bytes per lane) are all loaded at once, straight into
+// the MFMA operand registers, so every workgroup has its whole 64 KB in
+// flight.  The four waves' C tiles are summed through LDS into one fp32
+// partial per (tile, slice), stored in C-fragment order, plus (fused RMS) the
+// slice's row sums of squares.
+template <bool RMS>
+__global__ __launch_bounds__(256) void gemm_splitk_kernel(GemmArgs g, int nsl) {
+    __shared__ __attribute__((aligned(16))) float red[4][16][kWave][4];  // wave, C tile, lane, register
+    __shared__ float ssq_l[4][64];
+    const int nt = blockIdx.x, sl = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
+    const int r16 = lane % 16, kg = lane / 16;
+    const int64_t n0 = (int64_t)nt * kSplitBN, k0 = (int64_t)sl * kSplitKS + 64 * w;
+    const uint16_t *A = static_cast<const uint16_t *>(g.A);
+    const uint16_t *W = static_cast<const uint16_t *>(g.W);
+    const int64_t tiles = (g.N + kSplitBN - 1) / kSplitBN;
+    float *part = reinterpret_cast<float *>(g.ws);
+    float *ssq_part = part + tiles * nsl * 4096;
+
+    uint4 a[4][2], b[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int64_t k = k0 + 32 * ks + 8 * kg;
+            const int64_t row = 16 * i + r16, col = n0 + 16 * i + r16;
+            a[i][ks] = row < g.M ? *reinterpret_cast<const uint4 *>(A + row * g.lda + k) : make_uint4(0, 0, 0, 0);
+            b[i][ks] = col < g.N ? *reinterpret_cast<const uint4 *>(W + col * g.ldw + k) : make_uint4(0, 0, 0, 0);
+        }
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = mfma16(a[mi][ks], b[nj][ks], acc[mi][nj]);
+    if constexpr (RMS) {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            float s = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const uint32_t wv[4] = {a[mi][ks].x, a[mi][ks].y, a[mi][ks].z, a[mi][ks].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = bf16_lo(wv[e]), hi = bf16_hi(wv[e]);
+                    s = fmaf(lo, lo, fmaf(hi, hi, s));
+                }
+            }
+            s += __shfl_xor(s, 16);
+            s += __shfl_xor(s, 32);
+            if (kg == 0) ssq_l[w][16 * mi + r16] = s;
+        }
+    }
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj)
+            *reinterpret_cast<f32x4 *>(&red[w][mi * 4 + nj][lane][0]) = acc[mi][nj];
+    __syncthreads();
+
+    // partial of this slice, C-fragment order: float4 q = tile * 64 + lane
+    float *mine = part + ((int64_t)nt * nsl + sl) * 4096;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = tid + 256 * i;
+        const float *r0 = &red[0][q / kWave][q % kWave][0];
+        f32x4 v = *reinterpret_cast<const f32x4 *>(r0);
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) v += *reinterpret_cast<const f32x4 *>(r0 + ww * 16 * kWave * 4);
+        *reinterpret_cast<f32x4 *>(mine + 4 * q) = v;
+    }
+    if (RMS && tid < 64)
+        ssq_part[((int64_t)nt * nsl + sl) * 64 + tid] = ssq_l[0][tid] + ssq_l[1][tid] + ssq_l[2][tid] + ssq_l[3][tid];
+}
+
+// Pass 2.  Four workgroups per column tile, one float4 of the tile's C
+// fragments per thread: sums the slices' partials (all loads in flight),
+// scales (row scale, or the inverse RMS from the slices' sums of squares) and
+// writes bf16 C.
+template <bool RMS, int NSL>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
+    __shared__ float scale[64];
+    const int nt = blockIdx.x / 4, quarter = blockIdx.x % 4, tid = threadIdx.x;
+    const int64_t n0 = (int64_t)nt * kSplitBN;
+    const int64_t tiles = (g.N + kSplitBN - 1) / kSplitBN;
+    const float *part = reinterpret_cast<const float *>(g.ws) + (int64_t)nt * NSL * 4096;
+    const float *ssq_part = reinterpret_cast<const float *>(g.ws) + tiles * NSL * 4096 + (int64_t)nt * NSL * 64;
+    const int q = quarter * 256 + tid, tile = q / kWave, ln = q % kWave;
+    f32x4 p[NSL];
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) p[s] = *reinterpret_cast<const f32x4 *>(part + (int64_t)s * 4096 + 4 * q);
+    if (tid < 64) {
+        float sc = (g.row_scale && tid < g.M) ? g.row_scale[tid] : 1.0f;
+        if constexpr (RMS) {
+            float tot = 0.f;
+#pragma unroll
+            for (int s = 0; s < NSL; ++s) tot += ssq_part[s * 64 + tid];
+            sc *= rms_scale(tot, g.K, g.rms_eps);
+        }
+        scale[tid] = sc;
+    }
+    __syncthreads();
+    f32x4 v = p[0];
+#pragma unroll
+    for (int s = 1; s < NSL; ++s) v += p[s];
+    uint16_t *C = static_cast<uint16_t *>(g.C);
+    const int64_t col = n0 + 16 * (tile % 4) + ln % 16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (tile / 4) + 4 * (ln / 16) + r;
+        if (row < g.M && col < g.N) C[row * g.ldc + col] = (uint16_t)f32_to_bf16(v[r] * scale[row]);
+    }
+}
+
+template <bool RMS>
+hipError_t launch_splitk(const GemmArgs &g, hipStream_t stream) {
+    const int nsl = (int)(g.K / kSplitKS);
+    const unsigned tiles = (unsigned)((g.N + kSplitBN - 1) / kSplitBN);
+    gemm_splitk_kernel<RMS><<<dim3(tiles, (unsigned)nsl), dim3(256), 0, stream>>>(g, nsl);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 grid(tiles * 4), block(256);
+    switch (nsl) {
+        case 2: splitk_reduce_kernel<RMS, 2><<<grid, block, 0, stream>>>(g); break;
+        case 4: splitk_reduce_kernel<RMS, 4><<<grid, block, 0, stream>>>(g); break;
+        case 8: splitk_reduce_kernel<RMS, 8><<<grid, block, 0, stream>>>(g); break;
+        case 16: splitk_reduce_kernel<RMS, 16><<<grid, block, 0, stream>>>(g); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <bool RMS, int BM, int BN, int WM, int WN, int GM>
 hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
     const int64_t tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
@@ -463,6 +604,8 @@ hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
 
 template <bool RMS>
 hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
+    const size_t ws_need = splitk_workspace_bytes(g.M, g.N, g.K);
+    if (g.ws && ws_need > 0 && g.ws_bytes >= ws_need) return launch_splitk<RMS>(g, stream);
     if (g.M <= 64 && g.K % kSkCK == 0) {
         // Measured on MI355X at M = 64, K = 2048: the unrolled streaming kernel
         // is fastest for wide outputs, the LDS-staged one for narrow outputs.
@@ -479,6 +622,17 @@ hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
 }
 
 }  // namespace
+
+size_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    // Measured on MI355X at M = 64, K = 2048 (graph-replayed): split-K beats the
+    // LDS-staged kernel for N = 2048 (8.2 vs 8.6 us) but loses to the unrolled
+    // streaming kernel for N = 6144 (17.3 vs 14.7 us), so wide outputs keep it.
+    if (M < 1 || M > 64 || N < 1 || N > 4096 || K % kSplitKS != 0) return 0;
+    const int64_t nsl = K / kSplitKS;
+    if (nsl != 2 && nsl != 4 && nsl != 8 && nsl != 16) return 0;  // K in {512, 1024, 2048, 4096}
+    const size_t tiles = (size_t)((N + kSplitBN - 1) / kSplitBN);
+    return tiles * nsl * (4096 + 64) * sizeof(float);
+}
 
 hipError_t launch_row_rms(const RmsArgs &a, hipStream_t stream) {
     if (a.M == 0) return hipSuccess;

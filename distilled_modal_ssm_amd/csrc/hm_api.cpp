@@ -265,7 +265,8 @@ hm_status hyena_row_rms(const void *x, int64_t M, int64_t D, int64_t ld, float e
 }
 
 static hm_status dense_impl(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *W, int64_t ldw,
-                     const float *row_scale, bool rms, float eps, void *C, int64_t ldc, void *stream) {
+                     const float *row_scale, bool rms, float eps, void *C, int64_t ldc, void *workspace,
+                     size_t ws_bytes, void *stream) {
     if (M < 0 || N < 0 || K < 1) return HM_ERR_INVALID_ARG;
     if (lda < K || ldw < K || ldc < N) return HM_ERR_INVALID_ARG;
     if (M > kMaxElems / lda || N > kMaxElems / ldw || M > kMaxElems / (ldc > 0 ? ldc : 1))
@@ -276,6 +277,11 @@ static hm_status dense_impl(int64_t M, int64_t N, int64_t K, const void *A, int6
     if (!aligned(A, 16) || !aligned(W, 16) || !aligned(C, 2) || (row_scale && !aligned(row_scale, 4)))
         return HM_ERR_UNSUPPORTED;
     if (((M + 127) / 128) * ((N + 255) / 256) > INT32_MAX) return HM_ERR_UNSUPPORTED;
+    const size_t ws_need = hm::splitk_workspace_bytes(M, N, K);
+    if (workspace && ws_need > 0) {
+        if (ws_bytes < ws_need) return HM_ERR_WORKSPACE;
+        if (!aligned(workspace, 256)) return HM_ERR_UNSUPPORTED;
+    }
     hm::GemmArgs g;
     g.M = M;
     g.N = N;
@@ -289,19 +295,40 @@ static hm_status dense_impl(int64_t M, int64_t N, int64_t K, const void *A, int6
     g.ldc = ldc;
     g.rms = rms;
     g.rms_eps = eps;
+    g.ws = (workspace && ws_need > 0) ? static_cast<unsigned char *>(workspace) : nullptr;
+    g.ws_bytes = ws_bytes;
     const hipError_t err = hm::launch_gemm(g, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
 }
 
 hm_status hyena_dense_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *W,
                            int64_t ldw, const float *row_scale, void *C, int64_t ldc, void *stream) {
-    return dense_impl(M, N, K, A, lda, W, ldw, row_scale, false, 0.0f, C, ldc, stream);
+    return dense_impl(M, N, K, A, lda, W, ldw, row_scale, false, 0.0f, C, ldc, nullptr, 0, stream);
 }
 
 hm_status hyena_dense_rms_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *W,
                                int64_t ldw, float eps, void *C, int64_t ldc, void *stream) {
     if (!(eps >= 0.0f)) return HM_ERR_INVALID_ARG;
-    return dense_impl(M, N, K, A, lda, W, ldw, nullptr, true, eps, C, ldc, stream);
+    return dense_impl(M, N, K, A, lda, W, ldw, nullptr, true, eps, C, ldc, nullptr, 0, stream);
+}
+
+hm_status hyena_dense_workspace(int64_t M, int64_t N, int64_t K, size_t *bytes) {
+    if (!bytes || M < 0 || N < 0 || K < 1) return HM_ERR_INVALID_ARG;
+    *bytes = hm::splitk_workspace_bytes(M, N, K);
+    return HM_OK;
+}
+
+hm_status hyena_dense_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *W,
+                              int64_t ldw, const float *row_scale, void *C, int64_t ldc, void *workspace,
+                              size_t ws_bytes, void *stream) {
+    return dense_impl(M, N, K, A, lda, W, ldw, row_scale, false, 0.0f, C, ldc, workspace, ws_bytes, stream);
+}
+
+hm_status hyena_dense_rms_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *W,
+                                  int64_t ldw, float eps, void *C, int64_t ldc, void *workspace, size_t ws_bytes,
+                                  void *stream) {
+    if (!(eps >= 0.0f)) return HM_ERR_INVALID_ARG;
+    return dense_impl(M, N, K, A, lda, W, ldw, nullptr, true, eps, C, ldc, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

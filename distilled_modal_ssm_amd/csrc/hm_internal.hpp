@@ -171,7 +171,16 @@ struct GemmArgs {
     int64_t ldc;
     bool rms;                // also scale row m by 1/sqrt(mean_k A[m][k]^2 + rms_eps)
     float rms_eps;
+    unsigned char *ws = nullptr;  // split-K workspace (M <= 64), or null
+    size_t ws_bytes = 0;
 };
+
+// Split-K path of the small-M GEMM: 64-column tiles x 256-wide K slices write
+// fp32 partials, a second pass sums them per tile.  Workspace: partials
+// [tiles][slices][64*64] fp32, then row sums of squares [tiles][slices][64]
+// fp32.  0 bytes when the shape does not take this path.
+constexpr int kSplitBN = 64, kSplitKS = 256;
+size_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; none synchronises.

@@ -52,6 +52,9 @@ class HyenaStack:
         self.qkvd = torch.empty((B, 3 * D), dtype=bf, **e)
         self.yd = torch.empty((B, D), dtype=bf, **e)
         self.states = [op.new_state() for op in self.ops]
+        # split-K scratch of the generation-step projections
+        ws = max(hb.hyena_dense_workspace(B, 3 * D, D), hb.hyena_dense_workspace(B, D, D))
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, **e) if ws > 0 else None
 
     def _bf16(self, w):
         torch = self.torch
@@ -64,7 +67,8 @@ class HyenaStack:
 
     def _layer(self, l, x, out, M, qkv, y, rows_time, prefill: bool):
         D = self.D
-        hb.hyena_dense_rms_bf16(M, 3 * D, D, x, D, self.w_in[l], D, RMS_EPS, qkv, 3 * D)
+        ws = None if prefill else self.ws
+        hb.hyena_dense_rms_bf16(M, 3 * D, D, x, D, self.w_in[l], D, RMS_EPS, qkv, 3 * D, workspace=ws)
         if prefill:
             B, L = rows_time
             q3 = qkv.view(B, L, 3 * D)
@@ -72,7 +76,7 @@ class HyenaStack:
                                 state_out=self.states[l])
         else:
             self.ops[l].decode_step(qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:], self.states[l], y=y)
-        hb.hyena_dense_bf16(M, D, D, y, D, self.w_out[l], D, None, out, D)
+        hb.hyena_dense_bf16(M, D, D, y, D, self.w_out[l], D, None, out, D, workspace=ws)
 
     def prefill(self, x_in, record=None):
         """x_in: [B][L][D] bf16 prompt input.  Returns the stack output [B*L][D].

@@ -236,6 +236,32 @@ hm_status hyena_dense_rms_bf16(int64_t M, int64_t N, int64_t K, const void *A, i
                                const void *W, int64_t ldw, float eps, void *C, int64_t ldc,
                                void *stream);
 
+/*
+ * The same two products with a caller-owned workspace that enables the
+ * split-K path for small M (the generation step: M <= 64, N <= 4096, K in
+ * {512, 1024, 2048, 4096}; wider outputs stream their weights faster without
+ * it).  There, a workgroup owns 64 output columns and one 256-wide
+ * K slice and writes a float32 partial to the workspace; a second pass sums
+ * each column tile's partials and writes C.  Results equal the workspace-less
+ * calls up to float32 summation order.
+ *
+ * hyena_dense_workspace: bytes needed for (M, N, K); 0 when the shape does not
+ * take the split-K path (then workspace is ignored and may be NULL).
+ * Workspace contract: 256-byte aligned, contents irrelevant (scratch), reusable
+ * by any later call on the same stream if large enough; calls that share a
+ * workspace must not run concurrently.  Too small -> HM_ERR_WORKSPACE;
+ * misaligned -> HM_ERR_UNSUPPORTED; other errors as above.
+ */
+hm_status hyena_dense_workspace(int64_t M, int64_t N, int64_t K, size_t *bytes);
+
+hm_status hyena_dense_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                              const void *W, int64_t ldw, const float *row_scale, void *C,
+                              int64_t ldc, void *workspace, size_t ws_bytes, void *stream);
+
+hm_status hyena_dense_rms_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
+                                  const void *W, int64_t ldw, float eps, void *C, int64_t ldc,
+                                  void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

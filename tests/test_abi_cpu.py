@@ -233,3 +233,33 @@ def test_dense_and_rms_validation(lib):
         with pytest.raises(hb.HMError) as e:
             hb.hyena_row_rms(a["x"], a["M"], a["D"], a["ld"], a["eps"], a["out"], stream=0)
         assert e.value.status == status, kw
+
+
+def test_split_k_workspace_contract(lib):
+    """Workspace sizes of the small-M split-K path and its validation."""
+    need = hb.hyena_dense_workspace(64, 2048, 2048)
+    tiles, slices = 2048 // 64, 2048 // 256
+    assert need == tiles * slices * (4096 + 64) * 4
+    assert hb.hyena_dense_workspace(64, 6144, 2048) == 0  # wide outputs: streaming kernel
+    assert hb.hyena_dense_workspace(37, 96, 1024) == 2 * 4 * (4096 + 64) * 4
+    # shapes outside the path need none: M > 64, K not a multiple of 256, a single slice
+    assert hb.hyena_dense_workspace(65, 6144, 2048) == 0
+    assert hb.hyena_dense_workspace(64, 2048, 320) == 0
+    assert hb.hyena_dense_workspace(64, 2048, 256) == 0
+    assert hb.hyena_dense_workspace(64, 2048, 1536) == 0  # 6 slices: not a supported slice count
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_dense_workspace(-1, 8, 256)
+    assert e.value.status == hb.HM_ERR_INVALID_ARG
+
+    def call(ws, nbytes, M=64):
+        hb.hyena_dense_bf16(M, 2048, 2048, FAKE, 2048, FAKE, 2048, None, FAKE, 2048, stream=0,
+                            workspace=ws, ws_bytes=nbytes)
+
+    for ws, nbytes, status in [(FAKE, need - 1, hb.HM_ERR_WORKSPACE), (FAKE + 16, need, hb.HM_ERR_UNSUPPORTED)]:
+        with pytest.raises(hb.HMError) as e:
+            call(ws, nbytes)
+        assert e.value.status == status
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_dense_rms_bf16(64, 2048, 2048, FAKE, 2048, FAKE, 2048, 1e-6, FAKE, 2048, stream=0,
+                                workspace=FAKE, ws_bytes=16)
+    assert e.value.status == hb.HM_ERR_WORKSPACE

@@ -90,6 +90,41 @@ def test_dense_strided_operands():
     assert torch.all(C[:, N:] == 5.0).item()
 
 
+def test_dense_split_k_shared_workspace():
+    """The small-M split-K path (workspace given) against the oracle, on calls in
+    a row that share one workspace (filled with garbage first): wide then narrow
+    outputs, ragged rows and columns, two to eight K slices, fused RMS and a row
+    scale."""
+    torch = require_gpu()
+    rng = np.random.default_rng(77)
+    shapes = [(64, 4096, 2048, "rms"), (64, 2048, 2048, "plain"), (37, 96, 1024, "scaled"),
+              (64, 4096, 4096, "plain"), (1, 200, 512, "rms"), (64, 2048, 2048, "rms"),
+              (64, 6144, 2048, "rms")]  # the last is wider than the split-K path: workspace ignored
+    need = max(hb.hyena_dense_workspace(M, N, K) for M, N, K, _ in shapes)
+    assert hb.hyena_dense_workspace(64, 6144, 2048) == 0
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
+    for M, N, K, kind in shapes:
+        a = _bits(rng, (M, K), 2.0)
+        w = _bits(rng, (N, K), 0.02)
+        sc = rng.uniform(0.5, 2.0, M).astype(np.float32)
+        A, W = to_dev(a, "bf16"), to_dev(w, "bf16")
+        C = torch.full((M, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        log(f"split-K dense M={M} N={N} K={K} {kind}")
+        ref = oracle.dense(oracle.bf16_to_f64(a), oracle.bf16_to_f64(w))
+        if kind == "rms":
+            hb.hyena_dense_rms_bf16(M, N, K, A, K, W, K, 1e-6, C, N, workspace=ws)
+            ref = ref * oracle.rms_inv(oracle.bf16_to_f64(a), 1e-6)[:, None]
+        else:
+            S = torch.from_numpy(sc).cuda() if kind == "scaled" else None
+            hb.hyena_dense_bf16(M, N, K, A, K, W, K, S, C, N, workspace=ws)
+            if kind == "scaled":
+                ref = ref * sc[:, None]
+        torch.cuda.synchronize()
+        err = rel_err(to_np64(C), ref)
+        print(f"split-K {M}x{N}x{K} {kind}: rel err {err:.2e}")
+        assert err <= 8e-3, (M, N, K, kind)
+
+
 @pytest.mark.parametrize("M,D,ld", [(64, 2048, 2048), (1000, 2048, 6144), (5, 100, 100)])
 def test_row_rms(M, D, ld):
     torch = require_gpu()
