@@ -171,6 +171,7 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (1-5; 5 = projected stack)")
     ap.add_argument("--decode-mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fir", action="store_true", help="skip the explicit-filter decode baseline")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (for counter calibration)")
@@ -508,12 +509,57 @@ def main():
         "wall_s_timed": t_wall,
         "roofline": roofline,
     }
+    if not args.no_fir:
+        for window in (0, 256):
+            res[f"fir_baseline_w{window}"] = fir_baseline(cfg, op, k, v, dq, dk, dv, window,
+                                                          ms_decode_launch, stream)
     if args.calibrate_copy:
         calibration_copy()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (float64 oracle)")
         res["cpu_baseline"] = cpu_baseline(cfg, params, inp, dec)
     emit(args, res)
+
+
+def fir_baseline(cfg, op, k, v, dq, dk, dv, window, ms_modal_step, stream):
+    """The non-distilled decode on the same workload, outside the timed step:
+    the prompt's u cached (not timed), then S generated tokens through the
+    explicit filter (window 0 = every past step), captured in a HIP graph."""
+    import torch
+    from distilled_modal_ssm_amd import binding as hb
+    log(f"[bench] explicit-filter decode baseline, window {window or 'full'}")
+    fir = hb.FirHyena(op, cfg.L + cfg.S)
+    fir.fill(k, v)
+    h = op.filter(cfg.L + cfg.S)
+    yf = torch.empty((cfg.S, cfg.B, cfg.D), dtype=op.tdtype, device=op.device)
+
+    def run():
+        for s in range(cfg.S):
+            fir.step(h, cfg.L + s, dq[s], dk[s], dv[s], window=window, y=yf[s])
+
+    run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / cfg.S
+    sb = cfg.act_bytes
+    rows = [min(cfg.L + s, window - 1 if window else cfg.L + s) for s in range(cfg.S)]
+    byts = float(np.mean([cfg.B * cfg.D * (r * sb + 5 * sb) for r in rows]))
+    del graph, fir, yf
+    torch.cuda.synchronize()
+    gbs = byts / ms_step * 1e-6
+    return {"window": window, "decode_us_per_step": ms_step * 1e3,
+            "decode_tokens_per_s": cfg.B / (ms_step / 1e3),
+            "algorithmic_bytes_per_step": byts, "hbm_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "modal_decode_speedup": ms_step / ms_modal_step}
 
 
 if __name__ == "__main__":

@@ -42,6 +42,9 @@ EXPORTS = (
     "hyena_dense_workspace",
     "hyena_dense_bf16_ex",
     "hyena_dense_rms_bf16_ex",
+    "hyena_fir_workspace",
+    "hyena_fir_decode_step",
+    "hyena_fir_cache_fill",
 )
 
 
@@ -112,6 +115,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "hyena_dense_bf16": ([i64, i64, i64, p, i64, p, i64, p, p, i64, p], ctypes.c_int),
             "hyena_dense_rms_bf16": ([i64, i64, i64, p, i64, p, i64, ctypes.c_float, p, i64, p], ctypes.c_int),
             "hyena_dense_workspace": ([i64, i64, i64, ctypes.POINTER(sz)], ctypes.c_int),
+            "hyena_fir_workspace": ([D, ctypes.POINTER(sz)], ctypes.c_int),
+            "hyena_fir_decode_step": ([D, p, i64, i64, i64, p, p, p, i64, p, i64, p, i64, p, sz, p], ctypes.c_int),
+            "hyena_fir_cache_fill": ([D, i64, p, p, i64, p, i64, p], ctypes.c_int),
             "hyena_dense_bf16_ex": ([i64, i64, i64, p, i64, p, i64, p, p, i64, p, sz, p], ctypes.c_int),
             "hyena_dense_rms_bf16_ex": ([i64, i64, i64, p, i64, p, i64, ctypes.c_float, p, i64, p, sz, p],
                                         ctypes.c_int),
@@ -261,6 +267,26 @@ def hyena_dense_workspace(M, N, K) -> int:
     return n.value
 
 
+def hyena_fir_workspace(desc: hm_desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().hyena_fir_workspace(ctypes.byref(desc), ctypes.byref(n)), "hyena_fir_workspace")
+    return n.value
+
+
+def hyena_fir_decode_step(desc: hm_desc, h, h_len, window, t, q, k, v, ld_in, y, ld_y, u_cache, cache_len,
+                          workspace, ws_bytes=None, stream=None) -> None:
+    st = load().hyena_fir_decode_step(ctypes.byref(desc), _ptr(h), h_len, window, t, _ptr(q), _ptr(k), _ptr(v),
+                                      ld_in, _ptr(y), ld_y, _ptr(u_cache), cache_len, _ptr(workspace),
+                                      _ws_bytes(workspace, ws_bytes), _stream(stream))
+    _check(st, "hyena_fir_decode_step")
+
+
+def hyena_fir_cache_fill(desc: hm_desc, L, k, v, ld_in, u_cache, cache_len, stream=None) -> None:
+    st = load().hyena_fir_cache_fill(ctypes.byref(desc), L, _ptr(k), _ptr(v), ld_in, _ptr(u_cache), cache_len,
+                                     _stream(stream))
+    _check(st, "hyena_fir_cache_fill")
+
+
 # ----------------------------------------------------------------- tensor helpers
 
 
@@ -347,3 +373,35 @@ class ModalHyena:
         h = self.torch.empty((self.H, L), dtype=self.torch.float32, device=self.device)
         hyena_filter_materialize(self.desc, L, h, stream)
         return h
+
+
+class FirHyena:
+    """The explicit-filter (non-distilled) decode baseline on the same shapes as
+    a :class:`ModalHyena`: a u cache [B][cache_len][D] in the activation dtype
+    and the pass-1 workspace, allocated once with torch."""
+
+    def __init__(self, op: ModalHyena, cache_len: int):
+        torch = op.torch
+        self.op, self.torch = op, torch
+        self.cache_len = int(cache_len)
+        self.cache = torch.zeros((op.B, self.cache_len, op.D), dtype=op.tdtype, device=op.device)
+        n = hyena_fir_workspace(op.desc)
+        self.ws = torch.empty(max(n, 256), dtype=torch.uint8, device=op.device)
+
+    def fill(self, k, v, stream=None):
+        """Cache rows 0 .. L-1 from a prompt's k, v [B][L][ld] views."""
+        L = int(k.shape[1])
+        ld = _row_stride(k, (v,))
+        hyena_fir_cache_fill(self.op.desc, L, k, v, ld, self.cache, self.cache_len, stream)
+
+    def step(self, h, t: int, q, k, v, window: int = 0, y=None, stream=None):
+        """One generated token at position t through the taps h [H][>= min(t+1, W)];
+        q, k, v: [B][ld] rows with one row stride."""
+        if y is None:
+            y = self.torch.empty((self.op.B, self.op.D), dtype=self.op.tdtype, device=self.op.device)
+        for x in (q, k, v, y):
+            if x.dim() != 2 or x.stride(1) != 1 or (x.shape[0] > 1 and x is not y and x.stride(0) != q.stride(0)):
+                raise ValueError("FIR step needs [B][D] rows with unit channel stride and one row stride for q, k, v")
+        hyena_fir_decode_step(self.op.desc, h, int(h.shape[-1]), window, t, q, k, v, q.stride(0), y,
+                              y.stride(0), self.cache, self.cache_len, self.ws, stream=stream)
+        return y

@@ -1,0 +1,178 @@
+// fir.hip -- the non-distilled Hyena decode baseline: one generated token
+// through the explicit long filter instead of the modal recurrence.
+//
+// Per (batch row b, channel c in head g) at step t, with u = k v kept in a
+// cache in the activation dtype:
+//     y_t = q_t * sum_{j=0}^{min(t, W-1)} h[g][j] u_{t-j},
+// the causal long convolution of the Hyena operator (StripedHyena article,
+// Hyena層次結構) evaluated directly: O(t) work and O(t) memory per token, the
+// cost the distilled recurrence removes (Laughing Hyena Distillery review,
+// 研究动机与目标 and 主要发现).  W = 0 uses every past step; W > 0 truncates the
+// filter to its first W taps.
+//
+// Bound: HBM.  A step reads the cached rows [t-W+1, t) of every batch row
+// (B * rows * D * s_act bytes) and writes one row; the filter taps are tiny.
+// Pass 1 splits the rows into R ranges: workgroup (512-channel block, range,
+// batch row), each lane 8 adjacent channels (16- or 32-byte loads), the 4
+// waves striding over the range's rows, fp32 partial sums per range.  Pass 2
+// sums the ranges, adds the current token's h[0] u_t, gates with q, writes y
+// and appends u_t to the cache.
+#include "hm_internal.hpp"
+
+namespace hm {
+namespace {
+
+constexpr int kFirBlk = 512;  // channels per pass-1 workgroup (64 lanes x 8)
+
+template <int ACT> struct Row8;  // 8 adjacent channels of one cache row
+template <> struct Row8<kBF16> {
+    uint4 w;
+    __device__ void load(const void *p) { w = *reinterpret_cast<const uint4 *>(p); }
+    __device__ void get(float *o) const {
+        const uint32_t v[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            o[2 * e] = bf16_lo(v[e]);
+            o[2 * e + 1] = bf16_hi(v[e]);
+        }
+    }
+};
+template <> struct Row8<kF32> {
+    float4 a, b;
+    __device__ void load(const void *p) {
+        a = reinterpret_cast<const float4 *>(p)[0];
+        b = reinterpret_cast<const float4 *>(p)[1];
+    }
+    __device__ void get(float *o) const {
+        o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+        o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+    }
+};
+
+template <int ACT>
+__global__ __launch_bounds__(256) void fir_partial_kernel(FirArgs a) {
+    using T = typename Act<ACT>::T;
+    __shared__ float red[4][kWave][8];
+    const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+    const int64_t c0 = (int64_t)blockIdx.x * kFirBlk + 8 * lane;
+    const int r = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int64_t n = a.t - a.lo;                       // cached rows in the window
+    const int64_t chunk = (n + a.R - 1) / a.R;
+    const int64_t s_begin = a.lo + (int64_t)r * chunk;
+    const int64_t s_end = (s_begin + chunk < a.t) ? s_begin + chunk : a.t;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    if (c0 < a.s.D) {
+        const int64_t g = c0 / a.s.P;
+        const float *hg = a.h + g * a.h_len + a.t;      // tap of row s: hg[-s]
+        const T *base = static_cast<const T *>(a.cache) + (b * a.cache_len) * a.s.D + c0;
+        int64_t s = s_begin + w;
+        // four rows per wave in flight
+        for (; s + 12 < s_end; s += 16) {
+            Row8<ACT> x[4];
+            float hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i].load(base + (s + 4 * i) * a.s.D);
+                hv[i] = hg[-(s + 4 * i)];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float u[8];
+                x[i].get(u);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(hv[i], u[e], acc[e]);
+            }
+        }
+        for (; s < s_end; s += 4) {
+            Row8<ACT> x;
+            x.load(base + s * a.s.D);
+            const float hv = hg[-s];
+            float u[8];
+            x.get(u);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(hv, u[e], acc[e]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[w][lane][e] = acc[e];
+    __syncthreads();
+    if (w == 0 && c0 < a.s.D) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = red[0][lane][e] + red[1][lane][e] + red[2][lane][e] + red[3][lane][e];
+        float *dst = a.part + ((int64_t)r * a.s.B + b) * a.s.D + c0;
+        reinterpret_cast<float4 *>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
+        reinterpret_cast<float4 *>(dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(256) void fir_finish_kernel(FirArgs a) {
+    using A = Act<ACT>;
+    using T = typename A::T;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= a.s.B * a.s.D) return;
+    const int64_t b = i / a.s.D, c = i - b * a.s.D;
+    const int64_t g = c / a.s.P;
+    const float u = A::ld(static_cast<const T *>(a.k) + b * a.ld_in + c) *
+                    A::ld(static_cast<const T *>(a.v) + b * a.ld_in + c);
+    T *slot = static_cast<T *>(a.cache) + (b * a.cache_len + a.t) * a.s.D + c;
+    A::st(slot, u);
+    const float uq = A::ld(slot);  // u as the cache holds it (rounded to the activation dtype)
+    float tot = a.h[g * a.h_len] * uq;
+    for (int r = 0; r < a.R; ++r) tot += a.part[((int64_t)r * a.s.B + b) * a.s.D + c];
+    A::st(static_cast<T *>(a.y) + b * a.ld_y + c, A::ld(static_cast<const T *>(a.q) + b * a.ld_in + c) * tot);
+}
+
+template <int ACT>
+__global__ __launch_bounds__(256) void fir_fill_kernel(FirArgs a, int64_t L, int64_t total) {
+    using A = Act<ACT>;
+    using T = typename A::T;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t c = i % a.s.D, bt = i / a.s.D, t = bt % L, b = bt / L;
+        const int64_t in = (b * L + t) * a.ld_in + c;
+        const float u = A::ld(static_cast<const T *>(a.k) + in) * A::ld(static_cast<const T *>(a.v) + in);
+        A::st(static_cast<T *>(a.cache) + (b * a.cache_len + t) * a.s.D + c, u);
+    }
+}
+
+}  // namespace
+
+int fir_ranges(int64_t B, int64_t D) {
+    const int64_t blocks = B * ((D + kFirBlk - 1) / kFirBlk);
+    int64_t R = (2048 + blocks - 1) / (blocks > 0 ? blocks : 1);  // ~2048 workgroups in pass 1
+    if (R < 1) R = 1;
+    if (R > 64) R = 64;
+    return (int)R;
+}
+
+hipError_t launch_fir_decode(const FirArgs &a, hipStream_t stream) {
+    const dim3 g1((unsigned)((a.s.D + kFirBlk - 1) / kFirBlk), (unsigned)a.R, (unsigned)a.s.B);
+    const dim3 g2((unsigned)((a.s.B * a.s.D + 255) / 256));
+    if (a.s.act == kBF16) {
+        fir_partial_kernel<kBF16><<<g1, dim3(256), 0, stream>>>(a);
+        fir_finish_kernel<kBF16><<<g2, dim3(256), 0, stream>>>(a);
+    } else {
+        fir_partial_kernel<kF32><<<g1, dim3(256), 0, stream>>>(a);
+        fir_finish_kernel<kF32><<<g2, dim3(256), 0, stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fir_fill(const FirArgs &a, int64_t L, hipStream_t stream) {
+    const int64_t total = a.s.B * L * a.s.D;
+    if (total == 0) return hipSuccess;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (a.s.act == kBF16)
+        fir_fill_kernel<kBF16><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(a, L, total);
+    else
+        fir_fill_kernel<kF32><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(a, L, total);
+    return hipGetLastError();
+}
+
+}  // namespace hm

@@ -245,6 +245,85 @@ hm_status hyena_filter_materialize(const hm_desc *desc, int64_t L, float *h_out,
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
 }
 
+static hm_status fir_check(const hm_desc *desc, const void *cache, int64_t cache_len) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if (cache_len < 1 || desc->batch > kMaxElems / cache_len || desc->batch * cache_len > kMaxElems / desc->channels)
+        return HM_ERR_INVALID_ARG;
+    if (desc->batch > 0 && !cache) return HM_ERR_INVALID_ARG;
+    if (desc->channels % 8 != 0 || (desc->channels / desc->heads) % 8 != 0) return HM_ERR_UNSUPPORTED;
+    if (desc->batch > 0 && !aligned(cache, 16)) return HM_ERR_UNSUPPORTED;
+    return HM_OK;
+}
+
+hm_status hyena_fir_workspace(const hm_desc *desc, size_t *bytes) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if (!bytes) return HM_ERR_INVALID_ARG;
+    *bytes = (size_t)hm::fir_ranges(desc->batch, desc->channels) * desc->batch * desc->channels * sizeof(float);
+    return HM_OK;
+}
+
+hm_status hyena_fir_cache_fill(const hm_desc *desc, int64_t L, const void *k, const void *v, int64_t ld_in,
+                               void *u_cache, int64_t cache_len, void *stream) {
+    hm_status st = fir_check(desc, u_cache, cache_len);
+    if (st != HM_OK) return st;
+    if (L < 0 || L > cache_len) return HM_ERR_INVALID_ARG;
+    if (desc->batch == 0 || L == 0) return HM_OK;
+    if ((st = check_act(desc, k)) != HM_OK || (st = check_act(desc, v)) != HM_OK) return st;
+    if (ld_in < desc->channels || desc->batch * L > kMaxElems / ld_in) return HM_ERR_INVALID_ARG;
+    hm::FirArgs a{};
+    a.s = shape_of(desc);
+    a.k = k;
+    a.v = v;
+    a.ld_in = ld_in;
+    a.cache = u_cache;
+    a.cache_len = cache_len;
+    const hipError_t err = hm::launch_fir_fill(a, L, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+hm_status hyena_fir_decode_step(const hm_desc *desc, const float *h, int64_t h_len, int64_t window, int64_t t,
+                                const void *q, const void *k, const void *v, int64_t ld_in, void *y,
+                                int64_t ld_y, void *u_cache, int64_t cache_len, void *workspace,
+                                size_t ws_bytes, void *stream) {
+    hm_status st = fir_check(desc, u_cache, cache_len);
+    if (st != HM_OK) return st;
+    if (t < 0 || t >= cache_len || window < 0) return HM_ERR_INVALID_ARG;
+    const int64_t taps = (window == 0 || window > t + 1) ? t + 1 : window;
+    if (!h || h_len < taps || h_len > kMaxElems / desc->heads) return HM_ERR_INVALID_ARG;
+    if (!aligned(h, 4)) return HM_ERR_UNSUPPORTED;
+    if (desc->batch == 0) return HM_OK;
+    if ((st = check_act(desc, q)) != HM_OK || (st = check_act(desc, k)) != HM_OK ||
+        (st = check_act(desc, v)) != HM_OK || (st = check_act(desc, y)) != HM_OK)
+        return st;
+    if (ld_in < desc->channels || ld_y < desc->channels) return HM_ERR_INVALID_ARG;
+    if (desc->batch > kMaxElems / ld_in || desc->batch > kMaxElems / ld_y) return HM_ERR_INVALID_ARG;
+    if (desc->batch > 65535) return HM_ERR_UNSUPPORTED;  // grid z
+    const int R = hm::fir_ranges(desc->batch, desc->channels);
+    const size_t need = (size_t)R * desc->batch * desc->channels * sizeof(float);
+    if (!workspace || ws_bytes < need) return HM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return HM_ERR_UNSUPPORTED;
+    hm::FirArgs a{};
+    a.s = shape_of(desc);
+    a.h = h;
+    a.h_len = h_len;
+    a.t = t;
+    a.lo = t + 1 - taps;
+    a.R = R;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.ld_in = ld_in;
+    a.y = y;
+    a.ld_y = ld_y;
+    a.cache = u_cache;
+    a.cache_len = cache_len;
+    a.part = static_cast<float *>(workspace);
+    const hipError_t err = hm::launch_fir_decode(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
 hm_status hyena_row_rms(const void *x, int64_t M, int64_t D, int64_t ld, float eps, float *inv_rms,
                         void *stream) {
     if (M < 0 || D < 1 || ld < D || M > kMaxElems / ld || !(eps >= 0.0f)) return HM_ERR_INVALID_ARG;

@@ -182,6 +182,26 @@ struct GemmArgs {
 constexpr int kSplitBN = 64, kSplitKS = 256;
 size_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+// Explicit-filter (non-distilled) decode step and its u cache.
+struct FirArgs {
+    OpShape s;
+    const float *h;     // [H][h_len] taps
+    int64_t h_len;
+    int64_t t;          // position of the token being generated
+    int64_t lo;         // first cached row in the window
+    int R;              // row ranges of pass 1
+    const void *q, *k, *v;
+    int64_t ld_in;
+    void *y;
+    int64_t ld_y;
+    void *cache;        // [B][cache_len][D] activation dtype
+    int64_t cache_len;
+    float *part;        // [R][B][D] fp32
+};
+int fir_ranges(int64_t B, int64_t D);
+hipError_t launch_fir_decode(const FirArgs &a, hipStream_t stream);
+hipError_t launch_fir_fill(const FirArgs &a, int64_t L, hipStream_t stream);
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; none synchronises.
 

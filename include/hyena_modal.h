@@ -262,6 +262,40 @@ hm_status hyena_dense_rms_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A
                                   const void *W, int64_t ldw, float eps, void *C, int64_t ldc,
                                   void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Non-distilled baseline: the Hyena operator's decode step through its
+ * explicit long filter (StripedHyena article, Hyena層次結構) instead of the
+ * modal recurrence -- the O(t)-per-token cost that distillation removes
+ * (Laughing Hyena Distillery review, 研究动机与目标).  Per batch row b and
+ * channel c in head g, at position t:
+ *     u_t = k v  (appended to the cache, rounded to the activation dtype)
+ *     y_t = q * sum_{j=0}^{min(t, W-1)} h[g][j] u_{t-j}
+ * with W = window (0: every past step; > 0: the filter truncated to W taps).
+ *
+ *   u_cache  [B][cache_len][D] activation dtype, rows 0 .. t-1 filled by
+ *            earlier steps or by hyena_fir_cache_fill; row t is written here.
+ *   h        [H][h_len] float32 taps (e.g. from hyena_filter_materialize),
+ *            h_len >= min(t + 1, W) (else HM_ERR_INVALID_ARG).
+ *   q, k, v  [B][ld_in], y [B][ld_y], one token per batch row.
+ *   workspace  float32 partial sums, hyena_fir_workspace bytes (256-byte
+ *            aligned; scratch).
+ * Requirements: D and D/H multiples of 8, u_cache 16-byte aligned (else
+ * HM_ERR_UNSUPPORTED); 0 <= t < cache_len.  The modal state is not used.
+ */
+hm_status hyena_fir_workspace(const hm_desc *desc, size_t *bytes);
+
+hm_status hyena_fir_decode_step(const hm_desc *desc, const float *h, int64_t h_len, int64_t window,
+                                int64_t t, const void *q, const void *k, const void *v, int64_t ld_in,
+                                void *y, int64_t ld_y, void *u_cache, int64_t cache_len,
+                                void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * u_cache[b][t][c] = k[b][t][c] v[b][t][c] (rounded to the activation dtype)
+ * for t < L: the prompt's rows of the cache.  k, v [B][L][ld_in].
+ */
+hm_status hyena_fir_cache_fill(const hm_desc *desc, int64_t L, const void *k, const void *v,
+                               int64_t ld_in, void *u_cache, int64_t cache_len, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,6 +15,9 @@ rms_inv(), dense()      the projected stack's per-token inverse RMS and a float6
                         matrix product (numpy's matmul as the library primitive).
 stack_layer()           one layer of the projected stack, teacher-forced on a given
                         input sequence (see ``stack_layer``'s docstring).
+fir_conv()              the same operator with an explicit (possibly truncated)
+                        filter over a cache of u rounded to the activation dtype:
+                        the non-distilled decode baseline.
 
 The operator, its readings and its pins are described at the top of
 ``modal_oracle.c``.
@@ -155,6 +158,65 @@ def modal_scan(params, q, k, v, state=None, channels=None, batch_axis=0, time_ax
     if rc:
         raise ValueError("oracle_modal_scan rejected its arguments")
     return y, state
+
+
+# ------------------------------------------------------------ explicit-filter (FIR) Hyena
+
+
+def round_to_act(x, act: str) -> np.ndarray:
+    """Round float64 values once to the activation dtype (IEEE round to nearest
+    even) and return them widened back to float64.  act: "f64" (no rounding),
+    "f32", or "bf16" (the top 16 bits of the float32 pattern, rounded on the
+    lower 16 with ties to even)."""
+    x = np.asarray(x, dtype=np.float64)
+    if act == "f64":
+        return x.copy()
+    f = x.astype(np.float32)  # round to nearest even, once
+    if act == "f32":
+        return f.astype(np.float64)
+    if act != "bf16":
+        raise ValueError(act)
+    if not np.array_equal(f.astype(np.float64), x):
+        raise ValueError("bf16 rounding expects float32-exact inputs (products of bf16 values are)")
+    bits = f.view(np.uint32).astype(np.uint64)
+    rounded = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16) << 16
+    return rounded.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _widen(a) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_to_f64(a)
+    return a.astype(np.float64)
+
+
+def fir_conv(h, q, k, v, act: str, window: int = 0, t_from: int = 0, heads=None) -> np.ndarray:
+    """The non-distilled Hyena operator evaluated as an explicit finite filter.
+
+    y[b,t,c] = q[b,t,c] * sum_{j=0}^{min(t, W-1)} h[g(c), j] * u[b, t-j, c],   t >= t_from,
+    with u = k v rounded once to the activation dtype ``act`` (an FIR cache keeps
+    past u in that dtype) and W = ``window`` (<= 0: every past step).
+    h: [H][>= T] float64 taps; q, k, v: [B][T][C] float32, bfloat16 bit patterns
+    (uint16) or float64; heads: the head of each of the C channels (default
+    c // (C / H)).  Returns y [B][T - t_from][C] float64.
+    """
+    h = np.asarray(h, dtype=np.float64)
+    q64, k64, v64 = _widen(q), _widen(k), _widen(v)
+    B, T, C = q64.shape
+    if heads is None:
+        heads = np.arange(C) // (C // h.shape[0])
+    W = T if window <= 0 else min(int(window), T)
+    if h.shape[1] < W:
+        raise ValueError("filter shorter than the window")
+    u = round_to_act(k64 * v64, act)
+    taps = h[np.asarray(heads)]  # [C][Lh]
+    y = np.zeros((B, T - t_from, C))
+    for j in range(W):
+        t0 = max(j, t_from)
+        if t0 >= T:
+            continue
+        y[:, t0 - t_from:, :] += taps[:, j][None, None, :] * u[:, t0 - j:T - j, :]
+    return y * q64[:, t_from:, :]
 
 
 # ------------------------------------------------------------ projected stack

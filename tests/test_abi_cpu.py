@@ -263,3 +263,40 @@ def test_split_k_workspace_contract(lib):
         hb.hyena_dense_rms_bf16(64, 2048, 2048, FAKE, 2048, FAKE, 2048, 1e-6, FAKE, 2048, stream=0,
                                 workspace=FAKE, ws_bytes=16)
     assert e.value.status == hb.HM_ERR_WORKSPACE
+
+
+def test_fir_validation(lib):
+    d = _desc(batch=2, channels=64, heads=4)
+    need = hb.hyena_fir_workspace(d)
+    assert need > 0 and need % (2 * 64 * 4) == 0
+
+    def step(**kw):
+        a = dict(h=FAKE, h_len=100, window=0, t=50, q=FAKE, k=FAKE, v=FAKE, ld_in=64, y=FAKE, ld_y=64,
+                 cache=FAKE, cache_len=200, ws=FAKE, ws_bytes=need, desc=d)
+        a.update(kw)
+        st = lib.hyena_fir_decode_step(ctypes.byref(a["desc"]), a["h"], a["h_len"], a["window"], a["t"],
+                                       a["q"], a["k"], a["v"], a["ld_in"], a["y"], a["ld_y"], a["cache"],
+                                       a["cache_len"], a["ws"], a["ws_bytes"], None)
+        return st
+
+    cases = [
+        (dict(t=200), hb.HM_ERR_INVALID_ARG),                 # t beyond the cache
+        (dict(t=-1), hb.HM_ERR_INVALID_ARG),
+        (dict(window=-2), hb.HM_ERR_INVALID_ARG),
+        (dict(h_len=50), hb.HM_ERR_INVALID_ARG),              # full window needs t + 1 taps
+        (dict(h=None), hb.HM_ERR_INVALID_ARG),
+        (dict(ld_in=32), hb.HM_ERR_INVALID_ARG),
+        (dict(cache=FAKE + 8), hb.HM_ERR_UNSUPPORTED),        # cache rows must be 16-byte aligned
+        (dict(ws=None), hb.HM_ERR_WORKSPACE),
+        (dict(ws_bytes=need - 4), hb.HM_ERR_WORKSPACE),
+        (dict(ws=FAKE + 64), hb.HM_ERR_UNSUPPORTED),
+        (dict(desc=_desc(batch=2, channels=60, heads=4)), hb.HM_ERR_UNSUPPORTED),  # D not a multiple of 8
+        (dict(desc=_desc(batch=2, channels=48, heads=4)), hb.HM_ERR_UNSUPPORTED),  # head dim 12
+    ]
+    for kw, status in cases:
+        assert step(**kw) == status, kw
+    # a truncated window needs only W taps: validation passes up to the launch,
+    # which needs a GPU, so only the zero-batch call is made here
+    assert step(desc=_desc(batch=0, channels=64, heads=4), h_len=8, window=8) == hb.HM_OK
+    assert lib.hyena_fir_cache_fill(ctypes.byref(d), 201, FAKE, FAKE, 64, FAKE, 200, None) == hb.HM_ERR_INVALID_ARG
+    assert lib.hyena_fir_cache_fill(ctypes.byref(d), 0, FAKE, FAKE, 64, FAKE, 200, None) == hb.HM_OK

@@ -331,3 +331,59 @@ def test_rms_and_dense_special_cases():
     e[0, 11] = 1.0
     assert np.array_equal(oracle.dense(e, w)[0], w[:, 11])
     assert oracle.dense(x, w).shape == (3, 7)
+
+
+def test_fir_conv_full_window_equals_modal_recurrence(oracle_lib):
+    """The explicit-filter form over every past step is the modal recurrence:
+    float64 inputs (no cache rounding) and the float64 taps of the closed form."""
+    import oracle
+    rng = np.random.default_rng(21)
+    B, T, D, H, d = 2, 300, 8, 2, 5
+    params = _random_params(rng, H, d, 0.8, 0.999)
+    q, k, v = (rng.standard_normal((B, T, D)) for _ in range(3))
+    h = oracle_lib.filter_taps(params, T)
+    y_fir = oracle.fir_conv(h, q, k, v, "f64")
+    y_rec, _ = oracle_lib.modal_scan(params, q, k, v)
+    assert np.max(np.abs(y_fir - y_rec)) <= 1e-11 * np.max(np.abs(y_rec))
+    # decode-only outputs and a channel subset with explicit heads agree with the full run
+    sub = np.array([1, 6])
+    y_sub = oracle.fir_conv(h, q[:, :, sub], k[:, :, sub], v[:, :, sub], "f64", t_from=250,
+                            heads=sub // (D // H))
+    assert np.max(np.abs(y_sub - y_fir[:, 250:, sub])) <= 1e-14 * np.max(np.abs(y_rec))
+
+
+def test_fir_conv_truncated_window_closed_forms():
+    """W = 1 reduces to q h[0] u; an impulse u = e_0 with q = 1 returns the
+    first W taps and zeros after them."""
+    import oracle
+    rng = np.random.default_rng(22)
+    B, T, D, H = 1, 40, 4, 2
+    h = rng.standard_normal((H, T))
+    q, k, v = (rng.standard_normal((B, T, D)) for _ in range(3))
+    heads = np.arange(D) // (D // H)
+    y1 = oracle.fir_conv(h, q, k, v, "f64", window=1)
+    assert np.allclose(y1, q * h[heads, 0][None, None, :] * k * v, rtol=1e-15, atol=0)
+    kk = np.zeros((B, T, D))
+    kk[:, 0, :] = 1.0
+    for W in (1, 7, T):
+        y = oracle.fir_conv(h, np.ones((B, T, D)), kk, np.ones((B, T, D)), "f64", window=W)
+        expect = np.where(np.arange(T)[:, None] < W, h[heads].T[:T], 0.0)
+        assert np.array_equal(y[0], expect), W
+
+
+def test_fir_cache_rounding_to_bfloat16():
+    """The cache keeps u in the activation dtype: (1 + 2^-7)^2 = 1 + 2^-6 + 2^-14
+    rounds to 1 + 2^-6 in bfloat16 (ties-to-even elsewhere), exactly in float32."""
+    import oracle
+    one_p = np.uint16(0x3F81)  # 1 + 2^-7 in bfloat16
+    k = np.full((1, 1, 2), one_p, dtype=np.uint16)
+    h = np.array([[3.0]])
+    y_bf = oracle.fir_conv(h, np.full((1, 1, 2), np.uint16(0x3F80)), k, k, "bf16")
+    assert np.all(y_bf == 3.0 * (1 + 2 ** -6))
+    k32 = np.full((1, 1, 2), 1 + 2 ** -7, dtype=np.float32)
+    y32 = oracle.fir_conv(h, np.ones((1, 1, 2), np.float32), k32, k32, "f32")
+    assert np.all(y32 == 3.0 * (1 + 2 ** -6 + 2 ** -14))
+    # ties to even: 1 + 2^-8 (exactly halfway between 1 and 1 + 2^-7) rounds down to 1,
+    # 1 + 3 * 2^-8 rounds up to 1 + 2^-6
+    assert oracle.round_to_act(np.array([1 + 2 ** -8]), "bf16")[0] == 1.0
+    assert oracle.round_to_act(np.array([1 + 3 * 2 ** -8]), "bf16")[0] == 1 + 2 ** -6
