@@ -41,11 +41,13 @@ VALU_F32_PEAK_TFLOPS = 78.6    # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, unp
 
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "distilled_modal_ssm_amd", "csrc")
-# Sources whose change invalidates a hardware-counter measurement of a kernel.
+# Sources whose change invalidates a hardware-counter measurement of a kernel:
+# the kernel's own file (its code and launch configuration) and the shared
+# device header.
 KERNEL_SOURCES = {
-    "decode_step_fixed": ["decode.hip", "hm_internal.hpp", "hm_api.cpp"],
-    "chunk_mfma_kernel": ["prefill_mfma.hip", "prefill.hip", "hm_internal.hpp", "hm_api.cpp"],
-    "chunk_scan_kernel": ["prefill.hip", "hm_internal.hpp", "hm_api.cpp"],
+    "decode_step_fixed": ["decode.hip", "hm_internal.hpp"],
+    "chunk_mfma_kernel": ["prefill_mfma.hip", "prefill.hip", "hm_internal.hpp"],
+    "chunk_scan_kernel": ["prefill.hip", "hm_internal.hpp"],
 }
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read, 1 GiB written
 
