@@ -512,6 +512,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_fir:
+        res["fft_prefill"] = fft_prefill_baseline(cfg, op, q, k, v, ms_prefill, stream)
         for window in (0, 256):
             res[f"fir_baseline_w{window}"] = fir_baseline(cfg, op, k, v, dq, dk, dv, window,
                                                           ms_decode_launch, stream)
@@ -521,6 +522,37 @@ def main():
         log("[bench] cpu baseline (float64 oracle)")
         res["cpu_baseline"] = cpu_baseline(cfg, params, inp, dec)
     emit(args, res)
+
+
+def fft_prefill_baseline(cfg, op, q, k, v, ms_modal_prefill, stream):
+    """The same prompt through the FFT convolution (Hyena's own prefill), 20
+    calls timed with HIP events, outside the timed step; None beyond the
+    transform length the library supports."""
+    import torch
+    from distilled_modal_ssm_amd import binding as hb
+    if cfg.L > 4096:
+        return None
+    log("[bench] FFT prefill baseline")
+    n = hb.hyena_fft_prefill_workspace(op.desc, cfg.L)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=op.device)
+    yf = torch.empty((cfg.B, cfg.L, cfg.D), dtype=op.tdtype, device=op.device)
+
+    def call():
+        hb.hyena_fft_prefill(op.desc, cfg.L, q, k, v, cfg.D, yf, cfg.D, ws, n, stream)
+
+    call()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+    for e in ev:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    byts = 4 * cfg.act_bytes * cfg.B * cfg.L * cfg.D
+    del ws, yf
+    return {"ms": ms, "tokens_per_s": cfg.B * cfg.L / (ms / 1e3), "hbm_GBs": byts / ms * 1e-6,
+            "modal_prefill_speedup": ms / ms_modal_prefill}
 
 
 def fir_baseline(cfg, op, k, v, dq, dk, dv, window, ms_modal_step, stream):

@@ -45,6 +45,8 @@ EXPORTS = (
     "hyena_fir_workspace",
     "hyena_fir_decode_step",
     "hyena_fir_cache_fill",
+    "hyena_fft_prefill_workspace",
+    "hyena_fft_prefill",
 )
 
 
@@ -118,6 +120,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "hyena_fir_workspace": ([D, ctypes.POINTER(sz)], ctypes.c_int),
             "hyena_fir_decode_step": ([D, p, i64, i64, i64, p, p, p, i64, p, i64, p, i64, p, sz, p], ctypes.c_int),
             "hyena_fir_cache_fill": ([D, i64, p, p, i64, p, i64, p], ctypes.c_int),
+            "hyena_fft_prefill_workspace": ([D, i64, ctypes.POINTER(sz)], ctypes.c_int),
+            "hyena_fft_prefill": ([D, i64, p, p, p, i64, p, i64, p, sz, p], ctypes.c_int),
             "hyena_dense_bf16_ex": ([i64, i64, i64, p, i64, p, i64, p, p, i64, p, sz, p], ctypes.c_int),
             "hyena_dense_rms_bf16_ex": ([i64, i64, i64, p, i64, p, i64, ctypes.c_float, p, i64, p, sz, p],
                                         ctypes.c_int),
@@ -287,6 +291,19 @@ def hyena_fir_cache_fill(desc: hm_desc, L, k, v, ld_in, u_cache, cache_len, stre
     _check(st, "hyena_fir_cache_fill")
 
 
+def hyena_fft_prefill_workspace(desc: hm_desc, L: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().hyena_fft_prefill_workspace(ctypes.byref(desc), L, ctypes.byref(n)),
+           "hyena_fft_prefill_workspace")
+    return n.value
+
+
+def hyena_fft_prefill(desc: hm_desc, L, q, k, v, ld_in, y, ld_y, workspace, ws_bytes=None, stream=None) -> None:
+    st = load().hyena_fft_prefill(ctypes.byref(desc), L, _ptr(q), _ptr(k), _ptr(v), ld_in, _ptr(y), ld_y,
+                                  _ptr(workspace), _ws_bytes(workspace, ws_bytes), _stream(stream))
+    _check(st, "hyena_fft_prefill")
+
+
 # ----------------------------------------------------------------- tensor helpers
 
 
@@ -358,6 +375,17 @@ class ModalHyena:
         hyena_modal_prefill(self.desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out, ws, n,
                             stream, chunk, algo)
         return y, state_out
+
+    def fft_prefill(self, q, k, v, y=None, stream=None):
+        """The prompt through the FFT convolution (no state).  q, k, v: [B][L][ld] views."""
+        L = int(q.shape[1])
+        if y is None:
+            y = self.torch.empty((self.B, L, self.D), dtype=self.tdtype, device=self.device)
+        ld_in = _row_stride(q, (k, v))
+        n = hyena_fft_prefill_workspace(self.desc, L)
+        ws = self.torch.empty(max(n, 256), dtype=self.torch.uint8, device=self.device)
+        hyena_fft_prefill(self.desc, L, q, k, v, ld_in, y, _row_stride(y, ()), ws, n, stream)
+        return y
 
     def decode_step(self, q, k, v, state, y=None, stream=None):
         """q, k, v: [B][ld] rows.  Updates state in place; returns y [B][D]."""

@@ -324,6 +324,69 @@ hm_status hyena_fir_decode_step(const hm_desc *desc, const float *h, int64_t h_l
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
 }
 
+static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// FFT-prefill workspace: taps [H][L] fp32 | twiddles [N/2] | spectra [H][N] (complex fp32).
+static size_t fft_workspace_bytes(const hm_desc *desc, int64_t L, size_t *off_tw, size_t *off_spec) {
+    const int logn = hm::fft_log_n(L);
+    const size_t N = size_t(1) << logn;
+    *off_tw = align_up((size_t)desc->heads * L * sizeof(float));
+    *off_spec = align_up(*off_tw + N / 2 * 8);
+    return *off_spec + (size_t)desc->heads * N * 8;
+}
+
+hm_status hyena_fft_prefill_workspace(const hm_desc *desc, int64_t L, size_t *bytes) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if (!bytes || L < 0) return HM_ERR_INVALID_ARG;
+    if (L > (int64_t(1) << (hm::kFftMaxLogN - 1))) return HM_ERR_UNSUPPORTED;
+    size_t a, b;
+    *bytes = L == 0 ? 0 : fft_workspace_bytes(desc, L, &a, &b);
+    return HM_OK;
+}
+
+hm_status hyena_fft_prefill(const hm_desc *desc, int64_t L, const void *q, const void *k, const void *v,
+                            int64_t ld_in, void *y, int64_t ld_y, void *workspace, size_t ws_bytes, void *stream) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if (L < 0) return HM_ERR_INVALID_ARG;
+    if (L > (int64_t(1) << (hm::kFftMaxLogN - 1))) return HM_ERR_UNSUPPORTED;
+    if (desc->batch == 0 || L == 0) return HM_OK;
+    if ((desc->channels / desc->heads) % 2 != 0) return HM_ERR_UNSUPPORTED;  // channel pairs within a head
+    if (desc->batch > 65535 || desc->channels / 2 > INT32_MAX) return HM_ERR_UNSUPPORTED;
+    if ((st = check_act(desc, q)) != HM_OK || (st = check_act(desc, k)) != HM_OK ||
+        (st = check_act(desc, v)) != HM_OK || (st = check_act(desc, y)) != HM_OK)
+        return st;
+    if (ld_in < desc->channels || ld_y < desc->channels) return HM_ERR_INVALID_ARG;
+    if (desc->batch * L > kMaxElems / ld_in || desc->batch * L > kMaxElems / ld_y) return HM_ERR_INVALID_ARG;
+    size_t off_tw, off_spec;
+    const size_t need = fft_workspace_bytes(desc, L, &off_tw, &off_spec);
+    if (!workspace || ws_bytes < need) return HM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return HM_ERR_UNSUPPORTED;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    hm::FftArgs a{};
+    a.s = shape_of(desc);
+    a.L = L;
+    a.logn = hm::fft_log_n(L);
+    a.np = hm::fft_pairs_per_group(a.s.P, a.logn);
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.ld_in = ld_in;
+    a.y = y;
+    a.ld_y = ld_y;
+    a.h = reinterpret_cast<float *>(ws);
+    a.tw = reinterpret_cast<float2 *>(ws + off_tw);
+    a.spec = reinterpret_cast<float2 *>(ws + off_spec);
+    hm::FilterArgs f;
+    f.s = a.s;
+    f.L = L;
+    f.h = a.h;
+    hipError_t err = hm::launch_filter(f, static_cast<hipStream_t>(stream));
+    if (err == hipSuccess) err = hm::launch_fft_prefill(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
 hm_status hyena_row_rms(const void *x, int64_t M, int64_t D, int64_t ld, float eps, float *inv_rms,
                         void *stream) {
     if (M < 0 || D < 1 || ld < D || M > kMaxElems / ld || !(eps >= 0.0f)) return HM_ERR_INVALID_ARG;

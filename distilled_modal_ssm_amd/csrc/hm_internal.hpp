@@ -202,6 +202,26 @@ int fir_ranges(int64_t B, int64_t D);
 hipError_t launch_fir_decode(const FirArgs &a, hipStream_t stream);
 hipError_t launch_fir_fill(const FirArgs &a, int64_t L, hipStream_t stream);
 
+// FFT prefill (the convolution through transforms of length N = 2^logn >= 2L).
+struct FftArgs {
+    OpShape s;
+    int64_t L;
+    int logn;
+    int np;             // channel pairs per workgroup
+    const void *q, *k, *v;
+    int64_t ld_in;
+    void *y;
+    int64_t ld_y;
+    float *h;           // [H][L] taps (workspace)
+    float2 *tw;         // [N/2] twiddles (workspace)
+    float2 *spec;       // [H][N] filter spectra (workspace)
+};
+constexpr int kFftMaxLogN = 13;  // N <= 8192: prompts up to 4096 steps
+int fft_log_n(int64_t L);
+int fft_pairs_per_group(int64_t P, int logn);
+size_t fft_lds_bytes(int logn, int np);
+hipError_t launch_fft_prefill(const FftArgs &a, hipStream_t stream);
+
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; none synchronises.
 

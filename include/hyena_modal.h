@@ -296,6 +296,23 @@ hm_status hyena_fir_decode_step(const hm_desc *desc, const float *h, int64_t h_l
 hm_status hyena_fir_cache_fill(const hm_desc *desc, int64_t L, const void *k, const void *v,
                                int64_t ld_in, void *u_cache, int64_t cache_len, void *stream);
 
+/*
+ * Prefill through the FFT, Hyena's own evaluation of its long convolution
+ * (StripedHyena article, Hyena層次結構), for comparison with the modal prefill:
+ *     y[b][t][c] = q * sum_{s<=t} h_g[t-s] u[s],   u = k v,   t < L,
+ * with the filter taps materialised in float32 and the convolution computed
+ * as IFFT(FFT(u) FFT(h)) over N = the power of two >= 2L, float32 throughout.
+ * Same activation layouts as hyena_modal_prefill; no modal state in or out.
+ * Requirements: 1 <= L <= 4096 (else HM_ERR_UNSUPPORTED; L = 0 or B = 0 does
+ * nothing), D/H even.  Workspace (taps, twiddles, filter spectra):
+ * hyena_fft_prefill_workspace bytes, 256-byte aligned, scratch.
+ */
+hm_status hyena_fft_prefill_workspace(const hm_desc *desc, int64_t L, size_t *bytes);
+
+hm_status hyena_fft_prefill(const hm_desc *desc, int64_t L, const void *q, const void *k, const void *v,
+                            int64_t ld_in, void *y, int64_t ld_y, void *workspace, size_t ws_bytes,
+                            void *stream);
+
 #ifdef __cplusplus
 }
 #endif

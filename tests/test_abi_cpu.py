@@ -300,3 +300,27 @@ def test_fir_validation(lib):
     assert step(desc=_desc(batch=0, channels=64, heads=4), h_len=8, window=8) == hb.HM_OK
     assert lib.hyena_fir_cache_fill(ctypes.byref(d), 201, FAKE, FAKE, 64, FAKE, 200, None) == hb.HM_ERR_INVALID_ARG
     assert lib.hyena_fir_cache_fill(ctypes.byref(d), 0, FAKE, FAKE, 64, FAKE, 200, None) == hb.HM_OK
+
+
+def test_fft_prefill_validation(lib):
+    d = _desc(batch=2, channels=64, heads=4)
+    n = hb.hyena_fft_prefill_workspace(d, 2048)
+    # taps [4][2048] fp32, twiddles [2048] complex, spectra [4][4096] complex
+    assert n == 4 * 2048 * 4 + 2048 * 8 + 4 * 4096 * 8
+    assert hb.hyena_fft_prefill_workspace(d, 0) == 0
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_fft_prefill_workspace(d, 4097)
+    assert e.value.status == hb.HM_ERR_UNSUPPORTED
+
+    def call(L=2048, ws=FAKE, nbytes=n, desc=d, ld=64):
+        st = lib.hyena_fft_prefill(ctypes.byref(desc), L, FAKE, FAKE, FAKE, ld, FAKE, ld, ws, nbytes, None)
+        return st
+
+    assert call(L=4097) == hb.HM_ERR_UNSUPPORTED
+    assert call(L=-1) == hb.HM_ERR_INVALID_ARG
+    assert call(ws=None) == hb.HM_ERR_WORKSPACE
+    assert call(nbytes=n - 8) == hb.HM_ERR_WORKSPACE
+    assert call(ws=FAKE + 16) == hb.HM_ERR_UNSUPPORTED
+    assert call(ld=32) == hb.HM_ERR_INVALID_ARG
+    assert call(desc=_desc(batch=2, channels=12, heads=4)) == hb.HM_ERR_UNSUPPORTED  # head dim 3 is odd
+    assert call(L=0) == hb.HM_OK
