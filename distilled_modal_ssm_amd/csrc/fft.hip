@@ -15,11 +15,10 @@
 // Kernels: filter taps (the materialise kernel) into the workspace; twiddles
 // exp(-2 pi i k / N) in float64 rounded to float32; one forward transform per
 // head (the filter spectra); then one workgroup per (batch row, group of NP
-// channel pairs): u into LDS at bit-reversed positions, radix-2
-// decimation-in-time passes (natural-order spectrum), multiply by the head's
-// spectrum, decimation-in-frequency passes with conjugate twiddles (result at
-// bit-reversed positions), gate with q and store.  The transforms run in LDS
-// (N complex float32 per pair); HBM traffic equals the modal prefill's
+// channel pairs): u into LDS, Stockham passes (radix 16 in registers, then the
+// remaining radix; natural order in and out), multiply by the head's spectrum,
+// the inverse as conj(FFT(conj(.))), gate with q and store.  The transforms run
+// in LDS (N complex float32 per pair); HBM traffic equals the modal prefill's
 // (q, k, v read once, y written once), the work is O(L log L) per channel.
 // No end-of-prompt modal state comes out of this path.
 #include "hm_internal.hpp"
@@ -30,46 +29,112 @@ namespace {
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
     return make_float2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
 }
-__device__ __forceinline__ float2 cmul_conj(float2 a, float2 w) {  // a * conj(w)
-    return make_float2(a.x * w.x + a.y * w.y, a.y * w.x - a.x * w.y);
-}
-__device__ __forceinline__ unsigned bitrev(unsigned i, int logn) { return __brev(i) >> (32 - logn); }
+__device__ __forceinline__ float2 conj2(float2 a) { return make_float2(a.x, -a.y); }
 
-// In-place radix-2 DIT over NP transforms of length N = 2^logn held back to
-// back in x (input bit-reversed, output natural).  tw[k] = exp(-2 pi i k / N).
-__device__ void fft_dit(float2 *x, const float2 *tw, int logn, int np) {
-    const int N = 1 << logn;
-    for (int s = 1; s <= logn; ++s) {
-        const int half = 1 << (s - 1), stride = N >> s;
-        for (int i = threadIdx.x; i < np * (N / 2); i += blockDim.x) {
-            const int p = i / (N / 2), k = i % (N / 2);
-            const int j = k & (half - 1), a = ((k >> (s - 1)) << s) + j;
-            float2 *xp = x + p * N;
-            const float2 t = cmul(tw[j * stride], xp[a + half]);
-            const float2 u = xp[a];
-            xp[a] = make_float2(u.x + t.x, u.y + t.y);
-            xp[a + half] = make_float2(u.x - t.x, u.y - t.y);
-        }
-        __syncthreads();
-    }
+// LDS index with one pad entry per 16: the first Stockham pass writes with a
+// stride of R = 16 entries, which the pad spreads over all banks.
+__device__ __forceinline__ int pad(int i) { return i + (i >> 4); }
+constexpr int padded(int n) { return n + (n >> 4); }
+
+// cos / sin of 2 pi m / 16, m < 8
+__device__ constexpr float kC16[8] = {1.0f, 0.92387953251128674f, 0.70710678118654752f, 0.38268343236508977f,
+                                      0.0f, -0.38268343236508977f, -0.70710678118654752f, -0.92387953251128674f};
+__device__ constexpr float kS16[8] = {0.0f, 0.38268343236508977f, 0.70710678118654752f, 0.92387953251128674f,
+                                      1.0f, 0.92387953251128674f, 0.70710678118654752f, 0.38268343236508977f};
+
+constexpr int rev_bits(int i, int bits) {
+    int r = 0;
+    for (int b = 0; b < bits; ++b) r |= ((i >> b) & 1) << (bits - 1 - b);
+    return r;
 }
 
-// In-place radix-2 DIF with conjugate twiddles (the inverse transform without
-// its 1/N): input natural, output bit-reversed.
-__device__ void ifft_dif(float2 *x, const float2 *tw, int logn, int np) {
-    const int N = 1 << logn;
-    for (int s = logn; s >= 1; --s) {
-        const int half = 1 << (s - 1), stride = N >> s;
-        for (int i = threadIdx.x; i < np * (N / 2); i += blockDim.x) {
-            const int p = i / (N / 2), k = i % (N / 2);
-            const int j = k & (half - 1), a = ((k >> (s - 1)) << s) + j;
-            float2 *xp = x + p * N;
-            const float2 u = xp[a], v = xp[a + half];
-            xp[a] = make_float2(u.x + v.x, u.y + v.y);
-            xp[a + half] = cmul_conj(make_float2(u.x - v.x, u.y - v.y), tw[j * stride]);
+// In-register DFT of R points (R in {2, 4, 8, 16}): X[k] = sum_r v[r] exp(-2 pi i r k / R),
+// radix-2 decimation in time on the bit-reversed register order (all indices
+// compile-time constants).
+template <int R>
+__device__ __forceinline__ void dft_regs(float2 (&v)[R]) {
+    constexpr int LR = R == 2 ? 1 : R == 4 ? 2 : R == 8 ? 3 : 4;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int j = rev_bits(i, LR);
+        if (i < j) {
+            const float2 t = v[i];
+            v[i] = v[j];
+            v[j] = t;
         }
-        __syncthreads();
     }
+#pragma unroll
+    for (int len = 2; len <= R; len <<= 1)
+#pragma unroll
+        for (int i = 0; i < R; i += len)
+#pragma unroll
+            for (int k = 0; k < len / 2; ++k) {
+                const int m = k * (16 / len);  // exp(-2 pi i k / len) = exp(-2 pi i m / 16)
+                const float2 w = make_float2(kC16[m], -kS16[m]);
+                const float2 t = cmul(w, v[i + k + len / 2]);
+                const float2 a = v[i + k];
+                v[i + k] = make_float2(a.x + t.x, a.y + t.y);
+                v[i + k + len / 2] = make_float2(a.x - t.x, a.y - t.y);
+            }
+}
+
+// exp(-2 pi i k / N) for k < N from the half table tw[0 .. N/2)
+__device__ __forceinline__ float2 twiddle(const float2 *tw, int k, int half) {
+    const float2 w = tw[k < half ? k : k - half];
+    return k < half ? w : make_float2(-w.x, -w.y);
+}
+
+// One Stockham radix-R pass over N points (Ns = product of the radices
+// already applied): butterfly j reads x[j + r N/R], twiddles by
+// exp(-2 pi i (j mod Ns) r / (Ns R)), and writes x[(j / Ns) Ns R + j mod Ns +
+// r Ns] -- natural order in and out, in place through registers (read all,
+// barrier, write all).  256 threads.
+template <int R, int N>
+__device__ __forceinline__ void stockham_pass(float2 *x, const float2 *tw, int Ns) {
+    constexpr int nb = N / R;
+    constexpr int MI = nb > 256 ? (nb + 255) / 256 : 1;  // butterflies per thread
+    const int tid = threadIdx.x;
+    float2 v[MI][R];
+#pragma unroll
+    for (int it = 0; it < MI; ++it) {
+        const int j = tid + 256 * it;
+        if (j < nb) {
+            const int k = j & (Ns - 1), step = N / (Ns * R);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float2 a = x[pad(j + r * nb)];
+                v[it][r] = r == 0 ? a : cmul(twiddle(tw, k * r * step, N / 2), a);
+            }
+            dft_regs<R>(v[it]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < MI; ++it) {
+        const int j = tid + 256 * it;
+        if (j < nb) {
+            const int base = (j / Ns) * Ns * R + (j & (Ns - 1));
+#pragma unroll
+            for (int r = 0; r < R; ++r) x[pad(base + r * Ns)] = v[it][r];
+        }
+    }
+    __syncthreads();
+}
+
+// Forward transform of N = 2^LOGN points in place (natural order).  Radix 16
+// from N = 4096 up (256 butterflies per pass or more), radix 4 below, so every
+// thread holds a butterfly; then one pass of the remaining radix.
+template <int LOGN>
+__device__ void fft_forward(float2 *x, const float2 *tw) {
+    constexpr int N = 1 << LOGN;
+    constexpr int LR = LOGN >= 12 ? 4 : 2;  // log2 of the main radix
+    constexpr int MAIN = LOGN / LR, REST = LOGN % LR;
+    int Ns = 1;
+#pragma unroll
+    for (int p = 0; p < MAIN; ++p, Ns <<= LR) stockham_pass<(1 << LR), N>(x, tw, Ns);
+    if constexpr (REST == 3) stockham_pass<8, N>(x, tw, Ns);
+    if constexpr (REST == 2) stockham_pass<4, N>(x, tw, Ns);
+    if constexpr (REST == 1) stockham_pass<2, N>(x, tw, Ns);
 }
 
 __global__ __launch_bounds__(256) void fft_twiddle_kernel(float2 *tw, int logn) {
@@ -82,59 +147,75 @@ __global__ __launch_bounds__(256) void fft_twiddle_kernel(float2 *tw, int logn) 
 }
 
 // One workgroup per head: spectrum of the zero-padded taps.
+template <int LOGN>
 __global__ __launch_bounds__(256) void fft_filter_spectrum_kernel(FftArgs a) {
     extern __shared__ float2 lds[];
-    const int N = 1 << a.logn;
+    constexpr int N = 1 << LOGN;
     float2 *tw = lds, *x = lds + N / 2;
     const int64_t g = blockIdx.x;
     for (int i = threadIdx.x; i < N / 2; i += blockDim.x) tw[i] = a.tw[i];
-    for (int i = threadIdx.x; i < N; i += blockDim.x) {
-        const float v = i < a.L ? a.h[g * a.L + i] : 0.f;
-        x[bitrev((unsigned)i, a.logn)] = make_float2(v, 0.f);
-    }
+    for (int i = threadIdx.x; i < N; i += blockDim.x)
+        x[pad(i)] = make_float2(i < a.L ? a.h[g * a.L + i] : 0.f, 0.f);
     __syncthreads();
-    fft_dit(x, tw, a.logn, 1);
-    for (int i = threadIdx.x; i < N; i += blockDim.x) a.spec[g * N + i] = x[i];
+    fft_forward<LOGN>(x, tw);
+    for (int i = threadIdx.x; i < N; i += blockDim.x) a.spec[g * N + i] = x[pad(i)];
 }
 
-template <int ACT>
+// Workgroup = (batch row, NP channel pairs of one head).
+template <int ACT, int NP, int LOGN>
 __global__ __launch_bounds__(256) void fft_conv_kernel(FftArgs a) {
     using A = Act<ACT>;
     using T = typename A::T;
     extern __shared__ float2 lds[];
-    const int N = 1 << a.logn, np = a.np;
-    float2 *tw = lds, *x = lds + N / 2;
-    const int64_t b = blockIdx.y;
-    const int64_t c0 = (int64_t)blockIdx.x * 2 * np;  // first channel of the group (one head)
+    constexpr int N = 1 << LOGN, NPD = padded(1 << LOGN);
+    float2 *tw = lds, *xs = lds + N / 2;
+    // Neighbouring channel groups share the cache lines of every row: give
+    // each XCD (workgroups are dealt to the 8 XCDs round robin) a contiguous
+    // range of groups so those lines are fetched into one L2.
+    const int64_t nwg = (int64_t)gridDim.x * gridDim.y;
+    int64_t id = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    if (nwg % 8 == 0) id = (id % 8) * (nwg / 8) + id / 8;
+    const int64_t b = id / gridDim.x;
+    const int64_t c0 = (id % gridDim.x) * 2 * NP;
     const int64_t g = c0 / a.s.P;
     for (int i = threadIdx.x; i < N / 2; i += blockDim.x) tw[i] = a.tw[i];
-    // u = k v of the 2 np channels: pair p -> real part channel c0+2p, imaginary c0+2p+1
+    // u = k v: pair p holds channel c0+2p (real part) and c0+2p+1 (imaginary part)
     const T *kb = static_cast<const T *>(a.k) + b * a.L * a.ld_in + c0;
     const T *vb = static_cast<const T *>(a.v) + b * a.L * a.ld_in + c0;
-    for (int i = threadIdx.x; i < np * N; i += blockDim.x) {
-        const int p = i / N, t = i % N;
-        float2 z = make_float2(0.f, 0.f);
+    for (int t = threadIdx.x; t < N; t += blockDim.x) {
+        float uk[2 * NP];
         if (t < a.L) {
-            const int64_t o = (int64_t)t * a.ld_in + 2 * p;
-            z = make_float2(A::ld(kb + o) * A::ld(vb + o), A::ld(kb + o + 1) * A::ld(vb + o + 1));
+            const int64_t o = (int64_t)t * a.ld_in;
+#pragma unroll
+            for (int e = 0; e < 2 * NP; ++e) uk[e] = A::ld(kb + o + e) * A::ld(vb + o + e);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 2 * NP; ++e) uk[e] = 0.f;
         }
-        x[p * N + bitrev((unsigned)t, a.logn)] = z;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) xs[p * NPD + pad(t)] = make_float2(uk[2 * p], uk[2 * p + 1]);
     }
     __syncthreads();
-    fft_dit(x, tw, a.logn, np);
     const float2 *hs = a.spec + g * N;
-    for (int i = threadIdx.x; i < np * N; i += blockDim.x) x[i] = cmul(x[i], hs[i % N]);
-    __syncthreads();
-    ifft_dif(x, tw, a.logn, np);
+    for (int p = 0; p < NP; ++p) {
+        float2 *x = xs + p * NPD;
+        fft_forward<LOGN>(x, tw);
+        // inverse through the forward transform: conj(FFT(conj(X H)))
+        for (int i = threadIdx.x; i < N; i += blockDim.x) x[pad(i)] = conj2(cmul(x[pad(i)], hs[i]));
+        __syncthreads();
+        fft_forward<LOGN>(x, tw);
+    }
     const float inv_n = 1.0f / (float)N;
     const T *qb = static_cast<const T *>(a.q) + b * a.L * a.ld_in + c0;
     T *yb = static_cast<T *>(a.y) + b * a.L * a.ld_y + c0;
-    for (int i = threadIdx.x; i < np * a.L; i += blockDim.x) {
-        const int p = i / a.L, t = i % a.L;
-        const float2 r = x[p * N + bitrev((unsigned)t, a.logn)];
-        const int64_t oi = (int64_t)t * a.ld_in + 2 * p, oy = (int64_t)t * a.ld_y + 2 * p;
-        A::st(yb + oy, A::ld(qb + oi) * r.x * inv_n);
-        A::st(yb + oy + 1, A::ld(qb + oi + 1) * r.y * inv_n);
+    for (int t = threadIdx.x; t < a.L; t += blockDim.x) {
+        const int64_t oi = (int64_t)t * a.ld_in, oy = (int64_t)t * a.ld_y;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const float2 r = xs[p * NPD + pad(t)];  // conj of the result: imaginary part negated
+            A::st(yb + oy + 2 * p, A::ld(qb + oi + 2 * p) * r.x * inv_n);
+            A::st(yb + oy + 2 * p + 1, -A::ld(qb + oi + 2 * p + 1) * r.y * inv_n);
+        }
     }
 }
 
@@ -146,34 +227,66 @@ int fft_log_n(int64_t L) {
     return logn;
 }
 
-// One channel pair per workgroup: N/2 twiddles + N points of LDS (48 KB at
-// N = 4096, 96 KB at N = 8192).
-int fft_pairs_per_group(int64_t, int) { return 1; }
+// Channel pairs per workgroup: measured on MI355X (bf16, D = 2048), four pairs
+// win at N = 1024 (2.5 vs 3.0 ms for B = 256, L = 512) and one pair at
+// N = 4096 (0.95 vs 1.43 ms for B = 16, L = 2048), where four fill the LDS.
+int fft_pairs_per_group(int64_t P, int logn) {
+    int np = (logn <= 10) ? 4 : 1;
+    while (np > 1 && P % (2 * np) != 0) np >>= 1;
+    return np;
+}
 
-size_t fft_lds_bytes(int logn, int np) { return ((size_t)(1 << logn) / 2 + (size_t)np * (1 << logn)) * sizeof(float2); }
+size_t fft_lds_bytes(int logn, int np) {
+    const size_t N = size_t(1) << logn;
+    return (N / 2 + (size_t)np * (N + (N >> 4))) * sizeof(float2);
+}
+
+template <int ACT, int NP, int LOGN>
+static hipError_t launch_conv(const FftArgs &a, hipStream_t stream) {
+    const size_t lds = fft_lds_bytes(LOGN, NP);
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&fft_conv_kernel<ACT, NP, LOGN>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (err != hipSuccess) return err;
+    const dim3 grid((unsigned)(a.s.D / (2 * NP)), (unsigned)a.s.B);
+    fft_conv_kernel<ACT, NP, LOGN><<<grid, dim3(256), lds, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int LOGN>
+static hipError_t launch_logn(const FftArgs &a, hipStream_t stream) {
+    const size_t lds1 = fft_lds_bytes(LOGN, 1);
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(&fft_filter_spectrum_kernel<LOGN>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
+    if (err != hipSuccess) return err;
+    fft_filter_spectrum_kernel<LOGN><<<dim3((unsigned)a.s.H), dim3(256), lds1, stream>>>(a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const bool bf = a.s.act == kBF16;
+    switch (a.np) {
+        case 4: return bf ? launch_conv<kBF16, 4, LOGN>(a, stream) : launch_conv<kF32, 4, LOGN>(a, stream);
+        case 2: return bf ? launch_conv<kBF16, 2, LOGN>(a, stream) : launch_conv<kF32, 2, LOGN>(a, stream);
+        default: return bf ? launch_conv<kBF16, 1, LOGN>(a, stream) : launch_conv<kF32, 1, LOGN>(a, stream);
+    }
+}
 
 hipError_t launch_fft_prefill(const FftArgs &a, hipStream_t stream) {
     const int N = 1 << a.logn;
     fft_twiddle_kernel<<<dim3((unsigned)((N / 2 + 255) / 256)), dim3(256), 0, stream>>>(a.tw, a.logn);
-    hipError_t e0 = hipFuncSetAttribute(reinterpret_cast<const void *>(&fft_filter_spectrum_kernel),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)fft_lds_bytes(a.logn, 1));
-    if (e0 != hipSuccess) return e0;
-    fft_filter_spectrum_kernel<<<dim3((unsigned)a.s.H), dim3(256), fft_lds_bytes(a.logn, 1), stream>>>(a);
-    const dim3 grid((unsigned)(a.s.D / (2 * a.np)), (unsigned)a.s.B);
-    const size_t lds = fft_lds_bytes(a.logn, a.np);
-    hipError_t err;
-    if (a.s.act == kBF16) {
-        if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&fft_conv_kernel<kBF16>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-            return err;
-        fft_conv_kernel<kBF16><<<grid, dim3(256), lds, stream>>>(a);
-    } else {
-        if ((err = hipFuncSetAttribute(reinterpret_cast<const void *>(&fft_conv_kernel<kF32>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
-            return err;
-        fft_conv_kernel<kF32><<<grid, dim3(256), lds, stream>>>(a);
+    switch (a.logn) {
+        case 1: return launch_logn<1>(a, stream);
+        case 2: return launch_logn<2>(a, stream);
+        case 3: return launch_logn<3>(a, stream);
+        case 4: return launch_logn<4>(a, stream);
+        case 5: return launch_logn<5>(a, stream);
+        case 6: return launch_logn<6>(a, stream);
+        case 7: return launch_logn<7>(a, stream);
+        case 8: return launch_logn<8>(a, stream);
+        case 9: return launch_logn<9>(a, stream);
+        case 10: return launch_logn<10>(a, stream);
+        case 11: return launch_logn<11>(a, stream);
+        case 12: return launch_logn<12>(a, stream);
+        case 13: return launch_logn<13>(a, stream);
+        default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace hm
