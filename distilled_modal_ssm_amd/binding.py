@@ -47,6 +47,9 @@ EXPORTS = (
     "hyena_fir_cache_fill",
     "hyena_fft_prefill_workspace",
     "hyena_fft_prefill",
+    "hyena_distill_workspace",
+    "hyena_distill_grad",
+    "hyena_distill_adam_step",
 )
 
 
@@ -98,7 +101,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                 f"{path} not found: build it with `python -m distilled_modal_ssm_amd.build` "
                 "(or __graft_entry__.build()); there is no CPU fallback")
         lib = ctypes.CDLL(path)
-        i64, p, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        i64, p, sz, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
         D = ctypes.POINTER(hm_desc)
         sig = {
             "hm_abi_version": ([], ctypes.c_int),
@@ -122,6 +125,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "hyena_fir_cache_fill": ([D, i64, p, p, i64, p, i64, p], ctypes.c_int),
             "hyena_fft_prefill_workspace": ([D, i64, ctypes.POINTER(sz)], ctypes.c_int),
             "hyena_fft_prefill": ([D, i64, p, p, p, i64, p, i64, p, sz, p], ctypes.c_int),
+            "hyena_distill_workspace": ([D, i64, ctypes.POINTER(sz)], ctypes.c_int),
+            "hyena_distill_grad": ([D, i64, p, p, p, p, p, p, sz, p], ctypes.c_int),
+            "hyena_distill_adam_step": ([i64, i64, p, p, p, p, p, p, p, p, i64, f32, f32, f32, f32, f32, p],
+                                        ctypes.c_int),
             "hyena_dense_bf16_ex": ([i64, i64, i64, p, i64, p, i64, p, p, i64, p, sz, p], ctypes.c_int),
             "hyena_dense_rms_bf16_ex": ([i64, i64, i64, p, i64, p, i64, ctypes.c_float, p, i64, p, sz, p],
                                         ctypes.c_int),
@@ -302,6 +309,27 @@ def hyena_fft_prefill(desc: hm_desc, L, q, k, v, ld_in, y, ld_y, workspace, ws_b
     st = load().hyena_fft_prefill(ctypes.byref(desc), L, _ptr(q), _ptr(k), _ptr(v), ld_in, _ptr(y), ld_y,
                                   _ptr(workspace), _ws_bytes(workspace, ws_bytes), _stream(stream))
     _check(st, "hyena_fft_prefill")
+
+
+def hyena_distill_workspace(desc: hm_desc, L: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().hyena_distill_workspace(ctypes.byref(desc), L, ctypes.byref(n)), "hyena_distill_workspace")
+    return n.value
+
+
+def hyena_distill_grad(desc: hm_desc, L, h_target, loss, g_poles, g_res, g_skip, workspace, ws_bytes=None,
+                       stream=None) -> None:
+    st = load().hyena_distill_grad(ctypes.byref(desc), L, _ptr(h_target), _ptr(loss), _ptr(g_poles), _ptr(g_res),
+                                   _ptr(g_skip), _ptr(workspace), _ws_bytes(workspace, ws_bytes), _stream(stream))
+    _check(st, "hyena_distill_grad")
+
+
+def hyena_distill_adam_step(H, d, poles, residues, skip, g_poles, g_res, g_skip, m, v, step, lr, beta1=0.9,
+                            beta2=0.999, eps=1e-8, r_max=0.9999, stream=None) -> None:
+    st = load().hyena_distill_adam_step(H, d, _ptr(poles), _ptr(residues), _ptr(skip), _ptr(g_poles), _ptr(g_res),
+                                        _ptr(g_skip), _ptr(m), _ptr(v), step, lr, beta1, beta2, eps, r_max,
+                                        _stream(stream))
+    _check(st, "hyena_distill_adam_step")
 
 
 # ----------------------------------------------------------------- tensor helpers

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhyena_modal.so")
 
-SOURCES = ["hm_api.cpp", "decode.hip", "filter.hip", "prefill.hip", "prefill_mfma.hip", "dense.hip", "fir.hip", "fft.hip"]
+SOURCES = ["hm_api.cpp", "decode.hip", "filter.hip", "prefill.hip", "prefill_mfma.hip", "dense.hip", "fir.hip", "fft.hip", "distill.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

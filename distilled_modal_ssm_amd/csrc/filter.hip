@@ -44,19 +44,8 @@ __global__ __launch_bounds__(256) void filter_kernel(FilterArgs a) {
         const double lr = lf.x, li = lf.y, rr = rf.x, ri = rf.y;
         // tap t uses lambda^(t-1): the run starts at exponent t0 - 1, or at
         // tap 0 (the skip term, added below) followed by exponents 0, 1, ...
-        int64_t e = (t0 == 0) ? 0 : t0 - 1;
-        double pr = 1.0, pi = 0.0, br = lr, bi = li;
-        while (e != 0) {
-            if (e & 1) {
-                const double nr = pr * br - pi * bi;
-                pi = pr * bi + pi * br;
-                pr = nr;
-            }
-            const double nb = br * br - bi * bi;
-            bi = 2.0 * br * bi;
-            br = nb;
-            e >>= 1;
-        }
+        double pr, pi;
+        complex_pow(lr, li, (t0 == 0) ? 0 : t0 - 1, pr, pi);
         const int first = (t0 == 0) ? 1 : 0;
 #pragma unroll
         for (int j = 0; j < kRun; ++j) {

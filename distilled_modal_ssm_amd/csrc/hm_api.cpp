@@ -8,6 +8,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include "hm_internal.hpp"
 
 namespace {
@@ -384,6 +386,94 @@ hm_status hyena_fft_prefill(const hm_desc *desc, int64_t L, const void *q, const
     f.h = a.h;
     hipError_t err = hm::launch_filter(f, static_cast<hipStream_t>(stream));
     if (err == hipSuccess) err = hm::launch_fft_prefill(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+// Distillation workspace: residual [H][L] f64 | loss partials [H][tiles] f64 | gradient partials [H*d][chunks][4] f64.
+static size_t distill_layout(const hm_desc *desc, int64_t L, size_t *off_loss, size_t *off_grad, int *tiles,
+                             int *chunks) {
+    *tiles = hm::distill_tiles(L, desc->modes);
+    *chunks = (int)((L + hm::kDistillTile - 1) / hm::kDistillTile);
+    *off_loss = align_up((size_t)desc->heads * L * sizeof(double));
+    *off_grad = align_up(*off_loss + (size_t)desc->heads * *tiles * sizeof(double));
+    return *off_grad + (size_t)desc->heads * desc->modes * *chunks * 4 * sizeof(double);
+}
+
+static bool distill_l_ok(const hm_desc *desc, int64_t L) {
+    return L >= 1 && L <= kMaxElems / desc->heads && (L + hm::kDistillTile - 1) / hm::kDistillTile <= 65535 &&
+           (int64_t)desc->heads * ((L + 127) / 128) <= INT32_MAX;
+}
+
+hm_status hyena_distill_workspace(const hm_desc *desc, int64_t L, size_t *bytes) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if (!bytes || !distill_l_ok(desc, L)) return HM_ERR_INVALID_ARG;
+    size_t a, b;
+    int t, c;
+    *bytes = distill_layout(desc, L, &a, &b, &t, &c);
+    return HM_OK;
+}
+
+hm_status hyena_distill_grad(const hm_desc *desc, int64_t L, const float *h_target, float *loss, float *g_poles,
+                             float *g_res, float *g_skip, void *workspace, size_t ws_bytes, void *stream) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if (!distill_l_ok(desc, L)) return HM_ERR_INVALID_ARG;
+    if (!h_target || !loss || !g_poles || !g_res || !g_skip) return HM_ERR_INVALID_ARG;
+    if (!aligned(h_target, 4) || !aligned(loss, 4) || !aligned(g_poles, 4) || !aligned(g_res, 4) ||
+        !aligned(g_skip, 4))
+        return HM_ERR_UNSUPPORTED;
+    hm::DistillArgs a{};
+    size_t off_loss, off_grad;
+    const size_t need = distill_layout(desc, L, &off_loss, &off_grad, &a.tiles, &a.chunks);
+    if (!workspace || ws_bytes < need) return HM_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return HM_ERR_UNSUPPORTED;
+    unsigned char *ws = static_cast<unsigned char *>(workspace);
+    a.s = shape_of(desc);
+    a.L = L;
+    a.target = h_target;
+    a.e = reinterpret_cast<double *>(ws);
+    a.loss_part = reinterpret_cast<double *>(ws + off_loss);
+    a.grad_part = reinterpret_cast<double *>(ws + off_grad);
+    a.loss = loss;
+    a.g_poles = g_poles;
+    a.g_res = g_res;
+    a.g_skip = g_skip;
+    const hipError_t err = hm::launch_distill_grad(a, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+hm_status hyena_distill_adam_step(int64_t H, int64_t d, float *poles, float *residues, float *skip,
+                                  const float *g_poles, const float *g_res, const float *g_skip, float *m, float *v,
+                                  int64_t step, float lr, float beta1, float beta2, float eps, float r_max,
+                                  void *stream) {
+    if (H < 1 || d < 1 || d > HM_MAX_MODES || H > INT32_MAX / 64) return HM_ERR_INVALID_ARG;
+    if (!poles || !residues || !skip || !g_poles || !g_res || !g_skip || !m || !v) return HM_ERR_INVALID_ARG;
+    if (step < 1 || !(lr > 0.f) || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) ||
+        !(eps > 0.f) || !(r_max > 0.f && r_max < 1.f))
+        return HM_ERR_INVALID_ARG;
+    for (const void *p : {(const void *)poles, (const void *)residues, (const void *)skip, (const void *)g_poles,
+                          (const void *)g_res, (const void *)g_skip, (const void *)m, (const void *)v})
+        if (!aligned(p, 4)) return HM_ERR_UNSUPPORTED;
+    hm::AdamArgs a;
+    a.H = H;
+    a.d = d;
+    a.poles = poles;
+    a.residues = residues;
+    a.skip = skip;
+    a.g_poles = g_poles;
+    a.g_res = g_res;
+    a.g_skip = g_skip;
+    a.m = m;
+    a.v = v;
+    a.lr = lr;
+    a.beta1 = beta1;
+    a.beta2 = beta2;
+    a.eps = eps;
+    a.r_max = r_max;
+    a.bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
+    a.bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
+    const hipError_t err = hm::launch_distill_adam(a, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
 }
 

@@ -31,6 +31,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(hm_f32x2{a, b}, hm_bf16x2));
 }
 
+// lambda^e (e >= 0) in float64 by binary powering: at most 2 log2(e) complex
+// products, relative error ~1e-15 even for e ~ 64k and |lambda| ~ 0.9999.
+__device__ inline void complex_pow(double lr, double li, int64_t e, double &pr, double &pi) {
+    pr = 1.0;
+    pi = 0.0;
+    double br = lr, bi = li;
+    while (e != 0) {
+        if (e & 1) {
+            const double nr = pr * br - pi * bi;
+            pi = pr * bi + pi * br;
+            pr = nr;
+        }
+        const double nb = br * br - bi * bi;
+        bi = 2.0 * br * bi;
+        br = nb;
+        e >>= 1;
+    }
+}
+
 // Activation element access for float32 (ACT = kF32) or bfloat16 bit patterns.
 template <int ACT> struct Act;
 
@@ -221,6 +240,30 @@ int fft_log_n(int64_t L);
 int fft_pairs_per_group(int64_t P, int logn);
 size_t fft_lds_bytes(int logn, int np);
 hipError_t launch_fft_prefill(const FftArgs &a, hipStream_t stream);
+
+// Distillation objective: filter discrepancy against target taps, its gradient,
+// and an Adam step on the modal parameters.
+struct DistillArgs {
+    OpShape s;
+    int64_t L;
+    const float *target;  // [H][L]
+    double *e;            // [H][L] residual hhat - target
+    double *loss_part;    // [H][tiles]
+    double *grad_part;    // [H*d][chunks][4]
+    int tiles, chunks;
+    float *loss, *g_poles, *g_res, *g_skip;
+};
+constexpr int kDistillTile = 8192;  // taps per gradient workgroup
+int distill_tiles(int64_t L, int64_t d);  // residual workgroups per head
+hipError_t launch_distill_grad(const DistillArgs &a, hipStream_t stream);
+struct AdamArgs {
+    int64_t H, d;
+    float *poles, *residues, *skip;
+    const float *g_poles, *g_res, *g_skip;
+    float *m, *v;  // [H*d*4 + H]: poles (2/mode), residues (2/mode), skip
+    float lr, beta1, beta2, eps, r_max, bc1, bc2;
+};
+hipError_t launch_distill_adam(const AdamArgs &a, hipStream_t stream);
 
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error; none synchronises.

@@ -313,6 +313,37 @@ hm_status hyena_fft_prefill(const hm_desc *desc, int64_t L, const void *q, const
                             int64_t ld_in, void *y, int64_t ld_y, void *workspace, size_t ws_bytes,
                             void *stream);
 
+/*
+ * Distillation objective (Laughing Hyena Distillery review, 提出的方法: each
+ * filter is fitted by a modal filter under a filter-discrepancy objective).
+ * For the modal filter in desc (poles, residues, skip: the current fit) and
+ * target taps h_target [H][L] float32:
+ *     loss[g]   = sum_{t<L} (hhat_g[t] - h_g[t])^2,
+ *     hhat_g[0] = D_g,  hhat_g[t] = Re sum_n R_gn lambda_gn^(t-1),
+ * and its gradient: g_poles, g_res [H][d][2] (d/dRe, d/dIm of lambda and R),
+ * g_skip [H].  Float64 inside, float32 out.  L >= 1.  Workspace:
+ * hyena_distill_workspace bytes, 256-byte aligned, scratch.  batch is unused.
+ */
+hm_status hyena_distill_workspace(const hm_desc *desc, int64_t L, size_t *bytes);
+
+hm_status hyena_distill_grad(const hm_desc *desc, int64_t L, const float *h_target, float *loss,
+                             float *g_poles, float *g_res, float *g_skip, void *workspace,
+                             size_t ws_bytes, void *stream);
+
+/*
+ * One Adam step on the modal parameters in place (poles, residues [H][d][2],
+ * skip [H]) from the gradients above; m, v [H*d*4 + H] are the optimiser's
+ * moments (zero before step 1; layout per mode: Re/Im lambda, Re/Im R, then
+ * the H skips).  step >= 1 is the 1-based step count.  After the step every
+ * pole with |lambda| > r_max is scaled back to radius r_max (0 < r_max < 1),
+ * so the fitted recurrence stays stable.  Invalid hyper-parameters ->
+ * HM_ERR_INVALID_ARG.
+ */
+hm_status hyena_distill_adam_step(int64_t H, int64_t d, float *poles, float *residues, float *skip,
+                                  const float *g_poles, const float *g_res, const float *g_skip,
+                                  float *m, float *v, int64_t step, float lr, float beta1, float beta2,
+                                  float eps, float r_max, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

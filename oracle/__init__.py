@@ -15,6 +15,9 @@ rms_inv(), dense()      the projected stack's per-token inverse RMS and a float6
                         matrix product (numpy's matmul as the library primitive).
 stack_layer()           one layer of the projected stack, teacher-forced on a given
                         input sequence (see ``stack_layer``'s docstring).
+distill_loss_grad()     the filter discrepancy of a modal filter against target
+                        taps and its analytic gradient (the distillation objective);
+                        hankel_singular_values() of a filter.
 fir_conv()              the same operator with an explicit (possibly truncated)
                         filter over a cache of u rounded to the activation dtype:
                         the non-distilled decode baseline.
@@ -217,6 +220,50 @@ def fir_conv(h, q, k, v, act: str, window: int = 0, t_from: int = 0, heads=None)
             continue
         y[:, t0 - t_from:, :] += taps[:, j][None, None, :] * u[:, t0 - j:T - j, :]
     return y * q64[:, t_from:, :]
+
+
+# ------------------------------------------------------------ distillation objective
+
+
+def distill_loss_grad(params, h_target, L: int):
+    """Filter discrepancy of a modal filter against target taps and its
+    gradient, float64 (the objective modal distillation minimises):
+
+        J_g = sum_{t<L} (hhat_g[t] - h_g[t])^2,
+        hhat_g[0] = D_g,  hhat_g[t] = Re sum_n R_gn lambda_gn^(t-1).
+
+    With e = hhat - h and p_t = lambda^(t-1):
+        dJ/dD       = 2 e[0]
+        dJ/dRe R_n  = 2 sum_{t>=1} e[t] Re p_t,   dJ/dIm R_n = -2 sum e[t] Im p_t
+        dJ/dRe l_n  = 2 sum_{t>=2} e[t] Re(R_n (t-1) l_n^(t-2)),
+        dJ/dIm l_n  = -2 sum_{t>=2} e[t] Im(R_n (t-1) l_n^(t-2))
+    (hhat is the real part of a holomorphic function of lambda).
+    Returns (loss [H], g_poles [H][d][2], g_res [H][d][2], g_skip [H])."""
+    h_target = np.asarray(h_target, dtype=np.float64)
+    lam = params.poles[..., 0].astype(np.float64) + 1j * params.poles[..., 1].astype(np.float64)
+    R = params.residues[..., 0].astype(np.float64) + 1j * params.residues[..., 1].astype(np.float64)
+    H, d = lam.shape
+    hhat = filter_taps(params, L)
+    e = hhat - h_target[:, :L]
+    loss = np.sum(e * e, axis=1)
+    t = np.arange(1, L)
+    pw = lam[:, :, None] ** (t - 1)[None, None, :]                 # lambda^(t-1), t >= 1
+    et = e[:, None, 1:]
+    g_res = np.stack([2 * np.sum(et * pw.real, -1), -2 * np.sum(et * pw.imag, -1)], -1)
+    dl = np.zeros_like(pw)
+    if L > 2:
+        dl[:, :, 1:] = R[:, :, None] * (t[1:] - 1)[None, None, :] * lam[:, :, None] ** (t[1:] - 2)[None, None, :]
+    g_poles = np.stack([2 * np.sum(et * dl.real, -1), -2 * np.sum(et * dl.imag, -1)], -1)
+    g_skip = 2 * e[:, 0]
+    return loss, g_poles, g_res, g_skip
+
+
+def hankel_singular_values(h_row, n: int) -> np.ndarray:
+    """Singular values of the n x n Hankel matrix [h[i + j + 1]] of one filter
+    (taps from t = 1; the skip term h[0] is not part of the SSM's Hankel)."""
+    h_row = np.asarray(h_row, dtype=np.float64)
+    idx = np.arange(n)[:, None] + np.arange(n)[None, :] + 1
+    return np.linalg.svd(h_row[idx], compute_uv=False)
 
 
 # ------------------------------------------------------------ projected stack

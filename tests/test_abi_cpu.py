@@ -324,3 +324,26 @@ def test_fft_prefill_validation(lib):
     assert call(ld=32) == hb.HM_ERR_INVALID_ARG
     assert call(desc=_desc(batch=2, channels=12, heads=4)) == hb.HM_ERR_UNSUPPORTED  # head dim 3 is odd
     assert call(L=0) == hb.HM_OK
+
+
+def test_distill_validation(lib):
+    d = _desc(batch=0, channels=4, heads=4, modes=8)
+    n = hb.hyena_distill_workspace(d, 1000)
+    # residual [4][1000] f64 | loss partials [4][tiles] | gradient partials [4*8][1][4] f64
+    assert n >= 4 * 1000 * 8 + 4 * 8 * 4 * 8
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_distill_workspace(d, 0)
+    assert e.value.status == hb.HM_ERR_INVALID_ARG
+    st = lib.hyena_distill_grad(ctypes.byref(d), 1000, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, n - 8, None)
+    assert st == hb.HM_ERR_WORKSPACE
+    st = lib.hyena_distill_grad(ctypes.byref(d), 1000, None, FAKE, FAKE, FAKE, FAKE, FAKE, n, None)
+    assert st == hb.HM_ERR_INVALID_ARG
+
+    def adam(**kw):
+        a = dict(H=4, d=8, step=1, lr=1e-2, b1=0.9, b2=0.999, eps=1e-8, r_max=0.9999)
+        a.update(kw)
+        return lib.hyena_distill_adam_step(a["H"], a["d"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           a["step"], a["lr"], a["b1"], a["b2"], a["eps"], a["r_max"], None)
+    for kw in (dict(step=0), dict(lr=0.0), dict(b1=1.0), dict(b2=-0.1), dict(eps=0.0), dict(r_max=1.0),
+               dict(r_max=0.0), dict(d=65), dict(H=0)):
+        assert adam(**kw) == hb.HM_ERR_INVALID_ARG, kw

@@ -387,3 +387,53 @@ def test_fir_cache_rounding_to_bfloat16():
     # 1 + 3 * 2^-8 rounds up to 1 + 2^-6
     assert oracle.round_to_act(np.array([1 + 2 ** -8]), "bf16")[0] == 1.0
     assert oracle.round_to_act(np.array([1 + 3 * 2 ** -8]), "bf16")[0] == 1 + 2 ** -6
+
+
+def test_distill_gradient_matches_finite_differences(oracle_lib):
+    """The analytic gradient of the filter discrepancy against central
+    differences of the loss (each parameter perturbed in float64)."""
+    import oracle
+    rng = np.random.default_rng(31)
+    H, d, L = 2, 3, 60
+    params = _random_params(rng, H, d, 0.6, 0.95)
+    target = rng.standard_normal((H, L)) * 0.3
+    loss, g_poles, g_res, g_skip = oracle.distill_loss_grad(params, target, L)
+    assert np.all(loss > 0)
+
+    def loss_at(p):
+        return oracle.distill_loss_grad(p, target, L)[0]
+
+    from workloads import ModalParams
+    step = 1e-6
+    for name, arr, g in (("poles", params.poles, g_poles), ("residues", params.residues, g_res)):
+        for idx in [(0, 0, 0), (0, 2, 1), (1, 1, 0), (1, 2, 1)]:
+            plus, minus = arr.astype(np.float64).copy(), arr.astype(np.float64).copy()
+            plus[idx] += step
+            minus[idx] -= step
+            mk = lambda a: ModalParams(a, params.residues, params.skip) if name == "poles" else \
+                ModalParams(params.poles, a, params.skip)
+            fd = (loss_at(mk(plus))[idx[0]] - loss_at(mk(minus))[idx[0]]) / (2 * step)
+            assert abs(fd - g[idx]) <= 1e-5 * max(1.0, abs(fd)), (name, idx, fd, g[idx])
+    sp, sm = params.skip.astype(np.float64).copy(), params.skip.astype(np.float64).copy()
+    sp[1] += step
+    sm[1] -= step
+    fd = (loss_at(ModalParams(params.poles, params.residues, sp))[1] -
+          loss_at(ModalParams(params.poles, params.residues, sm))[1]) / (2 * step)
+    assert abs(fd - g_skip[1]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_distill_zero_at_generating_parameters_and_hankel_rank(oracle_lib):
+    """A filter generated by an order-d modal system: the objective and its
+    gradient vanish at the generating parameters, and its Hankel matrix has
+    rank 2d (d complex modes, real part taken)."""
+    import oracle
+    rng = np.random.default_rng(32)
+    H, d, L = 2, 4, 400
+    params = _random_params(rng, H, d, 0.7, 0.97)
+    target = oracle_lib.filter_taps(params, L)
+    loss, g_poles, g_res, g_skip = oracle.distill_loss_grad(params, target, L)
+    assert np.all(loss == 0.0)
+    assert np.all(g_poles == 0.0) and np.all(g_res == 0.0) and np.all(g_skip == 0.0)
+    sv = oracle.hankel_singular_values(target[0], 60)
+    assert sv[2 * d - 1] > 1e-8 * sv[0]
+    assert np.all(sv[2 * d:] <= 1e-10 * sv[0])
