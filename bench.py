@@ -184,20 +184,24 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(cfg, params, inp, dec):
-    """The float64 oracle (as it stands) on this host over the same workload."""
+def cpu_baseline(cfg, params, inp, dec, min_seconds: float = 10.0):
+    """The float64 oracle (as it stands) on this host over the same workload:
+    the full step (filter, prefill, decode steps) repeated until ``min_seconds``
+    of CPU time have passed (at most 20 repetitions), on an evenly spaced
+    channel subset when one repetition of the whole width would be too long."""
     import oracle
-    budget = 6e9  # mode-steps, ~10 s on 8 cores
+    budget = 6e9  # mode-steps per repetition, ~1 s on 16 cores
     per_channel = cfg.B * (cfg.L + cfg.S) * cfg.d
     n_sel = int(min(cfg.D, max(1, budget // per_channel)))
-    reps = int(max(1, min(3, budget // (per_channel * n_sel))))
     chans = np.linspace(0, cfg.D - 1, n_sel).round().astype(np.int64) if n_sel < cfg.D else None
+    reps = 0
     t0 = time.perf_counter()
-    for _ in range(reps):
+    while reps < 20 and (reps == 0 or time.perf_counter() - t0 < min_seconds):
         oracle.filter_taps(params, cfg.L)
         _, st = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"], channels=chans)
         oracle.modal_scan(params, dec["q"], dec["k"], dec["v"], state=st, channels=chans,
                           batch_axis=1, time_axis=0)
+        reps += 1
     dt = time.perf_counter() - t0
     tokens = cfg.B * (cfg.L + cfg.S) * (n_sel / cfg.D) * reps
     sample = (f"full step (filter, prefill L={cfg.L}, {cfg.S} decode steps) for "
@@ -217,10 +221,10 @@ def emit(args, res):
 
 def stack_cpu_baseline(cfg, layers, x0):
     """The float64 oracle on a bounded sample of the stack: one batch row through
-    the first two layers, over the prompt and then 64 generated steps whose
+    the first two layers, over the prompt and then all S generated steps whose
     inputs are that sample's own outputs fed back (as on the GPU)."""
     import oracle
-    nl, steps, D = 2, 64, cfg.D
+    nl, steps, D = 2, cfg.S, cfg.D
     w64 = [(oracle.bf16_to_f64(w_in), oracle.bf16_to_f64(w_out)) for _, w_in, w_out in layers[:nl]]
     t0 = time.perf_counter()
     cur, states = x0[:1], []
