@@ -8,20 +8,23 @@
 // natural operand order of the matrix cores: a 16x16x32 bf16 MFMA fragment is
 // 16 contiguous bytes of one row per lane (lane l: row l%16, k 8*(l/16)..+7).
 //
-// Two GEMM kernels:
+// GEMM kernels (the split-K pair for M <= 64 is described with its code):
 //   * gemm_tiled  (large M): workgroups on a BM x BN tile, K staged 64 at a
 //     time through double-buffered LDS (rows padded to 144 B so the 16-lane
 //     fragment reads hit distinct banks), (BM/WM) x (BN/WN) waves each owning a
 //     WM x WN sub-tile of 16x16x32 MFMAs.  Tiles are ordered so each XCD walks
 //     a contiguous range, grouped GM m-tiles at a time, to keep A and W in L2.
-//   * gemm_stream / gemm_skinny (M <= 64, the generation step): a workgroup
-//     owns 16-32 columns and all rows.  gemm_stream (wide outputs, K = 2048)
-//     streams A and W fragments through a register ring with its K loop
-//     unrolled; gemm_skinny stages contiguous A and W slabs through
+//   * gemm_stream_lds / gemm_skinny (M <= 64, the generation step): a
+//     workgroup owns 16-32 columns and all rows.  gemm_stream_lds (wide
+//     outputs, K = 2048) streams W fragments through a register ring with its
+//     K loop unrolled and stages A per wave through LDS in 128-byte row
+//     pieces; gemm_skinny stages contiguous A and W slabs through
 //     double-buffered LDS.  Both sum their K parts through LDS.  Every
 //     workgroup re-reads all of A (64 x K), so these are bound by L1->L2
 //     request throughput, not by the W stream alone.
 #include "hm_internal.hpp"
+
+#include <type_traits>
 
 namespace hm {
 namespace {
@@ -346,51 +349,64 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
     }
 }
 
-// Weight-streaming GEMM for a fixed K (fully unrolled).  Workgroup = 4 waves on
-// all M <= 64 rows x 16*NTW columns; wave w takes K quarter w (NSTEPS 32-wide
-// steps).  Each wave streams its A and W fragments straight from memory
-// through an R-deep register ring: the loads for step s+R are issued before
-// step s is multiplied.  The K loop is unrolled at compile time so that every
-// wait names exactly the load it needs (a rolled loop makes the compiler drain
-// all loads at the loop head, which serialises the HBM latency).  The four
-// quarters are summed through LDS.
-template <int NTW, int R, int NSTEPS, bool RMS>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
-    constexpr int BN = 16 * NTW;
-    __shared__ float red[4 * 64 * BN];
+// Weight-streaming GEMM for M <= 64 and K = 2048 (K loop fully unrolled).
+// Workgroup = 4 waves on all rows x BN = 16 NTW columns; wave w takes K
+// quarter w (16 steps of 32).  The weight fragments stream straight from
+// memory through an R-deep register ring: the loads for step s + R are issued
+// before step s is multiplied, and since the loop is unrolled every wait names
+// exactly the load it needs (a rolled loop drains all loads at its head, which
+// serialises the HBM latency).  A is re-read by every workgroup, so its
+// requests, not W's bytes, set the pace: the wave's 64 x 64 slab of A for each
+// 64-wide K chunk is loaded as 128-byte row pieces (8 lanes per row, half the
+// requests of fragment-shaped loads) two chunks ahead, written to a
+// wave-private LDS buffer (rows padded to 144 B) and read back as MFMA
+// fragments.  The buffers are private to the wave, so no workgroup barrier is
+// needed inside the K loop (LDS operations of one wave complete in order).
+// The four K quarters are summed through LDS, reusing the A buffers.
+constexpr int kAsLd = 72;  // bf16 per LDS row of the A chunk (64 + 8 pad)
+
+template <int NTW, int R, bool RMS>
+__global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
+    constexpr int BN = 16 * NTW, NCH = 8, NSTEPS = 2 * NCH;  // K quarter: 8 chunks of 64 = 16 steps of 32
+    __shared__ __attribute__((aligned(16))) uint16_t as[4][2][64 * kAsLd];
     __shared__ float red_ss[RMS ? 4 * 64 : 1];
+    static_assert(4 * 64 * BN * sizeof(float) <= sizeof(as), "the K-part sums reuse the A buffers");
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    // Every workgroup reads all of A.  Rotating the K order by the workgroup
-    // index (quarter and step) spreads the simultaneous A requests of all CUs
-    // over the L2 channels instead of hammering the same lines.
-    const int quarter = (w + (int)blockIdx.x) % 4, rot = (int)(blockIdx.x / 4) % NSTEPS;
-    const int64_t kbeg = (int64_t)quarter * NSTEPS * 32;
-    auto kstep = [&](int st) { return (st + rot) % NSTEPS; };
+    const int64_t kbeg = (int64_t)w * NSTEPS * 32;
     const uint16_t *A = static_cast<const uint16_t *>(g.A);
     const uint16_t *W = static_cast<const uint16_t *>(g.W);
     const int ko = 8 * (lane / 16);
-    const uint16_t *arow[4];
     const uint16_t *wrow[NTW];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int r = m * 16 + lane % 16;
-        arow[m] = A + (int64_t)(r < g.M ? r : 0) * g.lda + kbeg + ko;  // clamped rows are masked at the end
-    }
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
         const int64_t c = n0 + j * 16 + lane % 16;
-        wrow[j] = W + (c < g.N ? c : 0) * g.ldw + kbeg + ko;
+        wrow[j] = W + (c < g.N ? c : 0) * g.ldw + kbeg + ko;  // clamped columns are masked at the end
     }
-    uint4 ra[R][4], rw[R][NTW];
+    // A chunk piece i of lane l: row 8 i + l / 8, 16-byte piece l % 8 of the chunk's 128 bytes
+    const int arow0 = lane / 8, apiece = lane % 8;
+    const uint16_t *arow[8];
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) ra[i][m] = *reinterpret_cast<const uint4 *>(arow[m] + 32 * kstep(i));
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) rw[i][j] = *reinterpret_cast<const uint4 *>(wrow[j] + 32 * kstep(i));
+    for (int i = 0; i < 8; ++i) {
+        const int r = 8 * i + arow0;
+        arow[i] = A + (int64_t)(r < g.M ? r : 0) * g.lda + kbeg + 8 * apiece;  // clamped rows are masked at the end
     }
-    // keep the scheduler from sinking the ring loads towards their uses
+    // native vectors: the staging arrays stay in registers (struct copies into
+    // LDS kept them in scratch)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#define HM_LOAD_A(ra, ch)                                                                        \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) ra[i_] = *reinterpret_cast<const u32x4 *>(arow[i_] + 64 * (ch));
+#define HM_PUT_A(ra, buf)                                                                        \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_)                                             \
+        *reinterpret_cast<u32x4 *>(&as[w][buf][(8 * i_ + arow0) * kAsLd + 8 * apiece]) = ra[i_];
+    u32x4 ra0[8], ra1[8];
+    uint4 rw[R][NTW];
+    HM_LOAD_A(ra0, 0)
+    HM_LOAD_A(ra1, 1)
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) rw[i][j] = *reinterpret_cast<const uint4 *>(wrow[j] + 32 * i);
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc[4][NTW], ss[4];
 #pragma unroll
@@ -399,31 +415,45 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    // chunk pairs: chunk 2p in buffer 0 (registers ra0), 2p + 1 in buffer 1 (ra1);
+    // steps 4p .. 4p + 3 use ring slots 0 .. 3 (R = 4)
+    static_assert(R == 4, "ring slot = step mod 4");
+    auto steps = [&](auto bufc, int st0) {  // bufc: std::integral_constant, so ring slots are constants
+        constexpr int buf = decltype(bufc)::value;
 #pragma unroll
-    for (int st = 0; st < NSTEPS; ++st) {
-        const int i = st % R;
-        uint4 a[4], b[NTW];
+        for (int h = 0; h < 2; ++h) {
+            const int st = st0 + h, i = (2 * buf + h);  // st % 4 with st0 = 4p + 2 buf
+            uint4 a[4], b[NTW];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) a[m] = ra[i][m];
+            for (int m = 0; m < 4; ++m)
+                a[m] = *reinterpret_cast<const uint4 *>(&as[w][buf][(16 * m + lane % 16) * kAsLd + 32 * h + ko]);
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) b[j] = rw[i][j];
-        if (st + R < NSTEPS) {
+            for (int j = 0; j < NTW; ++j) b[j] = rw[i][j];
+            if (st + R < NSTEPS) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) ra[i][m] = *reinterpret_cast<const uint4 *>(arow[m] + 32 * kstep(st + R));
+                for (int j = 0; j < NTW; ++j) rw[i][j] = *reinterpret_cast<const uint4 *>(wrow[j] + 32 * (st + R));
+            }
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) rw[i][j] = *reinterpret_cast<const uint4 *>(wrow[j] + 32 * kstep(st + R));
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) acc[m][j] = mfma16(a[m], b[j], acc[m][j]);
+            if constexpr (RMS) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) ss[m] = mfma16(a[m], a[m], ss[m]);
+            }
         }
-        __builtin_amdgcn_sched_barrier(0);
+    };
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) acc[m][j] = mfma16(a[m], b[j], acc[m][j]);
-        if constexpr (RMS) {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) ss[m] = mfma16(a[m], a[m], ss[m]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int p = 0; p < NCH / 2; ++p) {
+        HM_PUT_A(ra0, 0)
+        if (2 * p + 2 < NCH) { HM_LOAD_A(ra0, 2 * p + 2) }
+        steps(std::integral_constant<int, 0>{}, 4 * p);
+        HM_PUT_A(ra1, 1)
+        if (2 * p + 3 < NCH) { HM_LOAD_A(ra1, 2 * p + 3) }
+        steps(std::integral_constant<int, 1>{}, 4 * p + 2);
     }
+#undef HM_LOAD_A
+#undef HM_PUT_A
     if constexpr (RMS) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -432,6 +462,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs g) {
             if (4 * (lane / 16) <= q && q < 4 * (lane / 16) + 4) red_ss[w * 64 + m * 16 + q] = dg;
         }
     }
+    __syncthreads();  // every wave is done with its A buffers, which now hold the K-part sums
+    float *red = reinterpret_cast<float *>(&as[0][0][0]);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -610,7 +642,7 @@ hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
         // Measured on MI355X at M = 64, K = 2048: the unrolled streaming kernel
         // is fastest for wide outputs, the LDS-staged one for narrow outputs.
         if (g.K == 2048 && g.N >= 4096)
-            gemm_stream_kernel<2, 4, 16, RMS><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
+            gemm_stream_lds_kernel<2, 4, RMS><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
         else
             gemm_skinny_kernel<16, RMS><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
         return hipGetLastError();

@@ -27,8 +27,9 @@ def _bits(rng, shape, std=1.0):
 
 @pytest.mark.parametrize("M,N,K", [
     (64, 6144, 2048),     # generation-step in_proj (weight streaming path)
+    (37, 4100, 2048),     # weight streaming path, ragged rows and columns
     (64, 2048, 2048),     # generation-step out_proj
-    (37, 96, 1024),       # ragged rows and columns, streaming path
+    (37, 96, 1024),       # ragged rows and columns, skinny path
     (300, 200, 128),      # tiled path, ragged M and N
     (1024, 768, 512),     # tiled path, several tiles
     (4096, 6144, 2048),   # tiled path at the prompt in_proj width
@@ -54,8 +55,8 @@ def test_dense_bf16(M, N, K, scaled):
     assert err <= 8e-3
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 6144, 2048), (64, 2048, 2048), (50, 100, 512), (700, 300, 256),
-                                   (2048, 6144, 2048)])
+@pytest.mark.parametrize("M,N,K", [(64, 6144, 2048), (37, 4100, 2048), (64, 2048, 2048), (50, 100, 512),
+                                   (700, 300, 256), (2048, 6144, 2048)])
 def test_dense_rms_fused(M, N, K):
     """in_proj with the inverse-RMS row scale computed inside the GEMM."""
     torch = require_gpu()
