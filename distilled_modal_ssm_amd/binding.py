@@ -82,7 +82,7 @@ class hm_prefill_opts(ctypes.Structure):
 
 
 class hm_prefill_info(ctypes.Structure):
-    _fields_ = [("algo", ctypes.c_int32), ("reserved", ctypes.c_int32), ("chunk", ctypes.c_int64),
+    _fields_ = [("algo", ctypes.c_int32), ("channel_tile", ctypes.c_int32), ("chunk", ctypes.c_int64),
                 ("n_chunks", ctypes.c_int64), ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -204,14 +204,15 @@ def hyena_modal_prefill_workspace(desc: hm_desc, L: int, chunk: int = 0, algo="a
 
 
 def hyena_modal_prefill_plan(desc: hm_desc, L: int, chunk: int = 0, algo="auto") -> dict:
-    """What a prefill would run: {"algo": "scan"|"mfma", "chunk", "n_chunks", "workspace_bytes"}."""
+    """What a prefill would run: {"algo": "scan"|"mfma", "channel_tile", "chunk", "n_chunks",
+    "workspace_bytes"}."""
     o = _opts(chunk, algo)
     info = hm_prefill_info()
     _check(load().hyena_modal_prefill_plan(ctypes.byref(desc), L, ctypes.byref(o), ctypes.byref(info)),
            "hyena_modal_prefill_plan")
     names = {HM_PREFILL_SCAN: "scan", HM_PREFILL_MFMA: "mfma"}
-    return {"algo": names[info.algo], "chunk": info.chunk, "n_chunks": info.n_chunks,
-            "workspace_bytes": info.workspace_bytes}
+    return {"algo": names[info.algo], "channel_tile": info.channel_tile, "chunk": info.chunk,
+            "n_chunks": info.n_chunks, "workspace_bytes": info.workspace_bytes}
 
 
 def hyena_modal_prefill(desc: hm_desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out,

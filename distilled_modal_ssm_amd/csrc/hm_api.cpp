@@ -149,7 +149,7 @@ hm_status plan_impl(const hm_desc *desc, int64_t L, const hm_prefill_opts *opts,
     const hm::PrefillPlan plan = hm::make_prefill_plan(shape_of(desc), L, chunk, algo);
     if (algo == hm::kAlgoMfma && plan.algo != hm::kAlgoMfma) return HM_ERR_UNSUPPORTED;
     info->algo = plan.algo == hm::kAlgoMfma ? HM_PREFILL_MFMA : HM_PREFILL_SCAN;
-    info->reserved = 0;
+    info->channel_tile = plan.algo == hm::kAlgoMfma ? hm::mfma_channel_tile(shape_of(desc)) : 0;
     info->chunk = plan.T;
     info->n_chunks = plan.NC;
     info->workspace_bytes = desc->batch > 0 ? plan.bytes : 0;

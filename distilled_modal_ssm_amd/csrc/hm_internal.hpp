@@ -273,11 +273,14 @@ hipError_t launch_filter(const FilterArgs &a, hipStream_t stream);
 PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk, int algo);
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // matrix-core prefill (prefill_mfma.hip)
-int mfma_channel_tile(int64_t d, int64_t P);  // channels per workgroup, 0 = not eligible
+int mfma_channel_tile(const OpShape &s);  // channels per workgroup, 0 = not eligible
 size_t mfma_table_bytes(int64_t H, int64_t d);
 size_t mfma_lam_bytes(int64_t H, int64_t d);
+// per-head tables; also lambda^T (carry scan) when the prompt is chunked
 hipError_t launch_mfma_tables(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_chunk_mfma(const PrefillArgs &a, const float2 *carry0, hipStream_t stream);
+// chunk end states S_c of chunks 0 .. NC-2 into carry slots 1 .. NC-1 (vec: 16-byte k, v pieces)
+hipError_t launch_chunk_mfma_state(const PrefillArgs &a, bool vec, hipStream_t stream);
 hipError_t launch_row_rms(const RmsArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
 

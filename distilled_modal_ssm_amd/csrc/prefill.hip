@@ -24,8 +24,15 @@
 //      X_c, streaming q, k, v in and y out; the lanes of the last chunk write
 //      the end-of-prompt state.  12 d + 5 float32 flops per element.
 //
-// Workspace (from make_prefill_plan): bf16 fragments of the Vandermonde
-// matrices in MFMA A-operand order, lambda^T, and NC chunk-state slots.
+// That is the lane-scan plan (any d, any head dimension).  A matrix-core plan
+// (prefill_mfma.hip) replaces steps 1 and 3 by its 64-step sub-block kernel:
+// the same contraction, chained through lambda^64, in a state-only pass, and
+// the full pass from the carries; step 2 is shared.
+//
+// Workspace (from make_prefill_plan): for the lane-scan plan, bf16 fragments of
+// the Vandermonde matrices in MFMA A-operand order; for a chunked prompt,
+// lambda^T and NC chunk-state slots; for the matrix-core plan, its per-head
+// sub-block tables.
 #include "hm_internal.hpp"
 
 namespace hm {
@@ -510,7 +517,7 @@ hipError_t launch_scan(const PrefillArgs &a, const float2 *carry0, hipStream_t s
 PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk, int algo) {
     PrefillPlan p{};
     p.L = L;
-    const int pt = mfma_channel_tile(s.d, s.P);
+    const int pt = mfma_channel_tile(s);
     p.algo = (algo == kAlgoScan || pt == 0) ? kAlgoScan : kAlgoMfma;
     if (L <= 0) {
         p.T = 0;
@@ -545,11 +552,13 @@ PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk, int al
     p.mtiles = mt <= 1 ? 1 : mt <= 2 ? 2 : mt <= 4 ? 4 : 8;
     size_t off = 0;
     if (p.NC > 1) {
-        const size_t frag = (size_t)s.H * p.mtiles * (p.T / 32) * kWave * 16;
-        p.off_vand_hi = off;
-        off = align256(off + frag);
-        p.off_vand_lo = off;
-        off = align256(off + frag);
+        if (p.algo == kAlgoScan) {  // the matrix-core path gets its chunk states from its own sub-block tables
+            const size_t frag = (size_t)s.H * p.mtiles * (p.T / 32) * kWave * 16;
+            p.off_vand_hi = off;
+            off = align256(off + frag);
+            p.off_vand_lo = off;
+            off = align256(off + frag);
+        }
         p.off_lamT = off;
         off = align256(off + (size_t)s.H * s.d * 8);
         p.off_carry = off;
@@ -585,6 +594,26 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
     }
     hipError_t err;
     const float2 *carry0 = a.state_in;
+    const int esz = s.act == kBF16 ? 2 : 4;
+    auto al16 = [](const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) % 16) == 0; };
+    // 16-byte k, v pieces for the chunk-state passes
+    const bool vec = (s.P % 8 == 0) && ((a.ld_in * esz) % 16 == 0) && al16(a.k) && al16(a.v);
+    if (a.plan.algo == kAlgoMfma) {
+        // Matrix-core plan.  Chunk states come from the state-only sub-block
+        // pass (either load width); the full pass needs 16-byte-aligned rows
+        // of q, k, v and y, else the lane scan runs from the same carries.
+        const bool full = mfma_aligned(a);
+        if (full || a.plan.NC > 1)
+            if ((err = launch_mfma_tables(a, stream)) != hipSuccess) return err;
+        if (a.plan.NC > 1) {
+            if ((err = launch_chunk_mfma_state(a, vec, stream)) != hipSuccess) return err;
+            carry_scan_kernel<<<dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, stream>>>(a);
+            if ((err = hipGetLastError()) != hipSuccess) return err;
+            carry0 = a.state_in ? reinterpret_cast<const float2 *>(a.ws + a.plan.off_carry) : nullptr;
+        }
+        if (full) return launch_chunk_mfma(a, carry0, stream);
+        return s.act == kBF16 ? launch_scan<kBF16>(a, carry0, stream) : launch_scan<kF32>(a, carry0, stream);
+    }
     if (a.plan.NC > 1) {
         const int64_t total = s.H * a.plan.mtiles * (a.plan.T / 32) * kWave;
         vand_tables_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream>>>(
@@ -592,18 +621,11 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
             reinterpret_cast<uint4 *>(a.ws + a.plan.off_vand_lo),
             reinterpret_cast<float2 *>(a.ws + a.plan.off_lamT));
         if ((err = hipGetLastError()) != hipSuccess) return err;
-        const int esz = s.act == kBF16 ? 2 : 4;
-        auto al16 = [](const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) % 16) == 0; };
-        const bool vec = (s.P % 8 == 0) && ((a.ld_in * esz) % 16 == 0) && al16(a.k) && al16(a.v);
         err = s.act == kBF16 ? launch_chunk_state<kBF16>(a, vec, stream) : launch_chunk_state<kF32>(a, vec, stream);
         if (err != hipSuccess) return err;
         carry_scan_kernel<<<dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, stream>>>(a);
         if ((err = hipGetLastError()) != hipSuccess) return err;
         carry0 = a.state_in ? reinterpret_cast<const float2 *>(a.ws + a.plan.off_carry) : nullptr;
-    }
-    if (a.plan.algo == kAlgoMfma && mfma_aligned(a)) {
-        if ((err = launch_mfma_tables(a, stream)) != hipSuccess) return err;
-        return launch_chunk_mfma(a, carry0, stream);
     }
     return s.act == kBF16 ? launch_scan<kBF16>(a, carry0, stream) : launch_scan<kF32>(a, carry0, stream);
 }

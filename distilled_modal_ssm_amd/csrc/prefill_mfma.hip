@@ -22,14 +22,24 @@
 // Work per element: 2*(64 + 4*D2) flops on the matrix cores (x3 for the split);
 // the kernel is bound by streaming q, k, v and y through HBM.
 //
-// Workgroup: one (batch row, head, tile of PT channels, chunk), 4 waves of PT/4
-// channels each.  Per sub-block: q, k, v for 64 steps x PT channels are loaded
-// one sub-block ahead (contiguous 16-byte pieces), u = k v is split and
-// transposed into LDS ([channel][step], the MFMA B operand), q stays in the
-// loading thread's registers, the Y accumulators go to an LDS tile that the
-// loading threads read back to gate (y = q Y) and write out as whole row
-// pieces.  Per-head table fragments (in A-operand lane order) sit in LDS.
+// Workgroup: one (batch row, head, tile of PT = 64 or 128 channels, chunk),
+// PT/16 waves of 16 channels each.  Per sub-block: q, k, v for 64 steps x PT
+// channels are loaded one sub-block ahead (contiguous 16-byte pieces), u = k v
+// is split and transposed into LDS ([channel][step], the MFMA B operand), q
+// stays in the loading thread's registers, the Y accumulators go to an LDS
+// tile that the loading threads read back to gate (y = q Y) and write out as
+// whole row pieces.  Per-head table fragments (in A-operand lane order) sit in
+// LDS.
+//
+// A prompt cut into chunks (when there are too few (row, head, tile) triples
+// to fill the GPU) first runs the same kernel in state-only form over every
+// chunk but the last: from a zero state it loads only k and v, does only
+// S = V U and X' = lambda^64 X + S, and writes the chunk's end state S_c.  A
+// carry scan then forms the state entering each chunk, which the full pass
+// starts from.
 #include "hm_internal.hpp"
+
+#include <type_traits>
 
 namespace hm {
 namespace {
@@ -75,7 +85,8 @@ __device__ inline void polar_pow(double lr, double li, double e, double &re, dou
 //   f in [8+4KC, NFRAG)    V tile (ms, kk): V[2n][j] = Re lam_n^(63-j), V[2n+1][j] = Im lam_n^(63-j)
 // stored as [head][f][hi, lo][lane] uint4; also lam64[head][D2/2] = lambda^64.
 template <int DD>
-__global__ __launch_bounds__(256) void mfma_tables_kernel(OpShape s, uint4 *frag, float2 *lam64) {
+__global__ __launch_bounds__(256) void mfma_tables_kernel(OpShape s, uint4 *frag, float2 *lam64, int64_t T,
+                                                          float2 *lamT) {
     using G = MfmaGeom<DD>;
     constexpr int D2 = G::D2, KC = G::KC, NFRAG = G::NFRAG;
     __shared__ double pr[65 * DD], pi[65 * DD];  // lambda_n^i, i <= 64
@@ -113,6 +124,12 @@ __global__ __launch_bounds__(256) void mfma_tables_kernel(OpShape s, uint4 *frag
     if (tid < D2 / 2)
         lam64[g * (D2 / 2) + tid] =
             tid < DD ? make_float2((float)pr[64 * DD + tid], (float)pi[64 * DD + tid]) : make_float2(0.f, 0.f);
+    if (lamT && tid < DD) {  // lambda^T for the carry scan of a chunked prompt
+        const float2 l = s.poles[(int64_t)g * DD + tid];
+        double re, im;
+        polar_pow(l.x, l.y, (double)T, re, im);
+        lamT[(int64_t)g * DD + tid] = make_float2((float)re, (float)im);
+    }
     __syncthreads();
     for (int idx = tid; idx < NFRAG * kWave; idx += 256) {
         const int f = idx / kWave, l = idx % kWave;
@@ -166,6 +183,16 @@ template <> struct Piece<kF32> {
         return v[e];
     }
 };
+// The same 8 channels read one element at a time (rows not 16-byte aligned).
+template <int ACT> struct PieceScalar {
+    float v[8];
+    __device__ void load(const void *p) {
+        const typename Act<ACT>::T *t = static_cast<const typename Act<ACT>::T *>(p);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = Act<ACT>::ld(t + e);
+    }
+    __device__ float get(int e) const { return v[e]; }
+};
 
 __device__ __forceinline__ void store8(uint16_t *p, const float *v) {
     uint32_t w[4];
@@ -193,25 +220,32 @@ __device__ __forceinline__ int u_index(int ch, int t) {
 // (8 channel groups of one row per 8 lanes) fall on disjoint banks.
 __device__ __forceinline__ int yt_index(int row, int col, int ld) { return row * ld + (col ^ (((col >> 5) & 1) << 2)); }
 
-template <int DD, int PT, int ACT>
-__global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const float2 *carry0) {
+// SO (state only): chunks 0 .. NC-2 of a chunked prompt, from a zero state,
+// reading k and v only; writes S_c to carry slot c + 1.  VEC: 16-byte row
+// pieces (else element loads, for rows that are not 16-byte aligned; the full
+// pass always needs them aligned).
+template <int DD, int PT, int ACT, bool SO, bool VEC>
+__global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const float2 *carry0) {
     using G = MfmaGeom<DD>;
     using T = typename Act<ACT>::T;
+    using PC = typename std::conditional<VEC, Piece<ACT>, PieceScalar<ACT>>::type;
     constexpr int D2 = G::D2, KC = G::KC, MTS = G::MTS, NFRAG = G::NFRAG;
-    constexpr int CW = PT / 4, NTW = CW / 16;  // channels and 16-wide tiles per wave
-    constexpr int RG = PT / 32;                // staging rows per thread
+    constexpr int NTHR = 4 * PT;               // PT / 16 waves
+    constexpr int CW = 16, NTW = 1;            // channels and 16-wide tiles per wave
+    constexpr int RG = 2;                      // staging rows per thread (two steps per 32-bit LDS word)
     constexpr int CG = PT / 8;                 // 8-channel groups per row
     constexpr int LX = D2 + 8;                 // LDS row of x (bf16), per channel
     constexpr int LQ = PT + 4;                 // LDS row of the Y tile (float), per step
-    static_assert(PT == 64, "staging writes two steps per 32-bit word");
-    static_assert((64 / RG) * CG == 256, "one staging piece group per thread");
+    static_assert(PT == 64 || PT == 128, "channel tile");
+    static_assert((64 / RG) * CG == NTHR, "one staging piece group per thread");
+    static_assert(VEC || SO, "the full pass loads 16-byte pieces");
 
     __shared__ uint4 tab[NFRAG * 2 * kWave];
     __shared__ __attribute__((aligned(16))) uint16_t uhi[PT * kLU];
     __shared__ __attribute__((aligned(16))) uint16_t ulo[PT * kLU];
-    __shared__ __attribute__((aligned(16))) uint16_t xhi[PT * LX];
-    __shared__ __attribute__((aligned(16))) uint16_t xlo[PT * LX];
-    __shared__ __attribute__((aligned(16))) float yt[kSubBlock * LQ];
+    __shared__ __attribute__((aligned(16))) uint16_t xhi[SO ? 8 : PT * LX];
+    __shared__ __attribute__((aligned(16))) uint16_t xlo[SO ? 8 : PT * LX];
+    __shared__ __attribute__((aligned(16))) float yt[SO ? 4 : kSubBlock * LQ];
     __shared__ float2 lamT[D2 / 2];
 
     const OpShape &s = a.s;
@@ -226,7 +260,7 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
     // per-head tables -> LDS
     {
         const uint4 *gt = reinterpret_cast<const uint4 *>(a.ws + a.plan.off_mfma_tab) + (int64_t)g * NFRAG * 2 * kWave;
-        for (int i = tid; i < NFRAG * 2 * kWave; i += 256) tab[i] = gt[i];
+        for (int i = tid; i < NFRAG * 2 * kWave; i += NTHR) tab[i] = gt[i];
         if (tid < D2 / 2)
             lamT[tid] = reinterpret_cast<const float2 *>(a.ws + a.plan.off_mfma_lam)[(int64_t)g * (D2 / 2) + tid];
     }
@@ -235,7 +269,7 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
     // (modes 8ms + 2(l/16) and +1, Re/Im interleaved) of channel cw + 16j + l%16
     f32x4 Xr[MTS][NTW];
     {
-        const float2 *src = (c == 0) ? carry0
+        const float2 *src = SO ? nullptr : (c == 0) ? carry0
                                      : reinterpret_cast<const float2 *>(a.ws + a.plan.off_carry) +
                                            c * (s.B * H * DD * P);
 #pragma unroll
@@ -264,7 +298,7 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
                 *reinterpret_cast<uint2 *>(&xlo[o]) = make_uint2(l01, l23);
             }
     };
-    write_x();
+    if constexpr (!SO) write_x();
 
     // staging role: RG rows x 8 channels
     const int cg = tid % CG, rg = tid / CG;
@@ -277,14 +311,14 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
     const T *vb = static_cast<const T *>(a.v) + (b * L + t_begin) * a.ld_in + ch0;
     T *yb = static_cast<T *>(a.y) + (b * L + t_begin) * a.ld_y + ch0;
 
-    Piece<ACT> pq[RG], pk[RG], pv[RG];
+    PC pq[RG], pk[RG], pv[RG];
     auto load = [&](int sb) {
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
             int row = sb * kSubBlock + rg * RG + r;
             row = row < nsteps ? row : nsteps - 1;  // clamped; rows past the prompt are masked in staging
             const int64_t o = (int64_t)row * a.ld_in;
-            pq[r].load(qb + o);
+            if constexpr (!SO) pq[r].load(qb + o);
             pk[r].load(kb + o);
             pv[r].load(vb + o);
         }
@@ -298,9 +332,11 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
     for (int sb = 0; sb < nsb; ++sb) {
         const int nv = (nsteps - sb * kSubBlock < kSubBlock) ? nsteps - sb * kSubBlock : kSubBlock;
         // ---- stage: u = k v split into hi/lo, transposed to [channel][step]; q stays in registers
-        Piece<ACT> cq[RG];
+        PC cq[RG];
+        if constexpr (!SO) {
 #pragma unroll
-        for (int r = 0; r < RG; ++r) cq[r] = pq[r];
+            for (int r = 0; r < RG; ++r) cq[r] = pq[r];
+        }
         {
             float uu[RG][8];
 #pragma unroll
@@ -340,12 +376,14 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
                 bh[j] = *reinterpret_cast<const uint4 *>(&uhi[o]);
                 bl[j] = *reinterpret_cast<const uint4 *>(&ulo[o]);
             }
+            if constexpr (!SO) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int f = mt * 2 + kk;
-                const uint4 ah = tab[(f * 2) * kWave + lane], al = tab[(f * 2 + 1) * kWave + lane];
+                for (int mt = 0; mt < 4; ++mt) {
+                    const int f = mt * 2 + kk;
+                    const uint4 ah = tab[(f * 2) * kWave + lane], al = tab[(f * 2 + 1) * kWave + lane];
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) Y[mt][j] = mfma3(ah, al, bh[j], bl[j], Y[mt][j]);
+                    for (int j = 0; j < NTW; ++j) Y[mt][j] = mfma3(ah, al, bh[j], bl[j], Y[mt][j]);
+                }
             }
 #pragma unroll
             for (int ms = 0; ms < MTS; ++ms) {
@@ -356,7 +394,7 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
             }
         }
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
+        for (int kc = 0; kc < (SO ? 0 : KC); ++kc) {
             uint4 xh[NTW], xl[NTW];
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
@@ -374,13 +412,15 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
         }
 
         // ---- Y tile -> LDS ([step][channel])
+        if constexpr (!SO) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+            for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int j = 0; j < NTW; ++j)
+                for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    yt[yt_index(16 * mt + 4 * (lane / 16) + r, cw + 16 * j + lane % 16, LQ)] = Y[mt][j][r];
+                    for (int r = 0; r < 4; ++r)
+                        yt[yt_index(16 * mt + 4 * (lane / 16) + r, cw + 16 * j + lane % 16, LQ)] = Y[mt][j][r];
+        }
 
         // ---- state hand-off
         if (nv == kSubBlock) {
@@ -395,7 +435,7 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
                         Xr[ms][j][2 * q2] = fmaf(lt.x, xr, fmaf(-lt.y, xi, S[ms][j][2 * q2]));
                         Xr[ms][j][2 * q2 + 1] = fmaf(lt.x, xi, fmaf(lt.y, xr, S[ms][j][2 * q2 + 1]));
                     }
-            write_x();
+            if constexpr (!SO) write_x();
         } else {
             // ragged final sub-block (end of the prompt): step the recurrence
             // over its nv steps on the vector ALUs, from u = hi + lo in LDS
@@ -425,7 +465,7 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
 
         // ---- gate y = q Y and store whole 8-channel pieces of valid rows
 #pragma unroll
-        for (int r = 0; r < RG; ++r) {
+        for (int r = 0; r < (SO ? 0 : RG); ++r) {
             const int row = rg * RG + r;
             if (row < nv) {
                 const float4 y0 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, 8 * cg, LQ)]);
@@ -439,14 +479,16 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
         }
     }
 
-    if (c == a.plan.NC - 1) {
+    if (SO || c == a.plan.NC - 1) {
+        float2 *const base = SO ? reinterpret_cast<float2 *>(a.ws + a.plan.off_carry) + (c + 1) * (s.B * H * DD * P)
+                                : a.state_out;
 #pragma unroll
         for (int ms = 0; ms < MTS; ++ms)
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
                 const int64_t p = p0 + cw + 16 * j + lane % 16;
                 const int n0 = 8 * ms + 2 * (lane / 16);
-                float2 *dst = a.state_out + ((b * H + g) * DD) * P + p;
+                float2 *dst = base + ((b * H + g) * DD) * P + p;
                 if (n0 < DD) dst[(int64_t)n0 * P] = make_float2(Xr[ms][j][0], Xr[ms][j][1]);
                 if (n0 + 1 < DD) dst[(int64_t)(n0 + 1) * P] = make_float2(Xr[ms][j][2], Xr[ms][j][3]);
             }
@@ -455,21 +497,47 @@ __global__ __launch_bounds__(256) void chunk_mfma_kernel(PrefillArgs a, const fl
 
 template <int DD, int PT>
 hipError_t launch_dd(const PrefillArgs &a, const float2 *carry0, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.s.H * (a.s.P / PT)), (unsigned)a.plan.NC, (unsigned)a.s.B);
+    const dim3 grid((unsigned)(a.s.H * (a.s.P / PT)), (unsigned)a.plan.NC, (unsigned)a.s.B), block(4 * PT);
     if (a.s.act == kBF16)
-        chunk_mfma_kernel<DD, PT, kBF16><<<grid, dim3(256), 0, stream>>>(a, carry0);
+        chunk_mfma_kernel<DD, PT, kBF16, false, true><<<grid, block, 0, stream>>>(a, carry0);
     else
-        chunk_mfma_kernel<DD, PT, kF32><<<grid, dim3(256), 0, stream>>>(a, carry0);
+        chunk_mfma_kernel<DD, PT, kF32, false, true><<<grid, block, 0, stream>>>(a, carry0);
     return hipGetLastError();
+}
+
+template <int DD, int PT>
+hipError_t launch_dd_state(const PrefillArgs &a, bool vec, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.s.H * (a.s.P / PT)), (unsigned)(a.plan.NC - 1), (unsigned)a.s.B), block(4 * PT);
+    if (a.s.act == kBF16) {
+        if (vec) chunk_mfma_kernel<DD, PT, kBF16, true, true><<<grid, block, 0, stream>>>(a, nullptr);
+        else chunk_mfma_kernel<DD, PT, kBF16, true, false><<<grid, block, 0, stream>>>(a, nullptr);
+    } else {
+        if (vec) chunk_mfma_kernel<DD, PT, kF32, true, true><<<grid, block, 0, stream>>>(a, nullptr);
+        else chunk_mfma_kernel<DD, PT, kF32, true, false><<<grid, block, 0, stream>>>(a, nullptr);
+    }
+    return hipGetLastError();
+}
+
+template <int PT>
+hipError_t launch_pt(const PrefillArgs &a, const float2 *carry0, bool state_only, bool vec, hipStream_t stream) {
+    switch (a.s.d) {
+        case 8: return state_only ? launch_dd_state<8, PT>(a, vec, stream) : launch_dd<8, PT>(a, carry0, stream);
+        case 16: return state_only ? launch_dd_state<16, PT>(a, vec, stream) : launch_dd<16, PT>(a, carry0, stream);
+        case 32: return state_only ? launch_dd_state<32, PT>(a, vec, stream) : launch_dd<32, PT>(a, carry0, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-// 64-channel tiles: on MI355X two 64-channel workgroups per CU (d <= 16) stream
-// faster than one 128-channel workgroup.
-int mfma_channel_tile(int64_t d, int64_t P) {
-    if (d != 8 && d != 16 && d != 32) return 0;
-    return (P % 64 == 0) ? 64 : 0;
+// Channel tile: 128 channels (8 waves, 256-byte row pieces) when that still
+// gives one workgroup per CU without cutting the prompt into chunks (measured
+// on MI355X: 2.8 % faster at B = 16, D = 2048 and 3.6 % at B = 256 than two
+// 64-channel workgroups per CU), else 64.
+int mfma_channel_tile(const OpShape &s) {
+    if (s.d != 8 && s.d != 16 && s.d != 32) return 0;
+    if (s.P % 128 == 0 && s.B * s.H * (s.P / 128) >= 256) return 128;
+    return (s.P % 64 == 0) ? 64 : 0;
 }
 
 size_t mfma_table_bytes(int64_t H, int64_t d) {
@@ -489,24 +557,30 @@ size_t mfma_lam_bytes(int64_t H, int64_t d) {
 hipError_t launch_mfma_tables(const PrefillArgs &a, hipStream_t stream) {
     uint4 *frag = reinterpret_cast<uint4 *>(a.ws + a.plan.off_mfma_tab);
     float2 *lam = reinterpret_cast<float2 *>(a.ws + a.plan.off_mfma_lam);
+    float2 *lamT = a.plan.NC > 1 ? reinterpret_cast<float2 *>(a.ws + a.plan.off_lamT) : nullptr;
     const dim3 grid((unsigned)a.s.H), block(256);
     switch (a.s.d) {
-        case 8: mfma_tables_kernel<8><<<grid, block, 0, stream>>>(a.s, frag, lam); break;
-        case 16: mfma_tables_kernel<16><<<grid, block, 0, stream>>>(a.s, frag, lam); break;
-        case 32: mfma_tables_kernel<32><<<grid, block, 0, stream>>>(a.s, frag, lam); break;
+        case 8: mfma_tables_kernel<8><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT); break;
+        case 16: mfma_tables_kernel<16><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT); break;
+        case 32: mfma_tables_kernel<32><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_mfma(const PrefillArgs &a, const float2 *carry0, hipStream_t stream) {
-    if (mfma_channel_tile(a.s.d, a.s.P) != 64) return hipErrorInvalidValue;
-    switch (a.s.d) {
-        case 8: return launch_dd<8, 64>(a, carry0, stream);
-        case 16: return launch_dd<16, 64>(a, carry0, stream);
-        case 32: return launch_dd<32, 64>(a, carry0, stream);
-        default: return hipErrorInvalidValue;
-    }
+    const int pt = mfma_channel_tile(a.s);
+    if (pt == 128) return launch_pt<128>(a, carry0, false, true, stream);
+    if (pt == 64) return launch_pt<64>(a, carry0, false, true, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_mfma_state(const PrefillArgs &a, bool vec, hipStream_t stream) {
+    if (a.plan.NC < 2) return hipSuccess;
+    const int pt = mfma_channel_tile(a.s);
+    if (pt == 128) return launch_pt<128>(a, nullptr, true, vec, stream);
+    if (pt == 64) return launch_pt<64>(a, nullptr, true, vec, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace hm

@@ -105,10 +105,13 @@ hm_status hyena_modal_prefill_workspace(const hm_desc *desc, int64_t L, size_t *
  *   state_out end-of-prompt state (may equal state_in).
  *   workspace device scratch of at least hyena_modal_prefill_workspace() bytes;
  *             its contents on entry do not matter.
- * The hot path splits the prompt into chunks: a chunk-local Vandermonde
- * contraction on the matrix cores, a carry scan over chunks, and an in-chunk
- * modal scan that produces y (the Hyena evaluation without materialising T_h,
- * StripedHyena article, "Hyena層次結構").
+ * Neither path materialises T_h (StripedHyena article, "Hyena層次結構").  On the
+ * matrix cores the prompt runs in 64-step sub-blocks: a causal Toeplitz product
+ * inside each, the modal state carried between them.  A prompt cut into
+ * chunks (too few batch rows x channel tiles to fill the GPU) first gets each
+ * chunk's end state from a state-only pass of the same sub-blocks, then a
+ * carry scan over chunks.  The vector-ALU path (any shape) does a chunk-local
+ * Vandermonde contraction, the carry scan, and an in-chunk modal scan.
  */
 hm_status hyena_modal_prefill(const hm_desc *desc, int64_t L,
                               const void *q, const void *k, const void *v, int64_t ld_in,
@@ -166,7 +169,7 @@ hm_status hyena_modal_prefill_workspace_ex(const hm_desc *desc, int64_t L,
  */
 typedef struct hm_prefill_info {
     int32_t algo;           /* hm_prefill_algo that runs */
-    int32_t reserved;       /* 0 */
+    int32_t channel_tile;   /* channels per matrix-core workgroup (64 or 128); 0 for the lane scan */
     int64_t chunk;          /* chunk length in steps (L when the prompt is one chunk; 0 when L = 0) */
     int64_t n_chunks;       /* number of chunks (0 when L = 0) */
     size_t workspace_bytes; /* as hyena_modal_prefill_workspace_ex */

@@ -135,6 +135,14 @@ def test_workspace_sizes_follow_the_chunk_plan(lib):
     # 32 chunk-state slots of B*D*d complex64 dominate
     assert big >= 32 * 4 * 4096 * 32 * 8
     assert hb.hyena_modal_prefill_workspace(d, 65536, chunk=4096, algo="scan") < big
+    # the matrix-core plan takes its chunk states from its own 64-step tables: no
+    # Vandermonde matrix that grows with the chunk length
+    one = _desc(batch=1, channels=4096, heads=32, modes=32)
+    slots = 4 * 1 * 4096 * 32 * 8
+    mf = hb.hyena_modal_prefill_workspace(one, 65536, chunk=16384, algo="mfma")
+    sc = hb.hyena_modal_prefill_workspace(one, 65536, chunk=16384, algo="scan")
+    assert slots <= mf < slots + (2 << 20) < sc
+    assert hb.hyena_modal_prefill_workspace(one, 65536, chunk=32768, algo="mfma") < mf
 
 
 def test_prefill_plan_choices(lib):
@@ -144,6 +152,14 @@ def test_prefill_plan_choices(lib):
     p = hb.hyena_modal_prefill_plan(w2, 2048)
     assert p["algo"] == "mfma" and p["n_chunks"] == 1 and p["chunk"] == 2048
     assert p["workspace_bytes"] == hb.hyena_modal_prefill_workspace(w2, 2048)
+    # 128-channel workgroups when batch x heads still gives 256 of them, else 64
+    assert p["channel_tile"] == 128
+    w4 = _desc(batch=4, channels=4096, heads=32, modes=32)
+    p = hb.hyena_modal_prefill_plan(w4, 65536)
+    assert p["channel_tile"] == 64 and p["n_chunks"] == 1
+    p = hb.hyena_modal_prefill_plan(_desc(batch=1, channels=4096, heads=32, modes=32), 65536)
+    assert p["channel_tile"] == 64 and p["n_chunks"] == 4
+    assert hb.hyena_modal_prefill_plan(w2, 2048, algo="scan")["channel_tile"] == 0
     # a single batch row over 4 heads: the prompt is cut into 64-step multiples
     few = _desc(batch=1, channels=256, heads=4, modes=8)
     p = hb.hyena_modal_prefill_plan(few, 4096)

@@ -302,21 +302,76 @@ def test_fused_qkv_buffer_and_strided_output(algo):
     assert torch.all(ybuf[:, :, D:] == 3.0).item()
 
 
-def test_odd_row_stride_scalar_paths():
-    """An odd row stride forces the scalar (unvectorised) load paths."""
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_odd_row_stride_scalar_paths(act):
+    """An odd row stride forces the scalar (unvectorised) load paths: on a
+    matrix-core plan cut into chunks, the state-only pass with element loads
+    and the lane scan from its carries."""
     torch = require_gpu()
     rng = np.random.default_rng(6)
     B, D, H, d, L = 2, 128, 2, 8, 200
     params = _rand_params(rng, H, d)
     ld = D + 1
-    big = [_rand_act(rng, (B, L, ld), "f32") for _ in range(3)]
-    dev = [to_dev(a, "f32") for a in big]
-    op = _op(params, B, D, "f32")
-    log("odd stride")
+    big = [_rand_act(rng, (B, L, ld), act) for _ in range(3)]
+    dev = [to_dev(a, act) for a in big]
+    op = _op(params, B, D, act)
+    assert op.plan(L, chunk=64)["algo"] == "mfma"
+    log(f"odd stride {act}")
     y, st = op.prefill(*(t[:, :, :D] for t in dev), chunk=64)
     torch.cuda.synchronize()
-    y_or, _ = oracle.modal_scan(params, *(np.ascontiguousarray(a[:, :, :D]) for a in big))
-    assert rel_err(to_np64(y), y_or) <= TOL["f32"]
+    y_or, st_or = oracle.modal_scan(params, *(np.ascontiguousarray(a[:, :, :D]) for a in big))
+    assert rel_err(to_np64(y), y_or) <= TOL[act]
+    assert rel_err(state_for_channels(st, np.arange(D), D // H), st_or) <= TOL[act]
+
+
+@pytest.mark.parametrize("d,act", [(8, "f32"), (16, "bf16"), (32, "f32")])
+def test_matrix_core_128_channel_tiles(d, act):
+    """Batch x heads large enough for 128-channel, 8-wave workgroups; whole
+    prompt, and cut into 64-step chunks (state-only pass at that tile)."""
+    torch = require_gpu()
+    rng = np.random.default_rng(40 + d)
+    B, D, H, L = 16, 2048, 16, 200
+    params = _rand_params(rng, H, d, 0.8, 0.999)
+    q_, k_, v_ = (_rand_act(rng, (B, L, D), act) for _ in range(3))
+    q, k, v = (to_dev(a, act) for a in (q_, k_, v_))
+    op = _op(params, B, D, act)
+    y_or, st_or = oracle.modal_scan(params, q_, k_, v_)
+    for chunk in (0, 64):
+        plan = op.plan(L, chunk=chunk)
+        assert plan["algo"] == "mfma" and plan["channel_tile"] == 128
+        log(f"128-channel tiles d={d} {act} chunk={chunk} plan={plan}")
+        y, st = op.prefill(q, k, v, chunk=chunk)
+        torch.cuda.synchronize()
+        e_y = rel_err(to_np64(y), y_or)
+        e_s = rel_err(state_for_channels(st, np.arange(D), D // H), st_or)
+        print(f"128-channel d={d} chunk={chunk}: y {e_y:.2e} state {e_s:.2e}")
+        assert e_y <= TOL[act] and e_s <= TOL[act]
+
+
+def test_long_prompt_single_batch_row_chunked():
+    """One batch row of the 64k-token workload: too few channel tiles for the
+    GPU, so the prompt is cut into chunks (state-only pass, carry scan, full
+    pass).  Sampled channels against the oracle."""
+    torch = require_gpu()
+    cfg = get_config(4)
+    params = modal_params(cfg)
+    inp = prompt_inputs(cfg, batches=[1])
+    op = _op(params, 1, cfg.D, cfg.act)
+    plan = op.plan(cfg.L)
+    assert plan["algo"] == "mfma" and plan["n_chunks"] > 1
+    q, k, v = (to_dev(inp[n], cfg.act) for n in "qkv")
+    log(f"single-row 64k prompt plan={plan}")
+    y, st = op.prefill(q, k, v)
+    torch.cuda.synchronize()
+    del q, k, v
+    chans = _sample_channels(cfg, 28, 404)
+    y_or, st_or = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"], channels=chans)
+    del inp
+    ct = torch.as_tensor(chans, device="cuda")
+    e_y = rel_err(to_np64(y.index_select(2, ct)), y_or)
+    e_s = rel_err(state_for_channels(st, chans, cfg.P), st_or)
+    print(f"single-row 64k prompt: y rel err {e_y:.3e}, state rel err {e_s:.3e}")
+    assert e_y <= TOL[cfg.act] and e_s <= TOL[cfg.act]
 
 
 def test_impulse_response_matches_filter():
