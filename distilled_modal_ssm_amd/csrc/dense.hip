@@ -619,7 +619,6 @@ hipError_t launch_splitk(const GemmArgs &g, hipStream_t stream) {
     switch (nsl) {
         case 2: splitk_reduce_kernel<RMS, 2><<<grid, block, 0, stream>>>(g); break;
         case 4: splitk_reduce_kernel<RMS, 4><<<grid, block, 0, stream>>>(g); break;
-        case 8: splitk_reduce_kernel<RMS, 8><<<grid, block, 0, stream>>>(g); break;
         case 16: splitk_reduce_kernel<RMS, 16><<<grid, block, 0, stream>>>(g); break;
         default: return hipErrorInvalidValue;
     }
@@ -636,15 +635,21 @@ hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
 
 template <bool RMS>
 hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
+    if (g.M <= 64 && g.K == 2048) {
+        // Measured on MI355X at M = 64 (graph-replayed, 24 distinct weights):
+        // 32 columns per workgroup for wide outputs (N = 6144: 13.6 us, 16
+        // columns 15.4 us), 16 for narrower ones (N = 2048: 6.9 us, against
+        // 8.9 us with 32 columns, 9.1 us split-K and 10.6 us skinny).
+        if (g.N >= 4096)
+            gemm_stream_lds_kernel<2, 4, RMS><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
+        else
+            gemm_stream_lds_kernel<1, 4, RMS><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
+        return hipGetLastError();
+    }
     const size_t ws_need = splitk_workspace_bytes(g.M, g.N, g.K);
     if (g.ws && ws_need > 0 && g.ws_bytes >= ws_need) return launch_splitk<RMS>(g, stream);
     if (g.M <= 64 && g.K % kSkCK == 0) {
-        // Measured on MI355X at M = 64, K = 2048: the unrolled streaming kernel
-        // is fastest for wide outputs, the LDS-staged one for narrow outputs.
-        if (g.K == 2048 && g.N >= 4096)
-            gemm_stream_lds_kernel<2, 4, RMS><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
-        else
-            gemm_skinny_kernel<16, RMS><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
+        gemm_skinny_kernel<16, RMS><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
         return hipGetLastError();
     }
     // 256 x 256 tile, 16 waves of 64 x 64 (4 per SIMD): measured on MI355X at
@@ -656,12 +661,12 @@ hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
 }  // namespace
 
 size_t splitk_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    // Measured on MI355X at M = 64, K = 2048 (graph-replayed): split-K beats the
-    // LDS-staged kernel for N = 2048 (8.2 vs 8.6 us) but loses to the unrolled
-    // streaming kernel for N = 6144 (17.3 vs 14.7 us), so wide outputs keep it.
-    if (M < 1 || M > 64 || N < 1 || N > 4096 || K % kSplitKS != 0) return 0;
+    // M <= 64 and N <= 4096 with K in {512, 1024, 4096}; K = 2048 always takes
+    // the streaming kernel, which is faster than split-K there (measured on
+    // MI355X at M = 64: 6.9 vs 9.1 us for N = 2048), so it needs no workspace.
+    if (M < 1 || M > 64 || N < 1 || N > 4096 || K % kSplitKS != 0 || K == 2048) return 0;
     const int64_t nsl = K / kSplitKS;
-    if (nsl != 2 && nsl != 4 && nsl != 8 && nsl != 16) return 0;  // K in {512, 1024, 2048, 4096}
+    if (nsl != 2 && nsl != 4 && nsl != 16) return 0;
     const size_t tiles = (size_t)((N + kSplitBN - 1) / kSplitBN);
     return tiles * nsl * (4096 + 64) * sizeof(float);
 }

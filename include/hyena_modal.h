@@ -241,9 +241,9 @@ hm_status hyena_dense_rms_bf16(int64_t M, int64_t N, int64_t K, const void *A, i
 
 /*
  * The same two products with a caller-owned workspace that enables the
- * split-K path for small M (the generation step: M <= 64, N <= 4096, K in
- * {512, 1024, 2048, 4096}; wider outputs stream their weights faster without
- * it).  There, a workgroup owns 64 output columns and one 256-wide
+ * split-K path for small M (M <= 64, N <= 4096, K in {512, 1024, 4096}; K =
+ * 2048 and wider outputs take weight-streaming kernels that are faster
+ * without it).  There, a workgroup owns 64 output columns and one 256-wide
  * K slice and writes a float32 partial to the workspace; a second pass sums
  * each column tile's partials and writes C.  Results equal the workspace-less
  * calls up to float32 summation order.

@@ -253,10 +253,14 @@ def test_dense_and_rms_validation(lib):
 
 def test_split_k_workspace_contract(lib):
     """Workspace sizes of the small-M split-K path and its validation."""
-    need = hb.hyena_dense_workspace(64, 2048, 2048)
-    tiles, slices = 2048 // 64, 2048 // 256
+    need = hb.hyena_dense_workspace(64, 2048, 1024)
+    tiles, slices = 2048 // 64, 1024 // 256
     assert need == tiles * slices * (4096 + 64) * 4
-    assert hb.hyena_dense_workspace(64, 6144, 2048) == 0  # wide outputs: streaming kernel
+    assert hb.hyena_dense_workspace(64, 4096, 4096) == (4096 // 64) * 16 * (4096 + 64) * 4
+    # K = 2048 takes the streaming kernel at any width; wider than 4096: no split-K
+    assert hb.hyena_dense_workspace(64, 2048, 2048) == 0
+    assert hb.hyena_dense_workspace(64, 6144, 2048) == 0
+    assert hb.hyena_dense_workspace(64, 6144, 1024) == 0
     assert hb.hyena_dense_workspace(37, 96, 1024) == 2 * 4 * (4096 + 64) * 4
     # shapes outside the path need none: M > 64, K not a multiple of 256, a single slice
     assert hb.hyena_dense_workspace(65, 6144, 2048) == 0
@@ -268,7 +272,7 @@ def test_split_k_workspace_contract(lib):
     assert e.value.status == hb.HM_ERR_INVALID_ARG
 
     def call(ws, nbytes, M=64):
-        hb.hyena_dense_bf16(M, 2048, 2048, FAKE, 2048, FAKE, 2048, None, FAKE, 2048, stream=0,
+        hb.hyena_dense_bf16(M, 2048, 1024, FAKE, 1024, FAKE, 1024, None, FAKE, 2048, stream=0,
                             workspace=ws, ws_bytes=nbytes)
 
     for ws, nbytes, status in [(FAKE, need - 1, hb.HM_ERR_WORKSPACE), (FAKE + 16, need, hb.HM_ERR_UNSUPPORTED)]:
@@ -276,7 +280,7 @@ def test_split_k_workspace_contract(lib):
             call(ws, nbytes)
         assert e.value.status == status
     with pytest.raises(hb.HMError) as e:
-        hb.hyena_dense_rms_bf16(64, 2048, 2048, FAKE, 2048, FAKE, 2048, 1e-6, FAKE, 2048, stream=0,
+        hb.hyena_dense_rms_bf16(64, 2048, 1024, FAKE, 1024, FAKE, 1024, 1e-6, FAKE, 2048, stream=0,
                                 workspace=FAKE, ws_bytes=16)
     assert e.value.status == hb.HM_ERR_WORKSPACE
 

@@ -28,7 +28,8 @@ def _bits(rng, shape, std=1.0):
 @pytest.mark.parametrize("M,N,K", [
     (64, 6144, 2048),     # generation-step in_proj (weight streaming path)
     (37, 4100, 2048),     # weight streaming path, ragged rows and columns
-    (64, 2048, 2048),     # generation-step out_proj
+    (64, 2048, 2048),     # generation-step out_proj (streaming, 16 columns per workgroup)
+    (21, 1000, 2048),     # streaming, 16 columns per workgroup, ragged
     (37, 96, 1024),       # ragged rows and columns, skinny path
     (300, 200, 128),      # tiled path, ragged M and N
     (1024, 768, 512),     # tiled path, several tiles
@@ -98,11 +99,12 @@ def test_dense_split_k_shared_workspace():
     scale."""
     torch = require_gpu()
     rng = np.random.default_rng(77)
-    shapes = [(64, 4096, 2048, "rms"), (64, 2048, 2048, "plain"), (37, 96, 1024, "scaled"),
-              (64, 4096, 4096, "plain"), (1, 200, 512, "rms"), (64, 2048, 2048, "rms"),
-              (64, 6144, 2048, "rms")]  # the last is wider than the split-K path: workspace ignored
+    shapes = [(64, 4096, 1024, "rms"), (64, 2048, 4096, "plain"), (37, 96, 1024, "scaled"),
+              (64, 4096, 4096, "plain"), (1, 200, 512, "rms"), (64, 2048, 1024, "rms"),
+              (64, 6144, 2048, "rms"),     # K = 2048: streaming kernel, workspace ignored
+              (50, 2048, 2048, "plain")]
     need = max(hb.hyena_dense_workspace(M, N, K) for M, N, K, _ in shapes)
-    assert hb.hyena_dense_workspace(64, 6144, 2048) == 0
+    assert hb.hyena_dense_workspace(64, 6144, 2048) == 0 and hb.hyena_dense_workspace(50, 2048, 2048) == 0
     ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda")
     for M, N, K, kind in shapes:
         a = _bits(rng, (M, K), 2.0)
