@@ -15,13 +15,12 @@
 //     WM x WN sub-tile of 16x16x32 MFMAs.  Tiles are ordered so each XCD walks
 //     a contiguous range, grouped GM m-tiles at a time, to keep A and W in L2.
 //   * gemm_stream_lds / gemm_skinny (M <= 64, the generation step): a
-//     workgroup owns 16-32 columns and all rows.  gemm_stream_lds (wide
-//     outputs, K = 2048) streams W fragments through a register ring with its
-//     K loop unrolled and stages A per wave through LDS in 128-byte row
-//     pieces; gemm_skinny stages contiguous A and W slabs through
-//     double-buffered LDS.  Both sum their K parts through LDS.  Every
-//     workgroup re-reads all of A (64 x K), so these are bound by L1->L2
-//     request throughput, not by the W stream alone.
+//     workgroup owns 16-32 columns and all rows.  gemm_stream_lds (K = 2048)
+//     loads A and W as 128-byte row pieces a few chunks ahead and stages them
+//     per wave through LDS, its K loop unrolled; gemm_skinny stages
+//     contiguous A and W slabs through double-buffered LDS.  Both sum their K
+//     parts through LDS.  Every workgroup re-reads all of A (64 x K), so these
+//     are bound by L1->L2 request throughput, not by the W stream alone.
 #include "hm_internal.hpp"
 
 #include <type_traits>
@@ -35,6 +34,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma16(const uint4 a, const uint4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
                                                     c, 0, 0, 0);
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1 in order.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
 }
 
 // Row sums of squares come from one extra MFMA per A fragment: the diagonal of
@@ -351,62 +359,61 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 
 // Weight-streaming GEMM for M <= 64 and K = 2048 (K loop fully unrolled).
 // Workgroup = 4 waves on all rows x BN = 16 NTW columns; wave w takes K
-// quarter w (16 steps of 32).  The weight fragments stream straight from
-// memory through an R-deep register ring: the loads for step s + R are issued
-// before step s is multiplied, and since the loop is unrolled every wait names
-// exactly the load it needs (a rolled loop drains all loads at its head, which
-// serialises the HBM latency).  A is re-read by every workgroup, so its
-// requests, not W's bytes, set the pace: the wave's 64 x 64 slab of A for each
-// 64-wide K chunk is loaded as 128-byte row pieces (8 lanes per row, half the
-// requests of fragment-shaped loads) two chunks ahead, written to a
-// wave-private LDS buffer (rows padded to 144 B) and read back as MFMA
+// quarter w (8 chunks of 64).  Both operands are loaded as 128-byte row pieces
+// (8 lanes per row, 8 rows per load instruction) -- measured on MI355X,
+// fragment-shaped loads (64 bytes of 16 rows per instruction) stream W 15-40 %
+// slower and double the requests for A, which every workgroup re-reads --
+// into registers (A two chunks ahead, W SW chunks ahead), then written to
+// wave-private LDS buffers (rows padded to 144 B) and read back as MFMA
 // fragments.  The buffers are private to the wave, so no workgroup barrier is
 // needed inside the K loop (LDS operations of one wave complete in order).
-// The four K quarters are summed through LDS, reusing the A buffers.
+// The loop is unrolled at compile time, so every wait names exactly the load
+// it needs.  The four K quarters are summed through LDS, reusing the A buffers.
 constexpr int kAsLd = 72;  // bf16 per LDS row of the A chunk (64 + 8 pad)
 
-template <int NTW, int R, bool RMS>
+template <int NTW, int SW, bool RMS>
 __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
-    constexpr int BN = 16 * NTW, NCH = 8, NSTEPS = 2 * NCH;  // K quarter: 8 chunks of 64 = 16 steps of 32
+    constexpr int BN = 16 * NTW, NCH = 8;  // K quarter: 8 chunks of 64
+    constexpr int WPL = BN / 8;            // W row pieces per lane per chunk (8 rows per load)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     __shared__ __attribute__((aligned(16))) uint16_t as[4][2][64 * kAsLd];
+    __shared__ __attribute__((aligned(16))) uint16_t wsm[4][2][BN * kAsLd];
     __shared__ float red_ss[RMS ? 4 * 64 : 1];
     static_assert(4 * 64 * BN * sizeof(float) <= sizeof(as), "the K-part sums reuse the A buffers");
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     const int64_t n0 = (int64_t)blockIdx.x * BN;
-    const int64_t kbeg = (int64_t)w * NSTEPS * 32;
+    const int64_t kbeg = (int64_t)w * NCH * 64;
     const uint16_t *A = static_cast<const uint16_t *>(g.A);
     const uint16_t *W = static_cast<const uint16_t *>(g.W);
     const int ko = 8 * (lane / 16);
-    const uint16_t *wrow[NTW];
-#pragma unroll
-    for (int j = 0; j < NTW; ++j) {
-        const int64_t c = n0 + j * 16 + lane % 16;
-        wrow[j] = W + (c < g.N ? c : 0) * g.ldw + kbeg + ko;  // clamped columns are masked at the end
-    }
-    // A chunk piece i of lane l: row 8 i + l / 8, 16-byte piece l % 8 of the chunk's 128 bytes
-    const int arow0 = lane / 8, apiece = lane % 8;
-    const uint16_t *arow[8];
+    // row piece of lane l in a load: row 8 i + l / 8, 16-byte piece l % 8 of the chunk's 128 bytes
+    const int prow = lane / 8, ppiece = lane % 8;
+    const uint16_t *arow[8], *wrow[WPL];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int r = 8 * i + arow0;
-        arow[i] = A + (int64_t)(r < g.M ? r : 0) * g.lda + kbeg + 8 * apiece;  // clamped rows are masked at the end
+        const int r = 8 * i + prow;
+        arow[i] = A + (int64_t)(r < g.M ? r : 0) * g.lda + kbeg + 8 * ppiece;  // clamped rows are masked at the end
     }
-    // native vectors: the staging arrays stay in registers (struct copies into
-    // LDS kept them in scratch)
-    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-#define HM_LOAD_A(ra, ch)                                                                        \
-    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_) ra[i_] = *reinterpret_cast<const u32x4 *>(arow[i_] + 64 * (ch));
-#define HM_PUT_A(ra, buf)                                                                        \
-    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_)                                             \
-        *reinterpret_cast<u32x4 *>(&as[w][buf][(8 * i_ + arow0) * kAsLd + 8 * apiece]) = ra[i_];
-    u32x4 ra0[8], ra1[8];
-    uint4 rw[R][NTW];
-    HM_LOAD_A(ra0, 0)
-    HM_LOAD_A(ra1, 1)
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+    for (int i = 0; i < WPL; ++i) {
+        const int64_t c = n0 + 8 * i + prow;
+        wrow[i] = W + (c < g.N ? c : 0) * g.ldw + kbeg + 8 * ppiece;  // clamped columns are masked at the end
+    }
+    // A two chunks ahead, W SW chunks ahead, in registers (native vectors, so
+    // they stay in registers); every index below is a compile-time constant
+    u32x4 ra[2][8], rw[SW][WPL];
+    auto load_a = [&](auto cc) {
+        constexpr int c = decltype(cc)::value;
 #pragma unroll
-        for (int j = 0; j < NTW; ++j) rw[i][j] = *reinterpret_cast<const uint4 *>(wrow[j] + 32 * i);
+        for (int i = 0; i < 8; ++i) ra[c % 2][i] = *reinterpret_cast<const u32x4 *>(arow[i] + 64 * c);
+    };
+    auto load_w = [&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+#pragma unroll
+        for (int i = 0; i < WPL; ++i) rw[c % SW][i] = *reinterpret_cast<const u32x4 *>(wrow[i] + 64 * c);
+    };
+    static_for<0, SW>([&](auto cc) { load_w(cc); });
+    static_for<0, 2>([&](auto cc) { load_a(cc); });
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc[4][NTW], ss[4];
 #pragma unroll
@@ -415,24 +422,29 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // chunk pairs: chunk 2p in buffer 0 (registers ra0), 2p + 1 in buffer 1 (ra1);
-    // steps 4p .. 4p + 3 use ring slots 0 .. 3 (R = 4)
-    static_assert(R == 4, "ring slot = step mod 4");
-    auto steps = [&](auto bufc, int st0) {  // bufc: std::integral_constant, so ring slots are constants
-        constexpr int buf = decltype(bufc)::value;
+    // chunk c: its A and W pieces go to the wave's LDS buffers c % 2 (the
+    // wave's LDS operations complete in order, so chunk c - 2's fragment reads
+    // of those buffers are done), the loads for chunks c + 2 (A) and c + SW (W)
+    // are issued into the freed registers, then two 32-wide MFMA steps
+    static_for<0, NCH>([&](auto cc) {
+        constexpr int c = decltype(cc)::value, buf = c % 2;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<u32x4 *>(&as[w][buf][(8 * i + prow) * kAsLd + 8 * ppiece]) = ra[buf][i];
+#pragma unroll
+        for (int i = 0; i < WPL; ++i)
+            *reinterpret_cast<u32x4 *>(&wsm[w][buf][(8 * i + prow) * kAsLd + 8 * ppiece]) = rw[c % SW][i];
+        if constexpr (c + 2 < NCH) load_a(std::integral_constant<int, c + 2>{});
+        if constexpr (c + SW < NCH) load_w(std::integral_constant<int, c + SW>{});
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int st = st0 + h, i = (2 * buf + h);  // st % 4 with st0 = 4p + 2 buf
             uint4 a[4], b[NTW];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
                 a[m] = *reinterpret_cast<const uint4 *>(&as[w][buf][(16 * m + lane % 16) * kAsLd + 32 * h + ko]);
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) b[j] = rw[i][j];
-            if (st + R < NSTEPS) {
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) rw[i][j] = *reinterpret_cast<const uint4 *>(wrow[j] + 32 * (st + R));
-            }
+            for (int j = 0; j < NTW; ++j)
+                b[j] = *reinterpret_cast<const uint4 *>(&wsm[w][buf][(16 * j + lane % 16) * kAsLd + 32 * h + ko]);
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -442,18 +454,7 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
                 for (int m = 0; m < 4; ++m) ss[m] = mfma16(a[m], a[m], ss[m]);
             }
         }
-    };
-#pragma unroll
-    for (int p = 0; p < NCH / 2; ++p) {
-        HM_PUT_A(ra0, 0)
-        if (2 * p + 2 < NCH) { HM_LOAD_A(ra0, 2 * p + 2) }
-        steps(std::integral_constant<int, 0>{}, 4 * p);
-        HM_PUT_A(ra1, 1)
-        if (2 * p + 3 < NCH) { HM_LOAD_A(ra1, 2 * p + 3) }
-        steps(std::integral_constant<int, 1>{}, 4 * p + 2);
-    }
-#undef HM_LOAD_A
-#undef HM_PUT_A
+    });
     if constexpr (RMS) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -637,13 +638,13 @@ template <bool RMS>
 hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
     if (g.M <= 64 && g.K == 2048) {
         // Measured on MI355X at M = 64 (graph-replayed, 24 distinct weights):
-        // 32 columns per workgroup for wide outputs (N = 6144: 13.6 us, 16
-        // columns 15.4 us), 16 for narrower ones (N = 2048: 6.9 us, against
-        // 8.9 us with 32 columns, 9.1 us split-K and 10.6 us skinny).
+        // 32 columns per workgroup for wide outputs (N = 6144: 12.5 us), 16 for
+        // narrower ones (N = 2048: 6.2 us, against 9.1 us split-K and 10.6 us
+        // skinny); W two chunks ahead (three or four: no faster).
         if (g.N >= 4096)
-            gemm_stream_lds_kernel<2, 4, RMS><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
+            gemm_stream_lds_kernel<2, 2, RMS><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
         else
-            gemm_stream_lds_kernel<1, 4, RMS><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
+            gemm_stream_lds_kernel<1, 2, RMS><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
         return hipGetLastError();
     }
     const size_t ws_need = splitk_workspace_bytes(g.M, g.N, g.K);
