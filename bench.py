@@ -187,7 +187,7 @@ def parse():
 def cpu_baseline(cfg, params, inp, dec, min_seconds: float = 10.0):
     """The float64 oracle (as it stands) on this host over the same workload:
     the full step (filter, prefill, decode steps) repeated until ``min_seconds``
-    of CPU time have passed (at most 20 repetitions), on an evenly spaced
+    of CPU time have passed (at most 100 repetitions), on an evenly spaced
     channel subset when one repetition of the whole width would be too long."""
     import oracle
     budget = 6e9  # mode-steps per repetition, ~1 s on 16 cores
@@ -196,7 +196,7 @@ def cpu_baseline(cfg, params, inp, dec, min_seconds: float = 10.0):
     chans = np.linspace(0, cfg.D - 1, n_sel).round().astype(np.int64) if n_sel < cfg.D else None
     reps = 0
     t0 = time.perf_counter()
-    while reps < 20 and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+    while reps < 100 and (reps == 0 or time.perf_counter() - t0 < min_seconds):
         oracle.filter_taps(params, cfg.L)
         _, st = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"], channels=chans)
         oracle.modal_scan(params, dec["q"], dec["k"], dec["v"], state=st, channels=chans,
