@@ -146,7 +146,9 @@ typedef struct hm_prefill_opts {
  * history enters through the modal state (readout rows Re(R lambda^i)), and the
  * state moves on with a 64-column Vandermonde product -- all three per-head
  * matrices shared by the head's channels (weight tying, Laughing Hyena
- * Distillery review, "提出的方法"), so they run on the matrix cores.
+ * Distillery review, "提出的方法"), so they run on the matrix cores.  With the
+ * prompt cut into chunks, the state each chunk hands on comes from a pass of
+ * the same sub-blocks that reads only k and v and keeps only the state.
  */
 hm_status hyena_modal_prefill_ex(const hm_desc *desc, int64_t L,
                                  const void *q, const void *k, const void *v, int64_t ld_in,
@@ -163,7 +165,9 @@ hm_status hyena_modal_prefill_workspace_ex(const hm_desc *desc, int64_t L,
  * GPU call): the in-chunk algorithm (HM_PREFILL_SCAN or HM_PREFILL_MFMA, never
  * AUTO), the chunk length, the number of chunks the prompt is cut into, and the
  * workspace size.  The answer assumes 16-byte aligned activation rows; with
- * unaligned rows an AUTO prefill falls back to the scan.  opts may be NULL
+ * unaligned rows an AUTO prefill runs the scan inside the chunks instead (a
+ * chunked matrix-core plan still takes its chunk states from the state-only
+ * sub-block pass, with element loads; same workspace).  opts may be NULL
  * (defaults).  HM_ERR_UNSUPPORTED when HM_PREFILL_MFMA is asked for a shape it
  * does not cover; other errors as for the workspace query.
  */
