@@ -219,6 +219,228 @@ __global__ __launch_bounds__(256) void fft_conv_kernel(FftArgs a) {
     }
 }
 
+// ------------------------------------------------------------ multi-pass transforms
+//
+// Past N = 8192 a transform no longer fits one workgroup's LDS, so it runs in
+// three passes over HBM (the four-step factorisation).  With N = NA NB,
+// t = ta + NA tb and k = kb + NB ka,
+//     X[kb + NB ka] = sum_ta W_NA^(ta ka) W_N^(ta kb) sum_tb x[ta + NA tb] W_NB^(tb kb)
+// (W_n = exp(-2 pi i / n)).  The work buffer z holds one complex value per
+// (batch row, frequency or time index, channel pair) in rows of D/2 pairs, and
+// a workgroup always takes kLongCB adjacent pairs of every row it touches, so
+// HBM sees whole 128-byte row pieces while the transforms run down the
+// columns of an LDS tile ([rows][kLongCB], all columns at once):
+//   pass 1, per ta: u = k v (or the filter taps) at t = ta + NA tb < L, zero
+//           beyond; length-NB transform over tb; times W_N^(ta kb); to z[kb][ta];
+//   pass 2, per kb: length-NA transform over ta (X[kb + NB ka] by ka); for the
+//           filter, stored as its spectrum [H][kb][ka]; for the convolution,
+//           times the head's spectrum, conjugated, transformed again, times
+//           W_N^(ta kb) -- the conjugate of the inverse's first half -- back to
+//           z[kb][ta];
+//   pass 3, per ta: length-NB transform over kb; y[ta + NA tb] is its
+//           conjugate over N, gated by q, for t < L.
+constexpr int kLongCB = 16;  // channel pairs (complex columns) per workgroup
+
+// One Stockham radix-R pass over the NS rows of an LDS tile x[NS][kLongCB]
+// (the same butterflies as stockham_pass, for every column).  256 threads.
+template <int R, int NS>
+__device__ __forceinline__ void tile_pass(float2 *x, const float2 *tw, int Ns) {
+    constexpr int CB = kLongCB, nb = NS / R, items = nb * CB, MI = (items + 255) / 256;
+    const int tid = threadIdx.x;
+    float2 v[MI][R];
+#pragma unroll
+    for (int it = 0; it < MI; ++it) {
+        const int i = tid + 256 * it;
+        if (i < items) {
+            const int ch = i % CB, j = i / CB;
+            const int k = j & (Ns - 1), step = NS / (Ns * R);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float2 a = x[(j + r * nb) * CB + ch];
+                v[it][r] = r == 0 ? a : cmul(twiddle(tw, k * r * step, NS / 2), a);
+            }
+            dft_regs<R>(v[it]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < MI; ++it) {
+        const int i = tid + 256 * it;
+        if (i < items) {
+            const int ch = i % CB, j = i / CB;
+            const int base = (j / Ns) * Ns * R + (j & (Ns - 1));
+#pragma unroll
+            for (int r = 0; r < R; ++r) x[(base + r * Ns) * CB + ch] = v[it][r];
+        }
+    }
+    __syncthreads();
+}
+
+// Forward transform of every column of the tile (2^LOGNS rows, natural order).
+template <int LOGNS>
+__device__ void tile_fft(float2 *x, const float2 *tw) {
+    constexpr int NS = 1 << LOGNS, MAIN = LOGNS / 4, REST = LOGNS % 4;
+    int Ns = 1;
+#pragma unroll
+    for (int p = 0; p < MAIN; ++p, Ns <<= 4) tile_pass<16, NS>(x, tw, Ns);
+    if constexpr (REST == 3) tile_pass<8, NS>(x, tw, Ns);
+    if constexpr (REST == 2) tile_pass<4, NS>(x, tw, Ns);
+    if constexpr (REST == 1) tile_pass<2, NS>(x, tw, Ns);
+}
+
+// exp(-2 pi i m / NS) for m < NS/2, from the N-point table (stride N / NS)
+template <int NS>
+__device__ __forceinline__ void load_subtable(float2 *tws, const float2 *tw, int64_t stride) {
+    for (int i = threadIdx.x; i < NS / 2; i += blockDim.x) tws[i] = tw[(int64_t)i * stride];
+}
+
+// Pass 1.  Workgroup = (ta, block of kLongCB pairs, batch row).  FILTER: the
+// columns are heads, x = their taps (imaginary part 0); else pair p is
+// channels 2p (real part) and 2p + 1 (imaginary part) of u = k v.
+template <int ACT, bool FILTER, int LOGNA, int LOGNB>
+__global__ __launch_bounds__(256) void fftl_pass1_kernel(FftArgs a, int64_t npairs) {
+    using A = Act<ACT>;
+    using T = typename A::T;
+    constexpr int NA = 1 << LOGNA, NB = 1 << LOGNB, CB = kLongCB;
+    constexpr int64_t N = (int64_t)NA * NB;
+    __shared__ float2 xs[NB * CB];
+    __shared__ float2 tws[NB / 2];
+    const int ta = blockIdx.x;
+    const int64_t p0 = (int64_t)blockIdx.y * CB, b = blockIdx.z;
+    load_subtable<NB>(tws, a.tw, NA);
+    if constexpr (FILTER) {
+        for (int e = threadIdx.x; e < NB * CB; e += 256) {
+            const int tb = e / CB, c = e % CB;
+            const int64_t t = ta + (int64_t)NA * tb, g = p0 + c;
+            xs[tb * CB + c] = make_float2((t < a.L && g < npairs) ? a.h[g * a.L + t] : 0.f, 0.f);
+        }
+    } else {
+        const T *kb = static_cast<const T *>(a.k) + b * a.L * a.ld_in;
+        const T *vb = static_cast<const T *>(a.v) + b * a.L * a.ld_in;
+        float *xf = reinterpret_cast<float *>(xs);  // pair c / 2, real (c even) or imaginary part
+        for (int e = threadIdx.x; e < NB * 2 * CB; e += 256) {
+            const int tb = e / (2 * CB), c = e % (2 * CB);
+            const int64_t t = ta + (int64_t)NA * tb, ch = 2 * p0 + c;
+            float u = 0.f;
+            if (t < a.L && ch < a.s.D) {
+                const int64_t o = t * a.ld_in + ch;
+                u = A::ld(kb + o) * A::ld(vb + o);
+            }
+            xf[tb * 2 * CB + c] = u;
+        }
+    }
+    __syncthreads();
+    tile_fft<LOGNB>(xs, tws);
+    float2 *zb = a.z + b * N * npairs;
+    for (int e = threadIdx.x; e < NB * CB; e += 256) {
+        const int kb = e / CB, c = e % CB;
+        const int64_t p = p0 + c;
+        if (p < npairs)
+            zb[((int64_t)kb * NA + ta) * npairs + p] = cmul(twiddle(a.tw, ta * kb, (int)(N / 2)), xs[kb * CB + c]);
+    }
+}
+
+// Pass 2.  Workgroup = (kb, block of kLongCB pairs, batch row).  FILTER: store
+// the spectra; else the spectrum product and the first half of the inverse,
+// in place.
+template <bool FILTER, int LOGNA, int LOGNB>
+__global__ __launch_bounds__(256) void fftl_pass2_kernel(FftArgs a, int64_t npairs) {
+    constexpr int NA = 1 << LOGNA, NB = 1 << LOGNB, CB = kLongCB;
+    constexpr int64_t N = (int64_t)NA * NB;
+    __shared__ float2 xs[NA * CB];
+    __shared__ float2 tws[NA / 2];
+    const int kb = blockIdx.x;
+    const int64_t p0 = (int64_t)blockIdx.y * CB, b = blockIdx.z;
+    load_subtable<NA>(tws, a.tw, NB);
+    float2 *zr = a.z + (b * N + (int64_t)kb * NA) * npairs;  // row ta at zr + ta npairs
+    for (int e = threadIdx.x; e < NA * CB; e += 256) {
+        const int ta = e / CB, c = e % CB;
+        const int64_t p = p0 + c;
+        xs[ta * CB + c] = p < npairs ? zr[(int64_t)ta * npairs + p] : make_float2(0.f, 0.f);
+    }
+    __syncthreads();
+    tile_fft<LOGNA>(xs, tws);
+    if constexpr (FILTER) {
+        for (int e = threadIdx.x; e < NA * CB; e += 256) {
+            const int ka = e / CB, c = e % CB;
+            const int64_t g = p0 + c;
+            if (g < npairs) a.spec[(g * NB + kb) * NA + ka] = xs[ka * CB + c];
+        }
+        return;
+    }
+    for (int e = threadIdx.x; e < NA * CB; e += 256) {
+        const int ka = e / CB, c = e % CB;
+        const int64_t p = p0 + c;
+        const int64_t g = (p < npairs ? 2 * p : 0) / a.s.P;  // both channels of a pair are in one head
+        xs[ka * CB + c] = conj2(cmul(xs[ka * CB + c], a.spec[(g * NB + kb) * NA + ka]));
+    }
+    __syncthreads();
+    tile_fft<LOGNA>(xs, tws);
+    for (int e = threadIdx.x; e < NA * CB; e += 256) {
+        const int ta = e / CB, c = e % CB;
+        const int64_t p = p0 + c;
+        if (p < npairs) zr[(int64_t)ta * npairs + p] = cmul(twiddle(a.tw, ta * kb, (int)(N / 2)), xs[ta * CB + c]);
+    }
+}
+
+// Pass 3.  Workgroup = (ta, block of kLongCB pairs, batch row): the second
+// half of the inverse, gate and store the steps t = ta + NA tb < L.
+template <int ACT, int LOGNA, int LOGNB>
+__global__ __launch_bounds__(256) void fftl_pass3_kernel(FftArgs a, int64_t npairs) {
+    using A = Act<ACT>;
+    using T = typename A::T;
+    constexpr int NA = 1 << LOGNA, NB = 1 << LOGNB, CB = kLongCB;
+    constexpr int64_t N = (int64_t)NA * NB;
+    __shared__ float2 xs[NB * CB];
+    __shared__ float2 tws[NB / 2];
+    const int ta = blockIdx.x;
+    const int64_t p0 = (int64_t)blockIdx.y * CB, b = blockIdx.z;
+    load_subtable<NB>(tws, a.tw, NA);
+    const float2 *zb = a.z + b * N * npairs;
+    for (int e = threadIdx.x; e < NB * CB; e += 256) {
+        const int kb = e / CB, c = e % CB;
+        const int64_t p = p0 + c;
+        xs[kb * CB + c] = p < npairs ? zb[((int64_t)kb * NA + ta) * npairs + p] : make_float2(0.f, 0.f);
+    }
+    __syncthreads();
+    tile_fft<LOGNB>(xs, tws);
+    const float inv_n = 1.0f / (float)N;
+    const T *qb = static_cast<const T *>(a.q) + b * a.L * a.ld_in;
+    T *yb = static_cast<T *>(a.y) + b * a.L * a.ld_y;
+    for (int e = threadIdx.x; e < NB * 2 * CB; e += 256) {
+        const int tb = e / (2 * CB), c = e % (2 * CB);
+        const int64_t t = ta + (int64_t)NA * tb, ch = 2 * p0 + c;
+        if (t >= a.L || ch >= a.s.D) continue;
+        const float2 r = xs[tb * CB + c / 2];
+        const float val = ((c & 1) ? -r.y : r.x) * inv_n;  // the conjugate: imaginary part negated
+        A::st(yb + t * a.ld_y + ch, A::ld(qb + t * a.ld_in + ch) * val);
+    }
+}
+
+template <int LOGNA, int LOGNB>
+hipError_t launch_long(const FftArgs &a, hipStream_t stream) {
+    constexpr int NA = 1 << LOGNA, NB = 1 << LOGNB, CB = kLongCB;
+    const dim3 block(256);
+    // filter spectra: one "batch row" whose columns are the heads
+    const int64_t H = a.s.H, np = a.s.D / 2;
+    const dim3 gf1(NA, (unsigned)((H + CB - 1) / CB), 1), gf2(NB, (unsigned)((H + CB - 1) / CB), 1);
+    fftl_pass1_kernel<kF32, true, LOGNA, LOGNB><<<gf1, block, 0, stream>>>(a, H);
+    fftl_pass2_kernel<true, LOGNA, LOGNB><<<gf2, block, 0, stream>>>(a, H);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const dim3 g1(NA, (unsigned)((np + CB - 1) / CB), (unsigned)a.s.B), g2(NB, g1.y, g1.z);
+    if (a.s.act == kBF16) {
+        fftl_pass1_kernel<kBF16, false, LOGNA, LOGNB><<<g1, block, 0, stream>>>(a, np);
+        fftl_pass2_kernel<false, LOGNA, LOGNB><<<g2, block, 0, stream>>>(a, np);
+        fftl_pass3_kernel<kBF16, LOGNA, LOGNB><<<g1, block, 0, stream>>>(a, np);
+    } else {
+        fftl_pass1_kernel<kF32, false, LOGNA, LOGNB><<<g1, block, 0, stream>>>(a, np);
+        fftl_pass2_kernel<false, LOGNA, LOGNB><<<g2, block, 0, stream>>>(a, np);
+        fftl_pass3_kernel<kF32, LOGNA, LOGNB><<<g1, block, 0, stream>>>(a, np);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 int fft_log_n(int64_t L) {
@@ -285,6 +507,11 @@ hipError_t launch_fft_prefill(const FftArgs &a, hipStream_t stream) {
         case 11: return launch_logn<11>(a, stream);
         case 12: return launch_logn<12>(a, stream);
         case 13: return launch_logn<13>(a, stream);
+        case 14: return launch_long<7, 7>(a, stream);
+        case 15: return launch_long<8, 7>(a, stream);
+        case 16: return launch_long<8, 8>(a, stream);
+        case 17: return launch_long<9, 8>(a, stream);
+        case 18: return launch_long<9, 9>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }

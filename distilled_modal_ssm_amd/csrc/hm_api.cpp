@@ -328,22 +328,35 @@ hm_status hyena_fir_decode_step(const hm_desc *desc, const float *h, int64_t h_l
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// FFT-prefill workspace: taps [H][L] fp32 | twiddles [N/2] | spectra [H][N] (complex fp32).
-static size_t fft_workspace_bytes(const hm_desc *desc, int64_t L, size_t *off_tw, size_t *off_spec) {
+// FFT-prefill workspace: taps [H][L] fp32 | twiddles [N/2] | spectra [H][N] (complex fp32)
+// | past N = 8192, the multi-pass work buffer [B][N][D/2] (complex fp32).
+static size_t fft_workspace_bytes(const hm_desc *desc, int64_t L, size_t *off_tw, size_t *off_spec,
+                                  size_t *off_z) {
     const int logn = hm::fft_log_n(L);
     const size_t N = size_t(1) << logn;
     *off_tw = align_up((size_t)desc->heads * L * sizeof(float));
     *off_spec = align_up(*off_tw + N / 2 * 8);
-    return *off_spec + (size_t)desc->heads * N * 8;
+    *off_z = align_up(*off_spec + (size_t)desc->heads * N * 8);
+    if (logn <= hm::kFftMaxLogN) return *off_z;
+    return *off_z + (size_t)desc->batch * N * (size_t)(desc->channels / 2) * 8;
+}
+
+static constexpr int64_t kFftMaxL = int64_t(1) << (hm::kFftMaxLogNLong - 1);
+
+// the multi-pass work buffer (B x N x D/2 complex) must stay addressable
+static bool fft_long_fits(const hm_desc *desc, int64_t L) {
+    const int logn = hm::fft_log_n(L);
+    if (logn <= hm::kFftMaxLogN) return true;
+    return desc->batch * (desc->channels / 2) <= kMaxElems / (int64_t(1) << logn);
 }
 
 hm_status hyena_fft_prefill_workspace(const hm_desc *desc, int64_t L, size_t *bytes) {
     hm_status st = check_desc(desc);
     if (st != HM_OK) return st;
     if (!bytes || L < 0) return HM_ERR_INVALID_ARG;
-    if (L > (int64_t(1) << (hm::kFftMaxLogN - 1))) return HM_ERR_UNSUPPORTED;
-    size_t a, b;
-    *bytes = L == 0 ? 0 : fft_workspace_bytes(desc, L, &a, &b);
+    if (L > kFftMaxL || (L > 0 && !fft_long_fits(desc, L))) return HM_ERR_UNSUPPORTED;
+    size_t a, b, c;
+    *bytes = L == 0 ? 0 : fft_workspace_bytes(desc, L, &a, &b, &c);
     return HM_OK;
 }
 
@@ -352,8 +365,9 @@ hm_status hyena_fft_prefill(const hm_desc *desc, int64_t L, const void *q, const
     hm_status st = check_desc(desc);
     if (st != HM_OK) return st;
     if (L < 0) return HM_ERR_INVALID_ARG;
-    if (L > (int64_t(1) << (hm::kFftMaxLogN - 1))) return HM_ERR_UNSUPPORTED;
+    if (L > kFftMaxL) return HM_ERR_UNSUPPORTED;
     if (desc->batch == 0 || L == 0) return HM_OK;
+    if (!fft_long_fits(desc, L)) return HM_ERR_UNSUPPORTED;
     if ((desc->channels / desc->heads) % 2 != 0) return HM_ERR_UNSUPPORTED;  // channel pairs within a head
     if (desc->batch > 65535 || desc->channels / 2 > INT32_MAX) return HM_ERR_UNSUPPORTED;
     if ((st = check_act(desc, q)) != HM_OK || (st = check_act(desc, k)) != HM_OK ||
@@ -361,8 +375,8 @@ hm_status hyena_fft_prefill(const hm_desc *desc, int64_t L, const void *q, const
         return st;
     if (ld_in < desc->channels || ld_y < desc->channels) return HM_ERR_INVALID_ARG;
     if (desc->batch * L > kMaxElems / ld_in || desc->batch * L > kMaxElems / ld_y) return HM_ERR_INVALID_ARG;
-    size_t off_tw, off_spec;
-    const size_t need = fft_workspace_bytes(desc, L, &off_tw, &off_spec);
+    size_t off_tw, off_spec, off_z;
+    const size_t need = fft_workspace_bytes(desc, L, &off_tw, &off_spec, &off_z);
     if (!workspace || ws_bytes < need) return HM_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return HM_ERR_UNSUPPORTED;
     unsigned char *ws = static_cast<unsigned char *>(workspace);
@@ -380,6 +394,7 @@ hm_status hyena_fft_prefill(const hm_desc *desc, int64_t L, const void *q, const
     a.h = reinterpret_cast<float *>(ws);
     a.tw = reinterpret_cast<float2 *>(ws + off_tw);
     a.spec = reinterpret_cast<float2 *>(ws + off_spec);
+    a.z = a.logn > hm::kFftMaxLogN ? reinterpret_cast<float2 *>(ws + off_z) : nullptr;
     hm::FilterArgs f;
     f.s = a.s;
     f.L = L;

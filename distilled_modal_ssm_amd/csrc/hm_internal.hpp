@@ -234,8 +234,10 @@ struct FftArgs {
     float *h;           // [H][L] taps (workspace)
     float2 *tw;         // [N/2] twiddles (workspace)
     float2 *spec;       // [H][N] filter spectra (workspace)
+    float2 *z;          // [B][N][D/2] transform of the channel pairs, multi-pass path only (workspace)
 };
-constexpr int kFftMaxLogN = 13;  // N <= 8192: prompts up to 4096 steps
+constexpr int kFftMaxLogN = 13;      // N <= 8192: one transform in one workgroup's LDS (prompts up to 4096)
+constexpr int kFftMaxLogNLong = 18;  // N <= 262144 in three passes over HBM (prompts up to 131072)
 int fft_log_n(int64_t L);
 int fft_pairs_per_group(int64_t P, int logn);
 size_t fft_lds_bytes(int logn, int np);

@@ -310,9 +310,13 @@ hm_status hyena_fir_cache_fill(const hm_desc *desc, int64_t L, const void *k, co
  * with the filter taps materialised in float32 and the convolution computed
  * as IFFT(FFT(u) FFT(h)) over N = the power of two >= 2L, float32 throughout.
  * Same activation layouts as hyena_modal_prefill; no modal state in or out.
- * Requirements: 1 <= L <= 4096 (else HM_ERR_UNSUPPORTED; L = 0 or B = 0 does
- * nothing), D/H even.  Workspace (taps, twiddles, filter spectra):
- * hyena_fft_prefill_workspace bytes, 256-byte aligned, scratch.
+ * Up to N = 8192 (L <= 4096) each transform runs inside one workgroup's LDS;
+ * beyond that, in three passes over HBM through a work buffer of B x N x D/2
+ * complex float32 in the workspace (4.3 GB per batch row of D = 4096 at
+ * L = 65536).
+ * Requirements: 1 <= L <= 131072 (else HM_ERR_UNSUPPORTED; L = 0 or B = 0
+ * does nothing), D/H even.  Workspace (taps, twiddles, filter spectra, the
+ * work buffer): hyena_fft_prefill_workspace bytes, 256-byte aligned, scratch.
  */
 hm_status hyena_fft_prefill_workspace(const hm_desc *desc, int64_t L, size_t *bytes);
 

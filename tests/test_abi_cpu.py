@@ -328,15 +328,22 @@ def test_fft_prefill_validation(lib):
     # taps [4][2048] fp32, twiddles [2048] complex, spectra [4][4096] complex
     assert n == 4 * 2048 * 4 + 2048 * 8 + 4 * 4096 * 8
     assert hb.hyena_fft_prefill_workspace(d, 0) == 0
+    # past N = 8192 the three-pass transform adds its work buffer [B][N][D/2] complex
+    al = lambda x: (x + 255) // 256 * 256
+    n_long = hb.hyena_fft_prefill_workspace(d, 4097)
+    off_z = al(al(4 * 4097 * 4) + 8192 * 8) + 4 * 16384 * 8
+    assert n_long == al(off_z) + 2 * 16384 * 32 * 8
+    assert hb.hyena_fft_prefill_workspace(d, 131072) > 2 * 262144 * 32 * 8
     with pytest.raises(hb.HMError) as e:
-        hb.hyena_fft_prefill_workspace(d, 4097)
+        hb.hyena_fft_prefill_workspace(d, 131073)
     assert e.value.status == hb.HM_ERR_UNSUPPORTED
 
     def call(L=2048, ws=FAKE, nbytes=n, desc=d, ld=64):
         st = lib.hyena_fft_prefill(ctypes.byref(desc), L, FAKE, FAKE, FAKE, ld, FAKE, ld, ws, nbytes, None)
         return st
 
-    assert call(L=4097) == hb.HM_ERR_UNSUPPORTED
+    assert call(L=131073) == hb.HM_ERR_UNSUPPORTED
+    assert call(L=4097) == hb.HM_ERR_WORKSPACE  # the 2048-step workspace lacks the work buffer
     assert call(L=-1) == hb.HM_ERR_INVALID_ARG
     assert call(ws=None) == hb.HM_ERR_WORKSPACE
     assert call(nbytes=n - 8) == hb.HM_ERR_WORKSPACE

@@ -29,8 +29,12 @@ def _params(rng, H, d, r_lo, r_hi):
 
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
-@pytest.mark.parametrize("B,D,H,d,L", [(1, 2, 1, 1, 1), (2, 8, 2, 3, 3), (3, 64, 4, 8, 257), (1, 32, 2, 16, 2048),
-                                       (2, 16, 1, 32, 4096)])
+@pytest.mark.parametrize("B,D,H,d,L", [
+    (1, 2, 1, 1, 1), (2, 8, 2, 3, 3), (3, 64, 4, 8, 257), (1, 32, 2, 16, 2048), (2, 16, 1, 32, 4096),
+    # three passes over HBM: every (NA, NB) split from N = 16384 to 262144; pair
+    # blocks ragged (24 and 17 pairs per row) and straddling heads
+    (2, 64, 4, 8, 4097), (1, 48, 3, 5, 9000), (1, 32, 2, 16, 20000), (1, 34, 1, 4, 40000),
+    (1, 16, 2, 8, 131072)])
 def test_fft_prefill_shapes(act, B, D, H, d, L):
     torch = require_gpu()
     rng = np.random.default_rng(B * 1000 + L + d)
@@ -46,9 +50,10 @@ def test_fft_prefill_shapes(act, B, D, H, d, L):
     assert err <= TOL[act]
 
 
-@pytest.mark.parametrize("ci", [2, 3])
+@pytest.mark.parametrize("ci", [2, 3, 4])
 def test_fft_prefill_workload_sampled(ci):
-    """Full-size width-2048 and batch-256 prompts; sampled channels and rows."""
+    """Full-size width-2048, batch-256 and 64k prompts (the last through the
+    three-pass transforms); sampled channels and rows."""
     torch = require_gpu()
     cfg = get_config(ci)
     params = modal_params(cfg)
@@ -57,7 +62,7 @@ def test_fft_prefill_workload_sampled(ci):
     log(f"fft prefill workload {ci}")
     y = op.fft_prefill(*(to_dev(inp[n], cfg.act) for n in "qkv"))
     torch.cuda.synchronize()
-    chans = np.array([0, 1, 127, 128, 777, 2046, 2047])
+    chans = np.unique([0, 1, 127, 128, 777, 2046, 2047, cfg.D - 1])
     rows = np.arange(cfg.B) if cfg.B <= 16 else np.array([0, 17, 200, 255])
     sub = {n: np.ascontiguousarray(inp[n][rows]) for n in "qkv"}
     y_or, _ = oracle.modal_scan(params, sub["q"], sub["k"], sub["v"], channels=chans)
