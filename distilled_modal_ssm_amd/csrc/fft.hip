@@ -294,7 +294,66 @@ __device__ __forceinline__ void load_subtable(float2 *tws, const float2 *tw, int
     for (int i = threadIdx.x; i < NS / 2; i += blockDim.x) tws[i] = tw[(int64_t)i * stride];
 }
 
-// Pass 1.  Workgroup = (ta, block of kLongCB pairs, batch row).  FILTER: the
+// Global <-> tile moves.  Every item of a workgroup's load is issued before
+// the first LDS store, so a thread has all its loads in flight at once (a loop
+// that stores each value as it arrives waits out one memory round trip per
+// item).  Column pairs move as 16-byte pieces when the row length is even.
+
+// Load columns p0 .. p0 + kLongCB - 1 of NR rows (row r at base + r rstride,
+// in complex elements) into the tile; columns >= npairs read as 0.
+template <int NR>
+__device__ __forceinline__ void tile_load(float2 *xs, const float2 *base, int64_t rstride, int64_t p0,
+                                          int64_t npairs) {
+    constexpr int CB = kLongCB, IT = NR * CB / 512;
+    static_assert(NR * CB % 512 == 0, "whole column pairs per thread");
+    const int tid = threadIdx.x;
+    float4 t[IT];
+    if ((npairs & 1) == 0) {  // p0 is even: a pair of columns is 16 aligned bytes, both in range or out
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = tid + 256 * i, r = e / (CB / 2), c = 2 * (e % (CB / 2));
+            t[i] = p0 + c < npairs ? *reinterpret_cast<const float4 *>(base + r * rstride + p0 + c)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = tid + 256 * i, r = e / (CB / 2), c = 2 * (e % (CB / 2));
+            const float2 lo = p0 + c < npairs ? base[r * rstride + p0 + c] : make_float2(0.f, 0.f);
+            const float2 hi = p0 + c + 1 < npairs ? base[r * rstride + p0 + c + 1] : make_float2(0.f, 0.f);
+            t[i] = make_float4(lo.x, lo.y, hi.x, hi.y);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int e = tid + 256 * i, r = e / (CB / 2), c = 2 * (e % (CB / 2));
+        *reinterpret_cast<float4 *>(&xs[r * CB + c]) = t[i];
+    }
+}
+
+// Store tile row r times W_N^(m r) (m = ta or kb, the fixed index of the
+// workgroup) to row r of the global block (row r at base + r rstride).
+template <int NR>
+__device__ __forceinline__ void tile_store_twiddled(const float2 *xs, float2 *base, int64_t rstride, int64_t p0,
+                                                    int64_t npairs, const float2 *tw, int m, int half) {
+    constexpr int CB = kLongCB, IT = NR * CB / 512;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int e = tid + 256 * i, r = e / (CB / 2), c = 2 * (e % (CB / 2));
+        const float2 w = twiddle(tw, m * r, half);
+        const float2 lo = cmul(w, xs[r * CB + c]), hi = cmul(w, xs[r * CB + c + 1]);
+        if ((npairs & 1) == 0) {
+            if (p0 + c < npairs)
+                *reinterpret_cast<float4 *>(base + r * rstride + p0 + c) = make_float4(lo.x, lo.y, hi.x, hi.y);
+        } else {
+            if (p0 + c < npairs) base[r * rstride + p0 + c] = lo;
+            if (p0 + c + 1 < npairs) base[r * rstride + p0 + c + 1] = hi;
+        }
+    }
+}
+
+// Pass 1.  Workgroup = (block of kLongCB pairs, ta, batch row).  FILTER: the
 // columns are heads, x = their taps (imaginary part 0); else pair p is
 // channels 2p (real part) and 2p + 1 (imaginary part) of u = k v.
 template <int ACT, bool FILTER, int LOGNA, int LOGNB>
@@ -303,61 +362,64 @@ __global__ __launch_bounds__(256) void fftl_pass1_kernel(FftArgs a, int64_t npai
     using T = typename A::T;
     constexpr int NA = 1 << LOGNA, NB = 1 << LOGNB, CB = kLongCB;
     constexpr int64_t N = (int64_t)NA * NB;
-    __shared__ float2 xs[NB * CB];
+    __shared__ __attribute__((aligned(16))) float2 xs[NB * CB];
     __shared__ float2 tws[NB / 2];
-    const int ta = blockIdx.x;
-    const int64_t p0 = (int64_t)blockIdx.y * CB, b = blockIdx.z;
+    const int ta = blockIdx.y;
+    const int64_t p0 = (int64_t)blockIdx.x * CB, b = blockIdx.z;
     load_subtable<NB>(tws, a.tw, NA);
     if constexpr (FILTER) {
-        for (int e = threadIdx.x; e < NB * CB; e += 256) {
-            const int tb = e / CB, c = e % CB;
+        constexpr int IT = NB * CB / 256;
+        float hv[IT];
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = threadIdx.x + 256 * i, tb = e / CB, c = e % CB;
             const int64_t t = ta + (int64_t)NA * tb, g = p0 + c;
-            xs[tb * CB + c] = make_float2((t < a.L && g < npairs) ? a.h[g * a.L + t] : 0.f, 0.f);
+            hv[i] = (t < a.L && g < npairs) ? a.h[g * a.L + t] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            xs[(e / CB) * CB + e % CB] = make_float2(hv[i], 0.f);
         }
     } else {
+        constexpr int IT = NB * 2 * CB / 256;  // one channel of one row per item
         const T *kb = static_cast<const T *>(a.k) + b * a.L * a.ld_in;
         const T *vb = static_cast<const T *>(a.v) + b * a.L * a.ld_in;
-        float *xf = reinterpret_cast<float *>(xs);  // pair c / 2, real (c even) or imaginary part
-        for (int e = threadIdx.x; e < NB * 2 * CB; e += 256) {
-            const int tb = e / (2 * CB), c = e % (2 * CB);
+        float kv[IT], vv[IT];
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = threadIdx.x + 256 * i, tb = e / (2 * CB), c = e % (2 * CB);
             const int64_t t = ta + (int64_t)NA * tb, ch = 2 * p0 + c;
-            float u = 0.f;
-            if (t < a.L && ch < a.s.D) {
-                const int64_t o = t * a.ld_in + ch;
-                u = A::ld(kb + o) * A::ld(vb + o);
-            }
-            xf[tb * 2 * CB + c] = u;
+            const bool in = t < a.L && ch < a.s.D;
+            const int64_t o = in ? t * a.ld_in + ch : 0;
+            kv[i] = in ? A::ld(kb + o) : 0.f;
+            vv[i] = in ? A::ld(vb + o) : 0.f;
         }
+        float *xf = reinterpret_cast<float *>(xs);  // pair c / 2, real (c even) or imaginary part
+#pragma unroll
+        for (int i = 0; i < IT; ++i) xf[threadIdx.x + 256 * i] = kv[i] * vv[i];
     }
     __syncthreads();
     tile_fft<LOGNB>(xs, tws);
-    float2 *zb = a.z + b * N * npairs;
-    for (int e = threadIdx.x; e < NB * CB; e += 256) {
-        const int kb = e / CB, c = e % CB;
-        const int64_t p = p0 + c;
-        if (p < npairs)
-            zb[((int64_t)kb * NA + ta) * npairs + p] = cmul(twiddle(a.tw, ta * kb, (int)(N / 2)), xs[kb * CB + c]);
-    }
+    // times W_N^(ta kb), to rows kb NA + ta of z
+    tile_store_twiddled<NB>(xs, a.z + b * N * npairs + (int64_t)ta * npairs, (int64_t)NA * npairs, p0, npairs,
+                            a.tw, ta, (int)(N / 2));
 }
 
-// Pass 2.  Workgroup = (kb, block of kLongCB pairs, batch row).  FILTER: store
+// Pass 2.  Workgroup = (block of kLongCB pairs, kb, batch row).  FILTER: store
 // the spectra; else the spectrum product and the first half of the inverse,
 // in place.
 template <bool FILTER, int LOGNA, int LOGNB>
 __global__ __launch_bounds__(256) void fftl_pass2_kernel(FftArgs a, int64_t npairs) {
     constexpr int NA = 1 << LOGNA, NB = 1 << LOGNB, CB = kLongCB;
     constexpr int64_t N = (int64_t)NA * NB;
-    __shared__ float2 xs[NA * CB];
+    __shared__ __attribute__((aligned(16))) float2 xs[NA * CB];
     __shared__ float2 tws[NA / 2];
-    const int kb = blockIdx.x;
-    const int64_t p0 = (int64_t)blockIdx.y * CB, b = blockIdx.z;
+    const int kb = blockIdx.y;
+    const int64_t p0 = (int64_t)blockIdx.x * CB, b = blockIdx.z;
     load_subtable<NA>(tws, a.tw, NB);
     float2 *zr = a.z + (b * N + (int64_t)kb * NA) * npairs;  // row ta at zr + ta npairs
-    for (int e = threadIdx.x; e < NA * CB; e += 256) {
-        const int ta = e / CB, c = e % CB;
-        const int64_t p = p0 + c;
-        xs[ta * CB + c] = p < npairs ? zr[(int64_t)ta * npairs + p] : make_float2(0.f, 0.f);
-    }
+    tile_load<NA>(xs, zr, npairs, p0, npairs);
     __syncthreads();
     tile_fft<LOGNA>(xs, tws);
     if constexpr (FILTER) {
@@ -367,23 +429,28 @@ __global__ __launch_bounds__(256) void fftl_pass2_kernel(FftArgs a, int64_t npai
             if (g < npairs) a.spec[(g * NB + kb) * NA + ka] = xs[ka * CB + c];
         }
         return;
-    }
-    for (int e = threadIdx.x; e < NA * CB; e += 256) {
-        const int ka = e / CB, c = e % CB;
-        const int64_t p = p0 + c;
-        const int64_t g = (p < npairs ? 2 * p : 0) / a.s.P;  // both channels of a pair are in one head
-        xs[ka * CB + c] = conj2(cmul(xs[ka * CB + c], a.spec[(g * NB + kb) * NA + ka]));
-    }
-    __syncthreads();
-    tile_fft<LOGNA>(xs, tws);
-    for (int e = threadIdx.x; e < NA * CB; e += 256) {
-        const int ta = e / CB, c = e % CB;
-        const int64_t p = p0 + c;
-        if (p < npairs) zr[(int64_t)ta * npairs + p] = cmul(twiddle(a.tw, ta * kb, (int)(N / 2)), xs[ta * CB + c]);
+    } else {
+        constexpr int IT = NA * CB / 256;
+        float2 hs[IT];
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = threadIdx.x + 256 * i, ka = e / CB, c = e % CB;
+            const int64_t p = p0 + c;
+            const int64_t g = (p < npairs ? 2 * p : 0) / a.s.P;  // both channels of a pair are in one head
+            hs[i] = a.spec[(g * NB + kb) * NA + ka];
+        }
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+            const int e = threadIdx.x + 256 * i;
+            xs[e] = conj2(cmul(xs[e], hs[i]));
+        }
+        __syncthreads();
+        tile_fft<LOGNA>(xs, tws);
+        tile_store_twiddled<NA>(xs, zr, npairs, p0, npairs, a.tw, kb, (int)(N / 2));
     }
 }
 
-// Pass 3.  Workgroup = (ta, block of kLongCB pairs, batch row): the second
+// Pass 3.  Workgroup = (block of kLongCB pairs, ta, batch row): the second
 // half of the inverse, gate and store the steps t = ta + NA tb < L.
 template <int ACT, int LOGNA, int LOGNB>
 __global__ __launch_bounds__(256) void fftl_pass3_kernel(FftArgs a, int64_t npairs) {
@@ -391,29 +458,33 @@ __global__ __launch_bounds__(256) void fftl_pass3_kernel(FftArgs a, int64_t npai
     using T = typename A::T;
     constexpr int NA = 1 << LOGNA, NB = 1 << LOGNB, CB = kLongCB;
     constexpr int64_t N = (int64_t)NA * NB;
-    __shared__ float2 xs[NB * CB];
+    __shared__ __attribute__((aligned(16))) float2 xs[NB * CB];
     __shared__ float2 tws[NB / 2];
-    const int ta = blockIdx.x;
-    const int64_t p0 = (int64_t)blockIdx.y * CB, b = blockIdx.z;
+    const int ta = blockIdx.y;
+    const int64_t p0 = (int64_t)blockIdx.x * CB, b = blockIdx.z;
     load_subtable<NB>(tws, a.tw, NA);
-    const float2 *zb = a.z + b * N * npairs;
-    for (int e = threadIdx.x; e < NB * CB; e += 256) {
-        const int kb = e / CB, c = e % CB;
-        const int64_t p = p0 + c;
-        xs[kb * CB + c] = p < npairs ? zb[((int64_t)kb * NA + ta) * npairs + p] : make_float2(0.f, 0.f);
-    }
+    tile_load<NB>(xs, a.z + b * N * npairs + (int64_t)ta * npairs, (int64_t)NA * npairs, p0, npairs);
     __syncthreads();
     tile_fft<LOGNB>(xs, tws);
     const float inv_n = 1.0f / (float)N;
     const T *qb = static_cast<const T *>(a.q) + b * a.L * a.ld_in;
     T *yb = static_cast<T *>(a.y) + b * a.L * a.ld_y;
-    for (int e = threadIdx.x; e < NB * 2 * CB; e += 256) {
-        const int tb = e / (2 * CB), c = e % (2 * CB);
+    constexpr int IT = NB * 2 * CB / 256;  // one channel of one row per item
+    float qv[IT];
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int e = threadIdx.x + 256 * i, tb = e / (2 * CB), c = e % (2 * CB);
+        const int64_t t = ta + (int64_t)NA * tb, ch = 2 * p0 + c;
+        qv[i] = (t < a.L && ch < a.s.D) ? A::ld(qb + t * a.ld_in + ch) : 0.f;
+    }
+    const float *xf = reinterpret_cast<const float *>(xs);
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+        const int e = threadIdx.x + 256 * i, tb = e / (2 * CB), c = e % (2 * CB);
         const int64_t t = ta + (int64_t)NA * tb, ch = 2 * p0 + c;
         if (t >= a.L || ch >= a.s.D) continue;
-        const float2 r = xs[tb * CB + c / 2];
-        const float val = ((c & 1) ? -r.y : r.x) * inv_n;  // the conjugate: imaginary part negated
-        A::st(yb + t * a.ld_y + ch, A::ld(qb + t * a.ld_in + ch) * val);
+        const float r = xf[e];  // pair c / 2: real part (c even) or imaginary part, conjugated
+        A::st(yb + t * a.ld_y + ch, qv[i] * ((c & 1) ? -r : r) * inv_n);
     }
 }
 
@@ -423,12 +494,13 @@ hipError_t launch_long(const FftArgs &a, hipStream_t stream) {
     const dim3 block(256);
     // filter spectra: one "batch row" whose columns are the heads
     const int64_t H = a.s.H, np = a.s.D / 2;
-    const dim3 gf1(NA, (unsigned)((H + CB - 1) / CB), 1), gf2(NB, (unsigned)((H + CB - 1) / CB), 1);
+    // x = pair block (fastest): workgroups that run together read neighbouring pieces of the same rows
+    const dim3 gf1((unsigned)((H + CB - 1) / CB), NA, 1), gf2((unsigned)((H + CB - 1) / CB), NB, 1);
     fftl_pass1_kernel<kF32, true, LOGNA, LOGNB><<<gf1, block, 0, stream>>>(a, H);
     fftl_pass2_kernel<true, LOGNA, LOGNB><<<gf2, block, 0, stream>>>(a, H);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const dim3 g1(NA, (unsigned)((np + CB - 1) / CB), (unsigned)a.s.B), g2(NB, g1.y, g1.z);
+    const dim3 g1((unsigned)((np + CB - 1) / CB), NA, (unsigned)a.s.B), g2(g1.x, NB, g1.z);
     if (a.s.act == kBF16) {
         fftl_pass1_kernel<kBF16, false, LOGNA, LOGNB><<<g1, block, 0, stream>>>(a, np);
         fftl_pass2_kernel<false, LOGNA, LOGNB><<<g2, block, 0, stream>>>(a, np);
