@@ -412,3 +412,80 @@ def test_bitwise_determinism():
     a2 = op.decode_step(q[:, 0], k[:, 0], v[:, 0], s2)
     torch.cuda.synchronize()
     assert torch.equal(a1, a2) and torch.equal(s1, s2)
+
+
+# ------------------------------------------------------------------ limits and degenerate filters
+
+
+@pytest.mark.parametrize("shape", [
+    # (B, D, H, d, L, act): the largest batch the launch grids take, with the
+    # largest mode count (lane scan) and the largest matrix-core mode count
+    (65535, 16, 2, 64, 70, "f32"),
+    (65535, 64, 1, 32, 70, "bf16"),
+])
+def test_maximum_batch_and_modes(shape):
+    torch = require_gpu()
+    B, D, H, d, L, act = shape
+    rng = np.random.default_rng(B + d)
+    params = _rand_params(rng, H, d, 0.5, 0.999)
+    op = _op(params, B, D, act)
+    log(f"maximum batch {shape} plan={op.plan(L)}")
+    dt = np.float32
+    gen = lambda: rng.standard_normal((B, L, D), dtype=dt)
+    q_, k_, v_ = gen(), gen(), gen()
+    if act == "bf16":
+        from workloads import round_to_bf16_bits
+        q_, k_, v_ = (round_to_bf16_bits(a) for a in (q_, k_, v_))
+    y, st = op.prefill(*(to_dev(a, act) for a in (q_, k_, v_)))
+    qd, kd, vd = (_rand_act(rng, (2, B, D), act) for _ in range(3))
+    ys = [op.decode_step(to_dev(qd[s], act), to_dev(kd[s], act), to_dev(vd[s], act), st) for s in range(2)]
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 4097, 33333, B - 1])
+    sub = lambda a: np.ascontiguousarray(a[rows])
+    y_or, st_or = oracle.modal_scan(params, sub(q_), sub(k_), sub(v_))
+    rt = torch.as_tensor(rows, device="cuda")
+    assert rel_err(to_np64(y.index_select(0, rt)), y_or) <= TOL[act]
+    yd_or, st2_or = oracle.modal_scan(params, np.ascontiguousarray(qd[:, rows]), np.ascontiguousarray(kd[:, rows]),
+                                      np.ascontiguousarray(vd[:, rows]), state=st_or, batch_axis=1, time_axis=0)
+    yd = np.stack([to_np64(t.index_select(0, rt)) for t in ys], 1)
+    assert rel_err(yd, yd_or) <= TOL[act]
+    assert rel_err(state_for_channels(st.index_select(0, rt), np.arange(D), D // H), st2_or) <= TOL[act]
+
+
+@pytest.mark.parametrize("algo", ["scan", "mfma"])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_degenerate_poles(algo, act):
+    """Poles at 0 (the filter stops after one tap past D), on the positive and
+    negative real axis, next to the unit circle (|lambda| = 1 - 1e-5) and tiny
+    (1e-3), one kind per head; whole prompt and chunked, then decode steps."""
+    torch = require_gpu()
+    rng = np.random.default_rng(77)
+    B, D, H, d, L = 2, 320, 5, 8, 300
+    r = np.zeros((H, d))
+    th = np.zeros((H, d))
+    r[1], th[1] = rng.uniform(0.5, 0.999, d), 0.0
+    r[2], th[2] = rng.uniform(0.5, 0.999, d), np.pi
+    r[3], th[3] = 1.0 - 1e-5, rng.uniform(0, np.pi, d)
+    r[4], th[4] = 1e-3, rng.uniform(0, np.pi, d)
+    poles = np.stack([r * np.cos(th), r * np.sin(th)], -1).astype(np.float32)
+    res = (rng.standard_normal((H, d, 2)) / np.sqrt(2 * d)).astype(np.float32)
+    params = ModalParams(poles, res, rng.standard_normal(H).astype(np.float32))
+    q_, k_, v_ = (_rand_act(rng, (B, L, D), act) for _ in range(3))
+    op = _op(params, B, D, act)
+    y_or, st_or = oracle.modal_scan(params, q_, k_, v_)
+    for chunk in (0, 64):
+        log(f"degenerate poles algo={algo} act={act} chunk={chunk}")
+        y, st = op.prefill(*(to_dev(a, act) for a in (q_, k_, v_)), chunk=chunk, algo=algo)
+        torch.cuda.synchronize()
+        assert rel_err(to_np64(y), y_or) <= TOL[act]
+        assert rel_err(state_for_channels(st, np.arange(D), D // H), st_or) <= TOL[act]
+    qd, kd, vd = (_rand_act(rng, (3, B, D), act) for _ in range(3))
+    ys = [op.decode_step(to_dev(qd[s], act), to_dev(kd[s], act), to_dev(vd[s], act), st) for s in range(3)]
+    torch.cuda.synchronize()
+    yd_or, _ = oracle.modal_scan(params, qd, kd, vd, state=st_or, batch_axis=1, time_axis=0)
+    assert rel_err(np.stack([to_np64(t) for t in ys], 1), yd_or) <= TOL[act]
+    # the filter of the zero-pole head: D, then Re sum R, then zeros
+    h = to_np64(op.filter(L))
+    assert h[0, 0] == np.float32(params.skip[0])
+    assert abs(h[0, 1] - float(res[0, :, 0].astype(np.float64).sum())) <= 1e-6
+    assert np.all(h[0, 2:] == 0.0)
