@@ -173,6 +173,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="workload index (1-5; 5 = projected stack)")
     ap.add_argument("--decode-mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-1thread", type=int, default=None, metavar="CONFIG",
+                    help=argparse.SUPPRESS)  # child process of the one-thread CPU baseline
     ap.add_argument("--no-fir", action="store_true", help="skip the explicit-filter decode baseline")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -332,13 +334,54 @@ def bench_stack(args, cfg, dev):
     emit(args, res)
 
 
+def cpu_one_thread(ci: int, min_seconds: float = 5.0):
+    """Child process of the CPU baseline (started with OMP_NUM_THREADS=1, no
+    GPU use): the oracle's full step on an evenly spaced channel subset,
+    repeated for ``min_seconds``; prints one JSON line."""
+    import oracle
+    from workloads import decode_inputs, get_config, modal_params, prompt_inputs
+    cfg = get_config(ci)
+    params = modal_params(cfg)
+    inp, dec = prompt_inputs(cfg), decode_inputs(cfg)
+    per_channel = cfg.B * (cfg.L + cfg.S) * cfg.d
+    n_sel = int(min(cfg.D, max(1, 2e8 // per_channel)))
+    chans = np.linspace(0, cfg.D - 1, n_sel).round().astype(np.int64) if n_sel < cfg.D else None
+    reps, t0 = 0, time.perf_counter()
+    while reps < 100 and (reps == 0 or time.perf_counter() - t0 < min_seconds):
+        oracle.filter_taps(params, cfg.L)
+        _, st = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"], channels=chans)
+        oracle.modal_scan(params, dec["q"], dec["k"], dec["v"], state=st, channels=chans,
+                          batch_axis=1, time_axis=0)
+        reps += 1
+    dt = time.perf_counter() - t0
+    print(json.dumps({"value": cfg.B * (cfg.L + cfg.S) * (n_sel / cfg.D) * reps / dt, "unit": "tokens/s",
+                      "cores": oracle.threads(),
+                      "sample": f"full step for {n_sel} of {cfg.D} channels x {cfg.B} rows, {reps} repetition(s), "
+                                f"{dt:.1f} s; tokens scaled by the channel fraction"}))
+
+
+def cpu_baseline_one_thread(cfg):
+    """The same oracle step on one thread, in a child process (the thread count
+    of the oracle's OpenMP runtime is fixed when it loads)."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-1thread", str(cfg.index)],
+                           env=env, capture_output=True, text=True, timeout=300)
+        return json.loads(r.stdout.strip().splitlines()[-1])
+    except Exception as e:  # reported, never fatal to the benchmark line
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
 def main():
     args = parse()
     if args.traffic_from:
         return write_traffic(args)
+    if args.cpu_1thread is not None:
+        return cpu_one_thread(args.cpu_1thread)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the path shards by batch rows and heads with no communication; see the design notes)",
+              "(the path would shard by batch rows and heads, with no communication)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -526,6 +569,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (float64 oracle)")
         res["cpu_baseline"] = cpu_baseline(cfg, params, inp, dec)
+        res["cpu_baseline"]["one_thread"] = cpu_baseline_one_thread(cfg)
     emit(args, res)
 
 
