@@ -489,3 +489,36 @@ def test_degenerate_poles(algo, act):
     assert h[0, 0] == np.float32(params.skip[0])
     assert abs(h[0, 1] - float(res[0, :, 0].astype(np.float64).sum())) <= 1e-6
     assert np.all(h[0, 2:] == 0.0)
+
+
+def test_state_checkpoint_roundtrip(tmp_path):
+    """The modal state is the generation checkpoint: prefill L steps, save the
+    state to a host file, restore it into fresh device memory, decode S steps;
+    the outputs and final state match one prefill over all L + S steps."""
+    torch = require_gpu()
+    cfg = get_config(2)
+    params = modal_params(cfg)
+    B, L, S = 4, 300, 20
+    rng = np.random.default_rng(91)
+    q_, k_, v_ = (_rand_act(rng, (B, L + S, cfg.D), "bf16") for _ in range(3))
+    op = _op(params, B, cfg.D, "bf16")
+    q, k, v = (to_dev(a, "bf16") for a in (q_, k_, v_))
+    log("checkpoint: prefill, save")
+    _, st = op.prefill(*(t[:, :L].contiguous() for t in (q, k, v)))
+    path = tmp_path / "state.npy"
+    np.save(path, st.cpu().numpy())
+    del st
+    torch.cuda.synchronize()
+    st2 = torch.from_numpy(np.load(path)).cuda()
+    log("checkpoint: restore, decode")
+    ys = [op.decode_step(q[:, L + s].contiguous(), k[:, L + s].contiguous(), v[:, L + s].contiguous(), st2)
+          for s in range(S)]
+    y_all, st_all = op.prefill(q, k, v)
+    torch.cuda.synchronize()
+    yd = np.stack([to_np64(t) for t in ys], 1)
+    y_or, st_or = oracle.modal_scan(params, q_, k_, v_)
+    assert rel_err(yd, y_or[:, L:]) <= TOL["bf16"]
+    assert rel_err(yd, to_np64(y_all[:, L:])) <= TOL["bf16"]
+    st_or_gpu = state_for_channels(st2, np.arange(cfg.D), cfg.P)
+    assert rel_err(st_or_gpu, st_or) <= TOL["f32"]
+    assert rel_err(state_for_channels(st_all, np.arange(cfg.D), cfg.P), st_or) <= TOL["f32"]
