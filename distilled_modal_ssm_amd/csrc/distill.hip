@@ -15,8 +15,9 @@
 // Kernels, all float64 inside: (1) residual -- one thread per (head, mode,
 // 32-tap run) evaluates R lambda^(t-1) by binary powering and a walk, the
 // workgroup sums the modes per tap in LDS, writes e and a partial sum of e^2;
-// (2) gradient -- one thread per (head, mode, 32-tap run) walks lambda^(t-2)
-// and lambda^(t-1) against e and reduces four sums per workgroup; (3) finish
+// (2) gradient -- per (head, mode, 8192-tap chunk), each thread walks
+// lambda^(t-2) and lambda^(t-1) over every 256th tap against e (coalesced
+// reads) and the workgroup reduces four sums; (3) finish
 // -- sums the partials into float32 loss and gradients.  The Adam step keeps
 // every |lambda| <= r_max < 1 (a stable recurrence).
 #include "hm_internal.hpp"
@@ -80,38 +81,46 @@ __global__ __launch_bounds__(256) void distill_residual_kernel(DistillArgs a) {
     if (threadIdx.x == 0) a.loss_part[g * a.tiles + tile] = red[0];
 }
 
-// Workgroup = (head g, mode n, chunk of 8192 taps); thread = 32-tap run.
+// Workgroup = (head g, mode n, chunk of 8192 taps).  Thread i takes the taps
+// chunk start + i + 256 j (j < 32), so a wave reads 64 consecutive residuals
+// per step; lambda^(t-1) and lambda^(t-2) advance by lambda^256 (binary
+// powering once per thread).
 __global__ __launch_bounds__(256) void distill_grad_kernel(DistillArgs a) {
     __shared__ double red[4][256];
     const int64_t L = a.L, d = a.s.d;
     const int64_t gn = blockIdx.x, chunk = blockIdx.y;
     const int64_t g = gn / d;
-    const int64_t t0 = chunk * kDistillTile + (int64_t)threadIdx.x * kRun;
+    const int64_t tf = chunk * kDistillTile + threadIdx.x;  // this thread's first tap
     double s[4] = {0.0, 0.0, 0.0, 0.0};
-    if (t0 < L) {
+    if (tf < L) {
         const float2 lf = a.s.poles[gn], rf = a.s.residues[gn];
         const double lr = lf.x, li = lf.y, rr = rf.x, ri = rf.y;
-        // p = lambda^(t-1), q = lambda^(t-2) at the run's first tap (t >= 2 for q)
-        double pr, pi, qr = 0.0, qi = 0.0;
-        complex_pow(lr, li, t0 >= 1 ? t0 - 1 : 0, pr, pi);
-        if (t0 >= 2) complex_pow(lr, li, t0 - 2, qr, qi);
-        for (int j = 0; j < kRun; ++j) {
-            const int64_t t = t0 + j;
-            if (t >= L) break;
-            if (t >= 1) {
-                const double e = a.e[g * L + t];
-                s[0] += e * pr;
-                s[1] += e * pi;
-                if (t >= 2) {
-                    const double k = (double)(t - 1);
-                    s[2] += e * k * (rr * qr - ri * qi);
-                    s[3] += e * k * (rr * qi + ri * qr);
-                }
-                qr = pr;
-                qi = pi;
-                const double nr = lr * pr - li * pi;
-                pi = lr * pi + li * pr;
+        const double *e = a.e + g * L;
+        int j0 = 0;
+        if (tf < 2) {  // tap 0 has no modal part; tap 1 has lambda^0 = 1 and no lambda^(t-2) term
+            if (tf == 1) s[0] += e[1];
+            j0 = 1;
+        }
+        const int64_t ts = tf + 256 * j0;
+        if (ts < L) {
+            double wr, wi, pr, pi, qr, qi;
+            complex_pow(lr, li, 256, wr, wi);
+            complex_pow(lr, li, ts - 1, pr, pi);  // lambda^(t-1)
+            complex_pow(lr, li, ts - 2, qr, qi);  // lambda^(t-2), t >= 2
+            for (int j = j0; j < kDistillTile / 256; ++j) {
+                const int64_t t = tf + 256 * (int64_t)j;
+                if (t >= L) break;
+                const double ev = e[t], k = (double)(t - 1);
+                s[0] += ev * pr;
+                s[1] += ev * pi;
+                s[2] += ev * k * (rr * qr - ri * qi);
+                s[3] += ev * k * (rr * qi + ri * qr);
+                double nr = pr * wr - pi * wi;
+                pi = pr * wi + pi * wr;
                 pr = nr;
+                nr = qr * wr - qi * wi;
+                qi = qr * wi + qi * wr;
+                qr = nr;
             }
         }
     }
@@ -127,6 +136,9 @@ __global__ __launch_bounds__(256) void distill_grad_kernel(DistillArgs a) {
     if (threadIdx.x < 4) a.grad_part[(gn * a.chunks + chunk) * 4 + threadIdx.x] = red[threadIdx.x][0];
 }
 
+// Threads sum each (head, mode)'s chunk partials into the gradients; wave w of
+// workgroup b sums head 4 b + w's loss partials (lanes stride over the tiles,
+// then a butterfly across the wave).
 __global__ __launch_bounds__(256) void distill_finish_kernel(DistillArgs a) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t H = a.s.H, d = a.s.d;
@@ -140,11 +152,17 @@ __global__ __launch_bounds__(256) void distill_finish_kernel(DistillArgs a) {
         a.g_poles[2 * i] = (float)(2.0 * s[2]);
         a.g_poles[2 * i + 1] = (float)(-2.0 * s[3]);
     }
-    if (i < H) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t g = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (g < H) {
         double l = 0.0;
-        for (int t = 0; t < a.tiles; ++t) l += a.loss_part[i * a.tiles + t];
-        a.loss[i] = (float)l;
-        a.g_skip[i] = (float)(2.0 * a.e[i * a.L]);
+        for (int t = lane; t < a.tiles; t += kWave) l += a.loss_part[g * a.tiles + t];
+#pragma unroll
+        for (int m = kWave / 2; m > 0; m >>= 1) l += __shfl_xor(l, m);
+        if (lane == 0) {
+            a.loss[g] = (float)l;
+            a.g_skip[g] = (float)(2.0 * a.e[g * a.L]);
+        }
     }
 }
 
@@ -208,8 +226,8 @@ hipError_t launch_distill_grad(const DistillArgs &a, hipStream_t stream) {
     if (err != hipSuccess) return err;
     distill_grad_kernel<<<dim3((unsigned)(a.s.H * d), (unsigned)a.chunks), dim3(256), 0, stream>>>(a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    const int64_t n = a.s.H * d > a.s.H ? a.s.H * d : a.s.H;
-    distill_finish_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(a);
+    const int64_t nb_grad = (a.s.H * d + 255) / 256, nb_loss = (a.s.H + 3) / 4;  // 4 waves per workgroup
+    distill_finish_kernel<<<dim3((unsigned)(nb_grad > nb_loss ? nb_grad : nb_loss)), dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
