@@ -53,19 +53,26 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 }
 
 // Grid: x = lane blocks over the channels of one batch row, y = batch row.
+// The block size BS is a compile-time constant and, when the lane blocks tile
+// the row exactly (FULL), there is no early exit: every argument load is then
+// issued at once at entry, instead of a block-size load, a branch and a second
+// round of loads (measured on MI355X: 3.00 -> 2.75 us per step at B = 16,
+// D = 2048, d = 16; the launch is latency-bound there).
 // A lane owns CPT adjacent channels (CPT = 2 only with SPLIT = 1) and DL of
 // their modes; SPLIT lanes share a channel when the batch is too small to fill
 // the GPU otherwise, and their partial outputs are summed with DPP.
-template <int DL, int SPLIT, int CPT, int ACT, bool UNIFORM>
-__global__ __launch_bounds__(256) void decode_step_fixed(DecodeArgs a) {
+template <int DL, int SPLIT, int CPT, int ACT, bool UNIFORM, int BS, bool FULL>
+__global__ __launch_bounds__(BS) void decode_step_fixed(DecodeArgs a) {
     using A = Act<ACT>;
     using T = typename A::T;
     constexpr int DP = DL * SPLIT;
     const int64_t P = a.s.P, H = a.s.H;
-    const int lane_id = (int)(blockIdx.x * blockDim.x + threadIdx.x);  // within the batch row
+    const int lane_id = (int)(blockIdx.x * BS + threadIdx.x);  // within the batch row
     const int part = lane_id % SPLIT;
     const int c = (lane_id / SPLIT) * CPT;
-    if (c >= a.s.D) return;
+    if constexpr (!FULL) {
+        if (c >= a.s.D) return;
+    }
     const int64_t b = blockIdx.y;
     int g = c / (int)P;
     if (UNIFORM) g = __builtin_amdgcn_readfirstlane(g);
@@ -167,10 +174,16 @@ hipError_t launch_fixed(const DecodeArgs &a, hipStream_t stream) {
     const int bs = (lanes * a.s.B >= 256 * 1024) ? 256 : 64;
     const dim3 grid((unsigned)((lanes + bs - 1) / bs), (unsigned)a.s.B), block(bs);
     const bool uniform = SPLIT == 1 && (a.s.P % (kWave * CPT) == 0);
-    if (uniform)
-        decode_step_fixed<DL, SPLIT, CPT, ACT, (SPLIT == 1)><<<grid, block, 0, stream>>>(a);
-    else
-        decode_step_fixed<DL, SPLIT, CPT, ACT, false><<<grid, block, 0, stream>>>(a);
+    const bool full = lanes % bs == 0;
+    if (bs == 256) {
+        if (uniform && full) decode_step_fixed<DL, SPLIT, CPT, ACT, (SPLIT == 1), 256, true><<<grid, block, 0, stream>>>(a);
+        else if (full) decode_step_fixed<DL, SPLIT, CPT, ACT, false, 256, true><<<grid, block, 0, stream>>>(a);
+        else decode_step_fixed<DL, SPLIT, CPT, ACT, false, 256, false><<<grid, block, 0, stream>>>(a);
+    } else {
+        if (uniform && full) decode_step_fixed<DL, SPLIT, CPT, ACT, (SPLIT == 1), 64, true><<<grid, block, 0, stream>>>(a);
+        else if (full) decode_step_fixed<DL, SPLIT, CPT, ACT, false, 64, true><<<grid, block, 0, stream>>>(a);
+        else decode_step_fixed<DL, SPLIT, CPT, ACT, false, 64, false><<<grid, block, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 
