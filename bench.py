@@ -42,10 +42,10 @@ VALU_F32_PEAK_TFLOPS = 78.6    # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, unp
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "distilled_modal_ssm_amd", "csrc")
 # Sources whose change invalidates a hardware-counter measurement of a kernel:
-# the kernel's own file (its code and launch configuration) and the shared
-# device header.
+# the kernel's own file (its code and launch configuration), the shared
+# device header and, where it adds flags for that file, the build script.
 KERNEL_SOURCES = {
-    "decode_step_fixed": ["decode.hip", "hm_internal.hpp"],
+    "decode_step_fixed": ["decode.hip", "hm_internal.hpp", "../build.py"],
     "chunk_mfma_kernel": ["prefill_mfma.hip", "prefill.hip", "hm_internal.hpp"],
     "chunk_scan_kernel": ["prefill.hip", "hm_internal.hpp"],
 }

@@ -28,9 +28,17 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The decode step is latency-bound at small batch: its
+# first kernel arguments (the pointers and sizes its first loads need) are
+# preloaded into SGPRs at wave launch instead of being fetched from the
+# argument segment (gfx950 kernarg preloading; the code keeps a prologue that
+# loads them for firmware without it).
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=9"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the GPU-only feature flag; drop that one warning
     noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
