@@ -163,46 +163,51 @@ __global__ __launch_bounds__(256) void mfma_tables_kernel(OpShape s, uint4 *frag
 
 // ------------------------------------------------------------------ sub-block kernel
 
-template <int ACT> struct Piece;  // 8 consecutive channels of one row
-template <> struct Piece<kBF16> {
-    uint4 w;
-    __device__ void load(const void *p) { w = *reinterpret_cast<const uint4 *>(p); }
-    __device__ float get(int e) const {
-        const uint32_t v[4] = {w.x, w.y, w.z, w.w};
-        return (e & 1) ? bf16_hi(v[e >> 1]) : bf16_lo(v[e >> 1]);
-    }
+// One thread's 8 channels of one row: channels e = 0..3 at the piece's
+// address, e = 4..7 at SPLIT elements further.  bf16 rows use one 16-byte piece
+// (SPLIT = 4), so consecutive lanes read consecutive 16 bytes.  float32 rows put
+// the two 16-byte halves half a channel tile apart (SPLIT = PT/2), so each load
+// instruction of a lane group still covers whole 128-byte lines.  The loads and
+// stores are non-temporal: every element is read or written exactly once.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32v4 __attribute__((ext_vector_type(4)));
+template <int ACT, int SPLIT> struct Piece;
+template <int SPLIT> struct Piece<kBF16, SPLIT> {
+    static_assert(SPLIT == 4, "bf16 pieces are 8 consecutive channels");
+    u32x4 w;
+    __device__ void load(const void *p) { w = __builtin_nontemporal_load(static_cast<const u32x4 *>(p)); }
+    __device__ float get(int e) const { return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]); }
 };
-template <> struct Piece<kF32> {
-    float4 a, b;
+template <int SPLIT> struct Piece<kF32, SPLIT> {
+    f32v4 a, b;
     __device__ void load(const void *p) {
-        a = reinterpret_cast<const float4 *>(p)[0];
-        b = reinterpret_cast<const float4 *>(p)[1];
+        const float *f = static_cast<const float *>(p);
+        a = __builtin_nontemporal_load(reinterpret_cast<const f32v4 *>(f));
+        b = __builtin_nontemporal_load(reinterpret_cast<const f32v4 *>(f + SPLIT));
     }
-    __device__ float get(int e) const {
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        return v[e];
-    }
+    __device__ float get(int e) const { return (e < 4) ? a[e] : b[e - 4]; }
 };
 // The same 8 channels read one element at a time (rows not 16-byte aligned).
-template <int ACT> struct PieceScalar {
+template <int ACT, int SPLIT> struct PieceScalar {
     float v[8];
     __device__ void load(const void *p) {
         const typename Act<ACT>::T *t = static_cast<const typename Act<ACT>::T *>(p);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = Act<ACT>::ld(t + e);
+        for (int e = 0; e < 8; ++e) v[e] = Act<ACT>::ld(t + (e & 3) + SPLIT * (e >> 2));
     }
     __device__ float get(int e) const { return v[e]; }
 };
 
-__device__ __forceinline__ void store8(uint16_t *p, const float *v) {
-    uint32_t w[4];
+template <int SPLIT> __device__ __forceinline__ void store8(uint16_t *p, const float *v) {
+    static_assert(SPLIT == 4, "bf16 pieces are 8 consecutive channels");
+    u32x4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
-    *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
 }
-__device__ __forceinline__ void store8(float *p, const float *v) {
-    reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-    reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+template <int SPLIT> __device__ __forceinline__ void store8(float *p, const float *v) {
+    __builtin_nontemporal_store(f32v4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32v4 *>(p));
+    __builtin_nontemporal_store(f32v4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32v4 *>(p + SPLIT));
 }
 
 // LDS row of u for one channel: 64 steps in 16-byte units of 8 steps, the unit
@@ -228,7 +233,9 @@ template <int DD, int PT, int ACT, bool SO, bool VEC>
 __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const float2 *carry0) {
     using G = MfmaGeom<DD>;
     using T = typename Act<ACT>::T;
-    using PC = typename std::conditional<VEC, Piece<ACT>, PieceScalar<ACT>>::type;
+    // a thread's channels: CGW * cg + (e & 3) + SPLIT * (e >> 2), e = 0..7
+    constexpr int SPLIT = (ACT == kF32) ? PT / 2 : 4, CGW = (ACT == kF32) ? 4 : 8;
+    using PC = typename std::conditional<VEC, Piece<ACT, SPLIT>, PieceScalar<ACT, SPLIT>>::type;
     constexpr int D2 = G::D2, KC = G::KC, MTS = G::MTS, NFRAG = G::NFRAG;
     constexpr int NTHR = 4 * PT;               // PT / 16 waves
     constexpr int CW = 16, NTW = 1;            // channels and 16-wide tiles per wave
@@ -302,7 +309,7 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
 
     // staging role: RG rows x 8 channels
     const int cg = tid % CG, rg = tid / CG;
-    const int64_t ch0 = (int64_t)g * P + p0 + 8 * cg;  // global channel of the piece
+    const int64_t ch0 = (int64_t)g * P + p0 + CGW * cg;  // global channel of the piece's element 0
     const int64_t t_begin = c * Tc;
     const int nsteps = (int)(((L - t_begin) < Tc) ? (L - t_begin) : Tc);
     const int nsb = (nsteps + kSubBlock - 1) / kSubBlock;
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
             for (int e = 0; e < 8; ++e) {
                 const uint32_t h = pack_bf16x2(uu[0][e], uu[1][e]);
                 const uint32_t lo = pack_bf16x2(uu[0][e] - bf16_lo(h), uu[1][e] - bf16_hi(h));
-                const int o = u_index(8 * cg + e, rg * RG);
+                const int o = u_index(CGW * cg + (e & 3) + SPLIT * (e >> 2), rg * RG);
                 *reinterpret_cast<uint32_t *>(&uhi[o]) = h;
                 *reinterpret_cast<uint32_t *>(&ulo[o]) = lo;
             }
@@ -468,13 +475,13 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
         for (int r = 0; r < (SO ? 0 : RG); ++r) {
             const int row = rg * RG + r;
             if (row < nv) {
-                const float4 y0 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, 8 * cg, LQ)]);
-                const float4 y1 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, 8 * cg + 4, LQ)]);
+                const float4 y0 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, CGW * cg, LQ)]);
+                const float4 y1 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, CGW * cg + SPLIT, LQ)]);
                 const float yy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
                 float v[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) v[e] = cq[r].get(e) * yy[e];
-                store8(reinterpret_cast<T *>(yb + (int64_t)(sb * kSubBlock + row) * a.ld_y), v);
+                store8<SPLIT>(reinterpret_cast<T *>(yb + (int64_t)(sb * kSubBlock + row) * a.ld_y), v);
             }
         }
     }
