@@ -303,20 +303,23 @@ def test_fused_qkv_buffer_and_strided_output(algo):
 
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
-def test_odd_row_stride_scalar_paths(act):
+@pytest.mark.parametrize("B,D,H,L,tile", [(2, 128, 2, 200, 64), (16, 2048, 16, 130, 128)])
+def test_odd_row_stride_scalar_paths(act, B, D, H, L, tile):
     """An odd row stride forces the scalar (unvectorised) load paths: on a
     matrix-core plan cut into chunks, the state-only pass with element loads
-    and the lane scan from its carries."""
+    and the lane scan from its carries, at both channel tiles (a float32
+    thread's two 4-channel halves sit half a tile apart)."""
     torch = require_gpu()
-    rng = np.random.default_rng(6)
-    B, D, H, d, L = 2, 128, 2, 8, 200
+    rng = np.random.default_rng(6 + tile)
+    d = 8
     params = _rand_params(rng, H, d)
     ld = D + 1
     big = [_rand_act(rng, (B, L, ld), act) for _ in range(3)]
     dev = [to_dev(a, act) for a in big]
     op = _op(params, B, D, act)
-    assert op.plan(L, chunk=64)["algo"] == "mfma"
-    log(f"odd stride {act}")
+    plan = op.plan(L, chunk=64)
+    assert plan["algo"] == "mfma" and plan["channel_tile"] == tile
+    log(f"odd stride {act} tile {tile}")
     y, st = op.prefill(*(t[:, :, :D] for t in dev), chunk=64)
     torch.cuda.synchronize()
     y_or, st_or = oracle.modal_scan(params, *(np.ascontiguousarray(a[:, :, :D]) for a in big))
