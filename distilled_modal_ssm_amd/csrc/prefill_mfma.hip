@@ -62,6 +62,8 @@ __device__ __forceinline__ f32x4 mfma3(const uint4 ah, const uint4 al, const uin
 __device__ __forceinline__ uint32_t bf16_bits(float x) { return f32_to_bf16(x); }
 __device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
 
+constexpr int kTabThreads = 512;  // threads of a tables workgroup (one head)
+
 // lambda^e in float64 from the polar form
 __device__ inline void polar_pow(double lr, double li, double e, double &re, double &im) {
     if (e == 0.0) {
@@ -78,25 +80,33 @@ __device__ inline void polar_pow(double lr, double li, double e, double &re, dou
 
 // ------------------------------------------------------------------ tables
 
-// One workgroup per head.  Fragment f of the head, lane l, holds the eight
+// One workgroup of 512 threads per head (every power below takes one pass),
+// with the head's poles and residues staged in LDS.  Fragment f of the head,
+// lane l, holds the eight
 // A-operand values of that lane (row l%16 of the tile, k 8*(l/16)..+7):
 //   f in [0, 8)            T tile (mt = f/2, kk = f%2): T[i][j] = h[i-j], j <= i
 //   f in [8, 8+4KC)        C tile (mt, kc): C[i][2n] = Re(R_n lam_n^i), C[i][2n+1] = -Im(R_n lam_n^i)
 //   f in [8+4KC, NFRAG)    V tile (ms, kk): V[2n][j] = Re lam_n^(63-j), V[2n+1][j] = Im lam_n^(63-j)
 // stored as [head][f][hi, lo][lane] uint4; also lam64[head][D2/2] = lambda^64.
 template <int DD>
-__global__ __launch_bounds__(256) void mfma_tables_kernel(OpShape s, uint4 *frag, float2 *lam64, int64_t T,
-                                                          float2 *lamT) {
+__global__ __launch_bounds__(kTabThreads) void mfma_tables_kernel(OpShape s, uint4 *frag, float2 *lam64,
+                                                                  int64_t T, float2 *lamT) {
     using G = MfmaGeom<DD>;
     constexpr int D2 = G::D2, KC = G::KC, NFRAG = G::NFRAG;
     __shared__ double pr[65 * DD], pi[65 * DD];  // lambda_n^i, i <= 64
     __shared__ double hh[kSubBlock];
+    __shared__ float2 pole[DD], res[DD];
     const int g = blockIdx.x, tid = threadIdx.x;
+    if (tid < DD) {
+        pole[tid] = s.poles[(int64_t)g * DD + tid];
+        res[tid] = s.residues[(int64_t)g * DD + tid];
+    }
+    __syncthreads();
     // lambda^i for i = 4 seg .. 4 seg + 3: the first from the polar form, the
     // rest by float64 complex products (relative error ~1e-16 per product)
-    for (int idx = tid; idx < 17 * DD; idx += 256) {
+    for (int idx = tid; idx < 17 * DD; idx += kTabThreads) {
         const int seg = idx / DD, n = idx % DD;
-        const float2 l = s.poles[(int64_t)g * DD + n];
+        const float2 l = pole[n];
         const double lr = l.x, li = l.y;
         double re, im;
         polar_pow(lr, li, (double)(4 * seg), re, im);
@@ -109,13 +119,13 @@ __global__ __launch_bounds__(256) void mfma_tables_kernel(OpShape s, uint4 *frag
         }
     }
     __syncthreads();
-    for (int m = tid; m < kSubBlock; m += 256) {
+    for (int m = tid; m < kSubBlock; m += kTabThreads) {
         double acc = 0.0;
         if (m == 0) {
             acc = s.skip[g];
         } else {
             for (int n = 0; n < DD; ++n) {
-                const float2 r = s.residues[(int64_t)g * DD + n];
+                const float2 r = res[n];
                 acc += (double)r.x * pr[(m - 1) * DD + n] - (double)r.y * pi[(m - 1) * DD + n];
             }
         }
@@ -125,13 +135,13 @@ __global__ __launch_bounds__(256) void mfma_tables_kernel(OpShape s, uint4 *frag
         lam64[g * (D2 / 2) + tid] =
             tid < DD ? make_float2((float)pr[64 * DD + tid], (float)pi[64 * DD + tid]) : make_float2(0.f, 0.f);
     if (lamT && tid < DD) {  // lambda^T for the carry scan of a chunked prompt
-        const float2 l = s.poles[(int64_t)g * DD + tid];
+        const float2 l = pole[tid];
         double re, im;
         polar_pow(l.x, l.y, (double)T, re, im);
         lamT[(int64_t)g * DD + tid] = make_float2((float)re, (float)im);
     }
     __syncthreads();
-    for (int idx = tid; idx < NFRAG * kWave; idx += 256) {
+    for (int idx = tid; idx < NFRAG * kWave; idx += kTabThreads) {
         const int f = idx / kWave, l = idx % kWave;
         const int r16 = l % 16, k8 = 8 * (l / 16);
         uint32_t hi[8], lo[8];
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(256) void mfma_tables_kernel(OpShape s, uint4 *frag
             } else if (f < 8 + 4 * KC) {
                 const int f2 = f - 8, i = 16 * (f2 / KC) + r16, k = 32 * (f2 % KC) + k8 + e, n = k / 2;
                 if (n < DD) {
-                    const float2 r = s.residues[(int64_t)g * DD + n];
+                    const float2 r = res[n];
                     const double a = pr[i * DD + n], b = pi[i * DD + n];
                     v = (k % 2 == 0) ? ((double)r.x * a - (double)r.y * b) : -((double)r.x * b + (double)r.y * a);
                 }
@@ -565,7 +575,7 @@ hipError_t launch_mfma_tables(const PrefillArgs &a, hipStream_t stream) {
     uint4 *frag = reinterpret_cast<uint4 *>(a.ws + a.plan.off_mfma_tab);
     float2 *lam = reinterpret_cast<float2 *>(a.ws + a.plan.off_mfma_lam);
     float2 *lamT = a.plan.NC > 1 ? reinterpret_cast<float2 *>(a.ws + a.plan.off_lamT) : nullptr;
-    const dim3 grid((unsigned)a.s.H), block(256);
+    const dim3 grid((unsigned)a.s.H), block(kTabThreads);
     switch (a.s.d) {
         case 8: mfma_tables_kernel<8><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT); break;
         case 16: mfma_tables_kernel<16><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT); break;
