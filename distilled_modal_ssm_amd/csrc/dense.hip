@@ -358,8 +358,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 }
 
 // Weight-streaming GEMM for M <= 64 and K = 2048 (K loop fully unrolled).
-// Workgroup = 4 waves on all rows x BN = 16 NTW columns; wave w takes K
-// quarter w (8 chunks of 64).  Both operands are loaded as 128-byte row pieces
+// Workgroup = 4 waves on MR rows (64, or 32 = one half of the rows) x BN =
+// 16 NTW columns; wave w takes K quarter w (8 chunks of 64).  Both operands are loaded as 128-byte row pieces
 // (8 lanes per row, 8 rows per load instruction) -- measured on MI355X,
 // fragment-shaped loads (64 bytes of 16 rows per instruction) stream W 15-40 %
 // slower and double the requests for A, which every workgroup re-reads --
@@ -371,28 +371,37 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // it needs.  The four K quarters are summed through LDS, reusing the A buffers.
 constexpr int kAsLd = 72;  // bf16 per LDS row of the A chunk (64 + 8 pad)
 
-template <int NTW, int SW, bool RMS>
+template <int NTW, int SW, bool RMS, int MR>
 __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
+    constexpr int MT = MR / 16, AL = MR / 8;  // m-tiles; A row-piece loads per chunk
     constexpr int BN = 16 * NTW, NCH = 8;  // K quarter: 8 chunks of 64
     constexpr int WPL = BN / 8;            // W row pieces per lane per chunk (8 rows per load)
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-    __shared__ __attribute__((aligned(16))) uint16_t as[4][2][64 * kAsLd];
+    __shared__ __attribute__((aligned(16))) uint16_t as[4][2][MR * kAsLd];
     __shared__ __attribute__((aligned(16))) uint16_t wsm[4][2][BN * kAsLd];
-    __shared__ float red_ss[RMS ? 4 * 64 : 1];
-    static_assert(4 * 64 * BN * sizeof(float) <= sizeof(as), "the K-part sums reuse the A buffers");
+    __shared__ float red_ss[RMS ? 4 * MR : 1];
+    static_assert(4 * MR * BN * sizeof(float) <= sizeof(as), "the K-part sums reuse the A buffers");
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-    const int64_t n0 = (int64_t)blockIdx.x * BN;
+    // MR = 32: the two row halves of a column tile sit 8 workgroups apart, on one XCD
+    int64_t tile = blockIdx.x, m0 = 0;
+    if constexpr (MR == 32) {
+        const int64_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+        m0 = 32 * (slot % 2);
+        tile = (slot / 2) * 8 + xcd;
+        if (tile * BN >= g.N || m0 >= g.M) return;
+    }
+    const int64_t n0 = tile * BN;
     const int64_t kbeg = (int64_t)w * NCH * 64;
     const uint16_t *A = static_cast<const uint16_t *>(g.A);
     const uint16_t *W = static_cast<const uint16_t *>(g.W);
     const int ko = 8 * (lane / 16);
     // row piece of lane l in a load: row 8 i + l / 8, 16-byte piece l % 8 of the chunk's 128 bytes
     const int prow = lane / 8, ppiece = lane % 8;
-    const uint16_t *arow[8], *wrow[WPL];
+    const uint16_t *arow[AL], *wrow[WPL];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = 8 * i + prow;
-        arow[i] = A + (int64_t)(r < g.M ? r : 0) * g.lda + kbeg + 8 * ppiece;  // clamped rows are masked at the end
+    for (int i = 0; i < AL; ++i) {
+        const int64_t r = m0 + 8 * i + prow;
+        arow[i] = A + (r < g.M ? r : 0) * g.lda + kbeg + 8 * ppiece;  // clamped rows are masked at the end
     }
 #pragma unroll
     for (int i = 0; i < WPL; ++i) {
@@ -401,11 +410,11 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
     }
     // A two chunks ahead, W SW chunks ahead, in registers (native vectors, so
     // they stay in registers); every index below is a compile-time constant
-    u32x4 ra[2][8], rw[SW][WPL];
+    u32x4 ra[2][AL], rw[SW][WPL];
     auto load_a = [&](auto cc) {
         constexpr int c = decltype(cc)::value;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ra[c % 2][i] = *reinterpret_cast<const u32x4 *>(arow[i] + 64 * c);
+        for (int i = 0; i < AL; ++i) ra[c % 2][i] = *reinterpret_cast<const u32x4 *>(arow[i] + 64 * c);
     };
     auto load_w = [&](auto cc) {
         constexpr int c = decltype(cc)::value;
@@ -415,7 +424,7 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
             // N = 6144 11.45 -> 11.02 us); the 16-column form measured slower with it
             // (N = 2048: 6.35 -> 7.85 us)
             const u32x4 *pw = reinterpret_cast<const u32x4 *>(wrow[i] + 64 * c);
-            if constexpr (NTW == 2)
+            if constexpr (NTW >= 2)
                 rw[c % SW][i] = __builtin_nontemporal_load(pw);
             else
                 rw[c % SW][i] = *pw;
@@ -424,9 +433,9 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
     static_for<0, SW>([&](auto cc) { load_w(cc); });
     static_for<0, 2>([&](auto cc) { load_a(cc); });
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc[4][NTW], ss[4];
+    f32x4 acc[MT][NTW], ss[MT];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < MT; ++m) {
         ss[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -438,7 +447,7 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
     static_for<0, NCH>([&](auto cc) {
         constexpr int c = decltype(cc)::value, buf = c % 2;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < AL; ++i)
             *reinterpret_cast<u32x4 *>(&as[w][buf][(8 * i + prow) * kAsLd + 8 * ppiece]) = ra[buf][i];
 #pragma unroll
         for (int i = 0; i < WPL; ++i)
@@ -447,50 +456,50 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
         if constexpr (c + SW < NCH) load_w(std::integral_constant<int, c + SW>{});
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            uint4 a[4], b[NTW];
+            uint4 a[MT], b[NTW];
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < MT; ++m)
                 a[m] = *reinterpret_cast<const uint4 *>(&as[w][buf][(16 * m + lane % 16) * kAsLd + 32 * h + ko]);
 #pragma unroll
             for (int j = 0; j < NTW; ++j)
                 b[j] = *reinterpret_cast<const uint4 *>(&wsm[w][buf][(16 * j + lane % 16) * kAsLd + 32 * h + ko]);
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int j = 0; j < NTW; ++j) acc[m][j] = mfma16(a[m], b[j], acc[m][j]);
             if constexpr (RMS) {
 #pragma unroll
-                for (int m = 0; m < 4; ++m) ss[m] = mfma16(a[m], a[m], ss[m]);
+                for (int m = 0; m < MT; ++m) ss[m] = mfma16(a[m], a[m], ss[m]);
             }
         }
     });
     if constexpr (RMS) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < MT; ++m) {
             int q;
             const float dg = diag_of(ss[m], lane, q);
-            if (4 * (lane / 16) <= q && q < 4 * (lane / 16) + 4) red_ss[w * 64 + m * 16 + q] = dg;
+            if (4 * (lane / 16) <= q && q < 4 * (lane / 16) + 4) red_ss[w * MR + m * 16 + q] = dg;
         }
     }
     __syncthreads();  // every wave is done with its A buffers, which now hold the K-part sums
     float *red = reinterpret_cast<float *>(&as[0][0][0]);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[(w * 64 + m * 16 + 4 * (lane / 16) + r) * BN + j * 16 + lane % 16] = acc[m][j][r];
+            for (int r = 0; r < 4; ++r) red[(w * MR + m * 16 + 4 * (lane / 16) + r) * BN + j * 16 + lane % 16] = acc[m][j][r];
     __syncthreads();
     uint16_t *C = static_cast<uint16_t *>(g.C);
-    for (int e = tid; e < 64 * BN; e += 256) {
-        const int row = e / BN, c = e % BN;
-        const int64_t col = n0 + c;
+    for (int e = tid; e < MR * BN; e += 256) {
+        const int lr = e / BN, c = e % BN;
+        const int64_t row = m0 + lr, col = n0 + c;
         if (row >= g.M || col >= g.N) continue;
-        const float sum = red[(0 * 64 + row) * BN + c] + red[(1 * 64 + row) * BN + c] +
-                          red[(2 * 64 + row) * BN + c] + red[(3 * 64 + row) * BN + c];
+        const float sum = red[(0 * MR + lr) * BN + c] + red[(1 * MR + lr) * BN + c] +
+                          red[(2 * MR + lr) * BN + c] + red[(3 * MR + lr) * BN + c];
         float sc = g.row_scale ? g.row_scale[row] : 1.0f;
         if constexpr (RMS)
-            sc *= rms_scale(red_ss[row] + red_ss[64 + row] + red_ss[128 + row] + red_ss[192 + row], g.K, g.rms_eps);
+            sc *= rms_scale(red_ss[lr] + red_ss[MR + lr] + red_ss[2 * MR + lr] + red_ss[3 * MR + lr], g.K, g.rms_eps);
         C[row * g.ldc + col] = (uint16_t)f32_to_bf16(sum * sc);
     }
 }
@@ -646,14 +655,27 @@ hipError_t launch_tiled(const GemmArgs &g, hipStream_t stream) {
 template <bool RMS>
 hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
     if (g.M <= 64 && g.K == 2048) {
-        // Measured on MI355X at M = 64 (graph-replayed, 24 distinct weights):
-        // 32 columns per workgroup for wide outputs (N = 6144: 12.5 us), 16 for
-        // narrower ones (N = 2048: 6.2 us, against 9.1 us split-K and 10.6 us
-        // skinny); W two chunks ahead (three or four: no faster).
-        if (g.N >= 4096)
-            gemm_stream_lds_kernel<2, 2, RMS><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
+        // M > 32: each workgroup takes 32 rows, so a column tile is two
+        // workgroups on one XCD that share its weights through L2, and every
+        // workgroup reads half of A.  48 columns for wide outputs and 16 for
+        // narrow ones give 256 workgroups (one per CU) at N = 6144 and N = 2048.
+        // Measured on MI355X at M = 64 (graph-replayed, 24 distinct weights),
+        // against 64-row workgroups of 32 / 16 columns: N = 6144 with the fused
+        // RMS 12.2 -> 10.7 us, N = 2048 6.3 -> 5.0 us; 32-row workgroups of 32
+        // columns (384 of them) 13.0 us.  The 64-row form measured ahead of
+        // split-K (9.1 us at N = 2048) and of the skinny kernel (10.6 us).
+        if (g.M > 32) {
+            if (g.N >= 4096) {
+                const int64_t tiles = (g.N + 47) / 48;
+                gemm_stream_lds_kernel<3, 2, RMS, 32><<<dim3((unsigned)(((tiles + 7) / 8) * 16)), dim3(256), 0, stream>>>(g);
+            } else {
+                const int64_t tiles = (g.N + 15) / 16;
+                gemm_stream_lds_kernel<1, 2, RMS, 32><<<dim3((unsigned)(((tiles + 7) / 8) * 16)), dim3(256), 0, stream>>>(g);
+            }
+        } else if (g.N >= 4096)
+            gemm_stream_lds_kernel<2, 2, RMS, 64><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);
         else
-            gemm_stream_lds_kernel<1, 2, RMS><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
+            gemm_stream_lds_kernel<1, 2, RMS, 64><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
         return hipGetLastError();
     }
     const size_t ws_need = splitk_workspace_bytes(g.M, g.N, g.K);

@@ -29,7 +29,8 @@ def _bits(rng, shape, std=1.0):
     (64, 6144, 2048),     # generation-step in_proj (weight streaming path)
     (37, 4100, 2048),     # weight streaming path, ragged rows and columns
     (64, 2048, 2048),     # generation-step out_proj (streaming, 16 columns per workgroup)
-    (21, 1000, 2048),     # streaming, 16 columns per workgroup, ragged
+    (45, 2000, 2048),     # streaming, two 32-row halves, 16 columns, ragged rows and columns
+    (21, 1000, 2048),     # streaming, one 64-row workgroup per 16 columns, ragged
     (37, 96, 1024),       # ragged rows and columns, skinny path
     (300, 200, 128),      # tiled path, ragged M and N
     (1024, 768, 512),     # tiled path, several tiles
@@ -56,7 +57,7 @@ def test_dense_bf16(M, N, K, scaled):
     assert err <= 8e-3
 
 
-@pytest.mark.parametrize("M,N,K", [(64, 6144, 2048), (37, 4100, 2048), (64, 2048, 2048), (50, 100, 512),
+@pytest.mark.parametrize("M,N,K", [(64, 6144, 2048), (37, 4100, 2048), (64, 2048, 2048), (45, 2000, 2048), (50, 100, 512),
                                    (700, 300, 256), (2048, 6144, 2048)])
 def test_dense_rms_fused(M, N, K):
     """in_proj with the inverse-RMS row scale computed inside the GEMM."""
