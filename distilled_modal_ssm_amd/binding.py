@@ -42,6 +42,8 @@ EXPORTS = (
     "hyena_dense_workspace",
     "hyena_dense_bf16_ex",
     "hyena_dense_rms_bf16_ex",
+    "hyena_layer_step_bf16",
+    "hyena_pack_in_proj_bf16",
     "hyena_fir_workspace",
     "hyena_fir_decode_step",
     "hyena_fir_cache_fill",
@@ -132,6 +134,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "hyena_dense_bf16_ex": ([i64, i64, i64, p, i64, p, i64, p, p, i64, p, sz, p], ctypes.c_int),
             "hyena_dense_rms_bf16_ex": ([i64, i64, i64, p, i64, p, i64, ctypes.c_float, p, i64, p, sz, p],
                                         ctypes.c_int),
+            "hyena_layer_step_bf16": ([D, p, i64, p, ctypes.c_float, p, p, i64, p], ctypes.c_int),
+            "hyena_pack_in_proj_bf16": ([i64, i64, p, i64, p, p], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -277,6 +281,24 @@ def hyena_dense_workspace(M, N, K) -> int:
     n = ctypes.c_size_t(0)
     _check(load().hyena_dense_workspace(M, N, K, ctypes.byref(n)), "hyena_dense_workspace")
     return n.value
+
+
+def hyena_pack_in_proj_bf16(D, K, w_in, ldw, w_packed, stream=None) -> None:
+    """w_packed row 48 G + 16 j + i = w_in row j D + 16 G + i (q, k, v rows of a 16-channel group adjacent)."""
+    _check(load().hyena_pack_in_proj_bf16(D, K, _ptr(w_in), ldw, _ptr(w_packed), _stream(stream)),
+           "hyena_pack_in_proj_bf16")
+
+
+def hyena_layer_step_bf16(desc: hm_desc, x, ldx, w_packed, eps, state, y, ld_y, stream=None) -> int:
+    """Fused generation step of a projected layer (in_proj with RMS + decode step).
+
+    Returns the library status without raising for HM_ERR_UNSUPPORTED, so a
+    caller can fall back to the two separate calls; other errors raise."""
+    st = load().hyena_layer_step_bf16(ctypes.byref(desc), _ptr(x), ldx, _ptr(w_packed), eps, _ptr(state), _ptr(y),
+                                      ld_y, _stream(stream))
+    if st != HM_ERR_UNSUPPORTED:
+        _check(st, "hyena_layer_step_bf16")
+    return st
 
 
 def hyena_fir_workspace(desc: hm_desc) -> int:

@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // it needs.  The four K quarters are summed through LDS, reusing the A buffers.
 constexpr int kAsLd = 72;  // bf16 per LDS row of the A chunk (64 + 8 pad)
 
-template <int NTW, int SW, bool RMS, int MR>
+template <int NTW, int SW, bool RMS, int MR, int FDL = 0>
 __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
     constexpr int MT = MR / 16, AL = MR / 8;  // m-tiles; A row-piece loads per chunk
     constexpr int BN = 16 * NTW, NCH = 8;  // K quarter: 8 chunks of 64
@@ -432,6 +432,22 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
     };
     static_for<0, SW>([&](auto cc) { load_w(cc); });
     static_for<0, 2>([&](auto cc) { load_a(cc); });
+    // Fused decode step (FDL modes): thread = (row dr of the half, channel pair
+    // dcp of the tile's 16 channels); its state is loaded here, so it arrives
+    // while the weights stream.
+    static_assert(FDL == 0 || (NTW == 3 && MR == 32 && RMS), "fused step: 48 columns = q, k, v of 16 channels");
+    const int dr = tid / 8, dcp = tid % 8;
+    const int64_t db = m0 + dr, dc = tile * 16 + 2 * dcp;
+    const int64_t dg = FDL ? dc / g.P : 0;
+    float2 *dst = nullptr;
+    f32x4 xs[FDL > 0 ? FDL : 1];
+    if constexpr (FDL > 0) {
+        if (db < g.M) {
+            dst = g.state + ((db * g.H + dg) * FDL) * g.P + (dc - dg * g.P);
+#pragma unroll
+            for (int n = 0; n < FDL; ++n) xs[n] = *reinterpret_cast<const f32x4 *>(dst + n * g.P);
+        }
+    }
     __builtin_amdgcn_sched_barrier(0);
     f32x4 acc[MT][NTW], ss[MT];
 #pragma unroll
@@ -490,6 +506,49 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) red[(w * MR + m * 16 + 4 * (lane / 16) + r) * BN + j * 16 + lane % 16] = acc[m][j][r];
     __syncthreads();
+    if constexpr (FDL > 0) {
+        // q, k, v rounded to bf16 exactly as the projection stores them, then
+        // the decode step with the arithmetic of decode_step_fixed (two
+        // channels per lane): y = q (D u + Re sum R x), x <- lambda x + u
+        float *qkv = reinterpret_cast<float *>(&wsm[0][0][0]);  // [MR][BN]; free after the K loop
+        for (int e = tid; e < MR * BN; e += 256) {
+            const int lr = e / BN, c = e % BN;
+            const int64_t row = m0 + lr;
+            float v = 0.f;
+            if (row < g.M) {
+                const float sum = red[(0 * MR + lr) * BN + c] + red[(1 * MR + lr) * BN + c] +
+                                  red[(2 * MR + lr) * BN + c] + red[(3 * MR + lr) * BN + c];
+                const float sc = rms_scale(red_ss[lr] + red_ss[MR + lr] + red_ss[2 * MR + lr] + red_ss[3 * MR + lr],
+                                           g.K, g.rms_eps);
+                v = bf16_lo(f32_to_bf16(sum * sc));
+            }
+            qkv[e] = v;
+        }
+        __syncthreads();
+        if (db < g.M) {
+            const float *qr = qkv + dr * BN + 2 * dcp;
+            const float q0 = qr[0], q1 = qr[1];
+            const float u0 = qr[16] * qr[32], u1 = qr[17] * qr[33];
+            const float2 *lam = g.poles + dg * FDL, *res = g.residues + dg * FDL;
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int n = 0; n < FDL; ++n) {
+                const float2 l = lam[n], r = res[n];
+                const f32x4 xo = xs[n];
+                acc0 = fmaf(r.x, xo[0], acc0);
+                acc0 = fmaf(-r.y, xo[1], acc0);
+                acc1 = fmaf(r.x, xo[2], acc1);
+                acc1 = fmaf(-r.y, xo[3], acc1);
+                const f32x4 xn = {fmaf(l.x, xo[0], fmaf(-l.y, xo[1], u0)), fmaf(l.x, xo[1], l.y * xo[0]),
+                                  fmaf(l.x, xo[2], fmaf(-l.y, xo[3], u1)), fmaf(l.x, xo[3], l.y * xo[2])};
+                __builtin_nontemporal_store(xn, reinterpret_cast<f32x4 *>(dst + n * g.P));
+            }
+            const float Dg = g.skip[dg];
+            __builtin_nontemporal_store(pack_bf16x2(q0 * fmaf(Dg, u0, acc0), q1 * fmaf(Dg, u1, acc1)),
+                                        reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(g.y) + db * g.ld_y + dc));
+        }
+        return;
+    }
     uint16_t *C = static_cast<uint16_t *>(g.C);
     for (int e = tid; e < MR * BN; e += 256) {
         const int lr = e / BN, c = e % BN;
@@ -712,6 +771,38 @@ hipError_t launch_row_rms(const RmsArgs &a, hipStream_t stream) {
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream) {
     if (g.M == 0 || g.N == 0) return hipSuccess;
     return g.rms ? launch_gemm_t<true>(g, stream) : launch_gemm_t<false>(g, stream);
+}
+
+hipError_t launch_layer_step(const GemmArgs &g, int d, hipStream_t stream) {
+    if (g.M == 0) return hipSuccess;
+    // column tiles of 48 = 16 channels; the two 32-row halves of a tile 8 workgroups apart
+    const int64_t tiles = g.N / 48;
+    const dim3 grid((unsigned)(((tiles + 7) / 8) * 16)), block(256);
+    switch (d) {
+        case 8: gemm_stream_lds_kernel<3, 2, true, 32, 8><<<grid, block, 0, stream>>>(g); break;
+        case 16: gemm_stream_lds_kernel<3, 2, true, 32, 16><<<grid, block, 0, stream>>>(g); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+namespace {
+// One workgroup per packed row: row 48 G + 16 j + i is in_proj row j D + 16 G + i.
+__global__ __launch_bounds__(256) void pack_in_proj_kernel(int64_t D, int64_t K, const uint16_t *w, int64_t ldw,
+                                                           uint16_t *out) {
+    const int64_t r = blockIdx.x, grp = r / 48, j = (r % 48) / 16, i = r % 16;
+    const uint16_t *src = w + (j * D + 16 * grp + i) * ldw;
+    uint16_t *dst = out + r * K;
+    for (int64_t k = threadIdx.x * 8; k < K; k += 256 * 8)
+        *reinterpret_cast<uint4 *>(dst + k) = *reinterpret_cast<const uint4 *>(src + k);
+}
+}  // namespace
+
+hipError_t launch_pack_in_proj(int64_t D, int64_t K, const void *w, int64_t ldw, void *out, hipStream_t stream) {
+    if (D == 0) return hipSuccess;
+    pack_in_proj_kernel<<<dim3((unsigned)(3 * D)), dim3(256), 0, stream>>>(D, K, static_cast<const uint16_t *>(w), ldw,
+                                                                          static_cast<uint16_t *>(out));
+    return hipGetLastError();
 }
 
 }  // namespace hm

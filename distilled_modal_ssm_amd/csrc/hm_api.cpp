@@ -578,4 +578,55 @@ hm_status hyena_dense_rms_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A
     return dense_impl(M, N, K, A, lda, W, ldw, nullptr, true, eps, C, ldc, workspace, ws_bytes, stream);
 }
 
+hm_status hyena_pack_in_proj_bf16(int64_t D, int64_t K, const void *w_in, int64_t ldw, void *w_packed,
+                                  void *stream) {
+    if (D < 0 || K < 1 || ldw < K) return HM_ERR_INVALID_ARG;
+    if (D == 0) return HM_OK;
+    if (!w_in || !w_packed) return HM_ERR_INVALID_ARG;
+    if (D % 16 != 0 || K % 8 != 0 || ldw % 8 != 0) return HM_ERR_UNSUPPORTED;
+    if (!aligned(w_in, 16) || !aligned(w_packed, 16)) return HM_ERR_UNSUPPORTED;
+    if (3 * D > INT32_MAX || 3 * D > kMaxElems / ldw) return HM_ERR_INVALID_ARG;
+    const hipError_t err = hm::launch_pack_in_proj(D, K, w_in, ldw, w_packed, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+hm_status hyena_layer_step_bf16(const hm_desc *desc, const void *x, int64_t ldx, const void *w_packed, float eps,
+                                float *state, void *y, int64_t ld_y, void *stream) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if (!(eps >= 0.0f)) return HM_ERR_INVALID_ARG;
+    const hm::OpShape s = shape_of(desc);
+    if (s.B == 0) return HM_OK;
+    if (!x || !w_packed || !state || !y) return HM_ERR_INVALID_ARG;
+    if (ldx < s.D || ld_y < s.D) return HM_ERR_INVALID_ARG;
+    if (s.act != hm::kBF16 || s.B > 64 || s.D != 2048 || (s.d != 8 && s.d != 16) || s.P % 16 != 0)
+        return HM_ERR_UNSUPPORTED;
+    if (ldx % 8 != 0 || ld_y % 2 != 0) return HM_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(state, 16) || !aligned(y, 4))
+        return HM_ERR_UNSUPPORTED;
+    hm::GemmArgs g;
+    g.M = s.B;
+    g.N = 3 * s.D;
+    g.K = s.D;
+    g.A = x;
+    g.lda = ldx;
+    g.W = w_packed;
+    g.ldw = s.D;
+    g.row_scale = nullptr;
+    g.C = nullptr;
+    g.ldc = 0;
+    g.rms = true;
+    g.rms_eps = eps;
+    g.state = reinterpret_cast<float2 *>(state);
+    g.poles = s.poles;
+    g.residues = s.residues;
+    g.skip = s.skip;
+    g.P = s.P;
+    g.H = s.H;
+    g.y = y;
+    g.ld_y = ld_y;
+    const hipError_t err = hm::launch_layer_step(g, (int)s.d, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
 }  // extern "C"

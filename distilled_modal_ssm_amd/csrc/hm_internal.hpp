@@ -192,6 +192,15 @@ struct GemmArgs {
     float rms_eps;
     unsigned char *ws = nullptr;  // split-K workspace (M <= 64), or null
     size_t ws_bytes = 0;
+    // Fused generation step of a projected layer (launch_layer_step only): W is
+    // the packed in_proj, and the epilogue runs the decode step on the columns
+    // instead of storing C.
+    float2 *state = nullptr;                      // [M][H][d][P] complex, in/out
+    const float2 *poles = nullptr, *residues = nullptr;  // [H][d]
+    const float *skip = nullptr;                  // [H]
+    int64_t P = 0, H = 0;
+    void *y = nullptr;                            // bf16 [M][ld_y]
+    int64_t ld_y = 0;
 };
 
 // Split-K path of the small-M GEMM: 64-column tiles x 256-wide K slices write
@@ -285,5 +294,10 @@ hipError_t launch_chunk_mfma(const PrefillArgs &a, const float2 *carry0, hipStre
 hipError_t launch_chunk_mfma_state(const PrefillArgs &a, bool vec, hipStream_t stream);
 hipError_t launch_row_rms(const RmsArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t stream);
+// Generation step of a projected layer: packed in_proj (fused RMS) + decode step
+// in one launch; M <= 64, K = 2048, N = 3 * channels, d in {8, 16}.
+hipError_t launch_layer_step(const GemmArgs &g, int d, hipStream_t stream);
+// in_proj weights [3D][K] -> packed rows: 48 G + 16 j + i <- j D + 16 G + i.
+hipError_t launch_pack_in_proj(int64_t D, int64_t K, const void *w, int64_t ldw, void *out, hipStream_t stream);
 
 }  // namespace hm

@@ -24,7 +24,7 @@ class HyenaStack:
     bfloat16 bit patterns, copied to the device).
     """
 
-    def __init__(self, layers, batch: int, prompt_len: int, device="cuda"):
+    def __init__(self, layers, batch: int, prompt_len: int, device="cuda", fused: bool = True):
         import torch
         self.torch = torch
         self.device = torch.device(device)
@@ -55,6 +55,15 @@ class HyenaStack:
         # split-K scratch of the generation-step projections
         ws = max(hb.hyena_dense_workspace(B, 3 * D, D), hb.hyena_dense_workspace(B, D, D))
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, **e) if ws > 0 else None
+        # generation step: in_proj and decode fused into one launch where the
+        # library supports the shape (packed in_proj rows), else two calls
+        self.w_in_packed = None
+        if fused and D % 16 == 0:
+            self.w_in_packed = []
+            for w in self.w_in:
+                wp = torch.empty_like(w)
+                hb.hyena_pack_in_proj_bf16(D, D, w, D, wp)
+                self.w_in_packed.append(wp)
 
     def _bf16(self, w):
         torch = self.torch
@@ -77,6 +86,17 @@ class HyenaStack:
         else:
             self.ops[l].decode_step(qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:], self.states[l], y=y)
         hb.hyena_dense_bf16(M, D, D, y, D, self.w_out[l], D, None, out, D, workspace=ws)
+
+    def _layer_step(self, l, x, out):
+        """One generated token through layer l: fused in_proj + decode when supported."""
+        D, B = self.D, self.B
+        if self.w_in_packed is not None:
+            st = hb.hyena_layer_step_bf16(self.ops[l].desc, x, D, self.w_in_packed[l], RMS_EPS, self.states[l],
+                                          self.yd, D)
+            if st == hb.HM_OK:
+                hb.hyena_dense_bf16(B, D, D, self.yd, D, self.w_out[l], D, None, out, D, workspace=self.ws)
+                return
+        self._layer(l, x, out, B, self.qkvd, self.yd, None, False)
 
     def prefill(self, x_in, record=None):
         """x_in: [B][L][D] bf16 prompt input.  Returns the stack output [B*L][D].
@@ -104,6 +124,6 @@ class HyenaStack:
             if record is not None:
                 record(l, src)
             dst = self.xd if l == self.nl - 1 else self.xd_mid[l % 2]
-            self._layer(l, src, dst, self.B, self.qkvd, self.yd, None, False)
+            self._layer_step(l, src, dst)
             src = dst
         return self.xd

@@ -270,6 +270,38 @@ hm_status hyena_dense_rms_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A
                                   void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * One generated token through a projected layer's in_proj and modal operator,
+ * in one launch (the generation step whose throughput the Laughing Hyena
+ * Distillery review compares at 1.3B width, 主要发现; the recurrence is the
+ * O(d)-per-token decode of the same section).  Per batch row b < B:
+ *   [q|k|v] = bf16( x[b] W_in^T / sqrt(mean_k x[b][k]^2 + eps) )   (as hyena_dense_rms_bf16)
+ *   then hyena_modal_decode_step on those q, k, v: y[b] and the state updated.
+ * The result equals those two calls bit for bit; q, k, v are never stored.
+ *   desc         operator descriptor; act_dtype HM_BF16, batch = B rows
+ *   x            bf16 [B][ldx], the layer input (D columns used)
+ *   w_packed     bf16 [3D][D], W_in [3D][D] packed by hyena_pack_in_proj_bf16
+ *   state        [B][H][d][P] complex float32, read and updated in place
+ *   y            bf16 [B][ld_y], the operator output (D columns written)
+ * Supported: B <= 64, D = 2048, d in {8, 16}, P a multiple of 16, ldx a
+ * multiple of 8, ld_y even, x / w_packed / state 16-byte and y 4-byte aligned
+ * (else HM_ERR_UNSUPPORTED: use the two separate calls).  Null pointers,
+ * ldx or ld_y < D, eps < 0 -> HM_ERR_INVALID_ARG.  y must not overlap x.
+ */
+hm_status hyena_layer_step_bf16(const hm_desc *desc, const void *x, int64_t ldx, const void *w_packed,
+                                float eps, float *state, void *y, int64_t ld_y, void *stream);
+
+/*
+ * Packs in_proj weights for hyena_layer_step_bf16: w_packed row 48 G + 16 j + i
+ * = w_in row j D + 16 G + i (j = 0, 1, 2 for q, k, v; G = 16-channel group),
+ * so one group's q, k and v rows are adjacent.
+ *   w_in     bf16 [3D][ldw] (K columns used), w_packed bf16 [3D][K] (caller-owned)
+ * D % 16, K % 8, ldw % 8 != 0 or misaligned (16 bytes) -> HM_ERR_UNSUPPORTED;
+ * D < 0, K < 1, ldw < K, null pointers -> HM_ERR_INVALID_ARG.
+ */
+hm_status hyena_pack_in_proj_bf16(int64_t D, int64_t K, const void *w_in, int64_t ldw, void *w_packed,
+                                  void *stream);
+
+/*
  * Non-distilled baseline: the Hyena operator's decode step through its
  * explicit long filter (StripedHyena article, Hyena層次結構) instead of the
  * modal recurrence -- the O(t)-per-token cost that distillation removes

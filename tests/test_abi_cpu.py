@@ -374,3 +374,39 @@ def test_distill_validation(lib):
     for kw in (dict(step=0), dict(lr=0.0), dict(b1=1.0), dict(b2=-0.1), dict(eps=0.0), dict(r_max=1.0),
                dict(r_max=0.0), dict(d=65), dict(H=0)):
         assert adam(**kw) == hb.HM_ERR_INVALID_ARG, kw
+
+
+def test_layer_step_and_pack_validation(lib):
+    """The fused generation step reports shapes it does not cover as a status
+    (the caller then makes the two separate calls); argument errors raise."""
+    base = dict(batch=64, channels=2048, heads=16, modes=16, act_dtype=hb.HM_BF16)
+
+    def step(desc_kw=None, **kw):
+        dk = dict(base)
+        dk.update(desc_kw or {})
+        a = dict(x=FAKE, ldx=2048, w=FAKE, eps=1e-6, state=FAKE, y=FAKE, ld_y=2048)
+        a.update(kw)
+        return hb.hyena_layer_step_bf16(_desc(**dk), a["x"], a["ldx"], a["w"], a["eps"], a["state"], a["y"],
+                                        a["ld_y"], stream=0)
+
+    for dk in [dict(channels=1024, heads=8), dict(modes=32), dict(batch=65), dict(act_dtype=hb.HM_F32),
+               dict(heads=256)]:  # heads=256: 8 channels per head
+        assert step(dk) == hb.HM_ERR_UNSUPPORTED, dk
+    for kw in [dict(ldx=2052), dict(ld_y=2049), dict(state=FAKE + 8), dict(y=FAKE + 2), dict(w=FAKE + 8)]:
+        assert step(**kw) == hb.HM_ERR_UNSUPPORTED, kw
+    for kw in [dict(x=None), dict(w=None), dict(state=None), dict(y=None), dict(eps=-1.0), dict(ldx=100),
+               dict(ld_y=100)]:
+        with pytest.raises(hb.HMError) as e:
+            step(**kw)
+        assert e.value.status == hb.HM_ERR_INVALID_ARG, kw
+    assert step(dict(batch=0)) == hb.HM_OK  # empty: no launch
+
+    for args, status in [((-1, 64, FAKE, 64, FAKE), hb.HM_ERR_INVALID_ARG),
+                         ((16, 64, None, 64, FAKE), hb.HM_ERR_INVALID_ARG),
+                         ((16, 64, FAKE, 32, FAKE), hb.HM_ERR_INVALID_ARG),    # ldw < K
+                         ((24, 64, FAKE, 64, FAKE), hb.HM_ERR_UNSUPPORTED),    # D not a multiple of 16
+                         ((16, 64, FAKE + 8, 64, FAKE), hb.HM_ERR_UNSUPPORTED)]:
+        with pytest.raises(hb.HMError) as e:
+            hb.hyena_pack_in_proj_bf16(*args, stream=0)
+        assert e.value.status == status, args
+    hb.hyena_pack_in_proj_bf16(0, 64, FAKE, 64, FAKE, stream=0)  # empty: no launch
