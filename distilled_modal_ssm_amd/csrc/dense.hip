@@ -14,13 +14,18 @@
 //     fragment reads hit distinct banks), (BM/WM) x (BN/WN) waves each owning a
 //     WM x WN sub-tile of 16x16x32 MFMAs.  Tiles are ordered so each XCD walks
 //     a contiguous range, grouped GM m-tiles at a time, to keep A and W in L2.
-//   * gemm_stream_lds / gemm_skinny (M <= 64, the generation step): a
-//     workgroup owns 16-32 columns and all rows.  gemm_stream_lds (K = 2048)
-//     loads A and W as 128-byte row pieces a few chunks ahead and stages them
-//     per wave through LDS, its K loop unrolled; gemm_skinny stages
-//     contiguous A and W slabs through double-buffered LDS.  Both sum their K
-//     parts through LDS.  Every workgroup re-reads all of A (64 x K), so these
-//     are bound by L1->L2 request throughput, not by the W stream alone.
+//   * gemm_stream_lds / gemm_skinny (M <= 64, the generation step).
+//     gemm_stream_lds (K = 2048): a workgroup owns 16-48 columns and all 64
+//     rows or one 32-row half (the two halves of a tile on one XCD, sharing
+//     its weights through L2); it loads A and W as 128-byte row pieces a few
+//     chunks ahead and stages them per wave through LDS, its K loop unrolled.
+//     gemm_skinny: a workgroup owns 16 columns and all rows, contiguous A and
+//     W slabs through double-buffered LDS.  Both sum their K parts through
+//     LDS.  Every workgroup re-reads its rows of A, so these are bound by
+//     L1->L2 request throughput as much as by the W stream.
+//   * the fused generation step of a layer: gemm_stream_lds on in_proj
+//     weights packed so a 48-column tile is q, k, v of 16 channels, whose
+//     epilogue runs the modal decode step for them instead of storing C.
 #include "hm_internal.hpp"
 
 #include <type_traits>
