@@ -135,6 +135,29 @@ int main() {
                                    nullptr),
            HM_ERR_INVALID_ARG);
 
+    // fused generation step and its weight packing
+    hm_desc ls = ok;
+    ls.act_dtype = HM_BF16;
+    ls.batch = 64;
+    ls.channels = 2048;
+    ls.heads = 16;
+    ls.modes = 16;
+    EXPECT(hyena_layer_step_bf16(&ls, P, 2048, P, -1.0f, (float *)P, P, 2048, nullptr), HM_ERR_INVALID_ARG);
+    EXPECT(hyena_layer_step_bf16(&ls, nullptr, 2048, P, 1e-6f, (float *)P, P, 2048, nullptr), HM_ERR_INVALID_ARG);
+    EXPECT(hyena_layer_step_bf16(&ls, P, 100, P, 1e-6f, (float *)P, P, 2048, nullptr), HM_ERR_INVALID_ARG);
+    EXPECT(hyena_layer_step_bf16(&ls, P, 2052, P, 1e-6f, (float *)P, P, 2048, nullptr), HM_ERR_UNSUPPORTED);
+    EXPECT(hyena_layer_step_bf16(&ls, P, 2048, P, 1e-6f, (float *)(arena + 8), P, 2048, nullptr), HM_ERR_UNSUPPORTED);
+    hm_desc ls32 = ls;
+    ls32.modes = 32;
+    EXPECT(hyena_layer_step_bf16(&ls32, P, 2048, P, 1e-6f, (float *)P, P, 2048, nullptr), HM_ERR_UNSUPPORTED);
+    hm_desc ls0 = ls;
+    ls0.batch = 0;
+    EXPECT(hyena_layer_step_bf16(&ls0, P, 2048, P, 1e-6f, (float *)P, P, 2048, nullptr), HM_OK);  // empty: no launch
+    EXPECT(hyena_pack_in_proj_bf16(0, 64, P, 64, P, nullptr), HM_OK);  // empty: no launch
+    EXPECT(hyena_pack_in_proj_bf16(24, 64, P, 64, P, nullptr), HM_ERR_UNSUPPORTED);
+    EXPECT(hyena_pack_in_proj_bf16(16, 64, P, 32, P, nullptr), HM_ERR_INVALID_ARG);
+    EXPECT(hyena_pack_in_proj_bf16(16, 64, nullptr, 64, P, nullptr), HM_ERR_INVALID_ARG);
+
     std::printf(failures ? "abi: %d failures\n" : "abi ok\n", failures);
     return failures ? 1 : 0;
 }
