@@ -209,6 +209,30 @@ def test_stack_generation_fused_matches_separate_calls():
         assert torch.equal(a, b)
 
 
+def test_stack_generation_falls_back_when_fusion_does_not_cover_the_shape():
+    """D = 512 is outside the fused step (it returns HM_ERR_UNSUPPORTED without
+    launching): the stack then makes the two separate calls, with the same bits
+    as a stack built without fusion."""
+    torch = require_gpu()
+    import dataclasses
+    from distilled_modal_ssm_amd.stack import HyenaStack
+    cfg = dataclasses.replace(get_config(5), layers=2, L=64, B=8, D=512, H=4)
+    layers = [(modal_params(cfg, l), *dense_weights(cfg, l)) for l in range(cfg.layers)]
+    X = torch.randn(cfg.B, cfg.L, cfg.D, device="cuda").to(torch.bfloat16)
+    probe = HyenaStack(layers, cfg.B, cfg.L)
+    assert hb.hyena_layer_step_bf16(probe.ops[0].desc, probe.xd, cfg.D, probe.w_in_packed[0], 1e-6,
+                                    probe.states[0], probe.yd, cfg.D) == hb.HM_ERR_UNSUPPORTED
+    outs = {}
+    for fused in (False, True):
+        log(f"stack fallback fused={fused}")
+        st = HyenaStack(layers, cfg.B, cfg.L, fused=fused)
+        st.start_generation(st.prefill(X))
+        outs[fused] = [st.decode_step().clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    for a, b in zip(outs[False], outs[True]):
+        assert torch.equal(a, b)
+
+
 def test_stack_teacher_forced_full_size():
     torch = require_gpu()
     from distilled_modal_ssm_amd.stack import HyenaStack
