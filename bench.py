@@ -248,6 +248,16 @@ def stack_cpu_baseline(cfg, layers, x0):
                       f"generated steps, {dt:.1f} s; tokens scaled by the layer fraction"}
 
 
+def stack_token_bytes(cfg) -> int:
+    """HBM bytes a generated token of the projected stack must move: per layer the
+    bf16 weights (W_in 3D x D, W_out D x D), the modal state read and written
+    (16 d bytes per row and channel), and the bf16 activations: the layer input
+    read, the operator output written and read back by out_proj, the layer
+    output written (q, k, v stay on chip in the fused step)."""
+    D, B = cfg.D, cfg.B
+    return cfg.layers * (4 * D * D * 2 + B * D * 16 * cfg.d + 4 * B * D * 2)
+
+
 def bench_stack(args, cfg, dev):
     """Projected stack: prefill through all layers, then S generated tokens per
     batch row (one HIP graph per generated token, replayed)."""
@@ -301,7 +311,7 @@ def bench_stack(args, cfg, dev):
     D = cfg.D
     gemm_flops = cfg.layers * 2 * M * D * 4 * D          # in_proj (3D) + out_proj (D)
     hyena_flops = cfg.layers * (12 * cfg.d + 5) * M * D
-    decode_bytes = cfg.layers * (4 * D * D * 2 + cfg.B * D * (16 * cfg.d + 4 * 2) + 2 * cfg.B * 4 * D * 2)
+    decode_bytes = stack_token_bytes(cfg)
     prefill_tf = (gemm_flops + hyena_flops) / ms_prefill * 1e-9
     decode_gbs = decode_bytes / ms_tok * 1e-6
     if ms_prefill >= ms_decode:
