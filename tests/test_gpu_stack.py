@@ -151,14 +151,15 @@ def _layer_params(rng, H, d):
     return poles, res, rng.standard_normal(H).astype(np.float32)
 
 
-@pytest.mark.parametrize("B,d", [(64, 16), (40, 16), (1, 16), (64, 8)])
-def test_layer_step_fused_bit_exact(B, d):
+@pytest.mark.parametrize("B,d,H", [(64, 16, 16), (40, 16, 16), (1, 16, 16), (64, 8, 16), (33, 16, 32)])
+def test_layer_step_fused_bit_exact(B, d, H):
     """The fused generation step (packed in_proj with the RMS, then the decode
     step in the same launch) equals the two separate calls bit for bit, in y
-    and in the updated state; the packing is the stated row permutation."""
+    and in the updated state (head dims 128 and 64, a lone row in the second
+    32-row half); the packing is the stated row permutation."""
     torch = require_gpu()
     from distilled_modal_ssm_amd import ModalHyena
-    D, H = 2048, 16
+    D = 2048
     rng = np.random.default_rng(70 + B + d)
     poles, res, skip = _layer_params(rng, H, d)
     g = torch.Generator(device="cuda").manual_seed(80 + B + d)
@@ -166,7 +167,7 @@ def test_layer_step_fused_bit_exact(B, d):
     w_in = (torch.randn(3 * D, D, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
     op = ModalHyena(poles, res, skip, B, D, "bf16")
     state0 = torch.randn(op.new_state().shape, generator=g, device="cuda") * 0.3
-    log(f"layer step B={B} d={d}: separate calls")
+    log(f"layer step B={B} d={d} H={H}: separate calls")
     qkv = torch.empty(B, 3 * D, dtype=torch.bfloat16, device="cuda")
     hb.hyena_dense_rms_bf16(B, 3 * D, D, x, D, w_in, D, 1e-6, qkv, 3 * D)
     st_ref = state0.clone()
