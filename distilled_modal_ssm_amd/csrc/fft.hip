@@ -302,6 +302,10 @@ __device__ __forceinline__ void load_subtable(float2 *tws, const float2 *tw, int
 // Load columns p0 .. p0 + kLongCB - 1 of NR rows (row r at base + r rstride,
 // in complex elements) into the tile; columns >= npairs read as 0.
 template <int NR>
+// Tiles of the long transforms stream through HBM once per pass (the arrays are
+// far larger than the caches), so whole 16-byte column pairs are loaded and
+// stored non-temporally (measured on MI355X, B = 4, D = 4096, N = 131072:
+// 17.6 -> 15.7 ms for the prefill).
 __device__ __forceinline__ void tile_load(float2 *xs, const float2 *base, int64_t rstride, int64_t p0,
                                           int64_t npairs) {
     constexpr int CB = kLongCB, IT = NR * CB / 512;
@@ -312,8 +316,10 @@ __device__ __forceinline__ void tile_load(float2 *xs, const float2 *base, int64_
 #pragma unroll
         for (int i = 0; i < IT; ++i) {
             const int e = tid + 256 * i, r = e / (CB / 2), c = 2 * (e % (CB / 2));
-            t[i] = p0 + c < npairs ? *reinterpret_cast<const float4 *>(base + r * rstride + p0 + c)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+            typedef float f32v4 __attribute__((ext_vector_type(4)));
+            f32v4 v = {0.f, 0.f, 0.f, 0.f};
+            if (p0 + c < npairs) v = __builtin_nontemporal_load(reinterpret_cast<const f32v4 *>(base + r * rstride + p0 + c));
+            t[i] = make_float4(v.x, v.y, v.z, v.w);
         }
     } else {
 #pragma unroll
@@ -344,8 +350,9 @@ __device__ __forceinline__ void tile_store_twiddled(const float2 *xs, float2 *ba
         const float2 w = twiddle(tw, m * r, half);
         const float2 lo = cmul(w, xs[r * CB + c]), hi = cmul(w, xs[r * CB + c + 1]);
         if ((npairs & 1) == 0) {
+            typedef float f32v4 __attribute__((ext_vector_type(4)));
             if (p0 + c < npairs)
-                *reinterpret_cast<float4 *>(base + r * rstride + p0 + c) = make_float4(lo.x, lo.y, hi.x, hi.y);
+                __builtin_nontemporal_store(f32v4{lo.x, lo.y, hi.x, hi.y}, reinterpret_cast<f32v4 *>(base + r * rstride + p0 + c));
         } else {
             if (p0 + c < npairs) base[r * rstride + p0 + c] = lo;
             if (p0 + c + 1 < npairs) base[r * rstride + p0 + c + 1] = hi;
