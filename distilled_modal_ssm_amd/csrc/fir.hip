@@ -49,11 +49,23 @@ template <bool NT> struct Row8<kBF16, NT> {
         }
     }
 };
-template <bool NT> struct Row8<kF32, NT> {  // two 16-byte halves per lane: plain loads
+// float32: two 16-byte halves, adjacent (SPLIT = 4 floats) or half a block apart
+// (SPLIT = 256, so that each load instruction of a wave covers whole lines and
+// non-temporal loads stay efficient)
+template <bool NT> struct Row8<kF32, NT> {
     float4 a, b;
-    __device__ void load(const void *p) {
-        a = reinterpret_cast<const float4 *>(p)[0];
-        b = reinterpret_cast<const float4 *>(p)[1];
+    template <int SPLIT = 4> __device__ void load(const void *p) {
+        const float *f = static_cast<const float *>(p);
+        if constexpr (NT) {
+            typedef float f32v4 __attribute__((ext_vector_type(4)));
+            const f32v4 x = __builtin_nontemporal_load(reinterpret_cast<const f32v4 *>(f));
+            const f32v4 y = __builtin_nontemporal_load(reinterpret_cast<const f32v4 *>(f + SPLIT));
+            a = make_float4(x.x, x.y, x.z, x.w);
+            b = make_float4(y.x, y.y, y.z, y.w);
+        } else {
+            a = *reinterpret_cast<const float4 *>(f);
+            b = *reinterpret_cast<const float4 *>(f + SPLIT);
+        }
     }
     __device__ void get(float *o) const {
         o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
@@ -61,12 +73,16 @@ template <bool NT> struct Row8<kF32, NT> {  // two 16-byte halves per lane: plai
     }
 };
 
-template <int ACT, bool NT>
+// SPLIT: the lane's channels are c0 .. c0 + 3 and c0 + SPLIT .. + 3 (SPLIT = 4:
+// eight adjacent channels; SPLIT = 256, float32 with D a multiple of the block:
+// two halves half a block apart, possibly in different heads).
+template <int ACT, bool NT, int SPLIT = 4>
 __global__ __launch_bounds__(256) void fir_partial_kernel(FirArgs a) {
     using T = typename Act<ACT>::T;
+    static_assert(SPLIT == 4 || (ACT == kF32 && SPLIT == kFirBlk / 2), "lane channel layout");
     __shared__ float red[4][kWave][8];
     const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
-    const int64_t c0 = (int64_t)blockIdx.x * kFirBlk + 8 * lane;
+    const int64_t c0 = (int64_t)blockIdx.x * kFirBlk + (SPLIT == 4 ? 8 : 4) * lane;
     const int r = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int64_t n = a.t - a.lo;                       // cached rows in the window
@@ -77,35 +93,43 @@ __global__ __launch_bounds__(256) void fir_partial_kernel(FirArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
     if (c0 < a.s.D) {
-        const int64_t g = c0 / a.s.P;
-        const float *hg = a.h + g * a.h_len + a.t;      // tap of row s: hg[-s]
+        const int64_t g = c0 / a.s.P, g2 = (c0 + SPLIT) / a.s.P;
+        const float *hg = a.h + g * a.h_len + a.t;      // tap of row s: hg[-s] (channels e < 4)
+        const float *hg2 = a.h + g2 * a.h_len + a.t;    // channels e >= 4
         const T *base = static_cast<const T *>(a.cache) + (b * a.cache_len) * a.s.D + c0;
         int64_t s = s_begin + w;
         // four rows per wave in flight
         for (; s + 12 < s_end; s += 16) {
             Row8<ACT, NT> x[4];
-            float hv[4];
+            float hv[4], hv2[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                x[i].load(base + (s + 4 * i) * a.s.D);
+                if constexpr (ACT == kF32)
+                    x[i].template load<SPLIT>(base + (s + 4 * i) * a.s.D);
+                else
+                    x[i].load(base + (s + 4 * i) * a.s.D);
                 hv[i] = hg[-(s + 4 * i)];
+                hv2[i] = hg2[-(s + 4 * i)];
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float u[8];
                 x[i].get(u);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(hv[i], u[e], acc[e]);
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(e < 4 ? hv[i] : hv2[i], u[e], acc[e]);
             }
         }
         for (; s < s_end; s += 4) {
             Row8<ACT, NT> x;
-            x.load(base + s * a.s.D);
-            const float hv = hg[-s];
+            if constexpr (ACT == kF32)
+                x.template load<SPLIT>(base + s * a.s.D);
+            else
+                x.load(base + s * a.s.D);
+            const float hv = hg[-s], hv2 = hg2[-s];
             float u[8];
             x.get(u);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(hv, u[e], acc[e]);
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(e < 4 ? hv : hv2, u[e], acc[e]);
         }
     }
 #pragma unroll
@@ -116,8 +140,8 @@ __global__ __launch_bounds__(256) void fir_partial_kernel(FirArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] = red[0][lane][e] + red[1][lane][e] + red[2][lane][e] + red[3][lane][e];
         float *dst = a.part + ((int64_t)r * a.s.B + b) * a.s.D + c0;
-        reinterpret_cast<float4 *>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
-        reinterpret_cast<float4 *>(dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
+        *reinterpret_cast<float4 *>(dst) = make_float4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<float4 *>(dst + SPLIT) = make_float4(o[4], o[5], o[6], o[7]);
     }
 }
 
@@ -177,7 +201,13 @@ hipError_t launch_fir_decode(const FirArgs &a, hipStream_t stream) {
             fir_partial_kernel<kBF16, false><<<g1, dim3(256), 0, stream>>>(a);
         fir_finish_kernel<kBF16><<<g2, dim3(256), 0, stream>>>(a);
     } else {
-        fir_partial_kernel<kF32, false><<<g1, dim3(256), 0, stream>>>(a);
+        const int64_t window_bytes = a.s.B * (a.t - a.lo) * a.s.D * 4;
+        if (a.s.D % kFirBlk != 0)
+            fir_partial_kernel<kF32, false><<<g1, dim3(256), 0, stream>>>(a);
+        else if (window_bytes > (int64_t(256) << 20))
+            fir_partial_kernel<kF32, true, kFirBlk / 2><<<g1, dim3(256), 0, stream>>>(a);
+        else
+            fir_partial_kernel<kF32, false, kFirBlk / 2><<<g1, dim3(256), 0, stream>>>(a);
         fir_finish_kernel<kF32><<<g2, dim3(256), 0, stream>>>(a);
     }
     return hipGetLastError();

@@ -52,6 +52,30 @@ def test_fir_decode_small(act, window):
     assert rel_err(y_gpu, y_or) <= TOL[act]
 
 
+@pytest.mark.parametrize("window", [0, 17])
+def test_fir_decode_f32_block_split(window):
+    """float32 with D a multiple of the 512-channel block: a lane's two 4-channel
+    halves sit 256 channels apart, here in different heads (head dim 128)."""
+    torch = require_gpu()
+    B, D, H, d, L, S = 2, 1024, 8, 8, 100, 10
+    rng = np.random.default_rng(300 + window)
+    params = _params(rng, H, d)
+    q, k, v = (_rand(rng, (B, L + S, D), "f32") for _ in range(3))
+    h32 = oracle.filter_taps(params, L + S).astype(np.float32)
+    op = hb.ModalHyena(params.poles, params.residues, params.skip, B, D, "f32")
+    fir = hb.FirHyena(op, L + S)
+    log(f"fir f32 block split window={window}")
+    Q, K, V = (to_dev(a, "f32") for a in (q, k, v))
+    fir.fill(K[:, :L].contiguous(), V[:, :L].contiguous())
+    h = torch.from_numpy(h32).cuda()
+    ys = [fir.step(h, L + s, Q[:, L + s].contiguous(), K[:, L + s].contiguous(), V[:, L + s].contiguous(),
+                   window=window) for s in range(S)]
+    torch.cuda.synchronize()
+    y_gpu = np.stack([to_np64(t) for t in ys], 1)
+    y_or = oracle.fir_conv(h32.astype(np.float64), q, k, v, "f32", window=window, t_from=L)
+    assert rel_err(y_gpu, y_or) <= TOL["f32"]
+
+
 def test_fir_full_window_matches_modal_decode():
     """Over every past step, the explicit filter and the distilled recurrence are
     the same operator: the two GPU decode paths agree (float32 activations)."""
