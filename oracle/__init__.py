@@ -286,7 +286,7 @@ def dense(x: np.ndarray, w: np.ndarray) -> np.ndarray:
     return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
 
 
-def stack_layer(params, w_in, w_out, x_prompt, x_steps=None, eps: float = 1e-6):
+def stack_layer(params, w_in, w_out, x_prompt, x_steps=None, eps: float = 1e-6, _scan=None):
     """One layer of the projected stack in float64, teacher-forced.
 
     Layer input x (per token, width D) -> s = 1/rms(x) -> [q|k|v] = (x W_in^T) s
@@ -297,7 +297,11 @@ def stack_layer(params, w_in, w_out, x_prompt, x_steps=None, eps: float = 1e-6):
     [S][B][D] layer inputs of the generated steps (each one the actual input the
     layer received at that step).  Returns (out_prompt [B][L][D],
     out_steps [S][B][D] or None, state after the prompt, final state).
+    The generated steps continue the recurrence from the state the prompt left
+    (the decode step of the operator), so over prompt + steps the layer is the
+    same causal convolution as over one sequence of L + S tokens.
     """
+    scan = _scan or modal_scan
     D = x_prompt.shape[-1]
     w_in = bf16_to_f64(w_in) if w_in.dtype == np.uint16 else np.asarray(w_in, np.float64)
     w_out = bf16_to_f64(w_out) if w_out.dtype == np.uint16 else np.asarray(w_out, np.float64)
@@ -309,12 +313,12 @@ def stack_layer(params, w_in, w_out, x_prompt, x_steps=None, eps: float = 1e-6):
                 np.ascontiguousarray(qkv[..., 2 * D:]))
 
     q, k, v = project(x_prompt)
-    y, st_prompt = modal_scan(params, q, k, v)
+    y, st_prompt = scan(params, q, k, v)
     out_prompt = dense(y, w_out)
     out_steps, st = None, st_prompt
     if x_steps is not None:
         q, k, v = project(x_steps)
-        ys, st = modal_scan(params, q, k, v, state=st_prompt, batch_axis=1, time_axis=0)
+        ys, st = scan(params, q, k, v, state=st_prompt, batch_axis=1, time_axis=0)
         # ys is [B][S][D]; return step-major like the inputs
         out_steps = dense(np.ascontiguousarray(ys.transpose(1, 0, 2)), w_out)
     return out_prompt, out_steps, st_prompt, st
@@ -337,4 +341,4 @@ class Bound:
         return modal_scan(*a, _lib_handle=self._h, **kw)
 
     def stack_layer(self, *a, **kw):
-        raise NotImplementedError
+        return stack_layer(*a, _scan=self.modal_scan, **kw)

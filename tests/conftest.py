@@ -18,3 +18,17 @@ def oracle_lib():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Print the parity margins the GPU tests recorded (max err / max |oracle|)."""
+    try:
+        from _gpu_common import MARGINS
+    except ImportError:
+        return
+    if not MARGINS:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "parity: max |err| / max |oracle| (tolerance)")
+    for r in MARGINS:
+        tr.write_line(f"{r['case']:<44s} {r['phase']:<18s} {r['max_err_over_max_ref']:.3e}  (tol {r['tol']:.0e})")

@@ -307,6 +307,43 @@ def test_stack_layer_matches_unrolled_definition(oracle_lib):
     assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
+def test_stack_layer_generated_steps_match_unrolled_definition(oracle_lib):
+    """The generated-step leg of the projected layer: S steps fed one at a time
+    after an L-token prompt equal the unrolled definition over one sequence of
+    L + S tokens (rms -> in_proj -> brute-force causal convolution with the
+    closed-form filter -> out_proj), and the final state equals the Vandermonde
+    sum over all L + S inputs.  B != S and D != 3D, so a transposed [S][B][D]
+    output, a state not carried from the prompt, or steps projected without the
+    normalisation all change the result."""
+    rng = np.random.default_rng(13)
+    D, H, d, B, L, S = 8, 2, 3, 2, 20, 5
+    params = _random_params(rng, H, d, 0.6, 0.97)
+    w_in = rng.standard_normal((3 * D, D)) * 0.3
+    w_out = rng.standard_normal((D, D)) * 0.3
+    x_all = rng.standard_normal((B, L + S, D)) * rng.uniform(0.5, 2.0, (B, L + S, 1))
+    x_prompt = np.ascontiguousarray(x_all[:, :L])
+    x_steps = np.ascontiguousarray(x_all[:, L:].transpose(1, 0, 2))          # [S][B][D]
+    out_p, out_s, st_p, st_f = oracle_lib.stack_layer(params, w_in, w_out, x_prompt, x_steps)
+    s = 1 / np.sqrt((x_all ** 2).mean(-1, keepdims=True) + 1e-6)
+    qkv = np.einsum("btk,nk->btn", x_all, w_in) * s
+    q, k, v = qkv[..., :D], qkv[..., D:2 * D], qkv[..., 2 * D:]
+    ref = np.einsum("btk,nk->btn", _direct_conv(params, q, k, v), w_out)   # [B][L+S][D]
+    scale = np.max(np.abs(ref))
+    assert out_s.shape == (S, B, D)
+    assert np.max(np.abs(out_p - ref[:, :L])) <= 1e-12 * scale
+    assert np.max(np.abs(out_s - ref[:, L:].transpose(1, 0, 2))) <= 1e-12 * scale
+    # states: x_n after T inputs = sum_t lambda_n^(T-1-t) u_t, evaluated directly
+    lam = params.poles[..., 0].astype(np.float64) + 1j * params.poles[..., 1]
+    u = k * v
+    for T, st in ((L, st_p), (L + S, st_f)):
+        expo = (T - 1 - np.arange(T))[None, :]
+        for c in range(D):
+            g = c // (D // H)
+            ref_st = np.einsum("bt,nt->bn", u[:, :T, c], lam[g][:, None] ** expo)
+            got = st[:, c, :, 0] + 1j * st[:, c, :, 1]
+            assert np.max(np.abs(got - ref_st)) <= 1e-12 * np.max(np.abs(ref_st)), (T, c)
+
+
 def test_rms_and_dense_special_cases():
     """Pins of the projected stack's two helpers against closed forms, not their
     own formulas: a constant row has RMS |c|; a one-hot row of width n has RMS
@@ -420,6 +457,31 @@ def test_distill_gradient_matches_finite_differences(oracle_lib):
     fd = (loss_at(ModalParams(params.poles, params.residues, sp))[1] -
           loss_at(ModalParams(params.poles, params.residues, sm))[1]) / (2 * step)
     assert abs(fd - g_skip[1]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_distill_loss_and_gradient_hand_computed():
+    """A one-mode, three-tap case worked by hand: lambda = 0.5 + 0.5i,
+    R = 1 + 2i, D = 1 give hhat = [D, Re R, Re(R lambda)] = [1, 1, -0.5];
+    against the target [0.25, 0, 1] the residual is e = [0.75, 1, -1.5] and
+    J = 0.5625 + 1 + 2.25 = 3.8125.  By hand:
+      dJ/dD = 2 e0 = 1.5;
+      hhat[1] = Re R,  hhat[2] = Re R Re l - Im R Im l, so
+      dJ/dRe R = 2 (e1 + e2 Re l) = 0.5,   dJ/dIm R = 2 e2 (-Im l) = 1.5,
+      dJ/dRe l = 2 e2 Re R = -3,           dJ/dIm l = 2 e2 (-Im R) = 6.
+    Every value is a binary fraction, so float64 reproduces it exactly."""
+    import oracle
+    params = ModalParams(np.array([[[0.5, 0.5]]], np.float32), np.array([[[1.0, 2.0]]], np.float32),
+                         np.array([1.0], np.float32))
+    target = np.array([[0.25, 0.0, 1.0]])
+    loss, g_poles, g_res, g_skip = oracle.distill_loss_grad(params, target, 3)
+    assert loss[0] == 3.8125
+    assert g_skip[0] == 1.5
+    assert np.array_equal(g_res[0, 0], [0.5, 1.5])
+    assert np.array_equal(g_poles[0, 0], [-3.0, 6.0])
+    # two taps: lambda no longer enters, its gradient is exactly zero
+    loss2, g_poles2, g_res2, _ = oracle.distill_loss_grad(params, target[:, :2], 2)
+    assert loss2[0] == 0.5625 + 1.0
+    assert np.array_equal(g_poles2[0, 0], [0.0, 0.0]) and np.array_equal(g_res2[0, 0], [2.0, 0.0])
 
 
 def test_distill_zero_at_generating_parameters_and_hankel_rank(oracle_lib):

@@ -4,10 +4,15 @@ Each mutant is compiled from ``oracle/modal_oracle.c`` with one plausible
 mistake (a sign, an ordering, a dropped term, a wrong index), on the CPU.  The
 pins of ``test_oracle.py`` are then run against the mutant; at least one must
 fail.  This shows the pins constrain every part of the oracle's arithmetic.
+The projected layer (``oracle.stack_layer``, Python) gets the same treatment:
+its source is copied with one mistake planted and executed in the oracle
+module's namespace, and the stack pins must reject it.
 """
 
+import inspect
 import os
 import subprocess
+import textwrap
 
 import pytest
 
@@ -69,3 +74,55 @@ def test_unmutated_copy_passes_every_pin(tmp_path):
     copy = oracle.Bound(str(so))
     for pin in PIN_TESTS:
         pin(copy)
+
+
+# Mistakes planted in the Python source of oracle.stack_layer (generated-step leg
+# and its hand-off from the prompt).
+STACK_MUTANTS = {
+    "steps-start-from-zero-state": ("state=st_prompt, batch_axis=1", "state=None, batch_axis=1"),
+    "steps-output-reshaped-not-transposed": ("ys.transpose(1, 0, 2)",
+                                             "ys.reshape(ys.shape[1], ys.shape[0], ys.shape[2])"),
+    "steps-scanned-as-batch-major": ("batch_axis=1, time_axis=0", "batch_axis=0, time_axis=1"),
+    "final-state-is-prompt-state": ("return out_prompt, out_steps, st_prompt, st",
+                                    "return out_prompt, out_steps, st_prompt, st_prompt"),
+    "normalisation-dropped": ("dense(x, w_in) * rms_inv(x, eps)[..., None]", "dense(x, w_in)"),
+    "q-and-k-thirds-swapped": ("return (np.ascontiguousarray(qkv[..., :D]), np.ascontiguousarray(qkv[..., D:2 * D]),",
+                               "return (np.ascontiguousarray(qkv[..., D:2 * D]), np.ascontiguousarray(qkv[..., :D]),"),
+}
+
+STACK_PINS = [pins.test_stack_layer_matches_unrolled_definition,
+              pins.test_stack_layer_generated_steps_match_unrolled_definition]
+
+
+class _StackMutant:
+    """The oracle with its stack_layer replaced by a mutated copy."""
+
+    def __init__(self, old, new):
+        src = textwrap.dedent(inspect.getsource(oracle.stack_layer))
+        assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+        ns = dict(vars(oracle))
+        exec(compile(src.replace(old, new), "<stack_layer mutant>", "exec"), ns)
+        self.stack_layer = ns["stack_layer"]
+        self.modal_scan = oracle.modal_scan
+        self.filter_taps = oracle.filter_taps
+
+
+@pytest.mark.parametrize("name", sorted(STACK_MUTANTS))
+def test_stack_mutant_fails_a_pin(name):
+    mutant = _StackMutant(*STACK_MUTANTS[name])
+    failures = 0
+    for pin in STACK_PINS:
+        try:
+            pin(mutant)
+        except Exception:  # an assertion, or a shape the mistake made inconsistent
+            failures += 1
+    assert failures >= 1, f"no pin caught stack mutant {name}"
+
+
+def test_unmutated_stack_copy_passes_every_pin():
+    copy = _StackMutant("eps: float = 1e-6", "eps: float = 1e-6")
+    for pin in STACK_PINS:
+        pin(copy)
+    bound = oracle.Bound(oracle.build(force=False))
+    for pin in STACK_PINS:
+        pin(bound)
