@@ -24,6 +24,7 @@ HM_MAX_MODES = 64
 HM_F32, HM_BF16 = 0, 1
 HM_OK, HM_ERR_INVALID_ARG, HM_ERR_UNSUPPORTED, HM_ERR_WORKSPACE, HM_ERR_HIP = range(5)
 HM_PREFILL_AUTO, HM_PREFILL_SCAN, HM_PREFILL_MFMA = 0, 1, 2
+HM_NOALLOC_SCRATCH_BYTES = 16 << 20  # per-GPU scratch of hyena_modal_prefill_noalloc
 ALGOS = {"auto": HM_PREFILL_AUTO, "scan": HM_PREFILL_SCAN, "mfma": HM_PREFILL_MFMA}
 
 EXPORTS = (
@@ -34,6 +35,7 @@ EXPORTS = (
     "hyena_modal_prefill_plan",
     "hyena_modal_prefill",
     "hyena_modal_prefill_ex",
+    "hyena_modal_prefill_noalloc",
     "hyena_modal_decode_step",
     "hyena_filter_materialize",
     "hyena_row_rms",
@@ -116,6 +118,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "hyena_modal_prefill": ([D, i64, p, p, p, i64, p, i64, p, p, p, sz, p], ctypes.c_int),
             "hyena_modal_prefill_ex": ([D, i64, p, p, p, i64, p, i64, p, p, p, sz,
                                         ctypes.POINTER(hm_prefill_opts), p], ctypes.c_int),
+            "hyena_modal_prefill_noalloc": ([D, i64, p, p, p, i64, p, i64, p, p,
+                                             ctypes.POINTER(hm_prefill_opts), p], ctypes.c_int),
             "hyena_modal_decode_step": ([D, p, p, p, i64, p, i64, p, p], ctypes.c_int),
             "hyena_filter_materialize": ([D, i64, p, p], ctypes.c_int),
             "hyena_row_rms": ([p, i64, i64, i64, ctypes.c_float, p, p], ctypes.c_int),
@@ -230,6 +234,17 @@ def hyena_modal_prefill(desc: hm_desc, L, q, k, v, ld_in, y, ld_y, state_in, sta
     else:
         st = lib.hyena_modal_prefill(*args, _stream(stream))
     _check(st, "hyena_modal_prefill")
+
+
+def hyena_modal_prefill_noalloc(desc: hm_desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out,
+                                stream=None, chunk: int = 0, algo="auto") -> None:
+    """The prefill with the library's own per-GPU scratch as its workspace
+    (no allocation; calls that overlap on one GPU race)."""
+    o = _opts(chunk, algo)
+    st = load().hyena_modal_prefill_noalloc(ctypes.byref(desc), L, _ptr(q), _ptr(k), _ptr(v), ld_in, _ptr(y),
+                                            ld_y, _ptr(state_in), _ptr(state_out), ctypes.byref(o),
+                                            _stream(stream))
+    _check(st, "hyena_modal_prefill_noalloc")
 
 
 def hyena_modal_decode_step(desc: hm_desc, q, k, v, ld_in, y, ld_y, state, stream=None) -> None:

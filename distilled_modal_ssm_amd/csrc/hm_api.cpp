@@ -9,10 +9,37 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "hm_internal.hpp"
 
+// Device scratch of hyena_modal_prefill_noalloc: the prefill workspace for
+// callers that cannot allocate.  Each GPU the library runs on holds its own
+// copy of this array (HM_NOALLOC_SCRATCH_BYTES) from module load until the
+// process ends.  Host code never passes its name to a kernel: the name is a
+// host-side stand-in, and the device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[HM_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.  No allocation happens here.
+hm_status scratch_for_current_device(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return HM_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return HM_OK;
+}
 
 constexpr int64_t kMaxElems = int64_t(1) << 46;  // guard against int64 overflow in offsets
 
@@ -76,9 +103,12 @@ hm_status check_opts(const hm_prefill_opts *opts, int64_t *chunk, int *algo) {
     return HM_OK;
 }
 
+// use_scratch: take the workspace from the per-device `scratch` array instead
+// of the caller (workspace and ws_bytes are then ignored).
 hm_status prefill_impl(const hm_desc *desc, int64_t L, const void *q, const void *k, const void *v,
                        int64_t ld_in, void *y, int64_t ld_y, const float *state_in, float *state_out,
-                       void *workspace, size_t ws_bytes, void *stream, const hm_prefill_opts *opts) {
+                       void *workspace, size_t ws_bytes, void *stream, const hm_prefill_opts *opts,
+                       bool use_scratch = false) {
     hm_status st = check_desc(desc);
     if (st != HM_OK) return st;
     int64_t chunk;
@@ -107,11 +137,14 @@ hm_status prefill_impl(const hm_desc *desc, int64_t L, const void *q, const void
             !aligned(y, 16) || (ld_in * esz) % 16 != 0 || (ld_y * esz) % 16 != 0)
             return HM_ERR_UNSUPPORTED;
     }
-    if (s.B > 0 && plan.bytes > 0) {
+    if (use_scratch) {
+        if (s.B > 0 && plan.bytes > (size_t)HM_NOALLOC_SCRATCH_BYTES) return HM_ERR_WORKSPACE;
+    } else if (s.B > 0 && plan.bytes > 0) {
         if (!workspace || ws_bytes < plan.bytes) return HM_ERR_WORKSPACE;
         if (!aligned(workspace, 256)) return HM_ERR_UNSUPPORTED;
     }
     if (s.B == 0) return HM_OK;
+    if (use_scratch && (st = scratch_for_current_device(&workspace)) != HM_OK) return st;
     hm::PrefillArgs a;
     a.s = s;
     a.plan = plan;
@@ -201,6 +234,14 @@ hm_status hyena_modal_prefill_ex(const hm_desc *desc, int64_t L, const void *q, 
                                  size_t ws_bytes, const hm_prefill_opts *opts, void *stream) {
     return prefill_impl(desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out, workspace, ws_bytes,
                         stream, opts);
+}
+
+hm_status hyena_modal_prefill_noalloc(const hm_desc *desc, int64_t L, const void *q, const void *k,
+                                      const void *v, int64_t ld_in, void *y, int64_t ld_y,
+                                      const float *state_in, float *state_out,
+                                      const hm_prefill_opts *opts, void *stream) {
+    return prefill_impl(desc, L, q, k, v, ld_in, y, ld_y, state_in, state_out, nullptr, 0, stream, opts,
+                        /*use_scratch=*/true);
 }
 
 hm_status hyena_modal_decode_step(const hm_desc *desc, const void *q, const void *k, const void *v,

@@ -21,7 +21,9 @@
  *    owned by the caller.  The library never allocates or frees memory, keeps no
  *    pointer after returning, and never synchronises: work is enqueued on
  *    `stream` (a hipStream_t; NULL = the default stream) and completes
- *    asynchronously.  The library holds no mutable global state.
+ *    asynchronously.  The library holds no mutable global state, with one
+ *    exception: the per-GPU scratch array of hyena_modal_prefill_noalloc
+ *    (HM_NOALLOC_SCRATCH_BYTES on each device, for the life of the process).
  *  - Channel c (0 <= c < D) belongs to head g = c / (D / H).
  *  - Activations (q, k, v, y) are row-major: element (b, t, c) of a
  *    [B][T][width] tensor sits at element offset (b*T + t)*ld + c, where ld >= D
@@ -181,6 +183,31 @@ typedef struct hm_prefill_info {
 
 hm_status hyena_modal_prefill_plan(const hm_desc *desc, int64_t L, const hm_prefill_opts *opts,
                                    hm_prefill_info *info);
+
+/*
+ * The prefill of hyena_modal_prefill_ex without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that forbid hipMalloc).  The workspace comes from a scratch
+ * array inside the library, HM_NOALLOC_SCRATCH_BYTES on each GPU, held from
+ * library load until the process ends; its address on a device is looked up
+ * on the first call made with that device current.  The call allocates and
+ * frees nothing.
+ *   Arguments as hyena_modal_prefill_ex (opts may be NULL: automatic).
+ *   A plan whose workspace (hyena_modal_prefill_workspace_ex) exceeds
+ *   HM_NOALLOC_SCRATCH_BYTES -> HM_ERR_WORKSPACE, before any HIP call; other
+ *   errors as hyena_modal_prefill_ex.  A failed device lookup -> HM_ERR_HIP.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (two streams, two threads) race and give wrong results; calls on
+ * one stream are ordered and safe.  The scratch needs no clearing: every byte
+ * a call reads was written earlier in the same call.
+ */
+#define HM_NOALLOC_SCRATCH_BYTES (16 << 20) /* 16 MiB per GPU */
+
+hm_status hyena_modal_prefill_noalloc(const hm_desc *desc, int64_t L,
+                                      const void *q, const void *k, const void *v, int64_t ld_in,
+                                      void *y, int64_t ld_y,
+                                      const float *state_in, float *state_out,
+                                      const hm_prefill_opts *opts, void *stream);
 
 /*
  * One generation step for every batch row: reads the state before updating it,

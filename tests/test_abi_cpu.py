@@ -29,6 +29,8 @@ def _declared():
 
 def test_header_and_binding_agree():
     assert _declared() == set(hb.EXPORTS)
+    m = re.search(r"#define HM_NOALLOC_SCRATCH_BYTES \((\d+) << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == hb.HM_NOALLOC_SCRATCH_BYTES
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -410,3 +412,32 @@ def test_layer_step_and_pack_validation(lib):
             hb.hyena_pack_in_proj_bf16(*args, stream=0)
         assert e.value.status == status, args
     hb.hyena_pack_in_proj_bf16(0, 64, FAKE, 64, FAKE, stream=0)  # empty: no launch
+
+
+def test_noalloc_prefill_validation(lib):
+    """The allocation-free prefill validates like the workspace form, and a plan
+    whose workspace exceeds the built-in scratch is refused on the host."""
+    d = _desc(batch=2, channels=256, heads=2, modes=16)
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, ld_in=256, y=FAKE, ld_y=256, state_in=None, state_out=FAKE)
+
+    def call(dd=d, L=700, chunk=64, algo="scan", **kw):
+        a = dict(ok)
+        a.update(kw)
+        hb.hyena_modal_prefill_noalloc(dd, L, a["q"], a["k"], a["v"], a["ld_in"], a["y"], a["ld_y"],
+                                       a["state_in"], a["state_out"], stream=0, chunk=chunk, algo=algo)
+
+    for kw, status in [(dict(L=-1), hb.HM_ERR_INVALID_ARG), (dict(q=None), hb.HM_ERR_INVALID_ARG),
+                       (dict(state_out=None), hb.HM_ERR_INVALID_ARG), (dict(ld_y=8), hb.HM_ERR_INVALID_ARG),
+                       (dict(k=FAKE + 2), hb.HM_ERR_UNSUPPORTED), (dict(chunk=100), hb.HM_ERR_UNSUPPORTED),
+                       (dict(algo=7), hb.HM_ERR_INVALID_ARG)]:
+        with pytest.raises(hb.HMError) as e:
+            call(**kw)
+        assert e.value.status == status, kw
+    # the lane-scan plan of a long prompt in many chunks needs more than the scratch holds
+    big = _desc(batch=4, channels=4096, heads=32, modes=32)
+    assert hb.hyena_modal_prefill_workspace(big, 65536, chunk=2048, algo="scan") > 16 << 20
+    with pytest.raises(hb.HMError) as e:
+        call(dd=big, L=65536, chunk=2048, algo="scan", ld_in=4096, ld_y=4096)
+    assert e.value.status == hb.HM_ERR_WORKSPACE
+    # B = 0 enqueues nothing and needs no device
+    hb.hyena_modal_prefill_noalloc(_desc(batch=0), 128, None, None, None, 64, None, 64, None, None, stream=0)
