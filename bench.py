@@ -1,22 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the modal-SSM Hyena hot path on one MI355X.
 
-A step is one pass of the whole hot path over one batch of synthetic input:
-  1. materialise the first L filter taps of every head,
-  2. prefill over the L-token prompt -> y and the modal state: 64-step
-     sub-blocks as per-head Toeplitz / readout / Vandermonde products on the
-     matrix cores (the prompt split into chunks joined by a carry scan only when
-     batch x heads are too few to fill the GPU), or the vector-ALU modal scan for
-     shapes outside that path,
-  3. S generation steps (one decode launch per token, captured once in a HIP
-     graph and replayed), consuming the prefill state.
-Inputs are resident in HBM before the timed region starts.
+Default line (no arguments): the 24-layer projected stack at 1.3B width
+(B=64, D=2048, 16 heads, d=16, 2048-token prompt, 512 generated tokens fed
+back), which is the largest workload that fits one GPU.  A step is one pass
+of the whole hot path over one batch of synthetic input:
+  1. the prompt through all layers: per layer, the in_proj GEMM with the
+     per-token RMS fused, the modal prefill (64-step sub-blocks on the matrix
+     cores) and the out_proj GEMM;
+  2. S generated tokens, each through all layers (per layer: the fused
+     in_proj + decode-step kernel and the out_proj kernel), one HIP graph per
+     token captured once and replayed.
+Two operator workloads ride along in ``sub_workloads``, each timed the same
+way (filter taps, prefill, S decode steps as one graph replay):
+  batch256-decode-bf16 (the decode step that must stream HBM) and
+  long64k-f32 (the 64k-token prefill).
+``--config N`` runs a single workload (1-5) instead.
 
-Printed: one JSON line (last line of stdout).  value = whole-step tokens/s,
-B*(L+S) / step time; prefill and decode rates are reported beside it.
-The roofline object covers the kernel that dominates the step, measured live
-with HIP events on the stream the kernels run on; cpu_baseline times the float64
-oracle on this host's cores over the same workload (rank 0, N = 1 only).
+Inputs are resident in HBM before any timed region.  Every time comes from
+HIP events on the stream the library's kernels run on.  The ``roofline``
+object covers the unit of work that dominates each step; ``cpu_baseline``
+times the float64 oracle on this host over a bounded sample of the same
+workload, and the same oracle outputs give ``parity`` (max |err| / max
+|oracle| of the GPU's outputs on that sample).
 """
 
 from __future__ import annotations
@@ -29,6 +35,7 @@ import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -36,11 +43,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+METRIC = "decode tokens/sec and prefill tokens/sec at 1 GPU; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores
 VALU_F32_PEAK_TFLOPS = 78.6    # 256 CU x 64 lanes x 2 flop (FMA) x 2.4 GHz, unpacked float32
+TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 PROFILES = os.path.join(ROOT, "profiles")
-CSRC = os.path.join(ROOT, "distilled_modal_ssm_amd", "csrc")
+PKG = os.path.join(ROOT, "distilled_modal_ssm_amd")
+CSRC = os.path.join(PKG, "csrc")
 # Sources whose change invalidates a hardware-counter measurement of a kernel:
 # the kernel's own file (its code and launch configuration), the shared
 # device header and, where it adds flags for that file, the build script.
@@ -50,6 +61,52 @@ KERNEL_SOURCES = {
     "chunk_scan_kernel": ["prefill.hip", "hm_internal.hpp"],
 }
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read, 1 GiB written
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ provenance
+
+
+def source_fingerprint() -> str:
+    """sha256 (16 hex digits) over the library sources, the header, the Python
+    package and this file: identifies the code a result line came from, also
+    where no git metadata travels with the tree."""
+    files = sorted(glob.glob(os.path.join(CSRC, "*")) + glob.glob(os.path.join(ROOT, "include", "*.h")) +
+                   glob.glob(os.path.join(PKG, "*.py")) + [os.path.abspath(__file__)])
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def git_sha():
+    """HEAD's commit from .git when the tree has one (None elsewhere)."""
+    try:
+        head = open(os.path.join(ROOT, ".git", "HEAD")).read().strip()
+        if head.startswith("ref: "):
+            ref = head[5:]
+            p = os.path.join(ROOT, ".git", ref)
+            if os.path.exists(p):
+                return open(p).read().strip()
+            for line in open(os.path.join(ROOT, ".git", "packed-refs")):
+                if line.strip().endswith(ref):
+                    return line.split()[0]
+            return None
+        return head
+    except OSError:
+        return None
+
+
+def provenance() -> dict:
+    return {"git_sha": git_sha(), "source_fingerprint": source_fingerprint()}
+
+
+# ------------------------------------------------------------------ counter traffic
 
 
 def kernel_fingerprint(kernel: str) -> str:
@@ -161,8 +218,40 @@ def write_traffic(args):
     print(open(path).read())
 
 
-def log(*a):
-    print(*a, file=sys.stderr, flush=True)
+def write_trace_summary(args):
+    """Turn a rocprofv3 --kernel-trace --stats run of this benchmark into the
+    committed text summary: per-kernel calls and durations, plus the command."""
+    src, dst = args.summarize_trace
+    files = glob.glob(os.path.join(src, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {src}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    agg = {}
+    for r in rows:
+        a = agg.setdefault(r["Name"], [0, 0.0, float("inf"), 0.0])
+        n = int(r["Calls"])
+        a[0] += n
+        a[1] += float(r["TotalDurationNs"])
+        a[2] = min(a[2], float(r["MinNs"]))
+        a[3] = max(a[3], float(r["MaxNs"]))
+    total = sum(a[1] for a in agg.values())
+    lines = [f"# {args.summary_title or 'rocprofv3 kernel statistics'}", "",
+             "Command (run from the repository root on one MI355X):", "", f"    {args.traffic_cmd or '(not recorded)'}",
+             "", "rocprofv3 kernel statistics (durations per dispatch):", "",
+             f"{'kernel':<72s} {'calls':>7s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_ms':>9s} {'pct':>6s}"]
+    for name, a in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        short = name if len(name) <= 72 else name[:69] + "..."
+        lines.append(f"{short:<72s} {a[0]:>7d} {a[1] / a[0] / 1e3:>10.2f} {a[2] / 1e3:>10.2f} {a[3] / 1e3:>10.2f} "
+                     f"{a[1] / 1e6:>9.3f} {100 * a[1] / total:>6.2f}")
+    with open(dst, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(open(dst).read())
+
+
+# ------------------------------------------------------------------ arguments
 
 
 def parse():
@@ -170,204 +259,146 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", type=int, default=2, help="workload index (1-5; 5 = projected stack)")
-    ap.add_argument("--decode-mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--config", type=int, default=5, help="headline workload (1-5; 5 = projected stack)")
+    ap.add_argument("--sub", default=None,
+                    help="comma-separated operator workloads timed beside the headline "
+                         "(default: 3,4 with the stack headline, none otherwise; '' for none)")
+    ap.add_argument("--decode-mode", choices=["graph", "eager"], default="graph",
+                    help="generated steps as HIP graph replays (timing) or eager launches (counter runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-1thread", type=int, default=None, metavar="CONFIG",
                     help=argparse.SUPPRESS)  # child process of the one-thread CPU baseline
-    ap.add_argument("--no-fir", action="store_true", help="skip the explicit-filter decode baseline")
+    ap.add_argument("--no-extras", "--no-fir", dest="no_extras", action="store_true",
+                    help="skip the distillation, FFT-prefill and explicit-filter baselines")
     ap.add_argument("--json-out", default=None)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--fingerprint", action="store_true", help="print the source fingerprint and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="no GPU: write the traffic summary of --traffic-kernel from two rocprofv3 --pmc runs")
     ap.add_argument("--traffic-kernel", default="decode_step_fixed")
     ap.add_argument("--traffic-cmd", default=None, help="the profiling commands, ' ;; '-separated, for the summary")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_TXT"), default=None,
+                    help="no GPU: write a text summary of a rocprofv3 --kernel-trace --stats run "
+                         "(command from --traffic-cmd, title from --summary-title)")
+    ap.add_argument("--summary-title", default=None)
     return ap.parse_args()
 
 
-def cpu_baseline(cfg, params, inp, dec, min_seconds: float = 10.0):
-    """The float64 oracle (as it stands) on this host over the same workload:
-    the full step (filter, prefill, decode steps) repeated until ``min_seconds``
-    of CPU time have passed (at most 100 repetitions), on an evenly spaced
-    channel subset when one repetition of the whole width would be too long."""
-    import oracle
-    budget = 6e9  # mode-steps per repetition, ~1 s on 16 cores
+# ------------------------------------------------------------------ shared helpers
+
+
+def pct(x):
+    return {"p10": float(np.percentile(x, 10)), "p50": float(np.median(x)), "p90": float(np.percentile(x, 90))}
+
+
+def rel_err(got, ref) -> float:
+    scale = float(np.max(np.abs(ref))) if np.size(ref) else 0.0
+    if scale == 0.0:
+        return float(np.max(np.abs(got))) if np.size(got) else 0.0
+    return float(np.max(np.abs(got - ref))) / scale
+
+
+def to_f64(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def state_channels(state_t, chans, P) -> np.ndarray:
+    """[B][H][d][P][2] device state -> [B][len(chans)][d][2] float64 (the oracle's layout)."""
+    st = state_t.detach().cpu().numpy().astype(np.float64)
+    ch = np.asarray(chans)
+    return np.ascontiguousarray(st[:, ch // P, :, ch % P, :].transpose(1, 0, 2, 3))
+
+
+def channel_sample(cfg, budget):
+    """Evenly spaced channels so that the oracle's full step on them costs about
+    ``budget`` mode-steps (all channels when the budget allows)."""
     per_channel = cfg.B * (cfg.L + cfg.S) * cfg.d
     n_sel = int(min(cfg.D, max(1, budget // per_channel)))
-    chans = np.linspace(0, cfg.D - 1, n_sel).round().astype(np.int64) if n_sel < cfg.D else None
-    reps = 0
+    if n_sel >= cfg.D:
+        return np.arange(cfg.D, dtype=np.int64)
+    return np.linspace(0, cfg.D - 1, n_sel).round().astype(np.int64)
+
+
+def timed_events(stream, fn, n):
+    """n calls of fn bracketed by HIP events on `stream`; ms per call."""
+    import torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for e in ev:
+        e[0].record(stream)
+        fn()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+# ------------------------------------------------------------------ operator workloads
+
+
+def operator_cpu_baseline(cfg, params, inp, dec, gpu_sample, min_seconds: float = 10.0):
+    """The float64 oracle (as it stands) on this host over the same workload: the
+    full step (filter, prefill, decode steps) repeated until ``min_seconds`` of
+    CPU time have passed (at most 100 repetitions), on an evenly spaced channel
+    subset when one repetition of the whole width would be too long.  The first
+    repetition's outputs are compared with the GPU's on the same channels."""
+    import oracle
+    chans = channel_sample(cfg, 6e9)  # ~1 s per repetition on 16 cores
+    sel = None if len(chans) == cfg.D else chans
+    reps, first = 0, None
     t0 = time.perf_counter()
     while reps < 100 and (reps == 0 or time.perf_counter() - t0 < min_seconds):
         oracle.filter_taps(params, cfg.L)
-        _, st = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"], channels=chans)
-        oracle.modal_scan(params, dec["q"], dec["k"], dec["v"], state=st, channels=chans,
-                          batch_axis=1, time_axis=0)
+        y, st = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"], channels=sel)
+        yd, st2 = oracle.modal_scan(params, dec["q"], dec["k"], dec["v"], state=st, channels=sel,
+                                    batch_axis=1, time_axis=0)
+        if first is None:
+            first = (y, yd, st2)
         reps += 1
     dt = time.perf_counter() - t0
-    tokens = cfg.B * (cfg.L + cfg.S) * (n_sel / cfg.D) * reps
+    tokens = cfg.B * (cfg.L + cfg.S) * (len(chans) / cfg.D) * reps
     sample = (f"full step (filter, prefill L={cfg.L}, {cfg.S} decode steps) for "
-              f"{'all' if n_sel == cfg.D else n_sel} of {cfg.D} channels x {cfg.B} rows, {reps} repetition(s), "
+              f"{'all' if sel is None else len(chans)} of {cfg.D} channels x {cfg.B} rows, {reps} repetition(s), "
               f"{dt:.1f} s; tokens scaled by the channel fraction")
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+    base = {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
             "sample": sample}
-
-
-def emit(args, res):
-    line = json.dumps(res)
-    if args.json_out:
-        with open(args.json_out, "w") as f:
-            f.write(line + "\n")
-    print(line, flush=True)
-
-
-def stack_cpu_baseline(cfg, layers, x0):
-    """The float64 oracle on a bounded sample of the stack: one batch row through
-    the first two layers, over the prompt and then all S generated steps whose
-    inputs are that sample's own outputs fed back (as on the GPU)."""
-    import oracle
-    nl, steps, D = 2, cfg.S, cfg.D
-    w64 = [(oracle.bf16_to_f64(w_in), oracle.bf16_to_f64(w_out)) for _, w_in, w_out in layers[:nl]]
-    t0 = time.perf_counter()
-    cur, states = x0[:1], []
-    for l in range(nl):
-        out, _, st, _ = oracle.stack_layer(layers[l][0], w64[l][0], w64[l][1], cur)
-        states.append(st)
-        cur = out
-    xt = cur[:, -1, :]
-    for _ in range(steps):
-        for l in range(nl):
-            qkv = oracle.dense(xt, w64[l][0]) * oracle.rms_inv(xt)[..., None]
-            q, k, v = (np.ascontiguousarray(qkv[:, None, i * D:(i + 1) * D]) for i in range(3))
-            y, states[l] = oracle.modal_scan(layers[l][0], q, k, v, state=states[l])
-            xt = oracle.dense(y[:, 0, :], w64[l][1])
-    dt = time.perf_counter() - t0
-    tokens = (cfg.L + steps) * nl / cfg.layers  # one row, scaled by the layer fraction
-    return {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"1 of {cfg.B} batch rows, layers 0-1 of {cfg.layers}, {cfg.L}-token prompt + {steps} "
-                      f"generated steps, {dt:.1f} s; tokens scaled by the layer fraction"}
-
-
-def stack_token_bytes(cfg) -> int:
-    """HBM bytes a generated token of the projected stack must move: per layer the
-    bf16 weights (W_in 3D x D, W_out D x D), the modal state read and written
-    (16 d bytes per row and channel), and the bf16 activations: the layer input
-    read, the operator output written and read back by out_proj, the layer
-    output written (q, k, v stay on chip in the fused step)."""
-    D, B = cfg.D, cfg.B
-    return cfg.layers * (4 * D * D * 2 + B * D * 16 * cfg.d + 4 * B * D * 2)
-
-
-def bench_stack(args, cfg, dev):
-    """Projected stack: prefill through all layers, then S generated tokens per
-    batch row (one HIP graph per generated token, replayed)."""
-    import torch
-    from distilled_modal_ssm_amd.stack import HyenaStack
-    from workloads import dense_weights, modal_params, stack_prompt
-    layers = [(modal_params(cfg, l), *dense_weights(cfg, l)) for l in range(cfg.layers)]
-    st = HyenaStack(layers, cfg.B, cfg.L, device=dev)
-    x0 = stack_prompt(cfg)
-    X = torch.from_numpy(x0.view(np.int16)).view(torch.bfloat16).to(dev)
-    stream = torch.cuda.current_stream()
-
-    # capture one generated token (all layers) once
-    out = st.prefill(X)
-    st.start_generation(out)
-    st.decode_step()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        st.decode_step()
-    torch.cuda.synchronize()
-
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        o = st.prefill(X)
-        st.start_generation(o)
-        if ev:
-            ev[1].record(stream)
-        for _ in range(cfg.S):
-            graph.replay()
-        if ev:
-            ev[2].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_step = start.elapsed_time(stop) / args.steps
-    ph = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in evs])
-    ms_prefill, ms_decode = float(np.median(ph[:, 0])), float(np.median(ph[:, 1]))
-    ms_tok = ms_decode / cfg.S
-    M = cfg.B * cfg.L
-    D = cfg.D
-    gemm_flops = cfg.layers * 2 * M * D * 4 * D          # in_proj (3D) + out_proj (D)
-    hyena_flops = cfg.layers * (12 * cfg.d + 5) * M * D
-    decode_bytes = stack_token_bytes(cfg)
-    prefill_tf = (gemm_flops + hyena_flops) / ms_prefill * 1e-9
-    decode_gbs = decode_bytes / ms_tok * 1e-6
-    if ms_prefill >= ms_decode:
-        roof = {"bound": "mfma", "achieved": round(gemm_flops / ms_prefill * 1e-9, 2), "peak": 2500.0,
-                "unit": "TFLOP/s", "kernel": "prefill (gemm_tiled dominant)", "launch_ms": round(ms_prefill, 4)}
-        roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    else:
-        roof = {"bound": "hbm", "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "kernel": "generated token (weights + state stream)", "launch_ms": round(ms_tok, 5)}
-        roof["frac"] = round(decode_gbs / HBM_PEAK_GBS, 4)
-    roof["traffic"] = None
-    res = {
-        "metric": "decode tokens/sec and prefill tokens/sec at 1 GPU; % of HBM roofline",
-        "value": cfg.B * (cfg.L + cfg.S) / (ms_step / 1e3), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {cfg.describe()}", "B": cfg.B, "D": cfg.D, "H": cfg.H, "d": cfg.d,
-                   "L": cfg.L, "S": cfg.S, "layers": cfg.layers, "act_dtype": cfg.act,
-                   "decode_mode": "graph per generated token"},
-        "prefill_tokens_per_s": M / (ms_prefill / 1e3),
-        "decode_tokens_per_s": cfg.B / (ms_tok / 1e3),
-        "phase_ms": {"prefill": ms_prefill, "decode_total": ms_decode, "decode_per_token": ms_tok},
-        "prefill_rates": {"TFLOPs": prefill_tf, "mfma_frac_of_gemm_flops": gemm_flops / ms_prefill * 1e-9 / 2500.0},
-        "decode_rates": {"hbm_GBs": decode_gbs, "hbm_frac": decode_gbs / HBM_PEAK_GBS},
-        "roofline": roof,
-    }
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (float64 oracle, sampled)")
-        res["cpu_baseline"] = stack_cpu_baseline(cfg, layers, x0)
-    emit(args, res)
+    g_y, g_yd, g_st = gpu_sample(chans)
+    tol = TOL[cfg.act]
+    parity = {"sample": f"the cpu_baseline's first repetition: {len(chans)} channels x all {cfg.B} rows, "
+                        f"every prompt position and generated step",
+              "prefill_y": rel_err(g_y, first[0]), "decode_y": rel_err(g_yd, first[1]),
+              "final_state": rel_err(g_st, first[2]), "tolerance": tol}
+    parity["pass"] = bool(max(parity["prefill_y"], parity["decode_y"], parity["final_state"]) <= tol)
+    return base, parity
 
 
 def cpu_one_thread(ci: int, min_seconds: float = 5.0):
     """Child process of the CPU baseline (started with OMP_NUM_THREADS=1, no
-    GPU use): the oracle's full step on an evenly spaced channel subset,
-    repeated for ``min_seconds``; prints one JSON line."""
+    GPU use): the oracle's full step on one batch row and an evenly spaced
+    channel subset, repeated for ``min_seconds``; prints one JSON line."""
+    import dataclasses
+
     import oracle
     from workloads import decode_inputs, get_config, modal_params, prompt_inputs
     cfg = get_config(ci)
     params = modal_params(cfg)
-    inp, dec = prompt_inputs(cfg), decode_inputs(cfg)
-    per_channel = cfg.B * (cfg.L + cfg.S) * cfg.d
-    n_sel = int(min(cfg.D, max(1, 2e8 // per_channel)))
-    chans = np.linspace(0, cfg.D - 1, n_sel).round().astype(np.int64) if n_sel < cfg.D else None
+    inp = prompt_inputs(cfg, batches=[0])
+    dec = decode_inputs(cfg)
+    dec = {k: np.ascontiguousarray(v[:, :1]) for k, v in dec.items()}
+    one = dataclasses.replace(cfg, B=1)
+    chans = channel_sample(one, 2e8)
+    sel = None if len(chans) == cfg.D else chans
     reps, t0 = 0, time.perf_counter()
     while reps < 100 and (reps == 0 or time.perf_counter() - t0 < min_seconds):
         oracle.filter_taps(params, cfg.L)
-        _, st = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"], channels=chans)
-        oracle.modal_scan(params, dec["q"], dec["k"], dec["v"], state=st, channels=chans,
+        _, st = oracle.modal_scan(params, inp["q"], inp["k"], inp["v"], channels=sel)
+        oracle.modal_scan(params, dec["q"], dec["k"], dec["v"], state=st, channels=sel,
                           batch_axis=1, time_axis=0)
         reps += 1
     dt = time.perf_counter() - t0
-    print(json.dumps({"value": cfg.B * (cfg.L + cfg.S) * (n_sel / cfg.D) * reps / dt, "unit": "tokens/s",
+    print(json.dumps({"value": (cfg.L + cfg.S) * (len(chans) / cfg.D) * reps / dt, "unit": "tokens/s",
                       "cores": oracle.threads(),
-                      "sample": f"full step for {n_sel} of {cfg.D} channels x {cfg.B} rows, {reps} repetition(s), "
-                                f"{dt:.1f} s; tokens scaled by the channel fraction"}))
+                      "sample": f"full step for batch row 0, {len(chans)} of {cfg.D} channels, {reps} "
+                                f"repetition(s), {dt:.1f} s; tokens scaled by the channel fraction"}))
 
 
 def cpu_baseline_one_thread(cfg):
@@ -383,32 +414,14 @@ def cpu_baseline_one_thread(cfg):
         return {"error": f"{type(e).__name__}: {e}"}
 
 
-def main():
-    args = parse()
-    if args.traffic_from:
-        return write_traffic(args)
-    if args.cpu_1thread is not None:
-        return cpu_one_thread(args.cpu_1thread)
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the path would shard by batch rows and heads, with no communication)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def run_operator(args, cfg, dev) -> dict:
+    """One operator workload: filter taps, prefill, S decode steps per step."""
     import torch
     from distilled_modal_ssm_amd import ModalHyena
-    from workloads import decode_inputs, get_config, modal_params, prompt_inputs
+    from distilled_modal_ssm_amd import binding as hb
+    from workloads import decode_inputs, modal_params, prompt_inputs
 
-    if not torch.cuda.is_available():
-        log("bench.py needs a GPU")
-        sys.exit(1)
-    cfg = get_config(args.config)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    log(f"[bench] workload {cfg.index} {cfg.describe()}")
-    if cfg.layers:
-        return bench_stack(args, cfg, dev)
-
+    log(f"[bench] workload {cfg.index} {cfg.describe()}: inputs")
     params = modal_params(cfg)
     inp = prompt_inputs(cfg)
     dec = decode_inputs(cfg)
@@ -427,8 +440,7 @@ def main():
     state = op.new_state()
     h = torch.empty((cfg.H, cfg.L), dtype=torch.float32, device=dev)
     op.workspace(cfg.L)  # allocate once, outside the timed region
-
-    from distilled_modal_ssm_amd import binding as hb
+    stream = torch.cuda.current_stream()
 
     def filter_call():
         hb.hyena_filter_materialize(op.desc, cfg.L, h)
@@ -440,7 +452,7 @@ def main():
         for s in range(cfg.S):
             op.decode_step(dq[s], dk[s], dv[s], state, y=ys[s])
 
-    stream = torch.cuda.current_stream()
+    log(f"[bench] workload {cfg.index}: timing")
     if args.decode_mode == "graph":
         prefill_call()
         decode_eager()  # warm the launch path before capture
@@ -469,106 +481,86 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
         step(evs[i])
     stop.record(stream)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(stop)
-    ms_step = ms_total / args.steps
+    ms_step = start.elapsed_time(stop) / args.steps
     ph = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])] for e in evs])
     ms_filter, ms_prefill, ms_decode = (float(np.median(ph[:, i])) for i in range(3))
     ms_decode_launch = ms_decode / cfg.S
 
-    # outside the timed region: 20 prefill calls alone, and 10 replays of the
-    # S-step decode graph (per-launch spread of the decode kernel: see the
-    # rocprofv3 kernel-trace summaries, which time every dispatch)
-    torch.cuda.synchronize()
-    pf_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
-    for e in pf_ev:
-        e[0].record(stream)
-        prefill_call()
-        e[1].record(stream)
-    dg_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
-    for e in dg_ev:
-        e[0].record(stream)
-        decode_call()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    pf_ms = np.array([a.elapsed_time(b) for a, b in pf_ev])
-    dec_us = np.array([a.elapsed_time(b) * 1e3 / cfg.S for a, b in dg_ev])
-    pct = lambda x: {"p10": float(np.percentile(x, 10)), "p50": float(np.median(x)), "p90": float(np.percentile(x, 90))}
+    # outside the timed region: spreads of the prefill call and of the decode block
+    pf_ms = timed_events(stream, prefill_call, 20 if cfg.L * cfg.B * cfg.D < 2 ** 30 else 5)
+    dec_us = timed_events(stream, decode_call, 10) * 1e3 / cfg.S
 
     E = cfg.B * cfg.L * cfg.D
     sb = cfg.act_bytes
     decode_bytes = cfg.B * cfg.D * (16 * cfg.d + 4 * sb)
-    prefill_flops = (12 * cfg.d + 5) * E
     prefill_bytes = 4 * sb * E + 8 * cfg.B * cfg.D * cfg.d
+    prefill_flops = (12 * cfg.d + 5) * E
     plan = op.plan(cfg.L)
     if plan["algo"] == "mfma":
-        # matrix-core sub-blocks: the products are a few % of the bf16 MFMA peak;
-        # the pass streams q, k, v, y once, so HBM bounds it
-        prefill_roof = dict(bound="hbm", unit="GB/s", per_launch=prefill_bytes, peak=HBM_PEAK_GBS)
+        # matrix-core sub-blocks: the products are a few % of the MFMA peak and
+        # the pass streams q, k, v and y once, so HBM bounds it
+        prefill_roof = dict(bound="hbm", unit="GB/s", per_launch=prefill_bytes, peak=HBM_PEAK_GBS,
+                            kernel="chunk_mfma_kernel")
+        prefill_rates = {"hbm_GBs": prefill_bytes / ms_prefill * 1e-6,
+                         "hbm_frac": prefill_bytes / ms_prefill * 1e-6 / HBM_PEAK_GBS}
     else:
         # vector scan: one complex FMA pair per mode and step, on the vector ALUs
-        prefill_roof = dict(bound="alu", unit="TFLOP/s", per_launch=prefill_flops, peak=VALU_F32_PEAK_TFLOPS)
-    kernels = {
+        prefill_roof = dict(bound="alu", unit="TFLOP/s", per_launch=prefill_flops, peak=VALU_F32_PEAK_TFLOPS,
+                            kernel="chunk_scan_kernel")
+        prefill_rates = {"alu_TFLOPs": prefill_flops / ms_prefill * 1e-9,
+                         "alu_frac": prefill_flops / ms_prefill * 1e-9 / VALU_F32_PEAK_TFLOPS,
+                         "hbm_GBs": prefill_bytes / ms_prefill * 1e-6,
+                         "hbm_frac": prefill_bytes / ms_prefill * 1e-6 / HBM_PEAK_GBS}
+    units = {
         "decode_step": dict(bound="hbm", unit="GB/s", per_launch=decode_bytes, ms=ms_decode_launch,
-                            total_ms=ms_decode, peak=HBM_PEAK_GBS),
+                            total_ms=ms_decode, peak=HBM_PEAK_GBS, kernel="decode_step_fixed"),
         "prefill": dict(ms=ms_prefill, total_ms=ms_prefill, **prefill_roof),
     }
-    dom_name = max(kernels, key=lambda n: kernels[n]["total_ms"])
-    dom = kernels[dom_name]
+    dom = units[max(units, key=lambda n: units[n]["total_ms"])]
     scale = 1e-6 if dom["unit"] == "GB/s" else 1e-9  # bytes/ms -> GB/s ; flops/ms -> TFLOP/s
     achieved = dom["per_launch"] / dom["ms"] * scale
-    kname = "decode_step_fixed" if dom_name == "decode_step" else (
-        "chunk_mfma_kernel" if plan["algo"] == "mfma" else "chunk_scan_kernel")
     roofline = {"bound": dom["bound"], "achieved": round(achieved, 3), "peak": dom["peak"],
                 "unit": dom["unit"], "frac": round(achieved / dom["peak"], 4),
-                "traffic": read_traffic(kname, cfg.name),
-                "kernel": kname, "launch_ms": round(dom["ms"], 6),
-                "algorithmic_bytes_per_launch": decode_bytes if dom_name == "decode_step" else prefill_bytes}
-
-    tokens = cfg.B * (cfg.L + cfg.S)
+                "traffic": read_traffic(dom["kernel"], cfg.name),
+                "kernel": dom["kernel"], "launch_ms": round(dom["ms"], 6),
+                ("algorithmic_bytes_per_launch" if dom["unit"] == "GB/s" else "algorithmic_flops_per_launch"):
+                    dom["per_launch"]}
+    notes = []
+    if cfg.act == "f32" and plan["algo"] == "mfma":
+        notes.append("float32 activations and state; the prefill's matrix-core products take every operand "
+                     "as a sum of three bfloat16 parts (hi + mid + lo) with float32 accumulation")
+    if decode_bytes < 64e6:
+        notes.append("the decode step's state and activations fit in L2 and the Infinity Cache: its time is "
+                     "set by dispatch latency, not HBM")
     res = {
-        "metric": "decode tokens/sec and prefill tokens/sec at 1 GPU; % of HBM roofline",
-        "value": tokens / (ms_step / 1e3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "workload": f"{cfg.name}: {cfg.describe()}",
+        "config": {"workload": cfg.name, "B": cfg.B, "D": cfg.D, "H": cfg.H, "d": cfg.d, "L": cfg.L, "S": cfg.S,
+                   "act_dtype": cfg.act, "decode_mode": args.decode_mode},
+        "dtype": cfg.act,
+        "tokens_per_s": cfg.B * (cfg.L + cfg.S) / (ms_step / 1e3),
         "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: {cfg.describe()}", "B": cfg.B, "D": cfg.D, "H": cfg.H,
-                   "d": cfg.d, "L": cfg.L, "S": cfg.S, "act_dtype": cfg.act,
-                   "decode_mode": args.decode_mode},
         "prefill_plan": plan,
         "prefill_tokens_per_s": cfg.B * cfg.L / (ms_prefill / 1e3),
         "decode_tokens_per_s": cfg.B / (ms_decode_launch / 1e3),
         "phase_ms": {"filter": ms_filter, "prefill": ms_prefill, "decode_total": ms_decode,
                      "decode_per_step": ms_decode_launch},
         "decode_step_us_per_replay": pct(dec_us),
-        "prefill_ms_20_calls": pct(pf_ms),
-        "prefill_rates": {"alu_TFLOPs": prefill_flops / ms_prefill * 1e-9,
-                          "alu_frac": prefill_flops / ms_prefill * 1e-9 / VALU_F32_PEAK_TFLOPS,
-                          "hbm_GBs": prefill_bytes / ms_prefill * 1e-6,
-                          "hbm_frac": prefill_bytes / ms_prefill * 1e-6 / HBM_PEAK_GBS},
+        "prefill_ms_per_call": pct(pf_ms),
+        "prefill_rates": prefill_rates,
         "decode_rates": {"hbm_GBs": decode_bytes / ms_decode_launch * 1e-6,
                          "hbm_frac": decode_bytes / ms_decode_launch * 1e-6 / HBM_PEAK_GBS},
-        "wall_s_timed": t_wall,
         "roofline": roofline,
+        "notes": notes,
     }
-    if not args.no_fir:
+    if not args.no_extras:
         res["distill"] = distill_bench(cfg, params, stream)
         res["fft_prefill"] = fft_prefill_baseline(cfg, op, q, k, v, ms_prefill, stream)
         for window in (0, 256):
@@ -577,10 +569,268 @@ def main():
     if args.calibrate_copy:
         calibration_copy()
     if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (float64 oracle)")
-        res["cpu_baseline"] = cpu_baseline(cfg, params, inp, dec)
+        # one more whole step, so that y, ys and state hold exactly one step's
+        # outputs (the spreads above replayed the decode block on top of it)
+        step()
+        torch.cuda.synchronize()
+
+        def gpu_sample(chans):
+            ct = torch.as_tensor(chans, device=dev)
+            return (to_f64(y.index_select(2, ct)), to_f64(ys.index_select(2, ct)).transpose(1, 0, 2),
+                    state_channels(state, chans, cfg.P))
+
+        log(f"[bench] workload {cfg.index}: cpu baseline (float64 oracle) and parity")
+        res["cpu_baseline"], res["parity"] = operator_cpu_baseline(cfg, params, inp, dec, gpu_sample)
         res["cpu_baseline"]["one_thread"] = cpu_baseline_one_thread(cfg)
-    emit(args, res)
+    del q, k, v, dq, dk, dv, y, ys
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ projected stack
+
+
+def stack_token_bytes(cfg) -> int:
+    """HBM bytes a generated token of the projected stack must move: per layer the
+    bf16 weights (W_in 3D x D, W_out D x D), the modal state read and written
+    (16 d bytes per row and channel), and the bf16 activations: the layer input
+    read, the operator output written and read back by out_proj, the layer
+    output written (q, k, v stay on chip in the fused step)."""
+    D, B = cfg.D, cfg.B
+    return cfg.layers * (4 * D * D * 2 + B * D * 16 * cfg.d + 4 * B * D * 2)
+
+
+def stack_cpu_baseline(cfg, layers, rec_prompt, rec_steps, rows, min_seconds: float = 10.0):
+    """The float64 oracle on a bounded sample of the stack: layers 0, 1, ... in
+    turn (until ``min_seconds`` have passed, at least two) for the recorded
+    batch rows, each layer teacher-forced on the inputs the GPU's layer
+    received (the prompt and all S generated steps).  Tokens are scaled by the
+    row and layer fractions; the same outputs give the per-layer parity of the
+    GPU's layer outputs."""
+    import oracle
+    errs = []
+    t0 = time.perf_counter()
+    for l in range(cfg.layers):
+        if l >= 2 and time.perf_counter() - t0 >= min_seconds:
+            break
+        p, w_in, w_out = layers[l]
+        out_p, out_s, _, _ = oracle.stack_layer(p, oracle.bf16_to_f64(w_in), oracle.bf16_to_f64(w_out),
+                                                rec_prompt[l], rec_steps[l])
+        errs.append((rel_err(oracle.bf16_to_f64(rec_prompt[l + 1]), out_p),
+                     rel_err(oracle.bf16_to_f64(rec_steps[l + 1]), out_s)))
+    dt = time.perf_counter() - t0
+    nl = len(errs)
+    tokens = len(rows) * (cfg.L + cfg.S) * nl / cfg.layers
+    sample = (f"batch rows {list(map(int, rows))} of {cfg.B}, layers 0-{nl - 1} of {cfg.layers}, each "
+              f"teacher-forced on the GPU's inputs over the {cfg.L}-token prompt and {cfg.S} generated steps")
+    base = {"value": tokens / dt, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{sample}, {dt:.1f} s; tokens scaled by the row and layer fractions"}
+    worst = max(max(e) for e in errs)
+    parity = {"sample": sample,
+              "per_layer": [{"layer": l, "prompt_out": e[0], "generated_out": e[1]} for l, e in enumerate(errs)],
+              "worst": worst, "tolerance": TOL["bf16"], "pass": bool(worst <= TOL["bf16"])}
+    return base, parity
+
+
+def run_stack(args, cfg, dev) -> dict:
+    """Projected stack: prefill through all layers, then S generated tokens per
+    batch row (one HIP graph per generated token, replayed; or eager)."""
+    import torch
+    from distilled_modal_ssm_amd.stack import HyenaStack
+    from workloads import dense_weights, modal_params, stack_prompt
+
+    log(f"[bench] workload {cfg.index} {cfg.describe()}: weights and prompt")
+    with ThreadPoolExecutor(8) as ex:
+        ws = list(ex.map(lambda l: dense_weights(cfg, l), range(cfg.layers)))
+    layers = [(modal_params(cfg, l), *ws[l]) for l in range(cfg.layers)]
+    del ws
+    st = HyenaStack(layers, cfg.B, cfg.L, device=dev)
+    x0 = stack_prompt(cfg)
+    X = torch.from_numpy(x0.view(np.int16)).view(torch.bfloat16).to(dev)
+    stream = torch.cuda.current_stream()
+
+    log(f"[bench] workload {cfg.index}: timing ({args.decode_mode} generation)")
+    out = st.prefill(X)
+    st.start_generation(out)
+    st.decode_step()
+    torch.cuda.synchronize()
+    if args.decode_mode == "graph":
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            st.decode_step()
+        torch.cuda.synchronize()
+        token_call = graph.replay
+    else:
+        token_call = st.decode_step
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        o = st.prefill(X)
+        st.start_generation(o)
+        if ev:
+            ev[1].record(stream)
+        for _ in range(cfg.S):
+            token_call()
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    ph = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in evs])
+    ms_prefill, ms_decode = float(np.median(ph[:, 0])), float(np.median(ph[:, 1]))
+    ms_tok = ms_decode / cfg.S
+
+    M, D = cfg.B * cfg.L, cfg.D
+    gemm_flops = cfg.layers * 2 * M * D * 4 * D          # in_proj (3D) + out_proj (D)
+    hyena_flops = cfg.layers * (12 * cfg.d + 5) * M * D
+    token_bytes = stack_token_bytes(cfg)
+    decode_gbs = token_bytes / ms_tok * 1e-6
+    gemm_tf = gemm_flops / ms_prefill * 1e-9
+    if ms_prefill >= ms_decode:
+        roof = {"bound": "mfma", "achieved": round(gemm_tf, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "kernel": "prompt through all layers (in_proj/out_proj GEMMs dominant)",
+                "launch_ms": round(ms_prefill, 4), "algorithmic_flops_per_launch": gemm_flops}
+    else:
+        roof = {"bound": "hbm", "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "kernel": f"generated token: one graph launch of {cfg.layers} x (fused in_proj + decode step, "
+                          f"out_proj)",
+                "launch_ms": round(ms_tok, 5), "algorithmic_bytes_per_launch": token_bytes}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+
+    # outside the timed region: the generation kernels alone, each captured
+    # 24 times over the layers (cache-cold weights, as in the stack) and
+    # replayed; the prompt GEMMs of one layer eagerly
+    kern = stack_kernel_breakdown(cfg, st, X, stream)
+
+    res = {
+        "workload": f"{cfg.name}: {cfg.describe()}",
+        "config": {"workload": cfg.name, "B": cfg.B, "D": cfg.D, "H": cfg.H, "d": cfg.d, "L": cfg.L, "S": cfg.S,
+                   "layers": cfg.layers, "act_dtype": cfg.act,
+                   "decode_mode": "graph per generated token" if args.decode_mode == "graph" else "eager"},
+        "dtype": "bf16",
+        "tokens_per_s": cfg.B * (cfg.L + cfg.S) / (ms_step / 1e3),
+        "ms_per_step": ms_step,
+        "prefill_tokens_per_s": M / (ms_prefill / 1e3),
+        "decode_tokens_per_s": cfg.B / (ms_tok / 1e3),
+        "phase_ms": {"prefill": ms_prefill, "decode_total": ms_decode, "decode_per_token": ms_tok},
+        "prefill_rates": {"gemm_TFLOPs": gemm_tf, "gemm_mfma_frac": gemm_tf / MFMA_BF16_PEAK_TFLOPS,
+                          "all_TFLOPs": (gemm_flops + hyena_flops) / ms_prefill * 1e-9},
+        "decode_rates": {"hbm_GBs": decode_gbs, "hbm_frac": decode_gbs / HBM_PEAK_GBS,
+                         "algorithmic_bytes_per_token": token_bytes},
+        "kernels": kern,
+        "roofline": roof,
+    }
+    if args.calibrate_copy:
+        calibration_copy()
+    if not args.no_cpu_baseline:
+        log(f"[bench] workload {cfg.index}: recording layer inputs for the oracle sample")
+        rows = np.array([5, 58])
+        rec_p, rec_s = stack_record(cfg, st, X, rows, cfg.layers)
+        log(f"[bench] workload {cfg.index}: cpu baseline (float64 oracle, sampled) and parity")
+        res["cpu_baseline"], res["parity"] = stack_cpu_baseline(cfg, layers, rec_p, rec_s, rows)
+    del st, X
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def stack_record(cfg, st, X, rows, nl):
+    """One untimed pass (prompt, then S generated tokens, eager) that copies the
+    inputs of layers 0..nl (the outputs of layers 0..nl-1) for ``rows``."""
+    import torch
+    rt = torch.as_tensor(rows, device=X.device)
+    L, D, S = cfg.L, cfg.D, cfg.S
+    rec_p = torch.empty((nl + 1, len(rows), L, D), dtype=torch.bfloat16, device=X.device)
+    rec_s = torch.empty((nl + 1, S, len(rows), D), dtype=torch.bfloat16, device=X.device)
+
+    def rp(l, x):
+        if l <= nl:
+            rec_p[l] = x.view(cfg.B, L, D).index_select(0, rt)
+
+    out = st.prefill(X, record=rp)
+    if nl >= cfg.layers:
+        rec_p[nl] = out.view(cfg.B, L, D).index_select(0, rt)
+    st.start_generation(out)
+    for s in range(S):
+        def rd(l, x, s=s):
+            if l <= nl:
+                rec_s[l, s] = x.index_select(0, rt)
+        y = st.decode_step(record=rd)
+        if nl >= cfg.layers:
+            rec_s[nl, s] = y.index_select(0, rt)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return bits(rec_p), bits(rec_s)
+
+
+def stack_kernel_breakdown(cfg, st, X, stream) -> dict:
+    """Per-kernel times of the stack with HIP events: the generation step's two
+    kernels, each launched once per layer (24 distinct weights, so the weights
+    come from HBM as in the stack) inside one captured graph, replayed 10
+    times; and the prompt's two GEMMs of layer 0, eagerly."""
+    import torch
+    from distilled_modal_ssm_amd import binding as hb
+    from distilled_modal_ssm_amd.stack import RMS_EPS
+    B, D, L, nl = cfg.B, cfg.D, cfg.L, cfg.layers
+    out = {}
+    fusable = st.w_in_packed is not None and hb.hyena_layer_step_bf16(
+        st.ops[0].desc, st.xd, D, st.w_in_packed[0], RMS_EPS, st.states[0], st.yd, D) == hb.HM_OK
+    if fusable:
+        def fused():
+            for l in range(nl):
+                hb.hyena_layer_step_bf16(st.ops[l].desc, st.xd, D, st.w_in_packed[l], RMS_EPS, st.states[l],
+                                         st.yd, D)
+
+        def outp():
+            for l in range(nl):
+                hb.hyena_dense_bf16(B, D, D, st.yd, D, st.w_out[l], D, None, st.xd_mid[0], D, workspace=st.ws)
+
+        for name, fn, byts in (
+                ("fused_in_proj_decode", fused, 3 * D * D * 2 + B * D * 16 * cfg.d + 2 * B * D * 2),
+                ("out_proj", outp, D * D * 2 + 2 * B * D * 2)):
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            torch.cuda.synchronize()
+            us = timed_events(stream, g.replay, 10) * 1e3 / nl
+            out[name] = {"us_per_launch": pct(us), "algorithmic_bytes_per_launch": byts,
+                         "hbm_GBs": byts / np.median(us) * 1e-3,
+                         "hbm_frac": byts / np.median(us) * 1e-3 / HBM_PEAK_GBS}
+            del g
+    M = B * L
+    x = X.reshape(M, D)
+
+    def in_proj():
+        hb.hyena_dense_rms_bf16(M, 3 * D, D, x, D, st.w_in[0], D, RMS_EPS, st.qkv, 3 * D)
+
+    def out_proj_p():
+        hb.hyena_dense_bf16(M, D, D, st.y, D, st.w_out[0], D, None, st.x[0], D)
+
+    for name, fn, flops in (("prompt_in_proj", in_proj, 2 * M * 3 * D * D), ("prompt_out_proj", out_proj_p, 2 * M * D * D)):
+        fn()
+        ms = timed_events(stream, fn, 5)
+        out[name] = {"ms_per_launch": pct(ms), "algorithmic_flops_per_launch": flops,
+                     "TFLOPs": flops / np.median(ms) * 1e-9,
+                     "mfma_frac": flops / np.median(ms) * 1e-9 / MFMA_BF16_PEAK_TFLOPS}
+    return out
+
+
+# ------------------------------------------------------------------ f2-f4 baselines
 
 
 def distill_bench(cfg, params, stream, steps=300):
@@ -634,13 +884,7 @@ def fft_prefill_baseline(cfg, op, q, k, v, ms_modal_prefill, stream):
     call()
     torch.cuda.synchronize()
     multipass = cfg.L > 4096
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5 if multipass else 20)]
-    for e in ev:
-        e[0].record(stream)
-        call()
-        e[1].record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    ms = float(np.median(timed_events(stream, call, 5 if multipass else 20)))
     byts = 4 * cfg.act_bytes * cfg.B * cfg.L * cfg.D
     del ws, yf
     torch.cuda.empty_cache()
@@ -672,22 +916,89 @@ def fir_baseline(cfg, op, k, v, dq, dk, dv, window, ms_modal_step, stream):
         run()
     graph.replay()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    graph.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / cfg.S
+    ms_step = float(timed_events(stream, graph.replay, 1)[0]) / cfg.S
     sb = cfg.act_bytes
     rows = [min(cfg.L + s, window - 1 if window else cfg.L + s) for s in range(cfg.S)]
     byts = float(np.mean([cfg.B * cfg.D * (r * sb + 5 * sb) for r in rows]))
     del graph, fir, yf
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     gbs = byts / ms_step * 1e-6
     return {"window": window, "decode_us_per_step": ms_step * 1e3,
             "decode_tokens_per_s": cfg.B / (ms_step / 1e3),
             "algorithmic_bytes_per_step": byts, "hbm_GBs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
             "modal_decode_speedup": ms_step / ms_modal_step}
+
+
+# ------------------------------------------------------------------ main
+
+
+def emit(args, res):
+    line = json.dumps(res)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+    print(line, flush=True)
+
+
+def main():
+    args = parse()
+    if args.fingerprint:
+        print(json.dumps(provenance()))
+        return
+    if args.traffic_from:
+        return write_traffic(args)
+    if args.summarize_trace:
+        return write_trace_summary(args)
+    if args.cpu_1thread is not None:
+        return cpu_one_thread(args.cpu_1thread)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path would shard by batch rows and heads, with no communication)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from workloads import get_config
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = get_config(args.config)
+    subs = args.sub if args.sub is not None else ("3,4" if cfg.layers else "")
+    subs = [int(s) for s in subs.split(",") if s.strip()]
+    t_wall = time.perf_counter()
+    head = run_stack(args, cfg, dev) if cfg.layers else run_operator(args, cfg, dev)
+    res = {
+        "metric": METRIC,
+        "value": head.pop("tokens_per_s"),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head.pop("dtype"),
+        "data": "synthetic",
+        "config": head.pop("config"),
+    }
+    res["config"]["workload"] = head.pop("workload")
+    res.update(head)
+    res["provenance"] = provenance()
+    if subs:
+        res["sub_workloads"] = {}
+        for ci in subs:
+            sc = get_config(ci)
+            r = run_operator(args, sc, dev)
+            r["provenance"] = res["provenance"]
+            r["steps"], r["warmup"] = args.steps, args.warmup
+            res["sub_workloads"][sc.name] = r
+    res["wall_s"] = time.perf_counter() - t_wall
+    emit(args, res)
 
 
 if __name__ == "__main__":

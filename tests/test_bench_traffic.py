@@ -35,3 +35,44 @@ def test_traffic_summary_roundtrip(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "kernel_fingerprint", lambda kernel: "0" * 16)
     assert bench.read_traffic("decode_step_fixed", "width2048-bf16") is None
     assert bench.read_traffic("chunk_mfma_kernel", "width2048-bf16") is None
+
+
+def test_trace_summary_from_kernel_stats(tmp_path):
+    """rocprofv3 --stats rows of two processes are merged per kernel, sorted by
+    total time, with calls, mean/min/max per dispatch and the command."""
+    d = tmp_path / "trace" / "host"
+    d.mkdir(parents=True)
+    fields = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"]
+    for pid, rows in (("1", [("kA", 4, 4000, 500, 1500), ("kB", 1, 9000, 9000, 9000)]),
+                      ("2", [("kA", 2, 2000, 800, 1200)])):
+        with open(d / f"{pid}_kernel_stats.csv", "w", newline="") as fh:
+            w = csv.DictWriter(fh, fieldnames=fields)
+            w.writeheader()
+            for name, calls, tot, lo, hi in rows:
+                w.writerow({"Name": name, "Calls": calls, "TotalDurationNs": tot, "AverageNs": tot / calls,
+                            "Percentage": 0, "MinNs": lo, "MaxNs": hi, "StdDev": 0})
+    out = tmp_path / "sum.txt"
+    args = argparse.Namespace(summarize_trace=(str(tmp_path / "trace"), str(out)), summary_title="t",
+                              traffic_cmd="rocprofv3 ... -- python3 bench.py")
+    bench.write_trace_summary(args)
+    lines = [l for l in out.read_text().splitlines() if l.startswith(("kA", "kB"))]
+    assert lines[0].split()[:2] == ["kB", "1"] and lines[1].split()[:2] == ["kA", "6"]
+    assert lines[1].split()[2:5] == ["1.00", "0.50", "1.50"]   # 6000 ns / 6 calls, min 500, max 1500
+    assert "python3 bench.py" in out.read_text()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "4"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU only" in r.stderr
+
+
+def test_stack_token_bytes_per_layer():
+    """Weights (W_in 3D x D, W_out D x D in bf16), the state read and written
+    (2 x 8 d bytes per row and channel) and four bf16 activation rows."""
+    from workloads import get_config
+    cfg = get_config(5)
+    D, B = 2048, 64
+    per_layer = 4 * D * D * 2 + B * D * 16 * 16 + 4 * B * D * 2
+    assert bench.stack_token_bytes(cfg) == 24 * per_layer == 1635778560
