@@ -285,7 +285,7 @@ PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk, int al
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // matrix-core prefill (prefill_mfma.hip)
 int mfma_channel_tile(const OpShape &s);  // channels per workgroup, 0 = not eligible
-size_t mfma_table_bytes(int64_t H, int64_t d);
+size_t mfma_table_bytes(int64_t H, int64_t d, int act);
 size_t mfma_lam_bytes(int64_t H, int64_t d);
 // per-head tables; also lambda^T (carry scan) when the prompt is chunked
 hipError_t launch_mfma_tables(const PrefillArgs &a, hipStream_t stream);

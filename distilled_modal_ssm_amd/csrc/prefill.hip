@@ -566,7 +566,7 @@ PrefillPlan make_prefill_plan(const OpShape &s, int64_t L, int64_t chunk, int al
     }
     if (p.algo == kAlgoMfma) {
         p.off_mfma_tab = off;
-        off = align256(off + mfma_table_bytes(s.H, s.d));
+        off = align256(off + mfma_table_bytes(s.H, s.d, s.act));
         p.off_mfma_lam = off;
         off = align256(off + mfma_lam_bytes(s.H, s.d));
     }

@@ -15,12 +15,20 @@
 // tying, Laughing Hyena Distillery review, "提出的方法"), so
 //     Y = T U + C X,      S = V U,      X' = lambda^64 (.) X + S
 // are dense GEMMs with N = channels.  They run as bf16 16x16x32 MFMAs with every
-// operand split into a high and a low bfloat16 part (hi*hi + hi*lo + lo*hi,
-// float32 accumulation, ~16 significant bits per product).  The state stays in
-// float32 registers from sub-block to sub-block.
+// operand split into bfloat16 parts and float32 accumulation:
+//   bfloat16 activations: high and low part (hi*hi + hi*lo + lo*hi, about 16
+//     significant bits per product; u = k v of two bfloat16 values is exact in
+//     the two parts);
+//   float32 activations: high, middle and low part, the six products down to
+//     2^-16 of the leading one (hi*hi + hi*mid + mid*hi + hi*lo + lo*hi +
+//     mid*mid), which keeps about 24 significant bits, float32 precision: the
+//     "bf16x6" splitting of Henry, Tang and Heinecke ("Leveraging the bfloat16
+//     artificial intelligence datatype for higher-precision computations",
+//     ARITH 2019).
+// The state stays in float32 registers from sub-block to sub-block.
 //
-// Work per element: 2*(64 + 4*D2) flops on the matrix cores (x3 for the split);
-// the kernel is bound by streaming q, k, v and y through HBM.
+// Work per element: 2*(64 + 4*D2) flops on the matrix cores (x3 or x6 for the
+// split); the kernel is bound by streaming q, k, v and y through HBM.
 //
 // Workgroup: one (batch row, head, tile of PT = 64 or 128 channels, chunk),
 // PT/16 waves of 16 channels each.  Per sub-block: q, k, v for 64 steps x PT
@@ -52,12 +60,27 @@ __device__ __forceinline__ f32x4 mfma(const uint4 a, const uint4 b, f32x4 c) {
                                                     c, 0, 0, 0);
 }
 
-// hi*hi + hi*lo + lo*hi
-__device__ __forceinline__ f32x4 mfma3(const uint4 ah, const uint4 al, const uint4 bh, const uint4 bl, f32x4 c) {
-    c = mfma(ah, bh, c);
-    c = mfma(ah, bl, c);
-    return mfma(al, bh, c);
+// Split products.  NP = 2: a = {hi, lo}: hi*hi + hi*lo + lo*hi.  NP = 3:
+// a = {hi, mid, lo}: the small terms first (lo*hi, hi*lo, mid*mid, mid*hi,
+// hi*mid), the leading hi*hi last.
+template <int NP>
+__device__ __forceinline__ f32x4 mfma_split(const uint4 (&a)[NP], const uint4 (&b)[NP], f32x4 c) {
+    if constexpr (NP == 2) {
+        c = mfma(a[0], b[0], c);
+        c = mfma(a[0], b[1], c);
+        return mfma(a[1], b[0], c);
+    } else {
+        c = mfma(a[2], b[0], c);
+        c = mfma(a[0], b[2], c);
+        c = mfma(a[1], b[1], c);
+        c = mfma(a[1], b[0], c);
+        c = mfma(a[0], b[1], c);
+        return mfma(a[0], b[0], c);
+    }
 }
+
+// bfloat16 parts of the table entries and of float32 operands
+constexpr int parts_of(int act) { return act == kF32 ? 3 : 2; }
 
 __device__ __forceinline__ uint32_t bf16_bits(float x) { return f32_to_bf16(x); }
 __device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
@@ -87,8 +110,9 @@ __device__ inline void polar_pow(double lr, double li, double e, double &re, dou
 //   f in [0, 8)            T tile (mt = f/2, kk = f%2): T[i][j] = h[i-j], j <= i
 //   f in [8, 8+4KC)        C tile (mt, kc): C[i][2n] = Re(R_n lam_n^i), C[i][2n+1] = -Im(R_n lam_n^i)
 //   f in [8+4KC, NFRAG)    V tile (ms, kk): V[2n][j] = Re lam_n^(63-j), V[2n+1][j] = Im lam_n^(63-j)
-// stored as [head][f][hi, lo][lane] uint4; also lam64[head][D2/2] = lambda^64.
-template <int DD>
+// stored as [head][f][part][lane] uint4 with NP parts (hi, lo or hi, mid, lo);
+// also lam64[head][D2/2] = lambda^64.
+template <int DD, int NP>
 __global__ __launch_bounds__(kTabThreads) void mfma_tables_kernel(OpShape s, uint4 *frag, float2 *lam64,
                                                                   int64_t T, float2 *lamT) {
     using G = MfmaGeom<DD>;
@@ -144,7 +168,7 @@ __global__ __launch_bounds__(kTabThreads) void mfma_tables_kernel(OpShape s, uin
     for (int idx = tid; idx < NFRAG * kWave; idx += kTabThreads) {
         const int f = idx / kWave, l = idx % kWave;
         const int r16 = l % 16, k8 = 8 * (l / 16);
-        uint32_t hi[8], lo[8];
+        uint32_t pt[NP][8];
         for (int e = 0; e < 8; ++e) {
             double v = 0.0;
             if (f < 8) {
@@ -161,13 +185,23 @@ __global__ __launch_bounds__(kTabThreads) void mfma_tables_kernel(OpShape s, uin
                 const int f3 = f - 8 - 4 * KC, row = 16 * (f3 / 2) + r16, j = 32 * (f3 % 2) + k8 + e, n = row / 2;
                 if (n < DD) v = (row % 2 == 0) ? pr[(63 - j) * DD + n] : pi[(63 - j) * DD + n];
             }
-            const float vf = (float)v;
-            hi[e] = bf16_bits(vf);
-            lo[e] = bf16_bits(vf - bf16_val(hi[e]));
+            if constexpr (NP == 2) {
+                const float vf = (float)v;
+                pt[0][e] = bf16_bits(vf);
+                pt[1][e] = bf16_bits(vf - bf16_val(pt[0][e]));
+            } else {
+                // parts of the float64 value: each remainder is exact in float64
+                pt[0][e] = bf16_bits((float)v);
+                const double r1 = v - (double)bf16_val(pt[0][e]);
+                pt[1][e] = bf16_bits((float)r1);
+                pt[2][e] = bf16_bits((float)(r1 - (double)bf16_val(pt[1][e])));
+            }
         }
-        uint4 *o = frag + ((int64_t)(g * NFRAG + f) * 2) * kWave + l;
-        o[0] = make_uint4(hi[0] | hi[1] << 16, hi[2] | hi[3] << 16, hi[4] | hi[5] << 16, hi[6] | hi[7] << 16);
-        o[kWave] = make_uint4(lo[0] | lo[1] << 16, lo[2] | lo[3] << 16, lo[4] | lo[5] << 16, lo[6] | lo[7] << 16);
+        uint4 *o = frag + ((int64_t)(g * NFRAG + f) * NP) * kWave + l;
+#pragma unroll
+        for (int q = 0; q < NP; ++q)
+            o[q * kWave] = make_uint4(pt[q][0] | pt[q][1] << 16, pt[q][2] | pt[q][3] << 16,
+                                      pt[q][4] | pt[q][5] << 16, pt[q][6] | pt[q][7] << 16);
     }
 }
 
@@ -239,7 +273,8 @@ __device__ __forceinline__ int yt_index(int row, int col, int ld) { return row *
 // reading k and v only; writes S_c to carry slot c + 1.  VEC: 16-byte row
 // pieces (else element loads, for rows that are not 16-byte aligned; the full
 // pass always needs them aligned).
-template <int DD, int PT, int ACT, bool SO, bool VEC>
+// PF: sub-blocks of q, k, v loads kept in flight (1 or 2).
+template <int DD, int PT, int ACT, bool SO, bool VEC, int PF>
 __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const float2 *carry0) {
     using G = MfmaGeom<DD>;
     using T = typename Act<ACT>::T;
@@ -247,6 +282,7 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
     constexpr int SPLIT = (ACT == kF32) ? PT / 2 : 4, CGW = (ACT == kF32) ? 4 : 8;
     using PC = typename std::conditional<VEC, Piece<ACT, SPLIT>, PieceScalar<ACT, SPLIT>>::type;
     constexpr int D2 = G::D2, KC = G::KC, MTS = G::MTS, NFRAG = G::NFRAG;
+    constexpr int NP = parts_of(ACT);          // bfloat16 parts per operand
     constexpr int NTHR = 4 * PT;               // PT / 16 waves
     constexpr int CW = 16, NTW = 1;            // channels and 16-wide tiles per wave
     constexpr int RG = 2;                      // staging rows per thread (two steps per 32-bit LDS word)
@@ -256,14 +292,15 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
     static_assert(PT == 64 || PT == 128, "channel tile");
     static_assert((64 / RG) * CG == NTHR, "one staging piece group per thread");
     static_assert(VEC || SO, "the full pass loads 16-byte pieces");
+    static_assert(PF == 1 || PF == 2, "prefetch depth");
 
-    __shared__ uint4 tab[NFRAG * 2 * kWave];
-    __shared__ __attribute__((aligned(16))) uint16_t uhi[PT * kLU];
-    __shared__ __attribute__((aligned(16))) uint16_t ulo[PT * kLU];
-    __shared__ __attribute__((aligned(16))) uint16_t xhi[SO ? 8 : PT * LX];
-    __shared__ __attribute__((aligned(16))) uint16_t xlo[SO ? 8 : PT * LX];
+    __shared__ uint4 tab[NFRAG * NP * kWave];
+    __shared__ __attribute__((aligned(16))) uint16_t ub[NP][PT * kLU];          // u parts, [channel][step]
+    __shared__ __attribute__((aligned(16))) uint16_t xb[NP][SO ? 8 : PT * LX];  // state parts, [channel][row]
     __shared__ __attribute__((aligned(16))) float yt[SO ? 4 : kSubBlock * LQ];
     __shared__ float2 lamT[D2 / 2];
+    static_assert(sizeof(tab) + sizeof(ub) + sizeof(xb) + sizeof(yt) + sizeof(lamT) <= 160 * 1024,
+                  "LDS of one workgroup");
 
     const OpShape &s = a.s;
     const int64_t P = s.P, H = s.H, L = a.plan.L, Tc = a.plan.T;
@@ -276,8 +313,8 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
 
     // per-head tables -> LDS
     {
-        const uint4 *gt = reinterpret_cast<const uint4 *>(a.ws + a.plan.off_mfma_tab) + (int64_t)g * NFRAG * 2 * kWave;
-        for (int i = tid; i < NFRAG * 2 * kWave; i += NTHR) tab[i] = gt[i];
+        const uint4 *gt = reinterpret_cast<const uint4 *>(a.ws + a.plan.off_mfma_tab) + (int64_t)g * NFRAG * NP * kWave;
+        for (int i = tid; i < NFRAG * NP * kWave; i += NTHR) tab[i] = gt[i];
         if (tid < D2 / 2)
             lamT[tid] = reinterpret_cast<const float2 *>(a.ws + a.plan.off_mfma_lam)[(int64_t)g * (D2 / 2) + tid];
     }
@@ -306,13 +343,15 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
         for (int ms = 0; ms < MTS; ++ms)
 #pragma unroll
             for (int j = 0; j < NTW; ++j) {
-                const f32x4 x = Xr[ms][j];
-                const uint32_t h01 = pack_bf16x2(x[0], x[1]), h23 = pack_bf16x2(x[2], x[3]);
-                const uint32_t l01 = pack_bf16x2(x[0] - bf16_lo(h01), x[1] - bf16_hi(h01));
-                const uint32_t l23 = pack_bf16x2(x[2] - bf16_lo(h23), x[3] - bf16_hi(h23));
+                f32x4 x = Xr[ms][j];
                 const int o = (cw + 16 * j + lane % 16) * LX + 16 * ms + 4 * (lane / 16);
-                *reinterpret_cast<uint2 *>(&xhi[o]) = make_uint2(h01, h23);
-                *reinterpret_cast<uint2 *>(&xlo[o]) = make_uint2(l01, l23);
+#pragma unroll
+                for (int q = 0; q < NP; ++q) {
+                    // each part is x rounded to bfloat16, then x minus that part (exact)
+                    const uint32_t p01 = pack_bf16x2(x[0], x[1]), p23 = pack_bf16x2(x[2], x[3]);
+                    *reinterpret_cast<uint2 *>(&xb[q][o]) = make_uint2(p01, p23);
+                    x = f32x4{x[0] - bf16_lo(p01), x[1] - bf16_hi(p01), x[2] - bf16_lo(p23), x[3] - bf16_hi(p23)};
+                }
             }
     };
     if constexpr (!SO) write_x();
@@ -328,16 +367,19 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
     const T *vb = static_cast<const T *>(a.v) + (b * L + t_begin) * a.ld_in + ch0;
     T *yb = static_cast<T *>(a.y) + (b * L + t_begin) * a.ld_y + ch0;
 
-    PC pq[RG], pk[RG], pv[RG];
-    auto load = [&](int sb) {
+    // q, k, v pieces of one sub-block: RG rows x 8 channels per thread
+    struct Buf {
+        PC q[RG], k[RG], v[RG];
+    };
+    auto load = [&](int sb, Buf &bf) {
 #pragma unroll
         for (int r = 0; r < RG; ++r) {
             int row = sb * kSubBlock + rg * RG + r;
             row = row < nsteps ? row : nsteps - 1;  // clamped; rows past the prompt are masked in staging
             const int64_t o = (int64_t)row * a.ld_in;
-            if constexpr (!SO) pq[r].load(qb + o);
-            pk[r].load(kb + o);
-            pv[r].load(vb + o);
+            if constexpr (!SO) bf.q[r].load(qb + o);
+            bf.k[r].load(kb + o);
+            bf.v[r].load(vb + o);
         }
     };
 
@@ -345,156 +387,181 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
     // and the first of the next, threads read the Y tile (written before the
     // second) and write the u tiles (last read before the second), so the two
     // phases touch disjoint LDS.
-    load(0);
-    for (int sb = 0; sb < nsb; ++sb) {
-        const int nv = (nsteps - sb * kSubBlock < kSubBlock) ? nsteps - sb * kSubBlock : kSubBlock;
-        // ---- stage: u = k v split into hi/lo, transposed to [channel][step]; q stays in registers
-        PC cq[RG];
-        if constexpr (!SO) {
-#pragma unroll
-            for (int r = 0; r < RG; ++r) cq[r] = pq[r];
-        }
-        {
-            float uu[RG][8];
-#pragma unroll
-            for (int r = 0; r < RG; ++r) {
-                const bool valid = rg * RG + r < nv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) uu[r][e] = valid ? pk[r].get(e) * pv[r].get(e) : 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t h = pack_bf16x2(uu[0][e], uu[1][e]);
-                const uint32_t lo = pack_bf16x2(uu[0][e] - bf16_lo(h), uu[1][e] - bf16_hi(h));
-                const int o = u_index(CGW * cg + (e & 3) + SPLIT * (e >> 2), rg * RG);
-                *reinterpret_cast<uint32_t *>(&uhi[o]) = h;
-                *reinterpret_cast<uint32_t *>(&ulo[o]) = lo;
-            }
-        }
-        if (sb + 1 < nsb) load(sb + 1);  // next sub-block in flight during the products
-        __syncthreads();
-
-        // ---- products
-        f32x4 Y[4][NTW], S[MTS][NTW];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) Y[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < MTS; ++i)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) S[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            uint4 bh[NTW], bl[NTW];
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int o = u_index(cw + 16 * j + lane % 16, 32 * kk + 8 * (lane / 16));
-                bh[j] = *reinterpret_cast<const uint4 *>(&uhi[o]);
-                bl[j] = *reinterpret_cast<const uint4 *>(&ulo[o]);
-            }
+    // One sub-block.  Its pieces are in `cur`; once staged, `cur` takes the
+    // loads of sub-block sb + PF, so PF sub-blocks of loads stay in flight.
+    auto sub_block = [&](int sb, Buf &cur) {
+            const int nv = (nsteps - sb * kSubBlock < kSubBlock) ? nsteps - sb * kSubBlock : kSubBlock;
+            // ---- stage: u = k v split into hi/lo, transposed to [channel][step]; q stays in registers
+            PC cq[RG];
             if constexpr (!SO) {
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const int f = mt * 2 + kk;
-                    const uint4 ah = tab[(f * 2) * kWave + lane], al = tab[(f * 2 + 1) * kWave + lane];
+                for (int r = 0; r < RG; ++r) cq[r] = cur.q[r];
+            }
+            {
+                float uu[RG][8];
 #pragma unroll
-                    for (int j = 0; j < NTW; ++j) Y[mt][j] = mfma3(ah, al, bh[j], bl[j], Y[mt][j]);
+                for (int r = 0; r < RG; ++r) {
+                    const bool valid = rg * RG + r < nv;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) uu[r][e] = valid ? cur.k[r].get(e) * cur.v[r].get(e) : 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int o = u_index(CGW * cg + (e & 3) + SPLIT * (e >> 2), rg * RG);
+                    float u0 = uu[0][e], u1 = uu[1][e];
+#pragma unroll
+                    for (int q = 0; q < NP; ++q) {
+                        const uint32_t w2 = pack_bf16x2(u0, u1);
+                        *reinterpret_cast<uint32_t *>(&ub[q][o]) = w2;
+                        u0 -= bf16_lo(w2);
+                        u1 -= bf16_hi(w2);
+                    }
+                }
+            }
+            if (sb + PF < nsb) load(sb + PF, cur);  // PF sub-blocks ahead stay in flight during the products
+            __syncthreads();
+
+            // ---- products
+            f32x4 Y[4][NTW], S[MTS][NTW];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) Y[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i = 0; i < MTS; ++i)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) S[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            auto afrag = [&](int f, uint4 (&av)[NP]) {
+#pragma unroll
+                for (int q = 0; q < NP; ++q) av[q] = tab[(f * NP + q) * kWave + lane];
+            };
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                uint4 bv[NTW][NP];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    const int o = u_index(cw + 16 * j + lane % 16, 32 * kk + 8 * (lane / 16));
+#pragma unroll
+                    for (int q = 0; q < NP; ++q) bv[j][q] = *reinterpret_cast<const uint4 *>(&ub[q][o]);
+                }
+                if constexpr (!SO) {
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt) {
+                        // T is causal: rows 0..31 against steps 32..63 are all zero
+                        if (kk == 1 && mt < 2) continue;
+                        uint4 av[NP];
+                        afrag(mt * 2 + kk, av);
+#pragma unroll
+                        for (int j = 0; j < NTW; ++j) Y[mt][j] = mfma_split<NP>(av, bv[j], Y[mt][j]);
+                    }
+                }
+#pragma unroll
+                for (int ms = 0; ms < MTS; ++ms) {
+                    uint4 av[NP];
+                    afrag(8 + 4 * KC + ms * 2 + kk, av);
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) S[ms][j] = mfma_split<NP>(av, bv[j], S[ms][j]);
                 }
             }
 #pragma unroll
-            for (int ms = 0; ms < MTS; ++ms) {
-                const int f = 8 + 4 * KC + ms * 2 + kk;
-                const uint4 ah = tab[(f * 2) * kWave + lane], al = tab[(f * 2 + 1) * kWave + lane];
+            for (int kc = 0; kc < (SO ? 0 : KC); ++kc) {
+                uint4 xv[NTW][NP];
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) S[ms][j] = mfma3(ah, al, bh[j], bl[j], S[ms][j]);
+                for (int j = 0; j < NTW; ++j) {
+                    const int o = (cw + 16 * j + lane % 16) * LX + 32 * kc + 8 * (lane / 16);
+#pragma unroll
+                    for (int q = 0; q < NP; ++q) xv[j][q] = *reinterpret_cast<const uint4 *>(&xb[q][o]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt) {
+                    uint4 av[NP];
+                    afrag(8 + mt * KC + kc, av);
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) Y[mt][j] = mfma_split<NP>(av, xv[j], Y[mt][j]);
+                }
             }
-        }
-#pragma unroll
-        for (int kc = 0; kc < (SO ? 0 : KC); ++kc) {
-            uint4 xh[NTW], xl[NTW];
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int o = (cw + 16 * j + lane % 16) * LX + 32 * kc + 8 * (lane / 16);
-                xh[j] = *reinterpret_cast<const uint4 *>(&xhi[o]);
-                xl[j] = *reinterpret_cast<const uint4 *>(&xlo[o]);
-            }
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const int f = 8 + mt * KC + kc;
-                const uint4 ah = tab[(f * 2) * kWave + lane], al = tab[(f * 2 + 1) * kWave + lane];
-#pragma unroll
-                for (int j = 0; j < NTW; ++j) Y[mt][j] = mfma3(ah, al, xh[j], xl[j], Y[mt][j]);
-            }
-        }
 
-        // ---- Y tile -> LDS ([step][channel])
-        if constexpr (!SO) {
+            // ---- Y tile -> LDS ([step][channel])
+            if constexpr (!SO) {
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int j = 0; j < NTW; ++j)
+                    for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        yt[yt_index(16 * mt + 4 * (lane / 16) + r, cw + 16 * j + lane % 16, LQ)] = Y[mt][j][r];
-        }
+                        for (int r = 0; r < 4; ++r)
+                            yt[yt_index(16 * mt + 4 * (lane / 16) + r, cw + 16 * j + lane % 16, LQ)] = Y[mt][j][r];
+            }
 
-        // ---- state hand-off
-        if (nv == kSubBlock) {
+            // ---- state hand-off
+            if (nv == kSubBlock) {
 #pragma unroll
-            for (int ms = 0; ms < MTS; ++ms)
+                for (int ms = 0; ms < MTS; ++ms)
 #pragma unroll
-                for (int j = 0; j < NTW; ++j)
+                    for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                    for (int q2 = 0; q2 < 2; ++q2) {
-                        const float2 lt = lamT[8 * ms + 2 * (lane / 16) + q2];
-                        const float xr = Xr[ms][j][2 * q2], xi = Xr[ms][j][2 * q2 + 1];
-                        Xr[ms][j][2 * q2] = fmaf(lt.x, xr, fmaf(-lt.y, xi, S[ms][j][2 * q2]));
-                        Xr[ms][j][2 * q2 + 1] = fmaf(lt.x, xi, fmaf(lt.y, xr, S[ms][j][2 * q2 + 1]));
-                    }
-            if constexpr (!SO) write_x();
-        } else {
-            // ragged final sub-block (end of the prompt): step the recurrence
-            // over its nv steps on the vector ALUs, from u = hi + lo in LDS
-#pragma unroll
-            for (int ms = 0; ms < MTS; ++ms)
-#pragma unroll
-                for (int j = 0; j < NTW; ++j)
-#pragma unroll
-                    for (int q2 = 0; q2 < 2; ++q2) {
-                        const int n = 8 * ms + 2 * (lane / 16) + q2;
-                        if (n >= DD) continue;
-                        const float2 l = s.poles[(int64_t)g * DD + n];
-                        float xr = Xr[ms][j][2 * q2], xi = Xr[ms][j][2 * q2 + 1];
-                        const int ch = cw + 16 * j + lane % 16;
-                        for (int t = 0; t < nv; ++t) {
-                            const int o = u_index(ch, t);
-                            const float u = bf16_val(uhi[o]) + bf16_val(ulo[o]);
-                            const float nr = fmaf(l.x, xr, fmaf(-l.y, xi, u));
-                            xi = fmaf(l.x, xi, l.y * xr);
-                            xr = nr;
+                        for (int q2 = 0; q2 < 2; ++q2) {
+                            const float2 lt = lamT[8 * ms + 2 * (lane / 16) + q2];
+                            const float xr = Xr[ms][j][2 * q2], xi = Xr[ms][j][2 * q2 + 1];
+                            Xr[ms][j][2 * q2] = fmaf(lt.x, xr, fmaf(-lt.y, xi, S[ms][j][2 * q2]));
+                            Xr[ms][j][2 * q2 + 1] = fmaf(lt.x, xi, fmaf(lt.y, xr, S[ms][j][2 * q2 + 1]));
                         }
-                        Xr[ms][j][2 * q2] = xr;
-                        Xr[ms][j][2 * q2 + 1] = xi;
-                    }
-        }
-        __syncthreads();
-
-        // ---- gate y = q Y and store whole 8-channel pieces of valid rows
+                if constexpr (!SO) write_x();
+            } else {
+                // ragged final sub-block (end of the prompt): step the recurrence
+                // over its nv steps on the vector ALUs, from u = the sum of its parts in LDS
 #pragma unroll
-        for (int r = 0; r < (SO ? 0 : RG); ++r) {
-            const int row = rg * RG + r;
-            if (row < nv) {
-                const float4 y0 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, CGW * cg, LQ)]);
-                const float4 y1 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, CGW * cg + SPLIT, LQ)]);
-                const float yy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-                float v[8];
+                for (int ms = 0; ms < MTS; ++ms)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = cq[r].get(e) * yy[e];
-                store8<SPLIT>(reinterpret_cast<T *>(yb + (int64_t)(sb * kSubBlock + row) * a.ld_y), v);
+                    for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                        for (int q2 = 0; q2 < 2; ++q2) {
+                            const int n = 8 * ms + 2 * (lane / 16) + q2;
+                            if (n >= DD) continue;
+                            const float2 l = s.poles[(int64_t)g * DD + n];
+                            float xr = Xr[ms][j][2 * q2], xi = Xr[ms][j][2 * q2 + 1];
+                            const int ch = cw + 16 * j + lane % 16;
+                            for (int t = 0; t < nv; ++t) {
+                                const int o = u_index(ch, t);
+                                float u = 0.f;
+#pragma unroll
+                                for (int q = NP - 1; q >= 0; --q) u += bf16_val(ub[q][o]);
+                                const float nr = fmaf(l.x, xr, fmaf(-l.y, xi, u));
+                                xi = fmaf(l.x, xi, l.y * xr);
+                                xr = nr;
+                            }
+                            Xr[ms][j][2 * q2] = xr;
+                            Xr[ms][j][2 * q2 + 1] = xi;
+                        }
             }
+            __syncthreads();
+
+            // ---- gate y = q Y and store whole 8-channel pieces of valid rows
+#pragma unroll
+            for (int r = 0; r < (SO ? 0 : RG); ++r) {
+                const int row = rg * RG + r;
+                if (row < nv) {
+                    const float4 y0 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, CGW * cg, LQ)]);
+                    const float4 y1 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, CGW * cg + SPLIT, LQ)]);
+                    const float yy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+                    float v[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = cq[r].get(e) * yy[e];
+                    store8<SPLIT>(reinterpret_cast<T *>(yb + (int64_t)(sb * kSubBlock + row) * a.ld_y), v);
+                }
+            }
+        };
+    Buf b0, b1;
+    load(0, b0);
+    if constexpr (PF == 2) {
+        if (nsb > 1) load(1, b1);
+        for (int sb = 0; sb < nsb; sb += 2) {
+            sub_block(sb, b0);
+            if (sb + 1 < nsb) sub_block(sb + 1, b1);
         }
+    } else {
+        for (int sb = 0; sb < nsb; ++sb) sub_block(sb, b0);
     }
+
 
     if (SO || c == a.plan.NC - 1) {
         float2 *const base = SO ? reinterpret_cast<float2 *>(a.ws + a.plan.off_carry) + (c + 1) * (s.B * H * DD * P)
@@ -512,13 +579,26 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
     }
 }
 
+// Load prefetch depth in sub-blocks.  float32 sub-blocks do twice the matrix-core
+// work of bfloat16 ones (six split products instead of three), which a single
+// sub-block of loads in flight no longer covers at one wave per SIMD.
+constexpr int kPfBF16 = 1, kPfF32 = 2;
+
+// float32 tiles of 128 channels take three bfloat16 parts of every operand and
+// do not fit the LDS at d = 32: the channel tile is 64 there.
+template <int DD, int PT> constexpr bool f32_tile_fits() { return !(DD == 32 && PT == 128); }
+
 template <int DD, int PT>
 hipError_t launch_dd(const PrefillArgs &a, const float2 *carry0, hipStream_t stream) {
     const dim3 grid((unsigned)(a.s.H * (a.s.P / PT)), (unsigned)a.plan.NC, (unsigned)a.s.B), block(4 * PT);
-    if (a.s.act == kBF16)
-        chunk_mfma_kernel<DD, PT, kBF16, false, true><<<grid, block, 0, stream>>>(a, carry0);
-    else
-        chunk_mfma_kernel<DD, PT, kF32, false, true><<<grid, block, 0, stream>>>(a, carry0);
+    if (a.s.act == kBF16) {
+        chunk_mfma_kernel<DD, PT, kBF16, false, true, kPfBF16><<<grid, block, 0, stream>>>(a, carry0);
+    } else {
+        if constexpr (f32_tile_fits<DD, PT>())
+            chunk_mfma_kernel<DD, PT, kF32, false, true, kPfF32><<<grid, block, 0, stream>>>(a, carry0);
+        else
+            return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
@@ -526,11 +606,15 @@ template <int DD, int PT>
 hipError_t launch_dd_state(const PrefillArgs &a, bool vec, hipStream_t stream) {
     const dim3 grid((unsigned)(a.s.H * (a.s.P / PT)), (unsigned)(a.plan.NC - 1), (unsigned)a.s.B), block(4 * PT);
     if (a.s.act == kBF16) {
-        if (vec) chunk_mfma_kernel<DD, PT, kBF16, true, true><<<grid, block, 0, stream>>>(a, nullptr);
-        else chunk_mfma_kernel<DD, PT, kBF16, true, false><<<grid, block, 0, stream>>>(a, nullptr);
+        if (vec) chunk_mfma_kernel<DD, PT, kBF16, true, true, kPfBF16><<<grid, block, 0, stream>>>(a, nullptr);
+        else chunk_mfma_kernel<DD, PT, kBF16, true, false, kPfBF16><<<grid, block, 0, stream>>>(a, nullptr);
     } else {
-        if (vec) chunk_mfma_kernel<DD, PT, kF32, true, true><<<grid, block, 0, stream>>>(a, nullptr);
-        else chunk_mfma_kernel<DD, PT, kF32, true, false><<<grid, block, 0, stream>>>(a, nullptr);
+        if constexpr (f32_tile_fits<DD, PT>()) {
+            if (vec) chunk_mfma_kernel<DD, PT, kF32, true, true, kPfF32><<<grid, block, 0, stream>>>(a, nullptr);
+            else chunk_mfma_kernel<DD, PT, kF32, true, false, kPfF32><<<grid, block, 0, stream>>>(a, nullptr);
+        } else {
+            return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }
@@ -553,15 +637,17 @@ hipError_t launch_pt(const PrefillArgs &a, const float2 *carry0, bool state_only
 // 64-channel workgroups per CU), else 64.
 int mfma_channel_tile(const OpShape &s) {
     if (s.d != 8 && s.d != 16 && s.d != 32) return 0;
-    if (s.P % 128 == 0 && s.B * s.H * (s.P / 128) >= 256) return 128;
+    const bool wide_fits = !(s.act == kF32 && s.d == 32);
+    if (wide_fits && s.P % 128 == 0 && s.B * s.H * (s.P / 128) >= 256) return 128;
     return (s.P % 64 == 0) ? 64 : 0;
 }
 
-size_t mfma_table_bytes(int64_t H, int64_t d) {
+size_t mfma_table_bytes(int64_t H, int64_t d, int act) {
+    const size_t np = (size_t)parts_of(act);
     switch (d) {
-        case 8: return (size_t)H * MfmaGeom<8>::NFRAG * 2 * kWave * 16;
-        case 16: return (size_t)H * MfmaGeom<16>::NFRAG * 2 * kWave * 16;
-        case 32: return (size_t)H * MfmaGeom<32>::NFRAG * 2 * kWave * 16;
+        case 8: return (size_t)H * MfmaGeom<8>::NFRAG * np * kWave * 16;
+        case 16: return (size_t)H * MfmaGeom<16>::NFRAG * np * kWave * 16;
+        case 32: return (size_t)H * MfmaGeom<32>::NFRAG * np * kWave * 16;
         default: return 0;
     }
 }
@@ -576,10 +662,20 @@ hipError_t launch_mfma_tables(const PrefillArgs &a, hipStream_t stream) {
     float2 *lam = reinterpret_cast<float2 *>(a.ws + a.plan.off_mfma_lam);
     float2 *lamT = a.plan.NC > 1 ? reinterpret_cast<float2 *>(a.ws + a.plan.off_lamT) : nullptr;
     const dim3 grid((unsigned)a.s.H), block(kTabThreads);
+    const bool f32 = a.s.act == kF32;
     switch (a.s.d) {
-        case 8: mfma_tables_kernel<8><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT); break;
-        case 16: mfma_tables_kernel<16><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT); break;
-        case 32: mfma_tables_kernel<32><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT); break;
+        case 8:
+            if (f32) mfma_tables_kernel<8, 3><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT);
+            else mfma_tables_kernel<8, 2><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT);
+            break;
+        case 16:
+            if (f32) mfma_tables_kernel<16, 3><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT);
+            else mfma_tables_kernel<16, 2><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT);
+            break;
+        case 32:
+            if (f32) mfma_tables_kernel<32, 3><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT);
+            else mfma_tables_kernel<32, 2><<<grid, block, 0, stream>>>(a.s, frag, lam, a.plan.T, lamT);
+            break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

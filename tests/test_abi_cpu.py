@@ -143,7 +143,7 @@ def test_workspace_sizes_follow_the_chunk_plan(lib):
     slots = 4 * 1 * 4096 * 32 * 8
     mf = hb.hyena_modal_prefill_workspace(one, 65536, chunk=16384, algo="mfma")
     sc = hb.hyena_modal_prefill_workspace(one, 65536, chunk=16384, algo="scan")
-    assert slots <= mf < slots + (2 << 20) < sc
+    assert slots <= mf < slots + (3 << 20) < sc
     assert hb.hyena_modal_prefill_workspace(one, 65536, chunk=32768, algo="mfma") < mf
 
 
@@ -162,6 +162,17 @@ def test_prefill_plan_choices(lib):
     p = hb.hyena_modal_prefill_plan(_desc(batch=1, channels=4096, heads=32, modes=32), 65536)
     assert p["channel_tile"] == 64 and p["n_chunks"] == 4
     assert hb.hyena_modal_prefill_plan(w2, 2048, algo="scan")["channel_tile"] == 0
+    # float32 keeps three bfloat16 parts of every operand: at d = 32 a 128-channel
+    # tile no longer fits the LDS, and its tables take 3/2 of the bfloat16 bytes
+    f32_32 = _desc(batch=16, channels=2048, heads=16, modes=32, act_dtype=hb.HM_F32)
+    assert hb.hyena_modal_prefill_plan(f32_32, 2048)["channel_tile"] == 64
+    assert hb.hyena_modal_prefill_plan(_desc(batch=16, channels=2048, heads=16, modes=16, act_dtype=hb.HM_F32),
+                                       2048)["channel_tile"] == 128
+    bf_32 = _desc(batch=16, channels=2048, heads=16, modes=32, act_dtype=hb.HM_BF16)
+    assert hb.hyena_modal_prefill_plan(bf_32, 2048)["channel_tile"] == 128
+    t_bf = hb.hyena_modal_prefill_workspace(bf_32, 2048)
+    t_f32 = hb.hyena_modal_prefill_workspace(f32_32, 2048)
+    assert t_f32 - 16 * 32 * 8 == (t_bf - 16 * 32 * 8) * 3 // 2  # tables grow by half; lambda^64 does not
     # a single batch row over 4 heads: the prompt is cut into 64-step multiples
     few = _desc(batch=1, channels=256, heads=4, modes=8)
     p = hb.hyena_modal_prefill_plan(few, 4096)
