@@ -863,8 +863,23 @@ def distill_bench(cfg, params, stream, steps=300):
     us = e0.elapsed_time(e1) * 1e3 / (steps - 1)
     h = hist.sum(1).cpu().numpy()
     del graph
-    return {"heads": cfg.H, "modes": cfg.d, "taps": cfg.L, "target_modes": 2 * cfg.d, "iterations": steps,
-            "us_per_iteration": us, "loss_first": float(h[0]), "loss_last": float(h[-1])}
+    out = {"heads": cfg.H, "modes": cfg.d, "taps": cfg.L, "target_modes": 2 * cfg.d, "iterations": steps,
+           "us_per_iteration": us, "loss_first": float(h[0]), "loss_last": float(h[-1])}
+    # the Prony-type start (host: Hankel order, matrix pencil, least squares), then Adam
+    from distilled_modal_ssm_amd.distill import hankel_order
+    t0 = time.perf_counter()
+    order = hankel_order(target, 64, 1e-6)
+    fit = ModalDistiller(target, cfg.d, init="fit")
+    t_init = time.perf_counter() - t0
+    first = float(fit.objective().sum().item())
+    hist2 = torch.empty((steps, cfg.H), dtype=torch.float32, device="cuda")
+    for i in range(steps):
+        fit.step(1e-5, loss=hist2[i], stream=stream)
+    last = float(fit.objective().sum().item())
+    out["fit_start"] = {"hankel_order_at_1e-6": [int(o) for o in order], "host_init_s": t_init,
+                        "loss_at_start": first, "adam_lr": 1e-5, "loss_after_adam": last,
+                        "below_default_start_first": float(h[0]) / max(last, 1e-30)}
+    return out
 
 
 def fft_prefill_baseline(cfg, op, q, k, v, ms_modal_prefill, stream):
@@ -933,8 +948,16 @@ def fir_baseline(cfg, op, k, v, dq, dk, dv, window, ms_modal_step, stream):
 # ------------------------------------------------------------------ main
 
 
+def _json_default(o):
+    if isinstance(o, np.generic):
+        return o.item()
+    if isinstance(o, np.ndarray):
+        return o.tolist()
+    raise TypeError(f"not JSON serialisable: {type(o).__name__}")
+
+
 def emit(args, res):
-    line = json.dumps(res)
+    line = json.dumps(res, default=_json_default)
     if args.json_out:
         with open(args.json_out, "w") as f:
             f.write(line + "\n")

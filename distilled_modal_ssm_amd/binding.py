@@ -54,6 +54,9 @@ EXPORTS = (
     "hyena_distill_workspace",
     "hyena_distill_grad",
     "hyena_distill_adam_step",
+    "hyena_hankel_singular_values",
+    "hyena_modal_order",
+    "hyena_modal_fit_init",
 )
 
 
@@ -140,6 +143,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         ctypes.c_int),
             "hyena_layer_step_bf16": ([D, p, i64, p, ctypes.c_float, p, p, i64, p], ctypes.c_int),
             "hyena_pack_in_proj_bf16": ([i64, i64, p, i64, p, p], ctypes.c_int),
+            "hyena_hankel_singular_values": ([p, i64, i64, p], ctypes.c_int),
+            "hyena_modal_order": ([p, i64, i64, i64, ctypes.c_double, p], ctypes.c_int),
+            "hyena_modal_fit_init": ([p, i64, i64, i64, f32, p, p, p], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -368,6 +374,48 @@ def hyena_distill_adam_step(H, d, poles, residues, skip, g_poles, g_res, g_skip,
                                         _ptr(g_skip), _ptr(m), _ptr(v), step, lr, beta1, beta2, eps, r_max,
                                         _stream(stream))
     _check(st, "hyena_distill_adam_step")
+
+
+# ----------------------------------------------------------------- host-side fit set-up
+
+
+def _host_f32(a):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+
+
+def hyena_hankel_singular_values(h, n: int):
+    """Singular values (decreasing) of the n x n Hankel matrix of one filter's taps h[1:]."""
+    import numpy as np
+    h = _host_f32(h)
+    sv = np.empty(n, dtype=np.float64)
+    _check(load().hyena_hankel_singular_values(h.ctypes.data, h.size, n, sv.ctypes.data),
+           "hyena_hankel_singular_values")
+    return sv
+
+
+def hyena_modal_order(h, n: int, rel_tol: float):
+    """Per head of h [H][L]: Hankel singular values above rel_tol x the largest."""
+    import numpy as np
+    h = _host_f32(h)
+    out = np.empty(h.shape[0], dtype=np.int64)
+    _check(load().hyena_modal_order(h.ctypes.data, h.shape[0], h.shape[1], n, rel_tol, out.ctypes.data),
+           "hyena_modal_order")
+    return out
+
+
+def hyena_modal_fit_init(h, d: int, r_max: float = 0.9999):
+    """Matrix-pencil / least-squares initial fit of h [H][L] (host arrays):
+    returns (poles [H][d][2], residues [H][d][2], skip [H]) float32."""
+    import numpy as np
+    h = _host_f32(h)
+    H, L = h.shape
+    poles = np.empty((H, d, 2), dtype=np.float32)
+    res = np.empty((H, d, 2), dtype=np.float32)
+    skip = np.empty(H, dtype=np.float32)
+    _check(load().hyena_modal_fit_init(h.ctypes.data, H, L, d, r_max, poles.ctypes.data, res.ctypes.data,
+                                       skip.ctypes.data), "hyena_modal_fit_init")
+    return poles, res, skip
 
 
 # ----------------------------------------------------------------- tensor helpers

@@ -414,6 +414,47 @@ hm_status hyena_distill_adam_step(int64_t H, int64_t d, float *poles, float *res
                                   float *m, float *v, int64_t step, float lr, float beta1, float beta2,
                                   float eps, float r_max, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Set-up of a distillation on the host (Laughing Hyena Distillery review,
+ * 提出的方法: the state dimension follows the spectrum of each filter's Hankel
+ * operator, and the filter is reduced by modal truncation with a Prony-like
+ * parametrisation).  These three run on the CPU: every pointer is a HOST
+ * pointer, float64 inside, and no GPU call is made.  Threads: one per head,
+ * up to the host's hardware threads.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Singular values, in decreasing order, of the n x n Hankel matrix
+ * Hk[i][j] = h[1 + i + j] of one filter h [L] (the taps after the skip).
+ * Requires L >= 2n (else HM_ERR_INVALID_ARG); n <= 4096 (else
+ * HM_ERR_UNSUPPORTED).  sv: n doubles.
+ */
+hm_status hyena_hankel_singular_values(const float *h, int64_t L, int64_t n, double *sv);
+
+/*
+ * Order of each head's filter, h [H][L]: the number of Hankel singular values
+ * (n x n, as above) above rel_tol times the largest.  A filter of d complex
+ * modes has order at most 2d (one per real dimension of its minimal
+ * realisation), so ceil(order / 2) modes suffice up to that tolerance.
+ * order: H int64.  0 < rel_tol < 1.
+ */
+hm_status hyena_modal_order(const float *h, int64_t H, int64_t L, int64_t n, double rel_tol, int64_t *order);
+
+/*
+ * Initial modal fit of each head's filter h [H][L] (h[g][0] is the skip):
+ * poles from the matrix pencil of the first taps with 2d exponentials (real
+ * taps give conjugate pairs; each pair is one mode, its upper half-plane
+ * member), each pole scaled back to radius r_max if it lies outside; then the
+ * residues that minimise sum_{1 <= t < L} (Re sum_n R_n lambda_n^(t-1) - h[t])^2
+ * for those poles; skip = h[g][0].  Modes beyond the filter's own order get
+ * zero residues.  A filter of at most d distinct modes is recovered up to
+ * rounding.  Outputs (host): poles, residues [H][d][2], skip [H], float32.
+ * 0 < r_max < 1; d <= HM_MAX_MODES; L must hold the pencil (about 6d taps;
+ * else HM_ERR_INVALID_ARG).
+ */
+hm_status hyena_modal_fit_init(const float *h, int64_t H, int64_t L, int64_t d, float r_max, float *poles,
+                               float *residues, float *skip);
+
 #ifdef __cplusplus
 }
 #endif

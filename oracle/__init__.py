@@ -17,7 +17,8 @@ stack_layer()           one layer of the projected stack, teacher-forced on a gi
                         input sequence (see ``stack_layer``'s docstring).
 distill_loss_grad()     the filter discrepancy of a modal filter against target
                         taps and its analytic gradient (the distillation objective);
-                        hankel_singular_values() of a filter.
+                        hankel_singular_values() of a filter; modal_fit_init(), the
+                        matrix-pencil / least-squares initial fit.
 fir_conv()              the same operator with an explicit (possibly truncated)
                         filter over a cache of u rounded to the activation dtype:
                         the non-distilled decode baseline.
@@ -256,6 +257,65 @@ def distill_loss_grad(params, h_target, L: int):
     g_poles = np.stack([2 * np.sum(et * dl.real, -1), -2 * np.sum(et * dl.imag, -1)], -1)
     g_skip = 2 * e[:, 0]
     return loss, g_poles, g_res, g_skip
+
+
+def modal_fit_init(h, d: int, r_max: float = 0.9999):
+    """Initial modal fit of each filter h [H][L] (float64): poles by the matrix
+    pencil method of Hua and Sarkar (IEEE Trans. ASSP, 1990), residues by
+    linear least squares, skip = h[0] -- the Prony-type reduction the
+    distillation review describes (提出的方法: modal truncation with a
+    Prony-like parametrisation).
+
+    For each head, with x_k = h[1 + k] (k < N = L - 1) and M = 2d real
+    exponentials (d complex modes and their conjugates):
+      1. window length n = min(2M + 8, N // 2), rows = min(N - n + 1, 2n);
+         Hankel data matrix Y[i][j] = x[i + j] (rows x n);
+      2. V = the top-M right singular vectors of Y (n x M);
+      3. Psi = least-squares solution of V[:-1] Psi = V[1:]; its eigenvalues
+         are the poles (the shifted windows span the same space);
+      4. modes: poles with Im > 0 (one of each conjugate pair) and real poles,
+         each scaled back to radius r_max if outside it;
+      5. residues R minimising sum_{t >= 1} (Re sum_n R_n lambda_n^(t-1) - h[t])^2
+         over all taps (columns Re lambda^(t-1) and -Im lambda^(t-1));
+      6. more than d modes: keep the d with the largest |R|^2 / (1 - |lambda|^2)
+         and solve step 5 again; fewer: pad with zero-residue poles at 0.
+    Returns (poles [H][d][2], residues [H][d][2], skip [H]) float64."""
+    h = np.atleast_2d(np.asarray(h, dtype=np.float64))
+    H, L = h.shape
+    N, M = L - 1, 2 * d
+    n = min(2 * M + 8, N // 2)
+    rows = min(N - n + 1, 2 * n)
+    t = np.arange(L - 1)
+
+    def residues_for(lam, taps):
+        pw = lam[None, :] ** t[:, None]                       # lambda^(t-1), t = 1 .. L-1
+        cols = np.concatenate([pw.real, -pw.imag], axis=1)
+        keep = np.any(cols != 0.0, axis=0)                    # a real pole has no imaginary column
+        sol = np.zeros(2 * lam.size)
+        sol[keep] = np.linalg.lstsq(cols[:, keep], taps, rcond=None)[0]
+        return sol[:lam.size] + 1j * sol[lam.size:]
+
+    poles = np.zeros((H, d, 2))
+    res = np.zeros((H, d, 2))
+    for g in range(H):
+        x = h[g, 1:]
+        Y = x[np.arange(rows)[:, None] + np.arange(n)[None, :]]
+        V = np.linalg.svd(Y)[2][:M].T
+        Psi = np.linalg.lstsq(V[:-1], V[1:], rcond=None)[0]
+        z = np.linalg.eigvals(Psi)
+        tol = 1e-9 * np.maximum(1.0, np.abs(z))
+        lam = np.concatenate([z[z.imag > tol], z[np.abs(z.imag) <= tol].real + 0j])
+        big = np.abs(lam) > r_max
+        lam[big] *= r_max / np.abs(lam[big])
+        R = residues_for(lam, x)
+        if lam.size > d:
+            energy = np.abs(R) ** 2 / np.maximum(1e-12, 1.0 - np.abs(lam) ** 2)
+            lam = lam[np.argsort(-energy)[:d]]
+            R = residues_for(lam, x)
+        k = lam.size
+        poles[g, :k] = np.stack([lam.real, lam.imag], -1)
+        res[g, :k] = np.stack([R.real, R.imag], -1)
+    return poles, res, h[:, 0].copy()
 
 
 def hankel_singular_values(h_row, n: int) -> np.ndarray:

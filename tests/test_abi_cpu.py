@@ -452,3 +452,72 @@ def test_noalloc_prefill_validation(lib):
     assert e.value.status == hb.HM_ERR_WORKSPACE
     # B = 0 enqueues nothing and needs no device
     hb.hyena_modal_prefill_noalloc(_desc(batch=0), 128, None, None, None, 64, None, 64, None, None, stream=0)
+
+
+def test_host_modal_fit_matches_oracle(lib):
+    """The library's host-side distillation set-up against the oracle: Hankel
+    singular values, the order they give, and the matrix-pencil fit (float32
+    taps in, float32 tables out) of d-mode and 2d-mode filters."""
+    import numpy as np
+
+    import oracle
+    from workloads.generate import ModalParams
+    rng = np.random.default_rng(51)
+    H, d, L = 4, 16, 2048
+    r = rng.uniform(0.8, 0.999, (H, d))
+    lam = r * np.exp(1j * rng.uniform(0.05, np.pi - 0.05, (H, d)))
+    R = (rng.standard_normal((H, d)) + 1j * rng.standard_normal((H, d))) / np.sqrt(2 * d)
+    p = ModalParams(np.stack([lam.real, lam.imag], -1).astype(np.float32),
+                    np.stack([R.real, R.imag], -1).astype(np.float32), rng.standard_normal(H).astype(np.float32))
+    h = oracle.filter_taps(p, L)
+    h32 = h.astype(np.float32)
+    sv_lib = hb.hyena_hankel_singular_values(h32[0], 80)
+    sv_or = oracle.hankel_singular_values(h32[0].astype(np.float64), 80)
+    assert np.max(np.abs(sv_lib - sv_or)) <= 1e-9 * sv_or[0]
+    # the order counts the singular values above the threshold: at most 2d (the real
+    # dimension of d complex modes), the same count as the oracle's spectrum gives
+    order = hb.hyena_modal_order(h32, 80, 1e-7)
+    for g in range(H):
+        sv = oracle.hankel_singular_values(h32[g].astype(np.float64), 80)
+        assert order[g] == np.sum(sv > 1e-7 * sv[0]) and 2 * d - 4 <= order[g] <= 2 * d
+    # fit: the d-mode filter is reproduced from its float32 taps
+    P, Rf, S = hb.hyena_modal_fit_init(h32, d)
+    h_fit = oracle.filter_taps(ModalParams(P, Rf, S), L)
+    assert np.max(np.abs(h_fit - h)) <= 1e-6 * np.max(np.abs(h))
+    Po, Ro, So = oracle.modal_fit_init(h32.astype(np.float64), d)
+    h_or = oracle.filter_taps(ModalParams(Po, Ro, So), L)
+    assert np.max(np.abs(h_or - h)) <= 1e-6 * np.max(np.abs(h))
+    # (clustered poles near the unit circle are ill-determined by float32 taps, so the
+    # filters are compared, not the poles; well-separated poles are compared below)
+    th = np.linspace(0.2, 2.9, 6)
+    lam_s = np.array([0.9, 0.8, 0.95, 0.7, 0.85, 0.6]) * np.exp(1j * th)
+    R_s = np.array([1.0, -0.5j, 0.3 + 0.2j, 0.7, -0.4, 0.25j])
+    ps = ModalParams(np.stack([lam_s.real, lam_s.imag], -1)[None].astype(np.float32),
+                     np.stack([R_s.real, R_s.imag], -1)[None].astype(np.float32), np.array([0.5], np.float32))
+    hs = oracle.filter_taps(ps, 300).astype(np.float32)
+    a = hb.hyena_modal_fit_init(hs, 6)[0][0]
+    b = oracle.modal_fit_init(hs.astype(np.float64), 6)[0][0]
+    a, b = a[:, 0] + 1j * a[:, 1], b[:, 0] + 1j * b[:, 1]
+    assert max(np.min(np.abs(a - z)) for z in b) <= 1e-5
+    assert max(np.min(np.abs(a - z)) for z in lam_s.astype(np.complex64)) <= 1e-5
+    # a 2d-mode filter truncated to d modes: the library's fit is as good as the oracle's
+    lam2 = np.concatenate([lam, lam[:, ::-1] * 0.98], 1)
+    R2 = np.concatenate([R, 0.5 * R], 1)
+    p2 = ModalParams(np.stack([lam2.real, lam2.imag], -1), np.stack([R2.real, R2.imag], -1), p.skip)
+    h2 = oracle.filter_taps(p2, L).astype(np.float32)
+    e_lib = np.sum((oracle.filter_taps(ModalParams(*hb.hyena_modal_fit_init(h2, d)), L) - h2) ** 2, 1)
+    e_or = np.sum((oracle.filter_taps(ModalParams(*oracle.modal_fit_init(h2.astype(np.float64), d)), L) - h2) ** 2, 1)
+    assert np.all(e_lib <= 1.01 * e_or + 1e-9)
+
+
+def test_host_modal_fit_validation(lib):
+    import numpy as np
+    h = np.ones((2, 100), np.float32)
+    for args in [(h, 0), (h, 65), (np.ones((2, 20), np.float32), 8)]:
+        with pytest.raises(hb.HMError):
+            hb.hyena_modal_fit_init(*args)
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_hankel_singular_values(h[0], 51)       # needs L >= 2n
+    assert e.value.status == hb.HM_ERR_INVALID_ARG
+    with pytest.raises(hb.HMError):
+        hb.hyena_modal_order(h, 10, 1.5)

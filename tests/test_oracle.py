@@ -499,3 +499,56 @@ def test_distill_zero_at_generating_parameters_and_hankel_rank(oracle_lib):
     sv = oracle.hankel_singular_values(target[0], 60)
     assert sv[2 * d - 1] > 1e-8 * sv[0]
     assert np.all(sv[2 * d:] <= 1e-10 * sv[0])
+
+
+def _modal_system(rng, H, d, r_lo, r_hi, th_lo=0.05, th_hi=np.pi - 0.05):
+    r = rng.uniform(r_lo, r_hi, (H, d))
+    lam = r * np.exp(1j * rng.uniform(th_lo, th_hi, (H, d)))
+    R = (rng.standard_normal((H, d)) + 1j * rng.standard_normal((H, d))) / np.sqrt(2 * d)
+    return lam, R, rng.standard_normal(H)
+
+
+def test_modal_fit_recovers_generating_parameters(oracle_lib):
+    """A filter generated by d distinct modes (float64 taps) is reproduced by
+    the matrix-pencil fit: the fitted poles are the generating poles (as a set,
+    upper half-plane), the residues match pole by pole, the skip is h[0].
+    A fit with more modes than the filter has puts zero residue on the rest."""
+    import oracle
+    rng = np.random.default_rng(41)
+    for H, d, L, lo, hi in ((3, 8, 400, 0.6, 0.97), (2, 16, 2048, 0.8, 0.999), (2, 1, 40, 0.5, 0.9)):
+        lam, R, D = _modal_system(rng, H, d, lo, hi)
+        p = ModalParams(np.stack([lam.real, lam.imag], -1), np.stack([R.real, R.imag], -1), D)
+        h = oracle_lib.filter_taps(p, L)
+        P, Rf, S = oracle.modal_fit_init(h, d)
+        assert np.array_equal(S, D)
+        for g in range(H):
+            got = P[g, :, 0] + 1j * P[g, :, 1]
+            order = [int(np.argmin(np.abs(got - z))) for z in lam[g]]
+            assert sorted(order) == list(range(d))
+            assert np.max(np.abs(got[order] - lam[g])) <= 1e-8
+            Rg = Rf[g, :, 0] + 1j * Rf[g, :, 1]
+            assert np.max(np.abs(Rg[order] - R[g])) <= 1e-6 * np.max(np.abs(R[g]))
+        # one more mode than the filter holds: the extra one carries (almost) nothing
+        P2, R2, S2 = oracle.modal_fit_init(h, d + 1)
+        h2 = oracle_lib.filter_taps(ModalParams(P2, R2, S2), L)
+        assert np.max(np.abs(h2 - h)) <= 1e-9 * np.max(np.abs(h))
+
+
+def test_modal_fit_keeps_the_strong_modes():
+    """Modal truncation: d strong modes plus d modes with residues 1e-7 times
+    smaller, fitted with d modes -- the fit finds the strong poles and leaves
+    an error of the order of the weak modes."""
+    import oracle
+    rng = np.random.default_rng(42)
+    H, d, L = 2, 4, 600
+    lam, R, D = _modal_system(rng, H, 2 * d, 0.7, 0.95)
+    R[:, d:] *= 1e-7
+    p = ModalParams(np.stack([lam.real, lam.imag], -1), np.stack([R.real, R.imag], -1), D)
+    import oracle as o
+    h = o.filter_taps(p, L)
+    P, Rf, S = oracle.modal_fit_init(h, d)
+    h_fit = o.filter_taps(ModalParams(P, Rf, S), L)
+    assert np.max(np.abs(h_fit - h)) <= 1e-5 * np.max(np.abs(h))
+    for g in range(H):
+        got = P[g, :, 0] + 1j * P[g, :, 1]
+        assert max(np.min(np.abs(got - z)) for z in lam[g, :d]) <= 1e-4
