@@ -788,19 +788,40 @@ def stack_kernel_breakdown(cfg, st, X, stream) -> dict:
     out = {}
     fusable = st.w_in_packed is not None and hb.hyena_layer_step_bf16(
         st.ops[0].desc, st.xd, D, st.w_in_packed[0], RMS_EPS, st.states[0], st.yd, D) == hb.HM_OK
-    if fusable:
-        def fused():
+    gens = []
+    if st.deferred:
+        def gate():
             for l in range(nl):
-                hb.hyena_layer_step_bf16(st.ops[l].desc, st.xd, D, st.w_in_packed[l], RMS_EPS, st.states[l],
-                                         st.yd, D)
+                n = (l + 1) % nl
+                hb.hyena_layer_gate_bf16(st.ops[l].desc, st.xd, st.xd.stride(0), st.w_in_packed[l], RMS_EPS,
+                                         st.rho[l], st.u_prev[l], st.yd, st.yd.stride(0), st.ops[n].desc,
+                                         st.states[n], st.u_prev[n], st.rho[n])
 
         def outp():
             for l in range(nl):
-                hb.hyena_dense_bf16(B, D, D, st.yd, D, st.w_out[l], D, None, st.xd_mid[0], D, workspace=st.ws)
+                hb.hyena_dense_bf16(B, D, D, st.yd, st.yd.stride(0), st.w_out[l], st.w_out[l].stride(0), None,
+                                    st.xd_mid[0], st.xd_mid[0].stride(0), workspace=st.ws)
 
-        for name, fn, byts in (
-                ("fused_in_proj_decode", fused, 3 * D * D * 2 + B * D * 16 * cfg.d + 2 * B * D * 2),
-                ("out_proj", outp, D * D * 2 + 2 * B * D * 2)):
+        # gate + the next layer's prepare: W_in, the layer input read, y written, rho read and u_prev
+        # written; the next layer's state read and written, its u_prev read and rho written
+        gens = [("gate_in_proj_prepare", gate,
+                 3 * D * D * 2 + 2 * B * D * 2 + 2 * B * D * 4 + B * D * 16 * cfg.d + 2 * B * D * 4),
+                ("out_proj", outp, D * D * 2 + 2 * B * D * 2)]
+    elif fusable:
+        def fused():
+            for l in range(nl):
+                hb.hyena_layer_step_bf16(st.ops[l].desc, st.xd, st.xd.stride(0), st.w_in_packed[l], RMS_EPS,
+                                         st.states[l], st.yd, st.yd.stride(0))
+
+        def outp():
+            for l in range(nl):
+                hb.hyena_dense_bf16(B, D, D, st.yd, st.yd.stride(0), st.w_out[l], st.w_out[l].stride(0), None,
+                                    st.xd_mid[0], st.xd_mid[0].stride(0), workspace=st.ws)
+
+        gens = [("fused_in_proj_decode", fused, 3 * D * D * 2 + B * D * 16 * cfg.d + 2 * B * D * 2),
+                ("out_proj", outp, D * D * 2 + 2 * B * D * 2)]
+    if gens:
+        for name, fn, byts in gens:
             fn()
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()

@@ -54,6 +54,8 @@ EXPORTS = (
     "hyena_distill_workspace",
     "hyena_distill_grad",
     "hyena_distill_adam_step",
+    "hyena_decode_prepare",
+    "hyena_layer_gate_bf16",
     "hyena_hankel_singular_values",
     "hyena_modal_order",
     "hyena_modal_fit_init",
@@ -143,6 +145,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         ctypes.c_int),
             "hyena_layer_step_bf16": ([D, p, i64, p, ctypes.c_float, p, p, i64, p], ctypes.c_int),
             "hyena_pack_in_proj_bf16": ([i64, i64, p, i64, p, p], ctypes.c_int),
+            "hyena_decode_prepare": ([D, p, p, p, p], ctypes.c_int),
+            "hyena_layer_gate_bf16": ([D, p, i64, p, ctypes.c_float, p, p, p, i64, D, p, p, p, p], ctypes.c_int),
             "hyena_hankel_singular_values": ([p, i64, i64, p], ctypes.c_int),
             "hyena_modal_order": ([p, i64, i64, i64, ctypes.c_double, p], ctypes.c_int),
             "hyena_modal_fit_init": ([p, i64, i64, i64, f32, p, p, p], ctypes.c_int),
@@ -374,6 +378,26 @@ def hyena_distill_adam_step(H, d, poles, residues, skip, g_poles, g_res, g_skip,
                                         _ptr(g_skip), _ptr(m), _ptr(v), step, lr, beta1, beta2, eps, r_max,
                                         _stream(stream))
     _check(st, "hyena_distill_adam_step")
+
+
+# ----------------------------------------------------------------- generation step, deferred state
+
+
+def hyena_decode_prepare(desc: hm_desc, state, u_prev, rho, stream=None) -> None:
+    _check(load().hyena_decode_prepare(ctypes.byref(desc), _ptr(state), _ptr(u_prev), _ptr(rho), _stream(stream)),
+           "hyena_decode_prepare")
+
+
+def hyena_layer_gate_bf16(desc: hm_desc, x, ldx, w_packed, eps, rho, u_prev, y, ld_y, next_desc=None,
+                          next_state=None, next_u_prev=None, next_rho=None, stream=None) -> int:
+    """Returns the status (HM_ERR_UNSUPPORTED lets a caller fall back)."""
+    nd = ctypes.byref(next_desc) if next_desc is not None else None
+    st = load().hyena_layer_gate_bf16(ctypes.byref(desc), _ptr(x), ldx, _ptr(w_packed), eps, _ptr(rho), _ptr(u_prev),
+                                      _ptr(y), ld_y, nd, _ptr(next_state), _ptr(next_u_prev), _ptr(next_rho),
+                                      _stream(stream))
+    if st not in (HM_OK, HM_ERR_UNSUPPORTED):
+        _check(st, "hyena_layer_gate_bf16")
+    return st
 
 
 # ----------------------------------------------------------------- host-side fit set-up

@@ -19,7 +19,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhyena_modal.so")
 
 SOURCES = ["hm_api.cpp", "decode.hip", "filter.hip", "prefill.hip", "prefill_mfma.hip", "dense.hip", "fir.hip", "fft.hip", "distill.hip",
-           "modal_fit.cpp"]
+           "gen_step.hip", "modal_fit.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -376,8 +376,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // it needs.  The four K quarters are summed through LDS, reusing the A buffers.
 constexpr int kAsLd = 72;  // bf16 per LDS row of the A chunk (64 + 8 pad)
 
-template <int NTW, int SW, bool RMS, int MR, int FDL = 0>
-__global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
+// FDL > 0: the fused decode epilogue (d = FDL modes); FDL < 0: the gate
+// epilogue of the deferred state, y = q (D u + rho), u_prev <- u.  PDD > 0: the
+// workgroup has 8 waves, and waves 4..7 run the prepare of g.prep (d = PDD)
+// while waves 0..3 stream the product: their loads wait on their own
+// counters, so the state stream does not hold up the K loop.
+template <int NTW, int SW, bool RMS, int MR, int FDL = 0, int PDD = 0>
+__global__ __launch_bounds__(PDD > 0 ? 512 : 256) void gemm_stream_lds_kernel(GemmArgs g) {
     constexpr int MT = MR / 16, AL = MR / 8;  // m-tiles; A row-piece loads per chunk
     constexpr int BN = 16 * NTW, NCH = 8;  // K quarter: 8 chunks of 64
     constexpr int WPL = BN / 8;            // W row pieces per lane per chunk (8 rows per load)
@@ -389,12 +394,22 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     // MR = 32: the two row halves of a column tile sit 8 workgroups apart, on one XCD
     int64_t tile = blockIdx.x, m0 = 0;
+    bool active = true;
     if constexpr (MR == 32) {
         const int64_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
         m0 = 32 * (slot % 2);
         tile = (slot / 2) * 8 + xcd;
-        if (tile * BN >= g.N || m0 >= g.M) return;
+        active = !(tile * BN >= g.N || m0 >= g.M);
     }
+    if constexpr (PDD > 0) {
+        if (w >= 4) {  // prepare waves: units of two channels, striding over the grid
+            const int64_t units = g.prep.B * (g.prep.D / 2);
+            for (int64_t u = (int64_t)blockIdx.x * 256 + (tid - 256); u < units; u += (int64_t)gridDim.x * 256)
+                prepare_unit<PDD>(g.prep, u);
+        }
+    }
+    if (!active) return;  // the whole workgroup: no barrier is left behind
+    const bool gemm_wave = (PDD == 0) || w < 4;
     const int64_t n0 = tile * BN;
     const int64_t kbeg = (int64_t)w * NCH * 64;
     const uint16_t *A = static_cast<const uint16_t *>(g.A);
@@ -435,14 +450,13 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
                 rw[c % SW][i] = *pw;
         }
     };
-    static_for<0, SW>([&](auto cc) { load_w(cc); });
-    static_for<0, 2>([&](auto cc) { load_a(cc); });
     // Fused decode step (FDL modes): thread = (row dr of the half, channel pair
     // dcp of the tile's 16 channels).  Its state is loaded only once the K loop
     // is done: loads retire in order, so state loads issued earlier would hold
     // up every later chunk wait (measured on MI355X, B = 64, D = 2048, d = 16:
     // 19.9 us with the loads at kernel start, 18.1 us at the epilogue).
     static_assert(FDL == 0 || (NTW == 3 && MR == 32 && RMS), "fused step: 48 columns = q, k, v of 16 channels");
+    static_assert(PDD == 0 || (FDL < 0 && NTW == 3 && MR == 32 && RMS), "prepare waves ride with the gate");
     const int dr = tid / 8, dcp = tid % 8;
     const int64_t db = m0 + dr, dc = tile * 16 + 2 * dcp;
     const int64_t dg = FDL ? dc / g.P : 0;
@@ -459,7 +473,6 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
             }
         }
     };
-    __builtin_amdgcn_sched_barrier(0);
     f32x4 acc[MT][NTW], ss[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -467,63 +480,71 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < NTW; ++j) acc[m][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // chunk c: its A and W pieces go to the wave's LDS buffers c % 2 (the
-    // wave's LDS operations complete in order, so chunk c - 2's fragment reads
-    // of those buffers are done), the loads for chunks c + 2 (A) and c + SW (W)
-    // are issued into the freed registers, then two 32-wide MFMA steps
-    static_for<0, NCH>([&](auto cc) {
-        constexpr int c = decltype(cc)::value, buf = c % 2;
+    if (gemm_wave) {
+        static_for<0, SW>([&](auto cc) { load_w(cc); });
+        static_for<0, 2>([&](auto cc) { load_a(cc); });
+        __builtin_amdgcn_sched_barrier(0);
+        // chunk c: its A and W pieces go to the wave's LDS buffers c % 2 (the
+        // wave's LDS operations complete in order, so chunk c - 2's fragment reads
+        // of those buffers are done), the loads for chunks c + 2 (A) and c + SW (W)
+        // are issued into the freed registers, then two 32-wide MFMA steps
+        static_for<0, NCH>([&](auto cc) {
+            constexpr int c = decltype(cc)::value, buf = c % 2;
 #pragma unroll
-        for (int i = 0; i < AL; ++i)
-            *reinterpret_cast<u32x4 *>(&as[w][buf][(8 * i + prow) * kAsLd + 8 * ppiece]) = ra[buf][i];
+            for (int i = 0; i < AL; ++i)
+                *reinterpret_cast<u32x4 *>(&as[w][buf][(8 * i + prow) * kAsLd + 8 * ppiece]) = ra[buf][i];
 #pragma unroll
-        for (int i = 0; i < WPL; ++i)
-            *reinterpret_cast<u32x4 *>(&wsm[w][buf][(8 * i + prow) * kAsLd + 8 * ppiece]) = rw[c % SW][i];
-        if constexpr (c + 2 < NCH) load_a(std::integral_constant<int, c + 2>{});
-        if constexpr (c + SW < NCH) load_w(std::integral_constant<int, c + SW>{});
+            for (int i = 0; i < WPL; ++i)
+                *reinterpret_cast<u32x4 *>(&wsm[w][buf][(8 * i + prow) * kAsLd + 8 * ppiece]) = rw[c % SW][i];
+            if constexpr (c + 2 < NCH) load_a(std::integral_constant<int, c + 2>{});
+            if constexpr (c + SW < NCH) load_w(std::integral_constant<int, c + SW>{});
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            uint4 a[MT], b[NTW];
+            for (int h = 0; h < 2; ++h) {
+                uint4 a[MT], b[NTW];
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
-                a[m] = *reinterpret_cast<const uint4 *>(&as[w][buf][(16 * m + lane % 16) * kAsLd + 32 * h + ko]);
+                for (int m = 0; m < MT; ++m)
+                    a[m] = *reinterpret_cast<const uint4 *>(&as[w][buf][(16 * m + lane % 16) * kAsLd + 32 * h + ko]);
 #pragma unroll
-            for (int j = 0; j < NTW; ++j)
-                b[j] = *reinterpret_cast<const uint4 *>(&wsm[w][buf][(16 * j + lane % 16) * kAsLd + 32 * h + ko]);
+                for (int j = 0; j < NTW; ++j)
+                    b[j] = *reinterpret_cast<const uint4 *>(&wsm[w][buf][(16 * j + lane % 16) * kAsLd + 32 * h + ko]);
 #pragma unroll
-            for (int m = 0; m < MT; ++m)
+                for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) acc[m][j] = mfma16(a[m], b[j], acc[m][j]);
-            if constexpr (RMS) {
+                    for (int j = 0; j < NTW; ++j) acc[m][j] = mfma16(a[m], b[j], acc[m][j]);
+                if constexpr (RMS) {
 #pragma unroll
-                for (int m = 0; m < MT; ++m) ss[m] = mfma16(a[m], a[m], ss[m]);
+                    for (int m = 0; m < MT; ++m) ss[m] = mfma16(a[m], a[m], ss[m]);
+                }
             }
-        }
-    });
-    if constexpr (RMS) {
+        });
+        if constexpr (RMS) {
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            int q;
-            const float dg = diag_of(ss[m], lane, q);
-            if (4 * (lane / 16) <= q && q < 4 * (lane / 16) + 4) red_ss[w * MR + m * 16 + q] = dg;
+            for (int m = 0; m < MT; ++m) {
+                int q;
+                const float dg = diag_of(ss[m], lane, q);
+                if (4 * (lane / 16) <= q && q < 4 * (lane / 16) + 4) red_ss[w * MR + m * 16 + q] = dg;
+            }
         }
     }
     load_state();
     __syncthreads();  // every wave is done with its A buffers, which now hold the K-part sums
     float *red = reinterpret_cast<float *>(&as[0][0][0]);
+    if (gemm_wave) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int j = 0; j < NTW; ++j)
+            for (int j = 0; j < NTW; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[(w * MR + m * 16 + 4 * (lane / 16) + r) * BN + j * 16 + lane % 16] = acc[m][j][r];
+                for (int r = 0; r < 4; ++r)
+                    red[(w * MR + m * 16 + 4 * (lane / 16) + r) * BN + j * 16 + lane % 16] = acc[m][j][r];
+    }
     __syncthreads();
-    if constexpr (FDL > 0) {
+    if constexpr (FDL != 0) {
         // q, k, v rounded to bf16 exactly as the projection stores them, then
         // the decode step with the arithmetic of decode_step_fixed (two
         // channels per lane): y = q (D u + Re sum R x), x <- lambda x + u
         float *qkv = reinterpret_cast<float *>(&wsm[0][0][0]);  // [MR][BN]; free after the K loop
-        for (int e = tid; e < MR * BN; e += 256) {
+        for (int e = tid; e < MR * BN && tid < 256; e += 256) {
             const int lr = e / BN, c = e % BN;
             const int64_t row = m0 + lr;
             float v = 0.f;
@@ -537,14 +558,28 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
             qkv[e] = v;
         }
         __syncthreads();
+        if constexpr (FDL < 0) {
+            // the gate of the deferred state: y = q (D u + rho), u_prev <- u
+            if (tid < 256 && db < g.M) {
+                const float *qr = qkv + dr * BN + 2 * dcp;
+                const float u0 = qr[16] * qr[32], u1 = qr[17] * qr[33];
+                const int64_t ldr = g.H * g.P;
+                const float2 rr = *reinterpret_cast<const float2 *>(g.rho + db * ldr + dc);
+                const float Dg = g.skip[dg];
+                __builtin_nontemporal_store(pack_bf16x2(qr[0] * fmaf(Dg, u0, rr.x), qr[1] * fmaf(Dg, u1, rr.y)),
+                                            reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(g.y) + db * g.ld_y + dc));
+                *reinterpret_cast<float2 *>(g.u_prev + db * ldr + dc) = make_float2(u0, u1);
+            }
+            return;
+        }
         if (db < g.M) {
             const float *qr = qkv + dr * BN + 2 * dcp;
             const float q0 = qr[0], q1 = qr[1];
             const float u0 = qr[16] * qr[32], u1 = qr[17] * qr[33];
-            const float2 *lam = g.poles + dg * FDL, *res = g.residues + dg * FDL;
+            const float2 *lam = g.poles + dg * (FDL > 0 ? FDL : 1), *res = g.residues + dg * (FDL > 0 ? FDL : 1);
             float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-            for (int n = 0; n < FDL; ++n) {
+            for (int n = 0; n < (FDL > 0 ? FDL : 0); ++n) {
                 const float2 l = lam[n], r = res[n];
                 const f32x4 xo = xs[n];
                 acc0 = fmaf(r.x, xo[0], acc0);
@@ -562,7 +597,7 @@ __global__ __launch_bounds__(256) void gemm_stream_lds_kernel(GemmArgs g) {
         return;
     }
     uint16_t *C = static_cast<uint16_t *>(g.C);
-    for (int e = tid; e < MR * BN; e += 256) {
+    for (int e = tid; e < MR * BN && tid < 256; e += 256) {
         const int lr = e / BN, c = e % BN;
         const int64_t row = m0 + lr, col = n0 + c;
         if (row >= g.M || col >= g.N) continue;
@@ -793,6 +828,20 @@ hipError_t launch_layer_step(const GemmArgs &g, int d, hipStream_t stream) {
     switch (d) {
         case 8: gemm_stream_lds_kernel<3, 2, true, 32, 8><<<grid, block, 0, stream>>>(g); break;
         case 16: gemm_stream_lds_kernel<3, 2, true, 32, 16><<<grid, block, 0, stream>>>(g); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_layer_gate(const GemmArgs &g, hipStream_t stream) {
+    if (g.M == 0) return hipSuccess;
+    const int64_t tiles = g.N / 48;
+    const dim3 grid((unsigned)(((tiles + 7) / 8) * 16));
+    switch (g.prep.B > 0 ? g.prep.d : 0) {
+        case 0: gemm_stream_lds_kernel<3, 2, true, 32, -1, 0><<<grid, dim3(256), 0, stream>>>(g); break;
+        case 8: gemm_stream_lds_kernel<3, 2, true, 32, -1, 8><<<grid, dim3(512), 0, stream>>>(g); break;
+        case 16: gemm_stream_lds_kernel<3, 2, true, 32, -1, 16><<<grid, dim3(512), 0, stream>>>(g); break;
+        case 32: gemm_stream_lds_kernel<3, 2, true, 32, -1, 32><<<grid, dim3(512), 0, stream>>>(g); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -631,6 +631,80 @@ hm_status hyena_pack_in_proj_bf16(int64_t D, int64_t K, const void *w_in, int64_
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
 }
 
+// ------------------------------------------------------------------ generation step, deferred state
+
+static hm_status prep_of(const hm_desc *desc, float *state, const float *u_prev, float *rho, hm::PrepArgs *p) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    const hm::OpShape s = shape_of(desc);
+    if (s.B > 0 && (!state || !u_prev || !rho)) return HM_ERR_INVALID_ARG;
+    if (!hm::prepare_supported(s.d) || s.P % 2 != 0) return HM_ERR_UNSUPPORTED;
+    if (s.B > 0 && (!aligned(state, 16) || !aligned(u_prev, 8) || !aligned(rho, 8))) return HM_ERR_UNSUPPORTED;
+    p->B = s.B;
+    p->D = s.D;
+    p->H = s.H;
+    p->P = s.P;
+    p->d = s.d;
+    p->state = reinterpret_cast<float2 *>(state);
+    p->u_prev = u_prev;
+    p->rho = rho;
+    p->poles = s.poles;
+    p->residues = s.residues;
+    return HM_OK;
+}
+
+hm_status hyena_decode_prepare(const hm_desc *desc, float *state, const float *u_prev, float *rho, void *stream) {
+    hm::PrepArgs p;
+    hm_status st = prep_of(desc, state, u_prev, rho, &p);
+    if (st != HM_OK) return st;
+    if (p.B == 0) return HM_OK;
+    const hipError_t err = hm::launch_prepare(p, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+hm_status hyena_layer_gate_bf16(const hm_desc *desc, const void *x, int64_t ldx, const void *w_packed, float eps,
+                                const float *rho, float *u_prev, void *y, int64_t ld_y, const hm_desc *next,
+                                float *next_state, const float *next_u_prev, float *next_rho, void *stream) {
+    hm_status st = check_desc(desc);
+    if (st != HM_OK) return st;
+    if (!(eps >= 0.0f)) return HM_ERR_INVALID_ARG;
+    hm::GemmArgs g;
+    if (next && (st = prep_of(next, next_state, next_u_prev, next_rho, &g.prep)) != HM_OK) return st;
+    const hm::OpShape s = shape_of(desc);
+    if (s.B == 0) {
+        if (g.prep.B == 0) return HM_OK;
+        const hipError_t err = hm::launch_prepare(g.prep, static_cast<hipStream_t>(stream));
+        return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+    }
+    if (!x || !w_packed || !rho || !u_prev || !y) return HM_ERR_INVALID_ARG;
+    if (ldx < s.D || ld_y < s.D) return HM_ERR_INVALID_ARG;
+    if (s.act != hm::kBF16 || s.B > 64 || s.D != 2048 || s.P % 16 != 0) return HM_ERR_UNSUPPORTED;
+    if (ldx % 8 != 0 || ld_y % 2 != 0) return HM_ERR_UNSUPPORTED;
+    if (!aligned(x, 16) || !aligned(w_packed, 16) || !aligned(y, 4) || !aligned(rho, 8) || !aligned(u_prev, 8))
+        return HM_ERR_UNSUPPORTED;
+    g.M = s.B;
+    g.N = 3 * s.D;
+    g.K = s.D;
+    g.A = x;
+    g.lda = ldx;
+    g.W = w_packed;
+    g.ldw = s.D;
+    g.row_scale = nullptr;
+    g.C = nullptr;
+    g.ldc = 0;
+    g.rms = true;
+    g.rms_eps = eps;
+    g.skip = s.skip;
+    g.P = s.P;
+    g.H = s.H;
+    g.y = y;
+    g.ld_y = ld_y;
+    g.rho = rho;
+    g.u_prev = u_prev;
+    const hipError_t err = hm::launch_layer_gate(g, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
 hm_status hyena_layer_step_bf16(const hm_desc *desc, const void *x, int64_t ldx, const void *w_packed, float eps,
                                 float *state, void *y, int64_t ld_y, void *stream) {
     hm_status st = check_desc(desc);

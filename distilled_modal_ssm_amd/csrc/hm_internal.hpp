@@ -179,6 +179,49 @@ struct RmsArgs {
     bool vec;        // rows 16-byte aligned and D % 8 == 0
 };
 
+// Deferred state of a generated token (the stack's generation step).  The
+// state of a layer is kept one input behind: s = x - u_prev, where x is the
+// modal state of the recurrence and u_prev the layer's last input u (real, so
+// it adds to the real part of every mode).  "Prepare" turns s and u_prev into
+// the readout of the coming token and the next deferred state,
+//     x = s + u_prev;  rho = Re sum_n R_n x_n;  s <- lambda x,
+// which needs nothing from the coming token; its gate is then
+//     y = q (D u + rho),  u_prev <- u.
+struct PrepArgs {
+    int64_t B = 0, D = 0, H = 0, P = 0, d = 0;  // B = 0: no prepare
+    float2 *state = nullptr;                    // s, [B][H][d][P] complex, in/out
+    const float *u_prev = nullptr;              // [B][D]
+    float *rho = nullptr;                       // [B][D] out
+    const float2 *poles = nullptr, *residues = nullptr;  // [H][d]
+};
+
+// Prepare of one unit: batch row b, channels c and c + 1 (c even, one head;
+// D / H even), unit = b D/2 + c/2.  16-byte state accesses, non-temporal (the
+// state is streamed once per token).
+template <int DD>
+__device__ __forceinline__ void prepare_unit(const PrepArgs &p, int64_t unit) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const int64_t half = p.D / 2, b = unit / half, c = 2 * (unit - b * half), g = c / p.P;
+    f4 *st = reinterpret_cast<f4 *>(p.state + ((b * p.H + g) * DD) * p.P + (c - g * p.P));
+    f4 v[DD];
+#pragma unroll
+    for (int n = 0; n < DD; ++n) v[n] = __builtin_nontemporal_load(st + n * (p.P / 2));
+    const float2 up = *reinterpret_cast<const float2 *>(p.u_prev + b * p.D + c);
+    const float2 *lam = p.poles + g * DD, *res = p.residues + g * DD;
+    float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+    for (int n = 0; n < DD; ++n) {
+        const float2 l = lam[n], r = res[n];
+        const float ar = v[n][0] + up.x, ai = v[n][1], br = v[n][2] + up.y, bi = v[n][3];
+        r0 = fmaf(r.x, ar, fmaf(-r.y, ai, r0));
+        r1 = fmaf(r.x, br, fmaf(-r.y, bi, r1));
+        __builtin_nontemporal_store(f4{fmaf(l.x, ar, -l.y * ai), fmaf(l.x, ai, l.y * ar), fmaf(l.x, br, -l.y * bi),
+                                       fmaf(l.x, bi, l.y * br)},
+                                    st + n * (p.P / 2));
+    }
+    *reinterpret_cast<float2 *>(p.rho + b * p.D + c) = make_float2(r0, r1);
+}
+
 struct GemmArgs {
     int64_t M, N, K;
     const void *A;  // bf16 [M][lda]
@@ -201,7 +244,17 @@ struct GemmArgs {
     int64_t P = 0, H = 0;
     void *y = nullptr;                            // bf16 [M][ld_y]
     int64_t ld_y = 0;
+    // Gate of a generated token with the deferred state (launch_layer_gate only):
+    // the epilogue computes y = q (D u + rho), u_prev <- u for its columns, and
+    // four extra waves per workgroup run the prepare `prep` of another layer.
+    const float *rho = nullptr;   // [M][H*P]
+    float *u_prev = nullptr;      // [M][H*P] out
+    PrepArgs prep;
 };
+
+bool prepare_supported(int64_t d);
+hipError_t launch_prepare(const PrepArgs &p, hipStream_t stream);
+hipError_t launch_layer_gate(const GemmArgs &g, hipStream_t stream);
 
 // Split-K path of the small-M GEMM: 64-column tiles x 256-wide K slices write
 // fp32 partials, a second pass sums them per tile.  Workspace: partials

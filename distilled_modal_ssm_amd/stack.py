@@ -7,6 +7,15 @@ bias, no residual.
 The stack's output at the last prompt position is the first generation input;
 each later generation input is the previous step's output.  Every computation
 is a library call; torch only provides device memory, views and streams.
+
+Generation paths, fastest first (chosen once, from the shape):
+  "deferred": per layer two launches with the state kept one input behind:
+      the gate (RMS-fused in_proj, u = k v, y = q (D u + rho)), whose launch
+      also prepares the next layer's readout from its state, then out_proj;
+      each layer holds s = x - u_prev, u_prev and rho;
+  "fused":    in_proj and decode step in one launch (hyena_layer_step_bf16),
+      then out_proj;
+  "separate": in_proj, decode step and out_proj as three calls.
 """
 
 from __future__ import annotations
@@ -24,7 +33,8 @@ class HyenaStack:
     bfloat16 bit patterns, copied to the device).
     """
 
-    def __init__(self, layers, batch: int, prompt_len: int, device="cuda", fused: bool = True):
+    def __init__(self, layers, batch: int, prompt_len: int, device="cuda", fused: bool = True,
+                 deferred: bool = True):
         import torch
         self.torch = torch
         self.device = torch.device(device)
@@ -57,12 +67,19 @@ class HyenaStack:
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, **e) if ws > 0 else None
         # generation step: in_proj and decode fused into one launch where the
         # library supports the shape (packed in_proj rows), else two calls
+        # deferred-state generation: the shapes hyena_layer_gate_bf16 and
+        # hyena_dense_prepare_bf16 cover (B <= 64, D in {1024, 2048}, d in {8, 16, 32})
+        self.deferred = bool(fused and deferred and B <= 64 and D == 2048 and D // self.ops[0].H % 16 == 0
+                             and all(op.d in (8, 16, 32) for op in self.ops))
+        if self.deferred:
+            self.u_prev = [torch.zeros((B, D), dtype=torch.float32, **e) for _ in range(self.nl)]
+            self.rho = [torch.zeros((B, D), dtype=torch.float32, **e) for _ in range(self.nl)]
         self.w_in_packed = None
         if fused and D % 16 == 0:
             self.w_in_packed = []
             for w in self.w_in:
-                wp = torch.empty_like(w)
-                hb.hyena_pack_in_proj_bf16(D, D, w, D, wp)
+                wp = torch.empty((3 * D, D), dtype=w.dtype, device=w.device)
+                hb.hyena_pack_in_proj_bf16(D, D, w, w.stride(0), wp)
                 self.w_in_packed.append(wp)
 
     def _bf16(self, w):
@@ -77,7 +94,8 @@ class HyenaStack:
     def _layer(self, l, x, out, M, qkv, y, rows_time, prefill: bool):
         D = self.D
         ws = None if prefill else self.ws
-        hb.hyena_dense_rms_bf16(M, 3 * D, D, x, D, self.w_in[l], D, RMS_EPS, qkv, 3 * D, workspace=ws)
+        hb.hyena_dense_rms_bf16(M, 3 * D, D, x, x.stride(0), self.w_in[l], self.w_in[l].stride(0), RMS_EPS, qkv,
+                                3 * D, workspace=ws)
         if prefill:
             B, L = rows_time
             q3 = qkv.view(B, L, 3 * D)
@@ -85,16 +103,29 @@ class HyenaStack:
                                 state_out=self.states[l])
         else:
             self.ops[l].decode_step(qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:], self.states[l], y=y)
-        hb.hyena_dense_bf16(M, D, D, y, D, self.w_out[l], D, None, out, D, workspace=ws)
+        hb.hyena_dense_bf16(M, D, D, y, y.stride(0), self.w_out[l], self.w_out[l].stride(0), None, out,
+                            out.stride(0), workspace=ws)
 
     def _layer_step(self, l, x, out):
         """One generated token through layer l: fused in_proj + decode when supported."""
         D, B = self.D, self.B
+        if self.deferred:
+            # the next layer's prepare rides in this gate's launch
+            nxt = (l + 1) % self.nl
+            st = hb.hyena_layer_gate_bf16(self.ops[l].desc, x, x.stride(0), self.w_in_packed[l], RMS_EPS,
+                                          self.rho[l], self.u_prev[l], self.yd, self.yd.stride(0),
+                                          self.ops[nxt].desc, self.states[nxt], self.u_prev[nxt], self.rho[nxt])
+            if st != hb.HM_OK:
+                raise hb.HMError(st, "hyena_layer_gate_bf16")
+            hb.hyena_dense_bf16(B, D, D, self.yd, self.yd.stride(0), self.w_out[l], self.w_out[l].stride(0),
+                                None, out, out.stride(0), workspace=self.ws)
+            return
         if self.w_in_packed is not None:
-            st = hb.hyena_layer_step_bf16(self.ops[l].desc, x, D, self.w_in_packed[l], RMS_EPS, self.states[l],
-                                          self.yd, D)
+            st = hb.hyena_layer_step_bf16(self.ops[l].desc, x, x.stride(0), self.w_in_packed[l], RMS_EPS,
+                                          self.states[l], self.yd, self.yd.stride(0))
             if st == hb.HM_OK:
-                hb.hyena_dense_bf16(B, D, D, self.yd, D, self.w_out[l], D, None, out, D, workspace=self.ws)
+                hb.hyena_dense_bf16(B, D, D, self.yd, self.yd.stride(0), self.w_out[l], self.w_out[l].stride(0),
+                                    None, out, out.stride(0), workspace=self.ws)
                 return
         self._layer(l, x, out, B, self.qkvd, self.yd, None, False)
 
@@ -114,8 +145,30 @@ class HyenaStack:
         return src
 
     def start_generation(self, prompt_out):
-        """Copy the output at the last prompt position into the step input buffer."""
+        """Copy the output at the last prompt position into the step input buffer
+        (deferred path: every layer's state s = the prefill's state, u_prev = 0,
+        and layer 0's readout prepared for the first generated token; every other
+        layer's prepare rides in the gate launch of the layer before it)."""
         self.xd.copy_(prompt_out.view(self.B, self.L, self.D)[:, -1, :])
+        if self.deferred:
+            for u in self.u_prev:
+                u.zero_()
+            hb.hyena_decode_prepare(self.ops[0].desc, self.states[0], self.u_prev[0], self.rho[0])
+
+    def state_of(self, l):
+        """Layer l's modal state x [B][H][d][P][2] between tokens (for inspection):
+        on the deferred path s + u_prev (u_prev added to the real part of every
+        mode) for layers 1.. (and layer 0 before the first token); layer 0 has
+        been prepared for the coming token (its stored s is lambda x): None."""
+        st = self.states[l]
+        if not self.deferred:
+            return st.clone()
+        if l == 0:
+            return None
+        B, H, d, P = st.shape[0], st.shape[1], st.shape[2], st.shape[3]
+        x = st.clone()
+        x[..., 0] += self.u_prev[l].view(B, H, 1, P)
+        return x
 
     def decode_step(self, record=None):
         """One generated token for every batch row: reads self.xd, writes the output back to self.xd."""

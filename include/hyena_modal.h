@@ -328,6 +328,54 @@ hm_status hyena_layer_step_bf16(const hm_desc *desc, const void *x, int64_t ldx,
 hm_status hyena_pack_in_proj_bf16(int64_t D, int64_t K, const void *w_in, int64_t ldw, void *w_packed,
                                   void *stream);
 
+/* ------------------------------------------------------------------------
+ * A generated token through a projected layer with the state kept one input
+ * behind (the stack's generation step: this gate, then out_proj).
+ *
+ * The decode recurrence (Laughing Hyena Distillery review, 主要发现)
+ *     y = q (D u + Re sum_n R_n x_n),   x_n <- lambda_n x_n + u
+ * is evaluated with the addition of u deferred by one token: the stored
+ * "deferred state" is s = x - u_prev, where u_prev is the layer's previous
+ * input u (u is real, so it enters the real part of every mode).  Then
+ *     prepare:  x = s + u_prev;  rho = Re sum_n R_n x_n;  s <- lambda x
+ * needs nothing from the coming token, and the gate of that token is
+ *     y = q (D u + rho),  u_prev <- u.
+ * The two agree with hyena_modal_decode_step up to float32 rounding.  A
+ * state from a prefill (or any state x) starts as s = x, u_prev = 0.  Between
+ * tokens the state in the usual sense is s + u_prev (u_prev added to the real
+ * parts) for a layer whose prepare has not yet run for the coming token.
+ * Layouts: s as the modal state [B][H][d][D/H] complex, 16-byte aligned;
+ * u_prev and rho float32 [B][D] (row stride D), 8-byte aligned; D/H even.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * prepare for every batch row and channel of desc (d in {8, 16, 32}, else
+ * HM_ERR_UNSUPPORTED): reads s and u_prev, writes rho and the new s in place.
+ */
+hm_status hyena_decode_prepare(const hm_desc *desc, float *state, const float *u_prev, float *rho, void *stream);
+
+/*
+ * The gate of one generated token for every batch row, on packed in_proj
+ * weights (hyena_pack_in_proj_bf16):
+ *   [q|k|v] = bf16( x W_in^T / sqrt(mean_k x[b][k]^2 + eps) )   (as hyena_dense_rms_bf16)
+ *   u = k v;  y = bf16( q (D_h u + rho) );  u_prev <- u
+ * with rho from the prepare of this token.  In the same launch, four extra
+ * waves per workgroup run hyena_decode_prepare of `next` (another operator:
+ * the next layer, whose prepare needs nothing from this one) unless next is
+ * NULL, so its state stream shares the launch with this weight stream.
+ *   x       bf16 [B][ldx], the layer input (D columns)
+ *   w_packed bf16 [3D][D] packed in_proj;  rho float32 [B][D] in;
+ *   u_prev  float32 [B][D] out;  y bf16 [B][ld_y]
+ *   next_state, next_u_prev, next_rho: as in hyena_decode_prepare for `next`
+ * Supported: act_dtype HM_BF16, B <= 64, D = 2048, D/H a multiple of 16,
+ * ldx a multiple of 8, ld_y even, x / w_packed 16-byte and y 4-byte aligned
+ * (else HM_ERR_UNSUPPORTED).  Null pointers, ldx or ld_y < D, eps < 0 ->
+ * HM_ERR_INVALID_ARG.  y must not overlap x.
+ */
+hm_status hyena_layer_gate_bf16(const hm_desc *desc, const void *x, int64_t ldx, const void *w_packed, float eps,
+                                const float *rho, float *u_prev, void *y, int64_t ld_y, const hm_desc *next,
+                                float *next_state, const float *next_u_prev, float *next_rho, void *stream);
+
 /*
  * Non-distilled baseline: the Hyena operator's decode step through its
  * explicit long filter (StripedHyena article, Hyena層次結構) instead of the

@@ -521,3 +521,36 @@ def test_host_modal_fit_validation(lib):
     assert e.value.status == hb.HM_ERR_INVALID_ARG
     with pytest.raises(hb.HMError):
         hb.hyena_modal_order(h, 10, 1.5)
+
+
+def test_deferred_generation_validation(lib):
+    """The prepare and the gate of the deferred state reject bad arguments on
+    the host, before any HIP call."""
+    d = _desc(batch=4, channels=2048, heads=16, modes=16, act_dtype=hb.HM_BF16)
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_decode_prepare(d, None, FAKE, FAKE, stream=0)
+    assert e.value.status == hb.HM_ERR_INVALID_ARG
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_decode_prepare(_desc(batch=4, channels=2048, heads=16, modes=12), FAKE, FAKE, FAKE, stream=0)
+    assert e.value.status == hb.HM_ERR_UNSUPPORTED          # d = 12 has no prepare kernel
+    with pytest.raises(hb.HMError) as e:
+        hb.hyena_decode_prepare(d, FAKE + 8, FAKE, FAKE, stream=0)
+    assert e.value.status == hb.HM_ERR_UNSUPPORTED          # state not 16-byte aligned
+    hb.hyena_decode_prepare(_desc(batch=0), None, None, None, stream=0)   # nothing to do
+    ok = dict(x=FAKE, ldx=2048, w=FAKE, eps=1e-6, rho=FAKE, u=FAKE, y=FAKE, ld_y=2048)
+
+    def gate(dd=d, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return hb.hyena_layer_gate_bf16(dd, a["x"], a["ldx"], a["w"], a["eps"], a["rho"], a["u"], a["y"], a["ld_y"],
+                                        stream=0)
+    for kw, status in [(dict(x=None), hb.HM_ERR_INVALID_ARG), (dict(ldx=100), hb.HM_ERR_INVALID_ARG),
+                       (dict(eps=-1.0), hb.HM_ERR_INVALID_ARG), (dict(rho=None), hb.HM_ERR_INVALID_ARG)]:
+        with pytest.raises(hb.HMError) as e:
+            gate(**kw)
+        assert e.value.status == status, kw
+    # shapes outside the launch report HM_ERR_UNSUPPORTED (the stack then takes another path)
+    assert gate(dd=_desc(batch=65, channels=2048, heads=16, modes=16, act_dtype=hb.HM_BF16)) == hb.HM_ERR_UNSUPPORTED
+    assert gate(dd=_desc(batch=4, channels=1024, heads=16, modes=16, act_dtype=hb.HM_BF16)) == hb.HM_ERR_UNSUPPORTED
+    assert gate(dd=_desc(batch=4, channels=2048, heads=16, modes=16)) == hb.HM_ERR_UNSUPPORTED  # float32
+    assert gate(x=FAKE + 2) == hb.HM_ERR_UNSUPPORTED

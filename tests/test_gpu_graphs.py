@@ -110,9 +110,10 @@ def test_prefill_graph_replays_chunked():
 
 
 def test_stack_token_graph_replays():
-    """One generated token through a two-layer projected stack (RMS-fused
-    in_proj, decode step, out_proj per layer), captured once and replayed
-    token after token, as the benchmark does."""
+    """One generated token through a two-layer projected stack (per layer the
+    gate with the RMS-fused in_proj, then out_proj with the next layer's
+    prepare), captured once and replayed token after token, as the benchmark
+    does."""
     torch = require_gpu()
     from distilled_modal_ssm_amd.stack import HyenaStack
     cfg = dataclasses.replace(get_config(5), layers=2, B=4, L=128)
@@ -123,17 +124,20 @@ def test_stack_token_graph_replays():
     out = st.prefill(X)
     st.start_generation(out)
     torch.cuda.synchronize()
+    # the generation state: every layer's state buffer and, on the deferred
+    # path, its u_prev and rho
+    gen = list(st.states) + (list(st.u_prev) + list(st.rho) if st.deferred else [])
     x_start = st.xd.clone()
-    s_start = [s.clone() for s in st.states]
+    s_start = [s.clone() for s in gen]
     tokens = 4
     ref = []
     for _ in range(tokens):
         ref.append(st.decode_step().clone())
-    s_ref = [s.clone() for s in st.states]
+    s_ref = [s.clone() for s in gen]
     torch.cuda.synchronize()
 
     st.xd.copy_(x_start)
-    for s, s0 in zip(st.states, s_start):
+    for s, s0 in zip(gen, s_start):
         s.copy_(s0)
     graph = torch.cuda.CUDAGraph()
     log("stack graph: capture")
@@ -141,7 +145,7 @@ def test_stack_token_graph_replays():
         st.decode_step()
     for r in range(REPLAYS):
         st.xd.copy_(x_start)
-        for s, s0 in zip(st.states, s_start):
+        for s, s0 in zip(gen, s_start):
             s.copy_(s0)
         for t in range(tokens):
             _busy(torch, x_start)
@@ -149,8 +153,8 @@ def test_stack_token_graph_replays():
             graph.replay()
             torch.cuda.synchronize()
             assert torch.equal(st.xd, ref[t]), f"pass {r} token {t}"
-        for s, s1 in zip(st.states, s_ref):
-            assert torch.equal(s, s1), f"pass {r}: states"
+        for s, s1 in zip(gen, s_ref):
+            assert torch.equal(s, s1), f"pass {r}: generation state"
 
 
 def test_fir_graph_replays():

@@ -199,7 +199,7 @@ def test_stack_generation_fused_matches_separate_calls():
     outs = {}
     for fused in (False, True):
         log(f"stack generation fused={fused}")
-        st = HyenaStack(layers, cfg.B, cfg.L, fused=fused)
+        st = HyenaStack(layers, cfg.B, cfg.L, fused=fused, deferred=False)
         st.start_generation(st.prefill(X))
         outs[fused] = [st.decode_step().clone() for _ in range(6)]
         outs[(fused, "state")] = [s.clone() for s in st.states]
@@ -208,6 +208,91 @@ def test_stack_generation_fused_matches_separate_calls():
         assert torch.equal(a, b), f"token {t}"
     for a, b in zip(outs[(False, "state")], outs[(True, "state")]):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("B,d,H", [(64, 16, 16), (40, 16, 16), (1, 8, 16), (33, 32, 32)])
+def test_deferred_gate_and_prepare_match_separate_calls(B, d, H):
+    """One generated token through a layer with the deferred state: prepare
+    (s, u_prev -> rho, lambda (s + u_prev)), then the gate (packed in_proj with
+    the RMS, u = k v, y = q (D u + rho)), against the separate in_proj and
+    decode calls on x = s + u_prev.  The products are the fused step's, so q, k
+    and v are the same bf16 values on both sides: y agrees to bf16 rounding
+    and the state to float32 rounding.  The prepare that rides in the gate's
+    launch equals the standalone prepare bit for bit."""
+    torch = require_gpu()
+    from distilled_modal_ssm_amd import ModalHyena
+    D = 2048
+    rng = np.random.default_rng(90 + B + d)
+    poles, res, skip = _layer_params(rng, H, d)
+    g = torch.Generator(device="cuda").manual_seed(100 + B + d)
+    x = torch.randn(B, D, generator=g, device="cuda").to(torch.bfloat16)
+    w_in = (torch.randn(3 * D, D, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+    wp = torch.empty_like(w_in)
+    hb.hyena_pack_in_proj_bf16(D, D, w_in, D, wp)
+    op = ModalHyena(poles, res, skip, B, D, "bf16")
+    s0 = torch.randn(op.new_state().shape, generator=g, device="cuda") * 0.3
+    u0 = torch.randn(B, D, generator=g, device="cuda") * 0.5
+    st_ref = s0.clone()
+    st_ref[..., 0] += u0.view(B, H, 1, D // H)
+    log(f"deferred B={B} d={d} H={H}: separate calls")
+    qkv = torch.empty(B, 3 * D, dtype=torch.bfloat16, device="cuda")
+    hb.hyena_dense_rms_bf16(B, 3 * D, D, x, D, w_in, D, 1e-6, qkv, 3 * D)
+    y_ref = torch.empty(B, D, dtype=torch.bfloat16, device="cuda")
+    op.decode_step(qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:], st_ref, y=y_ref)
+    log(f"deferred B={B} d={d}: prepare + gate")
+    s, u, rho = s0.clone(), u0.clone(), torch.empty(B, D, device="cuda")
+    hb.hyena_decode_prepare(op.desc, s, u, rho)
+    # another operator's prepare rides along in the gate's launch
+    poles2, res2, skip2 = _layer_params(rng, H, d)
+    op2 = ModalHyena(poles2, res2, skip2, B, D, "bf16")
+    s2 = torch.randn(op2.new_state().shape, generator=g, device="cuda")
+    u2 = torch.randn(B, D, generator=g, device="cuda")
+    s2a, rho2a = s2.clone(), torch.empty(B, D, device="cuda")
+    s2b, rho2b = s2.clone(), torch.empty(B, D, device="cuda")
+    hb.hyena_decode_prepare(op2.desc, s2b, u2, rho2b)
+    y = torch.full_like(y_ref, 7.0)
+    assert hb.hyena_layer_gate_bf16(op.desc, x, D, wp, 1e-6, rho, u, y, D, op2.desc, s2a, u2, rho2a) == hb.HM_OK
+    torch.cuda.synchronize()
+    assert rel_err(to_np64(y), to_np64(y_ref)) <= 1e-2
+    assert torch.equal(s2a, s2b) and torch.equal(rho2a, rho2b)
+    # u is this token's k v; the state after the token is s + u in the real parts
+    qf = qkv.float()
+    assert torch.equal(u, qf[:, D:2 * D] * qf[:, 2 * D:])
+    x_new = s.clone()
+    x_new[..., 0] += u.view(B, H, 1, D // H)
+    assert rel_err(to_np64(x_new), to_np64(st_ref)) <= 1e-5
+
+
+def test_stack_deferred_generation_matches_separate_calls():
+    """Generated tokens through a two-layer stack on the deferred path against
+    the separate calls, teacher-forced: after each token both stacks take the
+    separate path's output as the next input (the stack is chaotic, so free
+    running would amplify rounding differences).  Outputs agree to bf16
+    rounding.  Layer 1's input is layer 0's bf16 output, which the two paths
+    may round differently in the last place, so its state agrees to the bf16
+    scale (1e-2 of its largest value), not to float32."""
+    torch = require_gpu()
+    import dataclasses
+    from distilled_modal_ssm_amd.stack import HyenaStack
+    cfg = dataclasses.replace(get_config(5), layers=2, L=64)
+    layers = [(modal_params(cfg, l), *dense_weights(cfg, l)) for l in range(cfg.layers)]
+    X = torch.randn(cfg.B, cfg.L, cfg.D, device="cuda").to(torch.bfloat16)
+    ref = HyenaStack(layers, cfg.B, cfg.L, fused=False)
+    dfr = HyenaStack(layers, cfg.B, cfg.L)
+    assert dfr.deferred and not ref.deferred
+    log("stack deferred vs separate: prefill")
+    ref.start_generation(ref.prefill(X))
+    dfr.start_generation(dfr.prefill(X))
+    for t in range(6):
+        log(f"stack deferred vs separate: token {t}")
+        dfr.xd.copy_(ref.xd)
+        a, b = ref.decode_step().clone(), dfr.decode_step().clone()
+        torch.cuda.synchronize()
+        e = rel_err(to_np64(b), to_np64(a))
+        assert e <= 2e-2, f"token {t}: {e:.2e}"
+        es = rel_err(to_np64(dfr.state_of(1)), to_np64(ref.states[1]))
+        print(f"token {t}: output rel err {e:.2e}, layer-1 state rel err {es:.2e}")
+        assert es <= 1e-2
 
 
 def test_stack_generation_falls_back_when_fusion_does_not_cover_the_shape():

@@ -20,8 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HERE = os.path.join(ROOT, "tests", "sanitize")
 CSRC = os.path.join(ROOT, "distilled_modal_ssm_amd", "csrc")
 HIPCC = "/opt/rocm/bin/hipcc"
-LIB_SOURCES = ["hm_api.cpp", "decode.hip", "filter.hip", "prefill.hip", "prefill_mfma.hip", "dense.hip", "fir.hip",
-               "fft.hip", "distill.hip"]
+from distilled_modal_ssm_amd.build import SOURCES as LIB_SOURCES  # every source the library links
 # host-only instrumentation for hipcc
 HOST_SAN = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined -Xarch_host -fno-sanitize-recover=all"
 
