@@ -391,6 +391,7 @@ __global__ __launch_bounds__(PDD > 0 ? 512 : 256) void gemm_stream_lds_kernel(Ge
     __shared__ __attribute__((aligned(16))) uint16_t wsm[4][2][BN * kAsLd];
     __shared__ float red_ss[RMS ? 4 * MR : 1];
     static_assert(4 * MR * BN * sizeof(float) <= sizeof(as), "the K-part sums reuse the A buffers");
+    __shared__ unsigned arrivals;  // product waves past each epilogue sync point (PDD > 0)
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
     // MR = 32: the two row halves of a column tile sit 8 workgroups apart, on one XCD
     int64_t tile = blockIdx.x, m0 = 0;
@@ -402,10 +403,21 @@ __global__ __launch_bounds__(PDD > 0 ? 512 : 256) void gemm_stream_lds_kernel(Ge
         active = !(tile * BN >= g.N || m0 >= g.M);
     }
     if constexpr (PDD > 0) {
-        if (w >= 4) {  // prepare waves: units of two channels, striding over the grid
+        // Prepare waves: units of two channels, striding over the grid.  They
+        // take no part in the product and end here.  A barrier waits only for
+        // the workgroup's waves that have not ended, so the product's epilogue
+        // does not wait for the state stream (measured on MI355X, B = 64,
+        // D = 2048, d = 16: the first epilogue barrier waited 2.2 us for them).
+        // readfirstlane makes the exit a wave-uniform branch.  The product
+        // waves then synchronise through an LDS arrival count (gemm_sync below),
+        // not a barrier, which would wait for the prepare waves to end.
+        if (tid == 0) arrivals = 0;
+        __syncthreads();
+        if (__builtin_amdgcn_readfirstlane(w) >= 4) {
             const int64_t units = g.prep.B * (g.prep.D / 2);
             for (int64_t u = (int64_t)blockIdx.x * 256 + (tid - 256); u < units; u += (int64_t)gridDim.x * 256)
                 prepare_unit<PDD>(g.prep, u);
+            return;
         }
     }
     if (!active) return;  // the whole workgroup: no barrier is left behind
@@ -526,8 +538,21 @@ __global__ __launch_bounds__(PDD > 0 ? 512 : 256) void gemm_stream_lds_kernel(Ge
             }
         }
     }
+    // Workgroup sync of the product waves.  With prepare waves (PDD > 0) it is
+    // an LDS arrival count: lane 0 of each of the four product waves adds one
+    // (release), then the wave waits for the count to reach `target` (acquire).
+    // The four product waves of an active workgroup all reach both sync points.
+    auto gemm_sync = [&](unsigned target) {
+        if constexpr (PDD > 0) {
+            if (lane == 0) __hip_atomic_fetch_add(&arrivals, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            while (__hip_atomic_load(&arrivals, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+                __builtin_amdgcn_s_sleep(1);
+        } else {
+            __syncthreads();
+        }
+    };
     load_state();
-    __syncthreads();  // every wave is done with its A buffers, which now hold the K-part sums
+    gemm_sync(4);  // every wave is done with its A buffers, which now hold the K-part sums
     float *red = reinterpret_cast<float *>(&as[0][0][0]);
     if (gemm_wave) {
 #pragma unroll
@@ -538,62 +563,57 @@ __global__ __launch_bounds__(PDD > 0 ? 512 : 256) void gemm_stream_lds_kernel(Ge
                 for (int r = 0; r < 4; ++r)
                     red[(w * MR + m * 16 + 4 * (lane / 16) + r) * BN + j * 16 + lane % 16] = acc[m][j][r];
     }
-    __syncthreads();
+    gemm_sync(8);
     if constexpr (FDL != 0) {
-        // q, k, v rounded to bf16 exactly as the projection stores them, then
-        // the decode step with the arithmetic of decode_step_fixed (two
-        // channels per lane): y = q (D u + Re sum R x), x <- lambda x + u
-        float *qkv = reinterpret_cast<float *>(&wsm[0][0][0]);  // [MR][BN]; free after the K loop
-        for (int e = tid; e < MR * BN && tid < 256; e += 256) {
-            const int lr = e / BN, c = e % BN;
-            const int64_t row = m0 + lr;
-            float v = 0.f;
-            if (row < g.M) {
-                const float sum = red[(0 * MR + lr) * BN + c] + red[(1 * MR + lr) * BN + c] +
-                                  red[(2 * MR + lr) * BN + c] + red[(3 * MR + lr) * BN + c];
-                const float sc = rms_scale(red_ss[lr] + red_ss[MR + lr] + red_ss[2 * MR + lr] + red_ss[3 * MR + lr],
-                                           g.K, g.rms_eps);
-                v = bf16_lo(f32_to_bf16(sum * sc));
+        // Each thread's row dr and two channels: q, k, v straight from the
+        // K-part sums, rounded to bf16 exactly as the projection stores them
+        // (one inverse RMS per thread, all LDS reads in flight together; a
+        // staging pass over the tile with a scale per element took 1.5 us of
+        // the launch on MI355X), then the gate or the decode step.
+        if (tid >= 256 || db >= g.M) return;
+        const float sc = rms_scale(red_ss[dr] + red_ss[MR + dr] + red_ss[2 * MR + dr] + red_ss[3 * MR + dr], g.K,
+                                   g.rms_eps);
+        float qv[6];  // q, k, v of channels dc and dc + 1
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = 16 * j + 2 * dcp + h;
+                const float sum = red[(0 * MR + dr) * BN + c] + red[(1 * MR + dr) * BN + c] +
+                                  red[(2 * MR + dr) * BN + c] + red[(3 * MR + dr) * BN + c];
+                qv[2 * j + h] = bf16_lo(f32_to_bf16(sum * sc));
             }
-            qkv[e] = v;
-        }
-        __syncthreads();
+        const float q0 = qv[0], q1 = qv[1];
+        const float u0 = qv[2] * qv[4], u1 = qv[3] * qv[5];
         if constexpr (FDL < 0) {
             // the gate of the deferred state: y = q (D u + rho), u_prev <- u
-            if (tid < 256 && db < g.M) {
-                const float *qr = qkv + dr * BN + 2 * dcp;
-                const float u0 = qr[16] * qr[32], u1 = qr[17] * qr[33];
-                const int64_t ldr = g.H * g.P;
-                const float2 rr = *reinterpret_cast<const float2 *>(g.rho + db * ldr + dc);
-                const float Dg = g.skip[dg];
-                __builtin_nontemporal_store(pack_bf16x2(qr[0] * fmaf(Dg, u0, rr.x), qr[1] * fmaf(Dg, u1, rr.y)),
-                                            reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(g.y) + db * g.ld_y + dc));
-                *reinterpret_cast<float2 *>(g.u_prev + db * ldr + dc) = make_float2(u0, u1);
-            }
+            const int64_t ldr = g.H * g.P;
+            const float2 rr = *reinterpret_cast<const float2 *>(g.rho + db * ldr + dc);
+            const float Dg = g.skip[dg];
+            __builtin_nontemporal_store(pack_bf16x2(q0 * fmaf(Dg, u0, rr.x), q1 * fmaf(Dg, u1, rr.y)),
+                                        reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(g.y) + db * g.ld_y + dc));
+            *reinterpret_cast<float2 *>(g.u_prev + db * ldr + dc) = make_float2(u0, u1);
             return;
         }
-        if (db < g.M) {
-            const float *qr = qkv + dr * BN + 2 * dcp;
-            const float q0 = qr[0], q1 = qr[1];
-            const float u0 = qr[16] * qr[32], u1 = qr[17] * qr[33];
-            const float2 *lam = g.poles + dg * (FDL > 0 ? FDL : 1), *res = g.residues + dg * (FDL > 0 ? FDL : 1);
-            float acc0 = 0.f, acc1 = 0.f;
+        // the decode step with the arithmetic of decode_step_fixed (two
+        // channels per lane): y = q (D u + Re sum R x), x <- lambda x + u
+        const float2 *lam = g.poles + dg * (FDL > 0 ? FDL : 1), *res = g.residues + dg * (FDL > 0 ? FDL : 1);
+        float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-            for (int n = 0; n < (FDL > 0 ? FDL : 0); ++n) {
-                const float2 l = lam[n], r = res[n];
-                const f32x4 xo = xs[n];
-                acc0 = fmaf(r.x, xo[0], acc0);
-                acc0 = fmaf(-r.y, xo[1], acc0);
-                acc1 = fmaf(r.x, xo[2], acc1);
-                acc1 = fmaf(-r.y, xo[3], acc1);
-                const f32x4 xn = {fmaf(l.x, xo[0], fmaf(-l.y, xo[1], u0)), fmaf(l.x, xo[1], l.y * xo[0]),
-                                  fmaf(l.x, xo[2], fmaf(-l.y, xo[3], u1)), fmaf(l.x, xo[3], l.y * xo[2])};
-                __builtin_nontemporal_store(xn, reinterpret_cast<f32x4 *>(dst + n * g.P));
-            }
-            const float Dg = g.skip[dg];
-            __builtin_nontemporal_store(pack_bf16x2(q0 * fmaf(Dg, u0, acc0), q1 * fmaf(Dg, u1, acc1)),
-                                        reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(g.y) + db * g.ld_y + dc));
+        for (int n = 0; n < (FDL > 0 ? FDL : 0); ++n) {
+            const float2 l = lam[n], r = res[n];
+            const f32x4 xo = xs[n];
+            acc0 = fmaf(r.x, xo[0], acc0);
+            acc0 = fmaf(-r.y, xo[1], acc0);
+            acc1 = fmaf(r.x, xo[2], acc1);
+            acc1 = fmaf(-r.y, xo[3], acc1);
+            const f32x4 xn = {fmaf(l.x, xo[0], fmaf(-l.y, xo[1], u0)), fmaf(l.x, xo[1], l.y * xo[0]),
+                              fmaf(l.x, xo[2], fmaf(-l.y, xo[3], u1)), fmaf(l.x, xo[3], l.y * xo[2])};
+            __builtin_nontemporal_store(xn, reinterpret_cast<f32x4 *>(dst + n * g.P));
         }
+        const float Dg = g.skip[dg];
+        __builtin_nontemporal_store(pack_bf16x2(q0 * fmaf(Dg, u0, acc0), q1 * fmaf(Dg, u1, acc1)),
+                                    reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(g.y) + db * g.ld_y + dc));
         return;
     }
     uint16_t *C = static_cast<uint16_t *>(g.C);
