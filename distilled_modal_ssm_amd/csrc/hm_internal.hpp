@@ -197,27 +197,34 @@ struct PrepArgs {
 
 // Prepare of one unit: batch row b, channels c and c + 1 (c even, one head;
 // D / H even), unit = b D/2 + c/2.  16-byte state accesses, non-temporal (the
-// state is streamed once per token).
+// state is streamed once per token).  The modes go in two halves, each loaded
+// whole, then updated and stored, so the state's stores start after half of
+// its loads (measured on MI355X riding in the 24-layer stack's gate at batch
+// 64, d = 16: 16.6 -> 16.4 us per layer; quarters 16.7 us).
 template <int DD>
 __device__ __forceinline__ void prepare_unit(const PrepArgs &p, int64_t unit) {
     typedef float f4 __attribute__((ext_vector_type(4)));
+    constexpr int HB = DD / 2;
     const int64_t half = p.D / 2, b = unit / half, c = 2 * (unit - b * half), g = c / p.P;
     f4 *st = reinterpret_cast<f4 *>(p.state + ((b * p.H + g) * DD) * p.P + (c - g * p.P));
-    f4 v[DD];
-#pragma unroll
-    for (int n = 0; n < DD; ++n) v[n] = __builtin_nontemporal_load(st + n * (p.P / 2));
     const float2 up = *reinterpret_cast<const float2 *>(p.u_prev + b * p.D + c);
     const float2 *lam = p.poles + g * DD, *res = p.residues + g * DD;
     float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-    for (int n = 0; n < DD; ++n) {
-        const float2 l = lam[n], r = res[n];
-        const float ar = v[n][0] + up.x, ai = v[n][1], br = v[n][2] + up.y, bi = v[n][3];
-        r0 = fmaf(r.x, ar, fmaf(-r.y, ai, r0));
-        r1 = fmaf(r.x, br, fmaf(-r.y, bi, r1));
-        __builtin_nontemporal_store(f4{fmaf(l.x, ar, -l.y * ai), fmaf(l.x, ai, l.y * ar), fmaf(l.x, br, -l.y * bi),
-                                       fmaf(l.x, bi, l.y * br)},
-                                    st + n * (p.P / 2));
+    for (int h0 = 0; h0 < DD; h0 += HB) {
+        f4 v[HB];
+#pragma unroll
+        for (int n = 0; n < HB; ++n) v[n] = __builtin_nontemporal_load(st + (h0 + n) * (p.P / 2));
+#pragma unroll
+        for (int n = 0; n < HB; ++n) {
+            const float2 l = lam[h0 + n], r = res[h0 + n];
+            const float ar = v[n][0] + up.x, ai = v[n][1], br = v[n][2] + up.y, bi = v[n][3];
+            r0 = fmaf(r.x, ar, fmaf(-r.y, ai, r0));
+            r1 = fmaf(r.x, br, fmaf(-r.y, bi, r1));
+            __builtin_nontemporal_store(f4{fmaf(l.x, ar, -l.y * ai), fmaf(l.x, ai, l.y * ar), fmaf(l.x, br, -l.y * bi),
+                                           fmaf(l.x, bi, l.y * br)},
+                                        st + (h0 + n) * (p.P / 2));
+        }
     }
     *reinterpret_cast<float2 *>(p.rho + b * p.D + c) = make_float2(r0, r1);
 }

@@ -274,8 +274,13 @@ __device__ __forceinline__ int yt_index(int row, int col, int ld) { return row *
 // pieces (else element loads, for rows that are not 16-byte aligned; the full
 // pass always needs them aligned).
 // PF: sub-blocks of q, k, v loads kept in flight (1 or 2).
-template <int DD, int PT, int ACT, bool SO, bool VEC, int PF>
-__global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const float2 *carry0) {
+// RS: row parts per sub-block (1 or 2).  With RS = 2 the workgroup has twice
+// the waves: part 0 (the first PT / 16 waves) stages u, computes Y rows 0..31
+// and the first half of the state modes, and gates and stores y; part 1
+// computes Y rows 32..63 and the other half of the modes.  Both share the LDS
+// tables and the u and x tiles, and pass the same two barriers per sub-block.
+template <int DD, int PT, int ACT, bool SO, bool VEC, int PF, int RS>
+__global__ __launch_bounds__(4 * PT * RS) void chunk_mfma_kernel(PrefillArgs a, const float2 *carry0) {
     using G = MfmaGeom<DD>;
     using T = typename Act<ACT>::T;
     // a thread's channels: CGW * cg + (e & 3) + SPLIT * (e >> 2), e = 0..7
@@ -283,16 +288,18 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
     using PC = typename std::conditional<VEC, Piece<ACT, SPLIT>, PieceScalar<ACT, SPLIT>>::type;
     constexpr int D2 = G::D2, KC = G::KC, MTS = G::MTS, NFRAG = G::NFRAG;
     constexpr int NP = parts_of(ACT);          // bfloat16 parts per operand
-    constexpr int NTHR = 4 * PT;               // PT / 16 waves
+    constexpr int NTHR = 4 * PT * RS;          // PT / 16 waves per row part
+    constexpr int NSTG = 4 * PT;               // staging threads: row part 0
     constexpr int CW = 16, NTW = 1;            // channels and 16-wide tiles per wave
     constexpr int RG = 2;                      // staging rows per thread (two steps per 32-bit LDS word)
     constexpr int CG = PT / 8;                 // 8-channel groups per row
     constexpr int LX = D2 + 8;                 // LDS row of x (bf16), per channel
     constexpr int LQ = PT + 4;                 // LDS row of the Y tile (float), per step
     static_assert(PT == 64 || PT == 128, "channel tile");
-    static_assert((64 / RG) * CG == NTHR, "one staging piece group per thread");
+    static_assert((64 / RG) * CG == NSTG, "one staging piece group per staging thread");
     static_assert(VEC || SO, "the full pass loads 16-byte pieces");
     static_assert(PF == 1 || PF == 2, "prefetch depth");
+    static_assert(RS == 1 || (RS == 2 && MTS % 2 == 0), "row parts");
 
     __shared__ uint4 tab[NFRAG * NP * kWave];
     __shared__ __attribute__((aligned(16))) uint16_t ub[NP][PT * kLU];          // u parts, [channel][step]
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
     const int64_t c = blockIdx.y, b = blockIdx.z;
     const int64_t p0 = (int64_t)ct * PT;
     const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
-    const int cw = w * CW;  // first local channel of this wave
+    const int cw = (w % (PT / 16)) * CW;  // first local channel of this wave
 
     // per-head tables -> LDS
     {
@@ -319,85 +326,95 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
             lamT[tid] = reinterpret_cast<const float2 *>(a.ws + a.plan.off_mfma_lam)[(int64_t)g * (D2 / 2) + tid];
     }
 
-    // entering state in C-tile layout: Xr[ms][j] holds mode rows 16ms + 4(l/16) + 0..3
-    // (modes 8ms + 2(l/16) and +1, Re/Im interleaved) of channel cw + 16j + l%16
-    f32x4 Xr[MTS][NTW];
-    {
-        const float2 *src = SO ? nullptr : (c == 0) ? carry0
-                                     : reinterpret_cast<const float2 *>(a.ws + a.plan.off_carry) +
-                                           c * (s.B * H * DD * P);
-#pragma unroll
-        for (int ms = 0; ms < MTS; ++ms)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int64_t p = p0 + cw + 16 * j + lane % 16;
-                const int n0 = 8 * ms + 2 * (lane / 16);
-                float2 x0 = make_float2(0.f, 0.f), x1 = make_float2(0.f, 0.f);
-                if (src && n0 < DD) x0 = src[((b * H + g) * DD + n0) * P + p];
-                if (src && n0 + 1 < DD) x1 = src[((b * H + g) * DD + n0 + 1) * P + p];
-                Xr[ms][j] = f32x4{x0.x, x0.y, x1.x, x1.y};
-            }
-    }
-    auto write_x = [&]() {
-#pragma unroll
-        for (int ms = 0; ms < MTS; ++ms)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                f32x4 x = Xr[ms][j];
-                const int o = (cw + 16 * j + lane % 16) * LX + 16 * ms + 4 * (lane / 16);
-#pragma unroll
-                for (int q = 0; q < NP; ++q) {
-                    // each part is x rounded to bfloat16, then x minus that part (exact)
-                    const uint32_t p01 = pack_bf16x2(x[0], x[1]), p23 = pack_bf16x2(x[2], x[3]);
-                    *reinterpret_cast<uint2 *>(&xb[q][o]) = make_uint2(p01, p23);
-                    x = f32x4{x[0] - bf16_lo(p01), x[1] - bf16_hi(p01), x[2] - bf16_lo(p23), x[3] - bf16_hi(p23)};
-                }
-            }
-    };
-    if constexpr (!SO) write_x();
-
-    // staging role: RG rows x 8 channels
-    const int cg = tid % CG, rg = tid / CG;
-    const int64_t ch0 = (int64_t)g * P + p0 + CGW * cg;  // global channel of the piece's element 0
     const int64_t t_begin = c * Tc;
     const int nsteps = (int)(((L - t_begin) < Tc) ? (L - t_begin) : Tc);
     const int nsb = (nsteps + kSubBlock - 1) / kSubBlock;
-    const T *qb = static_cast<const T *>(a.q) + (b * L + t_begin) * a.ld_in + ch0;
-    const T *kb = static_cast<const T *>(a.k) + (b * L + t_begin) * a.ld_in + ch0;
-    const T *vb = static_cast<const T *>(a.v) + (b * L + t_begin) * a.ld_in + ch0;
-    T *yb = static_cast<T *>(a.y) + (b * L + t_begin) * a.ld_y + ch0;
 
-    // q, k, v pieces of one sub-block: RG rows x 8 channels per thread
-    struct Buf {
-        PC q[RG], k[RG], v[RG];
-    };
-    auto load = [&](int sb, Buf &bf) {
+    // The whole walk for row part HF: its Y rows [MT0, MT1), its state mode
+    // tiles [MS0, MS0 + MSN); part 0 also stages and gates.
+    auto walk = [&](auto hc) {
+        constexpr int HF = decltype(hc)::value;
+        constexpr bool STAGE = HF == 0;
+        constexpr int MT0 = RS == 1 ? 0 : 2 * HF, MT1 = RS == 1 ? 4 : 2 * HF + 2;
+        constexpr int MSN = MTS / RS, MS0 = HF * MSN;
+
+        // entering state in C-tile layout: Xr[i][j] holds mode rows 16ms + 4(l/16) + 0..3
+        // (modes 8ms + 2(l/16) and +1, Re/Im interleaved), ms = MS0 + i, of channel cw + 16j + l%16
+        f32x4 Xr[MSN][NTW];
+        {
+            const float2 *src = SO ? nullptr : (c == 0) ? carry0
+                                         : reinterpret_cast<const float2 *>(a.ws + a.plan.off_carry) +
+                                               c * (s.B * H * DD * P);
 #pragma unroll
-        for (int r = 0; r < RG; ++r) {
-            int row = sb * kSubBlock + rg * RG + r;
-            row = row < nsteps ? row : nsteps - 1;  // clamped; rows past the prompt are masked in staging
-            const int64_t o = (int64_t)row * a.ld_in;
-            if constexpr (!SO) bf.q[r].load(qb + o);
-            bf.k[r].load(kb + o);
-            bf.v[r].load(vb + o);
+            for (int i = 0; i < MSN; ++i)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    const int64_t p = p0 + cw + 16 * j + lane % 16;
+                    const int n0 = 8 * (MS0 + i) + 2 * (lane / 16);
+                    float2 x0 = make_float2(0.f, 0.f), x1 = make_float2(0.f, 0.f);
+                    if (src && n0 < DD) x0 = src[((b * H + g) * DD + n0) * P + p];
+                    if (src && n0 + 1 < DD) x1 = src[((b * H + g) * DD + n0 + 1) * P + p];
+                    Xr[i][j] = f32x4{x0.x, x0.y, x1.x, x1.y};
+                }
         }
-    };
-
-    // Two barriers per sub-block.  Between the second barrier of one sub-block
-    // and the first of the next, threads read the Y tile (written before the
-    // second) and write the u tiles (last read before the second), so the two
-    // phases touch disjoint LDS.
-    // One sub-block.  Its pieces are in `cur`; once staged, `cur` takes the
-    // loads of sub-block sb + PF, so PF sub-blocks of loads stay in flight.
-    auto sub_block = [&](int sb, Buf &cur) {
-            const int nv = (nsteps - sb * kSubBlock < kSubBlock) ? nsteps - sb * kSubBlock : kSubBlock;
-            // ---- stage: u = k v split into hi/lo, transposed to [channel][step]; q stays in registers
-            PC cq[RG];
-            if constexpr (!SO) {
+        auto write_x = [&]() {
 #pragma unroll
-                for (int r = 0; r < RG; ++r) cq[r] = cur.q[r];
+            for (int i = 0; i < MSN; ++i)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    f32x4 x = Xr[i][j];
+                    const int o = (cw + 16 * j + lane % 16) * LX + 16 * (MS0 + i) + 4 * (lane / 16);
+#pragma unroll
+                    for (int q = 0; q < NP; ++q) {
+                        // each part is x rounded to bfloat16, then x minus that part (exact)
+                        const uint32_t p01 = pack_bf16x2(x[0], x[1]), p23 = pack_bf16x2(x[2], x[3]);
+                        *reinterpret_cast<uint2 *>(&xb[q][o]) = make_uint2(p01, p23);
+                        x = f32x4{x[0] - bf16_lo(p01), x[1] - bf16_hi(p01), x[2] - bf16_lo(p23), x[3] - bf16_hi(p23)};
+                    }
+                }
+        };
+        if constexpr (!SO) write_x();
+
+        // staging role (row part 0): RG rows x 8 channels
+        const int cg = tid % CG, rg = tid / CG;
+        const int64_t ch0 = (int64_t)g * P + p0 + CGW * cg;  // global channel of the piece's element 0
+        const T *qb = static_cast<const T *>(a.q) + (b * L + t_begin) * a.ld_in + ch0;
+        const T *kb = static_cast<const T *>(a.k) + (b * L + t_begin) * a.ld_in + ch0;
+        const T *vb = static_cast<const T *>(a.v) + (b * L + t_begin) * a.ld_in + ch0;
+        T *yb = static_cast<T *>(a.y) + (b * L + t_begin) * a.ld_y + ch0;
+
+        // q, k, v pieces of one sub-block: RG rows x 8 channels per thread
+        struct Buf {
+            PC q[RG], k[RG], v[RG];
+        };
+        auto load = [&](int sb, Buf &bf) {
+#pragma unroll
+            for (int r = 0; r < RG; ++r) {
+                int row = sb * kSubBlock + rg * RG + r;
+                row = row < nsteps ? row : nsteps - 1;  // clamped; rows past the prompt are masked in staging
+                const int64_t o = (int64_t)row * a.ld_in;
+                if constexpr (!SO) bf.q[r].load(qb + o);
+                bf.k[r].load(kb + o);
+                bf.v[r].load(vb + o);
             }
-            {
+        };
+
+        // Two barriers per sub-block.  Between the second barrier of one sub-block
+        // and the first of the next, threads read the Y tile (written before the
+        // second) and write the u tiles (last read before the second), so the two
+        // phases touch disjoint LDS.  With two row parts the x tiles are written
+        // in that phase as well (both parts read all of x before the second).
+        // One sub-block.  Its pieces are in `cur`; once staged, `cur` takes the
+        // loads of sub-block sb + PF, so PF sub-blocks of loads stay in flight.
+        auto sub_block = [&](int sb, Buf &cur) {
+            const int nv = (nsteps - sb * kSubBlock < kSubBlock) ? nsteps - sb * kSubBlock : kSubBlock;
+            // ---- stage: u = k v split into parts, transposed to [channel][step]; q stays in registers
+            PC cq[RG];
+            if constexpr (STAGE) {
+                if constexpr (!SO) {
+#pragma unroll
+                    for (int r = 0; r < RG; ++r) cq[r] = cur.q[r];
+                }
                 float uu[RG][8];
 #pragma unroll
                 for (int r = 0; r < RG; ++r) {
@@ -417,18 +434,18 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
                         u1 -= bf16_hi(w2);
                     }
                 }
+                if (sb + PF < nsb) load(sb + PF, cur);  // PF sub-blocks ahead stay in flight during the products
             }
-            if (sb + PF < nsb) load(sb + PF, cur);  // PF sub-blocks ahead stay in flight during the products
             __syncthreads();
 
             // ---- products
-            f32x4 Y[4][NTW], S[MTS][NTW];
+            f32x4 Y[MT1 - MT0][NTW], S[MSN][NTW];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MT1 - MT0; ++i)
 #pragma unroll
                 for (int j = 0; j < NTW; ++j) Y[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < MTS; ++i)
+            for (int i = 0; i < MSN; ++i)
 #pragma unroll
                 for (int j = 0; j < NTW; ++j) S[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             auto afrag = [&](int f, uint4 (&av)[NP]) {
@@ -446,21 +463,21 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
                 }
                 if constexpr (!SO) {
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt) {
+                    for (int mt = MT0; mt < MT1; ++mt) {
                         // T is causal: rows 0..31 against steps 32..63 are all zero
                         if (kk == 1 && mt < 2) continue;
                         uint4 av[NP];
                         afrag(mt * 2 + kk, av);
 #pragma unroll
-                        for (int j = 0; j < NTW; ++j) Y[mt][j] = mfma_split<NP>(av, bv[j], Y[mt][j]);
+                        for (int j = 0; j < NTW; ++j) Y[mt - MT0][j] = mfma_split<NP>(av, bv[j], Y[mt - MT0][j]);
                     }
                 }
 #pragma unroll
-                for (int ms = 0; ms < MTS; ++ms) {
+                for (int i = 0; i < MSN; ++i) {
                     uint4 av[NP];
-                    afrag(8 + 4 * KC + ms * 2 + kk, av);
+                    afrag(8 + 4 * KC + (MS0 + i) * 2 + kk, av);
 #pragma unroll
-                    for (int j = 0; j < NTW; ++j) S[ms][j] = mfma_split<NP>(av, bv[j], S[ms][j]);
+                    for (int j = 0; j < NTW; ++j) S[i][j] = mfma_split<NP>(av, bv[j], S[i][j]);
                 }
             }
 #pragma unroll
@@ -473,52 +490,55 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
                     for (int q = 0; q < NP; ++q) xv[j][q] = *reinterpret_cast<const uint4 *>(&xb[q][o]);
                 }
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
+                for (int mt = MT0; mt < MT1; ++mt) {
                     uint4 av[NP];
                     afrag(8 + mt * KC + kc, av);
 #pragma unroll
-                    for (int j = 0; j < NTW; ++j) Y[mt][j] = mfma_split<NP>(av, xv[j], Y[mt][j]);
+                    for (int j = 0; j < NTW; ++j) Y[mt - MT0][j] = mfma_split<NP>(av, xv[j], Y[mt - MT0][j]);
                 }
             }
 
             // ---- Y tile -> LDS ([step][channel])
             if constexpr (!SO) {
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int mt = MT0; mt < MT1; ++mt)
 #pragma unroll
                     for (int j = 0; j < NTW; ++j)
 #pragma unroll
                         for (int r = 0; r < 4; ++r)
-                            yt[yt_index(16 * mt + 4 * (lane / 16) + r, cw + 16 * j + lane % 16, LQ)] = Y[mt][j][r];
+                            yt[yt_index(16 * mt + 4 * (lane / 16) + r, cw + 16 * j + lane % 16, LQ)] = Y[mt - MT0][j][r];
             }
 
             // ---- state hand-off
             if (nv == kSubBlock) {
 #pragma unroll
-                for (int ms = 0; ms < MTS; ++ms)
+                for (int i = 0; i < MSN; ++i)
 #pragma unroll
                     for (int j = 0; j < NTW; ++j)
 #pragma unroll
                         for (int q2 = 0; q2 < 2; ++q2) {
-                            const float2 lt = lamT[8 * ms + 2 * (lane / 16) + q2];
-                            const float xr = Xr[ms][j][2 * q2], xi = Xr[ms][j][2 * q2 + 1];
-                            Xr[ms][j][2 * q2] = fmaf(lt.x, xr, fmaf(-lt.y, xi, S[ms][j][2 * q2]));
-                            Xr[ms][j][2 * q2 + 1] = fmaf(lt.x, xi, fmaf(lt.y, xr, S[ms][j][2 * q2 + 1]));
+                            const float2 lt = lamT[8 * (MS0 + i) + 2 * (lane / 16) + q2];
+                            const float xr = Xr[i][j][2 * q2], xi = Xr[i][j][2 * q2 + 1];
+                            Xr[i][j][2 * q2] = fmaf(lt.x, xr, fmaf(-lt.y, xi, S[i][j][2 * q2]));
+                            Xr[i][j][2 * q2 + 1] = fmaf(lt.x, xi, fmaf(lt.y, xr, S[i][j][2 * q2 + 1]));
                         }
-                if constexpr (!SO) write_x();
+                // with two row parts the other part may still be reading the
+                // entering x (its C X products): the next x goes to LDS after
+                // the barrier below
+                if constexpr (!SO && RS == 1) write_x();
             } else {
                 // ragged final sub-block (end of the prompt): step the recurrence
                 // over its nv steps on the vector ALUs, from u = the sum of its parts in LDS
 #pragma unroll
-                for (int ms = 0; ms < MTS; ++ms)
+                for (int i = 0; i < MSN; ++i)
 #pragma unroll
                     for (int j = 0; j < NTW; ++j)
 #pragma unroll
                         for (int q2 = 0; q2 < 2; ++q2) {
-                            const int n = 8 * ms + 2 * (lane / 16) + q2;
+                            const int n = 8 * (MS0 + i) + 2 * (lane / 16) + q2;
                             if (n >= DD) continue;
                             const float2 l = s.poles[(int64_t)g * DD + n];
-                            float xr = Xr[ms][j][2 * q2], xi = Xr[ms][j][2 * q2 + 1];
+                            float xr = Xr[i][j][2 * q2], xi = Xr[i][j][2 * q2 + 1];
                             const int ch = cw + 16 * j + lane % 16;
                             for (int t = 0; t < nv; ++t) {
                                 const int o = u_index(ch, t);
@@ -529,53 +549,70 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
                                 xi = fmaf(l.x, xi, l.y * xr);
                                 xr = nr;
                             }
-                            Xr[ms][j][2 * q2] = xr;
-                            Xr[ms][j][2 * q2 + 1] = xi;
+                            Xr[i][j][2 * q2] = xr;
+                            Xr[i][j][2 * q2 + 1] = xi;
                         }
             }
             __syncthreads();
+            if constexpr (!SO && RS == 2) {
+                if (nv == kSubBlock) write_x();
+            }
 
             // ---- gate y = q Y and store whole 8-channel pieces of valid rows
+            if constexpr (STAGE) {
 #pragma unroll
-            for (int r = 0; r < (SO ? 0 : RG); ++r) {
-                const int row = rg * RG + r;
-                if (row < nv) {
-                    const float4 y0 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, CGW * cg, LQ)]);
-                    const float4 y1 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, CGW * cg + SPLIT, LQ)]);
-                    const float yy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-                    float v[8];
+                for (int r = 0; r < (SO ? 0 : RG); ++r) {
+                    const int row = rg * RG + r;
+                    if (row < nv) {
+                        const float4 y0 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, CGW * cg, LQ)]);
+                        const float4 y1 = *reinterpret_cast<const float4 *>(&yt[yt_index(row, CGW * cg + SPLIT, LQ)]);
+                        const float yy[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+                        float v[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = cq[r].get(e) * yy[e];
-                    store8<SPLIT>(reinterpret_cast<T *>(yb + (int64_t)(sb * kSubBlock + row) * a.ld_y), v);
+                        for (int e = 0; e < 8; ++e) v[e] = cq[r].get(e) * yy[e];
+                        store8<SPLIT>(reinterpret_cast<T *>(yb + (int64_t)(sb * kSubBlock + row) * a.ld_y), v);
+                    }
                 }
             }
         };
-    Buf b0, b1;
-    load(0, b0);
-    if constexpr (PF == 2) {
-        if (nsb > 1) load(1, b1);
-        for (int sb = 0; sb < nsb; sb += 2) {
-            sub_block(sb, b0);
-            if (sb + 1 < nsb) sub_block(sb + 1, b1);
-        }
-    } else {
-        for (int sb = 0; sb < nsb; ++sb) sub_block(sb, b0);
-    }
-
-
-    if (SO || c == a.plan.NC - 1) {
-        float2 *const base = SO ? reinterpret_cast<float2 *>(a.ws + a.plan.off_carry) + (c + 1) * (s.B * H * DD * P)
-                                : a.state_out;
-#pragma unroll
-        for (int ms = 0; ms < MTS; ++ms)
-#pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const int64_t p = p0 + cw + 16 * j + lane % 16;
-                const int n0 = 8 * ms + 2 * (lane / 16);
-                float2 *dst = base + ((b * H + g) * DD) * P + p;
-                if (n0 < DD) dst[(int64_t)n0 * P] = make_float2(Xr[ms][j][0], Xr[ms][j][1]);
-                if (n0 + 1 < DD) dst[(int64_t)(n0 + 1) * P] = make_float2(Xr[ms][j][2], Xr[ms][j][3]);
+        Buf b0, b1;
+        if constexpr (STAGE) load(0, b0);
+        if constexpr (PF == 2) {
+            if constexpr (STAGE) {
+                if (nsb > 1) load(1, b1);
             }
+            for (int sb = 0; sb < nsb; sb += 2) {
+                sub_block(sb, b0);
+                if (sb + 1 < nsb) sub_block(sb + 1, b1);
+            }
+        } else {
+            for (int sb = 0; sb < nsb; ++sb) sub_block(sb, b0);
+        }
+
+        if (SO || c == a.plan.NC - 1) {
+            float2 *const base = SO ? reinterpret_cast<float2 *>(a.ws + a.plan.off_carry) + (c + 1) * (s.B * H * DD * P)
+                                    : a.state_out;
+#pragma unroll
+            for (int i = 0; i < MSN; ++i)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    const int64_t p = p0 + cw + 16 * j + lane % 16;
+                    const int n0 = 8 * (MS0 + i) + 2 * (lane / 16);
+                    float2 *dst = base + ((b * H + g) * DD) * P + p;
+                    if (n0 < DD) dst[(int64_t)n0 * P] = make_float2(Xr[i][j][0], Xr[i][j][1]);
+                    if (n0 + 1 < DD) dst[(int64_t)(n0 + 1) * P] = make_float2(Xr[i][j][2], Xr[i][j][3]);
+                }
+        }
+    };
+    if constexpr (RS == 1) {
+        walk(std::integral_constant<int, 0>{});
+    } else {
+        // the row part is wave-uniform; readfirstlane makes the branch scalar, so
+        // each wave runs only its own part (and its own two barriers per sub-block)
+        if (__builtin_amdgcn_readfirstlane(w / (PT / 16)) == 0)
+            walk(std::integral_constant<int, 0>{});
+        else
+            walk(std::integral_constant<int, 1>{});
     }
 }
 
@@ -583,6 +620,11 @@ __global__ __launch_bounds__(4 * PT) void chunk_mfma_kernel(PrefillArgs a, const
 // work of bfloat16 ones (six split products instead of three), which a single
 // sub-block of loads in flight no longer covers at one wave per SIMD.
 constexpr int kPfBF16 = 1, kPfF32 = 2;
+// Row parts of the full pass (the state-only pass keeps one): two for float32
+// 64-channel tiles, whose three-part tables hold the workgroup to four waves
+// per CU otherwise (at 128 channels, 16 waves would spill).
+constexpr int kRsBF16 = 1;
+template <int PT> constexpr int rs_f32() { return PT == 64 ? 2 : 1; }
 
 // float32 tiles of 128 channels take three bfloat16 parts of every operand and
 // do not fit the LDS at d = 32: the channel tile is 64 there.
@@ -590,12 +632,14 @@ template <int DD, int PT> constexpr bool f32_tile_fits() { return !(DD == 32 && 
 
 template <int DD, int PT>
 hipError_t launch_dd(const PrefillArgs &a, const float2 *carry0, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.s.H * (a.s.P / PT)), (unsigned)a.plan.NC, (unsigned)a.s.B), block(4 * PT);
+    const dim3 grid((unsigned)(a.s.H * (a.s.P / PT)), (unsigned)a.plan.NC, (unsigned)a.s.B);
     if (a.s.act == kBF16) {
-        chunk_mfma_kernel<DD, PT, kBF16, false, true, kPfBF16><<<grid, block, 0, stream>>>(a, carry0);
+        chunk_mfma_kernel<DD, PT, kBF16, false, true, kPfBF16, kRsBF16><<<grid, dim3(4 * PT * kRsBF16), 0, stream>>>(
+            a, carry0);
     } else {
         if constexpr (f32_tile_fits<DD, PT>())
-            chunk_mfma_kernel<DD, PT, kF32, false, true, kPfF32><<<grid, block, 0, stream>>>(a, carry0);
+            chunk_mfma_kernel<DD, PT, kF32, false, true, kPfF32, rs_f32<PT>()>
+                <<<grid, dim3(4 * PT * rs_f32<PT>()), 0, stream>>>(a, carry0);
         else
             return hipErrorInvalidValue;
     }
@@ -606,12 +650,12 @@ template <int DD, int PT>
 hipError_t launch_dd_state(const PrefillArgs &a, bool vec, hipStream_t stream) {
     const dim3 grid((unsigned)(a.s.H * (a.s.P / PT)), (unsigned)(a.plan.NC - 1), (unsigned)a.s.B), block(4 * PT);
     if (a.s.act == kBF16) {
-        if (vec) chunk_mfma_kernel<DD, PT, kBF16, true, true, kPfBF16><<<grid, block, 0, stream>>>(a, nullptr);
-        else chunk_mfma_kernel<DD, PT, kBF16, true, false, kPfBF16><<<grid, block, 0, stream>>>(a, nullptr);
+        if (vec) chunk_mfma_kernel<DD, PT, kBF16, true, true, kPfBF16, 1><<<grid, block, 0, stream>>>(a, nullptr);
+        else chunk_mfma_kernel<DD, PT, kBF16, true, false, kPfBF16, 1><<<grid, block, 0, stream>>>(a, nullptr);
     } else {
         if constexpr (f32_tile_fits<DD, PT>()) {
-            if (vec) chunk_mfma_kernel<DD, PT, kF32, true, true, kPfF32><<<grid, block, 0, stream>>>(a, nullptr);
-            else chunk_mfma_kernel<DD, PT, kF32, true, false, kPfF32><<<grid, block, 0, stream>>>(a, nullptr);
+            if (vec) chunk_mfma_kernel<DD, PT, kF32, true, true, kPfF32, 1><<<grid, block, 0, stream>>>(a, nullptr);
+            else chunk_mfma_kernel<DD, PT, kF32, true, false, kPfF32, 1><<<grid, block, 0, stream>>>(a, nullptr);
         } else {
             return hipErrorInvalidValue;
         }
