@@ -48,6 +48,7 @@ EXPORTS = (
     "hyena_pack_in_proj_bf16",
     "hyena_fir_workspace",
     "hyena_fir_decode_step",
+    "hyena_fir_decode_step_ex",
     "hyena_fir_cache_fill",
     "hyena_fft_prefill_workspace",
     "hyena_fft_prefill",
@@ -133,6 +134,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
             "hyena_dense_workspace": ([i64, i64, i64, ctypes.POINTER(sz)], ctypes.c_int),
             "hyena_fir_workspace": ([D, ctypes.POINTER(sz)], ctypes.c_int),
             "hyena_fir_decode_step": ([D, p, i64, i64, i64, p, p, p, i64, p, i64, p, i64, p, sz, p], ctypes.c_int),
+            "hyena_fir_decode_step_ex": ([D, p, i64, i64, i64, p, p, p, i64, p, i64, p, i64, p, sz, ctypes.c_int32, p],
+                                         ctypes.c_int),
             "hyena_fir_cache_fill": ([D, i64, p, p, i64, p, i64, p], ctypes.c_int),
             "hyena_fft_prefill_workspace": ([D, i64, ctypes.POINTER(sz)], ctypes.c_int),
             "hyena_fft_prefill": ([D, i64, p, p, p, i64, p, i64, p, sz, p], ctypes.c_int),
@@ -332,11 +335,21 @@ def hyena_fir_workspace(desc: hm_desc) -> int:
     return n.value
 
 
+HM_FIR_LOADS_AUTO, HM_FIR_LOADS_PLAIN, HM_FIR_LOADS_NONTEMPORAL = 0, 1, 2
+
+
 def hyena_fir_decode_step(desc: hm_desc, h, h_len, window, t, q, k, v, ld_in, y, ld_y, u_cache, cache_len,
-                          workspace, ws_bytes=None, stream=None) -> None:
-    st = load().hyena_fir_decode_step(ctypes.byref(desc), _ptr(h), h_len, window, t, _ptr(q), _ptr(k), _ptr(v),
-                                      ld_in, _ptr(y), ld_y, _ptr(u_cache), cache_len, _ptr(workspace),
-                                      _ws_bytes(workspace, ws_bytes), _stream(stream))
+                          workspace, ws_bytes=None, stream=None, loads=None) -> None:
+    """loads: None for the library's default; else HM_FIR_LOADS_* (hyena_fir_decode_step_ex)."""
+    if loads is None:
+        st = load().hyena_fir_decode_step(ctypes.byref(desc), _ptr(h), h_len, window, t, _ptr(q), _ptr(k),
+                                          _ptr(v), ld_in, _ptr(y), ld_y, _ptr(u_cache), cache_len,
+                                          _ptr(workspace), _ws_bytes(workspace, ws_bytes), _stream(stream))
+    else:
+        st = load().hyena_fir_decode_step_ex(ctypes.byref(desc), _ptr(h), h_len, window, t, _ptr(q), _ptr(k),
+                                             _ptr(v), ld_in, _ptr(y), ld_y, _ptr(u_cache), cache_len,
+                                             _ptr(workspace), _ws_bytes(workspace, ws_bytes), int(loads),
+                                             _stream(stream))
     _check(st, "hyena_fir_decode_step")
 
 
@@ -560,14 +573,15 @@ class FirHyena:
         ld = _row_stride(k, (v,))
         hyena_fir_cache_fill(self.op.desc, L, k, v, ld, self.cache, self.cache_len, stream)
 
-    def step(self, h, t: int, q, k, v, window: int = 0, y=None, stream=None):
+    def step(self, h, t: int, q, k, v, window: int = 0, y=None, stream=None, loads=None):
         """One generated token at position t through the taps h [H][>= min(t+1, W)];
-        q, k, v: [B][ld] rows with one row stride."""
+        q, k, v: [B][ld] rows with one row stride.  loads: None (the library's
+        choice by window size) or HM_FIR_LOADS_PLAIN / HM_FIR_LOADS_NONTEMPORAL."""
         if y is None:
             y = self.torch.empty((self.op.B, self.op.D), dtype=self.op.tdtype, device=self.op.device)
         for x in (q, k, v, y):
             if x.dim() != 2 or x.stride(1) != 1 or (x.shape[0] > 1 and x is not y and x.stride(0) != q.stride(0)):
                 raise ValueError("FIR step needs [B][D] rows with unit channel stride and one row stride for q, k, v")
         hyena_fir_decode_step(self.op.desc, h, int(h.shape[-1]), window, t, q, k, v, q.stride(0), y,
-                              y.stride(0), self.cache, self.cache_len, self.ws, stream=stream)
+                              y.stride(0), self.cache, self.cache_len, self.ws, stream=stream, loads=loads)
         return y

@@ -193,21 +193,25 @@ int fir_ranges(int64_t B, int64_t D) {
 hipError_t launch_fir_decode(const FirArgs &a, hipStream_t stream) {
     const dim3 g1((unsigned)((a.s.D + kFirBlk - 1) / kFirBlk), (unsigned)a.R, (unsigned)a.s.B);
     const dim3 g2((unsigned)((a.s.B * a.s.D + 255) / 256));
+    // non-temporal cache loads for windows larger than the 256 MB Infinity Cache,
+    // unless the caller chose (a.loads)
+    const int64_t window_bytes = a.s.B * (a.t - a.lo) * a.s.D * (a.s.act == kBF16 ? 2 : 4);
+    const bool nt = a.loads == 0 ? window_bytes > (int64_t(256) << 20) : a.loads == 2;
     if (a.s.act == kBF16) {
-        const int64_t window_bytes = a.s.B * (a.t - a.lo) * a.s.D * 2;
-        if (window_bytes > (int64_t(256) << 20))
+        if (nt)
             fir_partial_kernel<kBF16, true><<<g1, dim3(256), 0, stream>>>(a);
         else
             fir_partial_kernel<kBF16, false><<<g1, dim3(256), 0, stream>>>(a);
         fir_finish_kernel<kBF16><<<g2, dim3(256), 0, stream>>>(a);
     } else {
-        const int64_t window_bytes = a.s.B * (a.t - a.lo) * a.s.D * 4;
-        if (a.s.D % kFirBlk != 0)
+        if (a.s.D % kFirBlk != 0) {
+            if (nt) return hipErrorInvalidValue;  // the host rejects this case first
             fir_partial_kernel<kF32, false><<<g1, dim3(256), 0, stream>>>(a);
-        else if (window_bytes > (int64_t(256) << 20))
+        } else if (nt) {
             fir_partial_kernel<kF32, true, kFirBlk / 2><<<g1, dim3(256), 0, stream>>>(a);
-        else
+        } else {
             fir_partial_kernel<kF32, false, kFirBlk / 2><<<g1, dim3(256), 0, stream>>>(a);
+        }
         fir_finish_kernel<kF32><<<g2, dim3(256), 0, stream>>>(a);
     }
     return hipGetLastError();

@@ -326,12 +326,15 @@ hm_status hyena_fir_cache_fill(const hm_desc *desc, int64_t L, const void *k, co
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
 }
 
-hm_status hyena_fir_decode_step(const hm_desc *desc, const float *h, int64_t h_len, int64_t window, int64_t t,
-                                const void *q, const void *k, const void *v, int64_t ld_in, void *y,
-                                int64_t ld_y, void *u_cache, int64_t cache_len, void *workspace,
-                                size_t ws_bytes, void *stream) {
+static hm_status fir_decode_impl(const hm_desc *desc, const float *h, int64_t h_len, int64_t window, int64_t t,
+                                 const void *q, const void *k, const void *v, int64_t ld_in, void *y,
+                                 int64_t ld_y, void *u_cache, int64_t cache_len, void *workspace,
+                                 size_t ws_bytes, int32_t loads, void *stream) {
     hm_status st = fir_check(desc, u_cache, cache_len);
     if (st != HM_OK) return st;
+    if (loads < 0 || loads > 2) return HM_ERR_INVALID_ARG;
+    // float32 non-temporal loads need the 512-channel block split
+    if (loads == 2 && desc->act_dtype == HM_F32 && desc->channels % 512 != 0) return HM_ERR_UNSUPPORTED;
     if (t < 0 || t >= cache_len || window < 0) return HM_ERR_INVALID_ARG;
     const int64_t taps = (window == 0 || window > t + 1) ? t + 1 : window;
     if (!h || h_len < taps || h_len > kMaxElems / desc->heads) return HM_ERR_INVALID_ARG;
@@ -363,8 +366,25 @@ hm_status hyena_fir_decode_step(const hm_desc *desc, const float *h, int64_t h_l
     a.cache = u_cache;
     a.cache_len = cache_len;
     a.part = static_cast<float *>(workspace);
+    a.loads = loads;
     const hipError_t err = hm::launch_fir_decode(a, static_cast<hipStream_t>(stream));
     return err == hipSuccess ? HM_OK : HM_ERR_HIP;
+}
+
+hm_status hyena_fir_decode_step(const hm_desc *desc, const float *h, int64_t h_len, int64_t window, int64_t t,
+                                const void *q, const void *k, const void *v, int64_t ld_in, void *y,
+                                int64_t ld_y, void *u_cache, int64_t cache_len, void *workspace,
+                                size_t ws_bytes, void *stream) {
+    return fir_decode_impl(desc, h, h_len, window, t, q, k, v, ld_in, y, ld_y, u_cache, cache_len, workspace,
+                           ws_bytes, HM_FIR_LOADS_AUTO, stream);
+}
+
+hm_status hyena_fir_decode_step_ex(const hm_desc *desc, const float *h, int64_t h_len, int64_t window, int64_t t,
+                                   const void *q, const void *k, const void *v, int64_t ld_in, void *y,
+                                   int64_t ld_y, void *u_cache, int64_t cache_len, void *workspace,
+                                   size_t ws_bytes, int32_t loads, void *stream) {
+    return fir_decode_impl(desc, h, h_len, window, t, q, k, v, ld_in, y, ld_y, u_cache, cache_len, workspace,
+                           ws_bytes, loads, stream);
 }
 
 static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }

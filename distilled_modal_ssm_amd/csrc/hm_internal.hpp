@@ -285,6 +285,7 @@ struct FirArgs {
     void *cache;        // [B][cache_len][D] activation dtype
     int64_t cache_len;
     float *part;        // [R][B][D] fp32
+    int loads = 0;      // cache loads: 0 by window size, 1 plain, 2 non-temporal
 };
 int fir_ranges(int64_t B, int64_t D);
 hipError_t launch_fir_decode(const FirArgs &a, hipStream_t stream);

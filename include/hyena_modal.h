@@ -404,6 +404,27 @@ hm_status hyena_fir_decode_step(const hm_desc *desc, const float *h, int64_t h_l
                                 void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * The same step with the cache's load policy chosen by the caller (for tests
+ * of both kernel forms at any size, and for callers who know whether the
+ * window stays cached between steps):
+ *   loads = HM_FIR_LOADS_AUTO (0): non-temporal loads when the window is larger
+ *           than 256 MB (the Infinity Cache), plain loads otherwise, as
+ *           hyena_fir_decode_step;
+ *           HM_FIR_LOADS_PLAIN (1): plain loads;
+ *           HM_FIR_LOADS_NONTEMPORAL (2): non-temporal loads.
+ * Results do not depend on the policy.  Other values -> HM_ERR_INVALID_ARG;
+ * non-temporal float32 loads need D a multiple of 512 (else
+ * HM_ERR_UNSUPPORTED).  Everything else as hyena_fir_decode_step.
+ */
+#define HM_FIR_LOADS_AUTO 0
+#define HM_FIR_LOADS_PLAIN 1
+#define HM_FIR_LOADS_NONTEMPORAL 2
+hm_status hyena_fir_decode_step_ex(const hm_desc *desc, const float *h, int64_t h_len, int64_t window,
+                                   int64_t t, const void *q, const void *k, const void *v, int64_t ld_in,
+                                   void *y, int64_t ld_y, void *u_cache, int64_t cache_len, void *workspace,
+                                   size_t ws_bytes, int32_t loads, void *stream);
+
+/*
  * u_cache[b][t][c] = k[b][t][c] v[b][t][c] (rounded to the activation dtype)
  * for t < L: the prompt's rows of the cache.  k, v [B][L][ld_in].
  */

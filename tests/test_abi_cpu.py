@@ -335,6 +335,27 @@ def test_fir_validation(lib):
     assert lib.hyena_fir_cache_fill(ctypes.byref(d), 0, FAKE, FAKE, 64, FAKE, 200, None) == hb.HM_OK
 
 
+def test_fir_load_policy_validation(lib):
+    """hyena_fir_decode_step_ex: the policy is checked on the host; float32
+    non-temporal loads need D a multiple of 512."""
+    def step(desc, loads):
+        need = hb.hyena_fir_workspace(desc)
+        D = desc.channels
+        return lib.hyena_fir_decode_step_ex(ctypes.byref(desc), FAKE, 100, 0, 50, FAKE, FAKE, FAKE, D, FAKE, D,
+                                            FAKE, 200, FAKE, need, loads, None)
+
+    f32, bf16 = hb.HM_F32, hb.HM_BF16
+    assert step(_desc(batch=2, channels=64, heads=4), 3) == hb.HM_ERR_INVALID_ARG
+    assert step(_desc(batch=2, channels=64, heads=4), -1) == hb.HM_ERR_INVALID_ARG
+    assert step(_desc(batch=2, channels=64, heads=4, act_dtype=f32), hb.HM_FIR_LOADS_NONTEMPORAL) == \
+        hb.HM_ERR_UNSUPPORTED
+    # accepted up to the launch (zero batch: nothing is launched)
+    for act, D in ((bf16, 64), (f32, 512), (f32, 64)):
+        for loads in (hb.HM_FIR_LOADS_AUTO, hb.HM_FIR_LOADS_PLAIN) + \
+                ((hb.HM_FIR_LOADS_NONTEMPORAL,) if act == bf16 or D % 512 == 0 else ()):
+            assert step(_desc(batch=0, channels=D, heads=4, act_dtype=act), loads) == hb.HM_OK, (act, D, loads)
+
+
 def test_fft_prefill_validation(lib):
     d = _desc(batch=2, channels=64, heads=4)
     n = hb.hyena_fft_prefill_workspace(d, 2048)

@@ -76,6 +76,34 @@ def test_fir_decode_f32_block_split(window):
     assert rel_err(y_gpu, y_or) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_fir_non_temporal_loads(act):
+    """Both cache-load forms at a small size (the library picks non-temporal
+    loads only for windows beyond 256 MB): each against the oracle, and the two
+    bit for bit, since only the load hint differs."""
+    torch = require_gpu()
+    B, D, H, d, L, S = 2, 1024, 8, 8, 100, 6  # D a multiple of 512 for the float32 block split
+    rng = np.random.default_rng(500 + (act == "bf16"))
+    params = _params(rng, H, d)
+    q, k, v = (_rand(rng, (B, L + S, D), act) for _ in range(3))
+    h32 = oracle.filter_taps(params, L + S).astype(np.float32)
+    op = hb.ModalHyena(params.poles, params.residues, params.skip, B, D, act)
+    Q, K, V = (to_dev(a, act) for a in (q, k, v))
+    h = torch.from_numpy(h32).cuda()
+    y_or = oracle.fir_conv(h32.astype(np.float64), q, k, v, act, window=0, t_from=L)
+    outs = {}
+    for loads in (hb.HM_FIR_LOADS_PLAIN, hb.HM_FIR_LOADS_NONTEMPORAL):
+        log(f"fir act={act} loads={loads}")
+        fir = hb.FirHyena(op, L + S)
+        fir.fill(K[:, :L].contiguous(), V[:, :L].contiguous())
+        ys = [fir.step(h, L + s, Q[:, L + s].contiguous(), K[:, L + s].contiguous(), V[:, L + s].contiguous(),
+                       loads=loads) for s in range(S)]
+        torch.cuda.synchronize()
+        outs[loads] = np.stack([to_np64(t) for t in ys], 1)
+        assert rel_err(outs[loads], y_or) <= TOL[act]
+    assert np.array_equal(outs[hb.HM_FIR_LOADS_PLAIN], outs[hb.HM_FIR_LOADS_NONTEMPORAL])
+
+
 def test_fir_full_window_matches_modal_decode():
     """Over every past step, the explicit filter and the distilled recurrence are
     the same operator: the two GPU decode paths agree (float32 activations)."""
