@@ -404,13 +404,13 @@ __global__ __launch_bounds__(PDD > 0 ? 512 : 256) void gemm_stream_lds_kernel(Ge
     }
     if constexpr (PDD > 0) {
         // Prepare waves: units of two channels, striding over the grid.  They
-        // take no part in the product and end here.  A barrier waits only for
-        // the workgroup's waves that have not ended, so the product's epilogue
-        // does not wait for the state stream (measured on MI355X, B = 64,
-        // D = 2048, d = 16: the first epilogue barrier waited 2.2 us for them).
-        // readfirstlane makes the exit a wave-uniform branch.  The product
-        // waves then synchronise through an LDS arrival count (gemm_sync below),
-        // not a barrier, which would wait for the prepare waves to end.
+        // take no part in the product and end here (readfirstlane makes the
+        // exit a wave-uniform branch).  A barrier counts every wave of the
+        // workgroup that has not ended, so a barrier in the epilogue would wait
+        // until the prepare waves end (measured on MI355X, B = 64, D = 2048,
+        // d = 16: 2.2 us); the product waves synchronise through an LDS arrival
+        // count instead (gemm_sync below).  The barrier here, before any wave
+        // leaves, orders the count's initialisation.
         if (tid == 0) arrivals = 0;
         __syncthreads();
         if (__builtin_amdgcn_readfirstlane(w) >= 4) {
