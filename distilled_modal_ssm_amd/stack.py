@@ -65,10 +65,10 @@ class HyenaStack:
         # split-K scratch of the generation-step projections
         ws = max(hb.hyena_dense_workspace(B, 3 * D, D), hb.hyena_dense_workspace(B, D, D))
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, **e) if ws > 0 else None
-        # generation step: in_proj and decode fused into one launch where the
-        # library supports the shape (packed in_proj rows), else two calls
-        # deferred-state generation: the shapes hyena_layer_gate_bf16 and
-        # hyena_dense_prepare_bf16 cover (B <= 64, D in {1024, 2048}, d in {8, 16, 32})
+        # generation step: the deferred state where hyena_layer_gate_bf16 covers
+        # the shape (B <= 64, D = 2048, D/H a multiple of 16, d in {8, 16, 32});
+        # else in_proj and decode fused into one launch (packed in_proj rows);
+        # else three calls
         self.deferred = bool(fused and deferred and B <= 64 and D == 2048 and D // self.ops[0].H % 16 == 0
                              and all(op.d in (8, 16, 32) for op in self.ops))
         if self.deferred:
