@@ -59,6 +59,15 @@ KERNEL_SOURCES = {
     "decode_step_fixed": ["decode.hip", "hm_internal.hpp", "../build.py"],
     "chunk_mfma_kernel": ["prefill_mfma.hip", "prefill.hip", "hm_internal.hpp"],
     "chunk_scan_kernel": ["prefill.hip", "hm_internal.hpp"],
+    # the projected stack's generated token: the gate (with the next layer's
+    # prepare riding along) and out_proj, both streaming GEMMs of dense.hip
+    "stack_token": ["dense.hip", "hm_internal.hpp"],
+}
+# Dispatches that make up one generated token of the stack, per layer (names as
+# the profiler prints them, matched by prefix).
+STACK_TOKEN_KERNELS = {
+    "gate": "gemm_stream_lds_kernel<3, 2, true, 32, -1,",
+    "out_proj": "gemm_stream_lds_kernel<1, 2, false, 32, 0, 0>",
 }
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read, 1 GiB written
 
@@ -163,24 +172,38 @@ def _counter_rows(directory: str, counter: str):
 
 def write_traffic(args):
     """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
-    of this benchmark with --calibrate-copy into the per-launch traffic summary."""
+    of this benchmark with --calibrate-copy (or, for the stack's generated
+    token, of --token-counters) into the per-launch traffic summary."""
     from workloads import get_config
     cfg = get_config(args.config)
     kernel = args.traffic_kernel
     fetch_dir, write_dir = args.traffic_from
+    # kernel name patterns and launches per unit: one dispatch of the kernel,
+    # or for the stack's token every layer's gate and out_proj
+    parts = ({k: (v, cfg.layers) for k, v in STACK_TOKEN_KERNELS.items()} if kernel == "stack_token"
+             else {kernel: (kernel, 1)})
     out = {}
+    per_part = []
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d, name)
-        k = np.array([float(r["Counter_Value"]) for r in rows if kernel in r["Kernel_Name"]])
         copies = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
-        if len(k) == 0 or not copies:
-            raise SystemExit(f"{name}: no dispatches of {kernel} or of the calibration copy in {d}")
+        if not copies:
+            raise SystemExit(f"{name}: no dispatch of the calibration copy in {d}")
         cal = max(copies)  # the 1 GiB copy is by far the largest copy dispatch
         factor = COPY_BYTES / (cal * 1024.0)
-        out[name] = dict(n=len(k), mean=k.mean(), lo=k.min(), hi=k.max(), copy_kib=cal, factor=factor,
-                         bytes=k.mean() * 1024.0 * factor)
+        kib = 0.0
+        for part, (pat, per_unit) in parts.items():
+            k = np.array([float(r["Counter_Value"]) for r in rows if pat in r["Kernel_Name"]])
+            if len(k) == 0:
+                raise SystemExit(f"{name}: no dispatches of {pat} in {d}")
+            kib += per_unit * k.mean()
+            per_part.append(f"# {name} {part} ({pat}...): {len(k)} dispatches, mean {k.mean():.1f} KiB "
+                            f"(min {k.min():.1f}, max {k.max():.1f}) x {per_unit} per launch")
+        out[name] = dict(kib=kib, copy_kib=cal, factor=factor, bytes=kib * 1024.0 * factor)
     sb = cfg.act_bytes
-    if kernel.startswith("decode"):
+    if kernel == "stack_token":
+        alg = stack_token_bytes(cfg)
+    elif kernel.startswith("decode"):
         alg = cfg.B * cfg.D * (16 * cfg.d + 4 * sb)
     else:
         alg = 4 * sb * cfg.B * cfg.L * cfg.D + 8 * cfg.B * cfg.D * cfg.d
@@ -196,10 +219,11 @@ def write_traffic(args):
         f"# {COPY_BYTES} bytes / (what the same counter reads for a plain {COPY_BYTES >> 30} GiB device copy).",
         "#",
     ]
+    lines += per_part + ["#"]
     for name in ("FETCH_SIZE", "WRITE_SIZE"):
         o = out[name]
-        lines.append(f"# {name}: {o['n']} dispatches, mean {o['mean']:.1f} KiB (min {o['lo']:.1f}, max {o['hi']:.1f}); "
-                     f"copy reads {o['copy_kib']:.1f} KiB -> factor {o['factor']:.4f} -> {o['bytes'] / 1e6:.3f} MB")
+        lines.append(f"# {name}: {o['kib']:.1f} KiB per launch; copy reads {o['copy_kib']:.1f} KiB -> "
+                     f"factor {o['factor']:.4f} -> {o['bytes'] / 1e6:.3f} MB")
     lines += [
         "#",
         f"kernel: {kernel}",
@@ -276,7 +300,11 @@ def parse():
     ap.add_argument("--fingerprint", action="store_true", help="print the source fingerprint and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="no GPU: write the traffic summary of --traffic-kernel from two rocprofv3 --pmc runs")
-    ap.add_argument("--traffic-kernel", default="decode_step_fixed")
+    ap.add_argument("--traffic-kernel", default="decode_step_fixed",
+                    help="decode_step_fixed, chunk_mfma_kernel, chunk_scan_kernel or stack_token")
+    ap.add_argument("--token-counters", type=int, default=None, metavar="N",
+                    help="for counter runs of the stack's generated token: the calibration copy, then N "
+                         "generated tokens launched eagerly from a synthetic state (no prompt, no graphs)")
     ap.add_argument("--traffic-cmd", default=None, help="the profiling commands, ' ;; '-separated, for the summary")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT_TXT"), default=None,
                     help="no GPU: write a text summary of a rocprofv3 --kernel-trace --stats run "
@@ -704,11 +732,11 @@ def run_stack(args, cfg, dev) -> dict:
                 "launch_ms": round(ms_prefill, 4), "algorithmic_flops_per_launch": gemm_flops}
     else:
         roof = {"bound": "hbm", "achieved": round(decode_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "kernel": f"generated token: one graph launch of {cfg.layers} x (fused in_proj + decode step, "
-                          f"out_proj)",
+                "kernel": f"generated token: one graph launch of {cfg.layers} x (gate with the next layer's "
+                          f"prepare, out_proj)",
                 "launch_ms": round(ms_tok, 5), "algorithmic_bytes_per_launch": token_bytes}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = read_traffic("stack_token", cfg.name) if roof["bound"] == "hbm" else None
 
     # outside the timed region: the generation kernels alone, each captured
     # 24 times over the layers (cache-cold weights, as in the stack) and
@@ -745,6 +773,39 @@ def run_stack(args, cfg, dev) -> dict:
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def token_counter_run(cfg, dev, n_tokens: int) -> None:
+    """Counter collection for the stack's generated token: the 1 GiB calibration
+    copy, then ``n_tokens`` generated tokens launched eagerly (the per-layer
+    gate with its ride-along prepare, and out_proj).  The state and the first
+    input are synthetic (no prompt pass); the kernels and their bytes are those
+    of the timed generation."""
+    import torch
+    from distilled_modal_ssm_amd.stack import HyenaStack
+    from workloads import dense_weights, modal_params
+
+    if not cfg.layers:
+        raise SystemExit("--token-counters needs the stack workload (--config 5)")
+    log(f"[bench] workload {cfg.index}: weights for the token counter run")
+    with ThreadPoolExecutor(8) as ex:
+        ws = list(ex.map(lambda l: dense_weights(cfg, l), range(cfg.layers)))
+    layers = [(modal_params(cfg, l), *ws[l]) for l in range(cfg.layers)]
+    del ws
+    st = HyenaStack(layers, cfg.B, 1, device=dev)
+    if not st.deferred:
+        raise SystemExit("the stack's shape does not take the deferred generation path")
+    g = torch.Generator(device=dev).manual_seed(11)
+    for s in st.states:
+        s.copy_(0.01 * torch.randn(s.shape, device=dev, generator=g))
+    st.start_generation(torch.randn(cfg.B, cfg.D, device=dev, generator=g).to(torch.bfloat16))
+    torch.cuda.synchronize()
+    calibration_copy()
+    for t in range(n_tokens):
+        log(f"[bench] token {t}")
+        st.decode_step()
+        torch.cuda.synchronize()
+    print(json.dumps({"token_counter_run": cfg.name, "tokens": n_tokens, "layers": cfg.layers}), flush=True)
 
 
 def stack_record(cfg, st, X, rows, nl):
@@ -1011,6 +1072,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = get_config(args.config)
+    if args.token_counters is not None:
+        return token_counter_run(cfg, dev, args.token_counters)
     subs = args.sub if args.sub is not None else ("3,4" if cfg.layers else "")
     subs = [int(s) for s in subs.split(",") if s.strip()]
     t_wall = time.perf_counter()

@@ -37,6 +37,28 @@ def test_traffic_summary_roundtrip(tmp_path, monkeypatch):
     assert bench.read_traffic("chunk_mfma_kernel", "width2048-bf16") is None
 
 
+def test_stack_token_traffic_sums_every_layer(tmp_path, monkeypatch):
+    """The stack's generated token is one launch of 24 gates and 24 out_projs:
+    its traffic is 24 x (mean gate + mean out_proj) per counter, scaled by the
+    copy, and other kernels in the run (the start-of-generation prepare) do not
+    count."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    gate = "void hm::(anonymous namespace)::gemm_stream_lds_kernel<3, 2, true, 32, -1, 16>(hm::GemmArgs)"
+    outp = "void hm::(anonymous namespace)::gemm_stream_lds_kernel<1, 2, false, 32, 0, 0>(hm::GemmArgs)"
+    prep = "void hm::(anonymous namespace)::prepare_kernel<16>(hm::PrepArgs)"
+    copy = "void at::native::elementwise_kernel<direct_copy_kernel_cuda>"
+    _csv(tmp_path / "f", "FETCH_SIZE", [(copy, 524288.0), (prep, 9999.0), (gate, 100.0), (outp, 10.0), (gate, 300.0),
+                                        (outp, 30.0)])
+    _csv(tmp_path / "w", "WRITE_SIZE", [(copy, 1048576.0), (prep, 9999.0), (gate, 50.0), (outp, 5.0)])
+    args = argparse.Namespace(config=5, traffic_kernel="stack_token",
+                              traffic_from=(str(tmp_path / "f"), str(tmp_path / "w")), traffic_cmd="a ;; b")
+    bench.write_traffic(args)
+    got = bench.read_traffic("stack_token", "stack24-bf16")
+    assert got == round(24 * ((200.0 + 20.0) * 2 + (50.0 + 5.0)) * 1024)
+    text = (tmp_path / "profiles" / "stack_token.stack24-bf16.traffic.txt").read_text()
+    assert "algorithmic_bytes_per_launch: 1635778560" in text
+
+
 def test_trace_summary_from_kernel_stats(tmp_path):
     """rocprofv3 --stats rows of two processes are merged per kernel, sorted by
     total time, with calls, mean/min/max per dispatch and the command."""
