@@ -8,14 +8,18 @@ of the whole hot path over one batch of synthetic input:
   1. the prompt through all layers: per layer, the in_proj GEMM with the
      per-token RMS fused, the modal prefill (64-step sub-blocks on the matrix
      cores) and the out_proj GEMM;
-  2. S generated tokens, each through all layers (per layer: the fused
-     in_proj + decode-step kernel and the out_proj kernel), one HIP graph per
-     token captured once and replayed.
+  2. S generated tokens, each through all layers (per layer: the gate kernel
+     -- in_proj with the RMS fused, u = k v, y = q (D u + rho), the next
+     layer's prepare riding along -- and the out_proj kernel), one HIP graph
+     per token captured once and replayed.
 Two operator workloads ride along in ``sub_workloads``, each timed the same
 way (filter taps, prefill, S decode steps as one graph replay):
   batch256-decode-bf16 (the decode step that must stream HBM) and
   long64k-f32 (the 64k-token prefill).
-``--config N`` runs a single workload (1-5) instead.
+``--config N`` runs a single workload (1-5) instead.  Counter runs use
+``--decode-mode eager --calibrate-copy`` (operator workloads) or
+``--token-counters N`` (the stack's generated token), and ``--traffic-from``
+turns their output into the committed traffic summaries.
 
 Inputs are resident in HBM before any timed region.  Every time comes from
 HIP events on the stream the library's kernels run on.  The ``roofline``
