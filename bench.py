@@ -901,8 +901,9 @@ def stack_kernel_breakdown(cfg, st, X, stream) -> dict:
     M = B * L
     x = X.reshape(M, D)
 
-    def in_proj():
-        hb.hyena_dense_rms_bf16(M, 3 * D, D, x, D, st.w_in[0], D, RMS_EPS, st.qkv, 3 * D)
+    def in_proj():  # as the stack's prompt: the row RMS pass, then the projection with the row scale
+        hb.hyena_row_rms(x, M, D, D, RMS_EPS, st.inv_rms)
+        hb.hyena_dense_bf16(M, 3 * D, D, x, D, st.w_in[0], D, st.inv_rms, st.qkv, 3 * D)
 
     def out_proj_p():
         hb.hyena_dense_bf16(M, D, D, st.y, D, st.w_out[0], D, None, st.x[0], D)

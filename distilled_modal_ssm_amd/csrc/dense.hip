@@ -241,6 +241,153 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
     }
 }
 
+// ------------------------------------------------------------------ prompt GEMM, direct loads
+
+// 256 x 256 tile, 8 waves of 64 x 128 (two per SIMD), K staged 32 at a time by
+// direct global -> LDS loads into four stage buffers, up to four stages ahead:
+// no staging registers and no LDS store instructions.  LDS rows are 64 bytes
+// (32 bf16) with the 16-byte chunks XOR-swizzled by row / 2 ^ row / 8, so a
+// fragment read (16 rows, one chunk each) covers all banks in every 8 lanes
+// (128 bytes) and in all 16 (256 bytes).  The K loop is unrolled at compile
+// time (NK stages) and each buffer is its own array, so every wait names
+// exactly the loads it needs.  The workgroup barrier is a bare s_barrier after
+// an explicit wait for the next stage's loads only (a __syncthreads would also
+// wait for the loads of the stages further ahead).  Each stage's A fragments
+// are read right after that barrier, before the previous stage's products;
+// the B fragments of column tile j are re-read as soon as the products that
+// use them are issued.  No fused RMS: with the sums of squares the kernel
+// spills; a separate row pass (hyena_row_rms) plus the row scale is faster.
+__device__ __forceinline__ int dl_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+template <int NK>
+__global__ __launch_bounds__(512) void gemm_dl8_kernel(GemmArgs g) {
+    constexpr int BM = 256, BN = 256, BK = 32, NB = 4;
+    __shared__ __attribute__((aligned(16))) uint16_t A0[BM * BK], A1[BM * BK], A2[BM * BK], A3[BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t W0[BN * BK], W1[BN * BK], W2[BN * BK], W3[BN * BK];
+
+    const int tiles_m = (int)(g.M / BM), tiles_n = (int)(g.N / BN);
+    const int nwg = tiles_m * tiles_n;
+    constexpr int GM = 4;
+    int id = blockIdx.x;
+    if (nwg % 8 == 0) id = (id % 8) * (nwg / 8) + id / 8;  // contiguous tile range per XCD
+    const int group = id / (GM * tiles_n);
+    const int first_m = group * GM;
+    const int gm = (tiles_m - first_m < GM) ? tiles_m - first_m : GM;
+    const int in_group = id - group * GM * tiles_n;
+    const int tm = first_m + in_group % gm, tn = in_group / gm;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = w % 4, wn = w / 4;  // the wave's 64 x 128 sub-tile
+    const uint16_t *A = static_cast<const uint16_t *>(g.A);
+    const uint16_t *W = static_cast<const uint16_t *>(g.W);
+
+    // direct loads: wave w stages row blocks 2 w and 2 w + 1 (16 rows each) of A and of W
+    uint32_t offa[2], offw[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int lr = 16 * (2 * w + h) + lane / 4;
+        const int lc = (lane % 4) ^ dl_swz(lr);
+        offa[h] = (uint32_t)(lr * g.lda + 8 * lc) * 2u;
+        offw[h] = (uint32_t)(lr * g.ldw + 8 * lc) * 2u;
+    }
+    const char *Ab = reinterpret_cast<const char *>(A + m0 * g.lda);
+    const char *Wb = reinterpret_cast<const char *>(W + n0 * g.ldw);
+    auto bufs = [&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+        uint16_t *a = b == 0 ? A0 : b == 1 ? A1 : b == 2 ? A2 : A3;
+        uint16_t *ww = b == 0 ? W0 : b == 1 ? W1 : b == 2 ? W2 : W3;
+        return std::make_pair(a, ww);
+    };
+    auto issue = [&](auto sc) {
+        constexpr int st = decltype(sc)::value;
+        const auto [as, ws] = bufs(std::integral_constant<int, st % NB>{});
+        const int64_t k0 = (int64_t)st * BK;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(Ab + 2 * k0 + offa[h]),
+                                             &as[16 * (2 * w + h) * BK], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(Wb + 2 * k0 + offw[h]),
+                                             &ws[16 * (2 * w + h) * BK], 16, 0, 0);
+        }
+    };
+    auto frag = [&](const uint16_t *buf, int row0) {
+        const int r = row0 + lane % 16, c = lane / 16;
+        return *reinterpret_cast<const uint4 *>(&buf[r * BK + 8 * (c ^ dl_swz(r))]);
+    };
+    // A fragments double-buffered; B fragments single: column tile j's read for
+    // the next stage follows the products that use tile j of this one
+    uint4 af[2][4], bf[8];
+    auto read_a = [&](auto sc) {
+        constexpr int st = decltype(sc)::value;
+        const auto [as, ws] = bufs(std::integral_constant<int, st % NB>{});
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[st % 2][i] = frag(as, 64 * wm + 16 * i);
+    };
+
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // stages in flight before stage st's barrier: up to st + NB - 1; the
+    // barrier needs stage st + 1's loads (read right after it)
+    static_for<0, (NK < NB ? NK : NB)>([&](auto sc) { issue(sc); });
+    {
+        constexpr int later = (NK < NB ? NK : NB) - 1;  // stages issued after stage 0
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt((4 * later) | (0x7 << 4));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    read_a(std::integral_constant<int, 0>{});
+    {
+        const auto [as, ws] = bufs(std::integral_constant<int, 0>{});
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bf[j] = frag(ws, 128 * wn + 16 * j);
+    }
+    static_for<0, NK>([&](auto sc) {
+        constexpr int st = decltype(sc)::value;
+        if constexpr (st + 1 < NK) {
+            // issued so far: stages .. min(st + NB - 1, NK - 1); wait for st + 1
+            constexpr int last = (st + NB - 1 < NK - 1) ? st + NB - 1 : NK - 1;
+            constexpr int after = last - (st + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt((4 * after) | (0x7 << 4));  // vmcnt(4 after), lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (st + NB < NK) issue(std::integral_constant<int, st + NB>{});
+            read_a(std::integral_constant<int, st + 1>{});
+        }
+        const auto [nas, nws] = bufs(std::integral_constant<int, (st + 1) % NB>{});
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(af[st % 2][i], bf[j], acc[i][j]);
+            if constexpr (st + 1 < NK) bf[j] = frag(nws, 128 * wn + 16 * j);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    // epilogue: C-tile lane l holds rows 4 (l / 16) .. + 3, column l % 16
+    uint16_t *C = static_cast<uint16_t *>(g.C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int lrow = 64 * wm + 16 * i + 4 * (lane / 16) + r;
+            const int64_t row = m0 + lrow;
+            float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t col = n0 + 128 * wn + 16 * j + lane % 16;
+                C[row * g.ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ skinny GEMM
 
 // Workgroup = 4 waves on all M <= 64 rows x BN columns.  K advances in slabs of
@@ -808,6 +955,15 @@ hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
     if (g.ws && ws_need > 0 && g.ws_bytes >= ws_need) return launch_splitk<RMS>(g, stream);
     if (g.M <= 64 && g.K % kSkCK == 0) {
         gemm_skinny_kernel<16, RMS><<<dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, stream>>>(g);
+        return hipGetLastError();
+    }
+    // Plain products (no fused RMS) of whole 256 x 256 tiles with K = 2048:
+    // measured on MI355X at M = 131072 (in_proj N = 6144 with a row scale,
+    // out_proj N = 2048) 2.87 and 1.00 ms against 3.27 and 1.10 ms for the
+    // tiled kernel below.
+    if (!RMS && g.M % 256 == 0 && g.N % 256 == 0 && g.K == 2048 && g.lda % 8 == 0 && g.ldw % 8 == 0 &&
+        g.lda < (1 << 20) && g.ldw < (1 << 20)) {
+        gemm_dl8_kernel<64><<<dim3((unsigned)((g.M / 256) * (g.N / 256))), dim3(512), 0, stream>>>(g);
         return hipGetLastError();
     }
     // 256 x 256 tile, 16 waves of 64 x 64 (4 per SIMD): measured on MI355X at

@@ -34,7 +34,9 @@ def _bits(rng, shape, std=1.0):
     (37, 96, 1024),       # ragged rows and columns, skinny path
     (300, 200, 128),      # tiled path, ragged M and N
     (1024, 768, 512),     # tiled path, several tiles
-    (4096, 6144, 2048),   # tiled path at the prompt in_proj width
+    (4096, 6144, 2048),   # direct-load path (whole 256 x 256 tiles, K = 2048) at the prompt in_proj width
+    (512, 2048, 2048),    # direct-load path at the prompt out_proj width
+    (512, 2048, 1024),    # whole tiles, K != 2048: tiled path
 ])
 @pytest.mark.parametrize("scaled", [False, True])
 def test_dense_bf16(M, N, K, scaled):
@@ -89,6 +91,26 @@ def test_dense_strided_operands():
     hb.hyena_dense_bf16(M, N, K, A, K + 64, W, K + 128, None, C, N + 32)
     torch.cuda.synchronize()
     ref = oracle.dense(oracle.bf16_to_f64(a[:, :K]), oracle.bf16_to_f64(w[:, :K]))
+    assert rel_err(to_np64(C[:, :N]), ref) <= 8e-3
+    assert torch.all(C[:, N:] == 5.0).item()
+
+
+def test_dense_direct_load_strided():
+    """The direct-load prompt GEMM (whole 256 x 256 tiles, K = 2048) with row
+    strides larger than K and N, and a row scale: the columns beyond N stay
+    untouched."""
+    torch = require_gpu()
+    rng = np.random.default_rng(5)
+    M, N, K = 512, 256, 2048
+    a = _bits(rng, (M, K + 64))
+    w = _bits(rng, (N, K + 128), 0.02)
+    sc = rng.uniform(0.5, 2.0, M).astype(np.float32)
+    A, W = to_dev(a, "bf16"), to_dev(w, "bf16")
+    C = torch.full((M, N + 32), 5.0, dtype=torch.bfloat16, device="cuda")
+    log("dense direct-load strided")
+    hb.hyena_dense_bf16(M, N, K, A, K + 64, W, K + 128, torch.from_numpy(sc).cuda(), C, N + 32)
+    torch.cuda.synchronize()
+    ref = oracle.dense(oracle.bf16_to_f64(a[:, :K]), oracle.bf16_to_f64(w[:, :K])) * sc[:, None]
     assert rel_err(to_np64(C[:, :N]), ref) <= 8e-3
     assert torch.all(C[:, N:] == 5.0).item()
 
