@@ -244,8 +244,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
 // ------------------------------------------------------------------ prompt GEMM, direct loads
 
 // 256 x 256 tile, 8 waves of 64 x 128 (two per SIMD), K staged 32 at a time by
-// direct global -> LDS loads into four stage buffers, up to four stages ahead:
-// no staging registers and no LDS store instructions.  LDS rows are 64 bytes
+// direct global -> LDS loads into four stage buffers, each stage's loads issued
+// four stages before its products: no staging registers and no LDS store
+// instructions.  LDS rows are 64 bytes
 // (32 bf16) with the 16-byte chunks XOR-swizzled by row / 2 ^ row / 8, so a
 // fragment read (16 rows, one chunk each) covers all banks in every 8 lanes
 // (128 bytes) and in all 16 (256 bytes).  The K loop is unrolled at compile
