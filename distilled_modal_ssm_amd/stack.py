@@ -6,7 +6,7 @@ of the in_proj output) -> out_proj (D -> D).  No bias, no residual.  For the
 prompt the inverse RMS is a row pass of its own (hyena_row_rms) whose result
 is the in_proj's row scale: the prompt GEMM without a fused sum of squares is
 the faster one at these shapes (measured on MI355X, B * L = 131072, D = 2048:
-0.09 + 2.87 ms against 3.56 ms fused).  A generated token's in_proj computes
+0.09 + 2.79 ms against 3.56 ms fused).  A generated token's in_proj computes
 its RMS inside the projection.
 The stack's output at the last prompt position is the first generation input;
 each later generation input is the previous step's output.  Every computation
