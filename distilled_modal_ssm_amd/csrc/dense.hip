@@ -333,15 +333,26 @@ __global__ __launch_bounds__(512) void gemm_dl8_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // The stage barrier: this wave's wait (an s_waitcnt immediate: vmcnt in
+    // bits 3:0, expcnt 6:4, lgkmcnt 11:8), then a bare s_barrier.  The signal
+    // fences keep the compiler from moving LDS accesses across it (the barrier
+    // builtin itself is not a memory operation to the compiler), the
+    // scheduling barriers keep the machine scheduler from doing so.
+    auto stage_barrier = [&](auto wc) {
+        constexpr int wait = decltype(wc)::value;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(wait);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    };
     // stages in flight before stage st's barrier: up to st + NB - 1; the
     // barrier needs stage st + 1's loads (read right after it)
     static_for<0, (NK < NB ? NK : NB)>([&](auto sc) { issue(sc); });
     {
         constexpr int later = (NK < NB ? NK : NB) - 1;  // stages issued after stage 0
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt((4 * later) | (0x7 << 4));
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
+        stage_barrier(std::integral_constant<int, (4 * later) | (0x7 << 4)>{});
     }
     read_a(std::integral_constant<int, 0>{});
     {
@@ -355,10 +366,7 @@ __global__ __launch_bounds__(512) void gemm_dl8_kernel(GemmArgs g) {
             // issued so far: stages .. min(st + NB - 1, NK - 1); wait for st + 1
             constexpr int last = (st + NB - 1 < NK - 1) ? st + NB - 1 : NK - 1;
             constexpr int after = last - (st + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_waitcnt((4 * after) | (0x7 << 4));  // vmcnt(4 after), lgkmcnt(0)
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
+            stage_barrier(std::integral_constant<int, (4 * after) | (0x7 << 4)>{});  // vmcnt(4 after), lgkmcnt(0)
             if constexpr (st + NB < NK) issue(std::integral_constant<int, st + NB>{});
             read_a(std::integral_constant<int, st + 1>{});
         }
