@@ -115,8 +115,19 @@ def git_sha():
         return None
 
 
+def build_info() -> dict:
+    """The commit the library was built from, as the build recorded it."""
+    try:
+        with open(os.path.join(PKG, "build_info.json")) as f:
+            return json.load(f)
+    except (OSError, ValueError):
+        return {}
+
+
 def provenance() -> dict:
-    return {"git_sha": git_sha(), "source_fingerprint": source_fingerprint()}
+    b = build_info()
+    return {"git_sha": git_sha(), "built_from_git_sha": b.get("git_sha"),
+            "built_sources_modified": b.get("sources_modified"), "source_fingerprint": source_fingerprint()}
 
 
 # ------------------------------------------------------------------ counter traffic

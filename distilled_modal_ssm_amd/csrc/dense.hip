@@ -222,7 +222,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
         __syncthreads();
     }
 
-    // epilogue: C-tile lane l holds rows 4*(l/16)..+3, column l%16
+    // epilogue: C-tile lane l holds rows 4*(l/16)..+3, column l%16.  The row
+    // scales are all loaded before the first store (the vector memory counter
+    // counts stores and loads in order: a load between the stores would wait
+    // for every store before it).
+    float rsc[MT][4];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane / 16) + r;
+            rsc[i][r] = (g.row_scale && row < g.M) ? g.row_scale[row] : 1.0f;
+        }
     uint16_t *C = static_cast<uint16_t *>(g.C);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
@@ -230,7 +241,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
         for (int r = 0; r < 4; ++r) {
             const int64_t row = m0 + wm * WM + i * 16 + 4 * (lane / 16) + r;
             if (row >= g.M) continue;
-            float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+            float sc = rsc[i][r];
             if constexpr (RMS) sc *= rs[wm * WM + i * 16 + 4 * (lane / 16) + r];
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
@@ -332,6 +343,19 @@ __global__ __launch_bounds__(512) void gemm_dl8_kernel(GemmArgs g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The row scales of the lane's 16 output rows, loaded during the last
+    // stage's products, before any output store: the vector memory counter
+    // counts stores and loads in order, so a scale loaded between the stores
+    // would wait for every store issued before it (16 store round trips per
+    // wave, one per row group).
+    float rsc[4][4];
+    auto load_scales = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                rsc[i][r] = g.row_scale ? g.row_scale[m0 + 64 * wm + 16 * i + 4 * (lane / 16) + r] : 1.0f;
+    };
 
     // The stage barrier: this wave's wait (an s_waitcnt immediate: vmcnt in
     // bits 3:0, expcnt 6:4, lgkmcnt 11:8), then a bare s_barrier.  The signal
@@ -371,6 +395,7 @@ __global__ __launch_bounds__(512) void gemm_dl8_kernel(GemmArgs g) {
             read_a(std::integral_constant<int, st + 1>{});
         }
         const auto [nas, nws] = bufs(std::integral_constant<int, (st + 1) % NB>{});
+        if constexpr (st + 1 == NK) load_scales();
         // a wave in its products outranks the other wave of its SIMD in the
         // barrier, load-issue and fragment-read part of a stage (measured on
         // MI355X, M = 131072, K = 2048: in_proj 2.87 -> 2.79 ms, out_proj
@@ -393,7 +418,7 @@ __global__ __launch_bounds__(512) void gemm_dl8_kernel(GemmArgs g) {
         for (int r = 0; r < 4; ++r) {
             const int lrow = 64 * wm + 16 * i + 4 * (lane / 16) + r;
             const int64_t row = m0 + lrow;
-            float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+            const float sc = rsc[i][r];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int64_t col = n0 + 128 * wn + 16 * j + lane % 16;
@@ -752,18 +777,32 @@ __global__ __launch_bounds__(PDD > 0 ? 512 : 256) void gemm_stream_lds_kernel(Ge
             const int64_t ldr = g.H * g.P;
             const float2 rr = *reinterpret_cast<const float2 *>(g.rho + db * ldr + dc);
             const float Dg = g.skip[dg];
-            __builtin_nontemporal_store(pack_bf16x2(q0 * fmaf(Dg, u0, rr.x), q1 * fmaf(Dg, u1, rr.y)),
-                                        reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(g.y) + db * g.ld_y + dc));
+            // y with a plain store: out_proj reads it next, and a streaming store
+            // sends it past the caches it is read back through (measured on
+            // MI355X, 24-layer stack at batch 64: 0.5152 -> 0.5128 ms per token)
+            *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(g.y) + db * g.ld_y + dc) =
+                pack_bf16x2(q0 * fmaf(Dg, u0, rr.x), q1 * fmaf(Dg, u1, rr.y));
             *reinterpret_cast<float2 *>(g.u_prev + db * ldr + dc) = make_float2(u0, u1);
             return;
         }
         // the decode step with the arithmetic of decode_step_fixed (two
         // channels per lane): y = q (D u + Re sum R x), x <- lambda x + u
-        const float2 *lam = g.poles + dg * (FDL > 0 ? FDL : 1), *res = g.residues + dg * (FDL > 0 ? FDL : 1);
+        // the head's poles and residues are read before the first state store:
+        // the vector memory counter counts stores and loads in order, so a load
+        // issued after a store is waited for together with the store
+        constexpr int NM = FDL > 0 ? FDL : 1;
+        const float2 *lam = g.poles + dg * NM, *res = g.residues + dg * NM;
+        float2 lv[NM], rv[NM];
+#pragma unroll
+        for (int n = 0; n < NM; ++n) {
+            lv[n] = lam[n];
+            rv[n] = res[n];
+        }
+        const float Dg = g.skip[dg];
         float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
         for (int n = 0; n < (FDL > 0 ? FDL : 0); ++n) {
-            const float2 l = lam[n], r = res[n];
+            const float2 l = lv[n], r = rv[n];
             const f32x4 xo = xs[n];
             acc0 = fmaf(r.x, xo[0], acc0);
             acc0 = fmaf(-r.y, xo[1], acc0);
@@ -773,7 +812,6 @@ __global__ __launch_bounds__(PDD > 0 ? 512 : 256) void gemm_stream_lds_kernel(Ge
                               fmaf(l.x, xo[2], fmaf(-l.y, xo[3], u1)), fmaf(l.x, xo[3], l.y * xo[2])};
             __builtin_nontemporal_store(xn, reinterpret_cast<f32x4 *>(dst + n * g.P));
         }
-        const float Dg = g.skip[dg];
         __builtin_nontemporal_store(pack_bf16x2(q0 * fmaf(Dg, u0, acc0), q1 * fmaf(Dg, u1, acc1)),
                                     reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(g.y) + db * g.ld_y + dc));
         return;
