@@ -70,7 +70,7 @@ KERNEL_SOURCES = {
 # Dispatches that make up one generated token of the stack, per layer (names as
 # the profiler prints them, matched by prefix).
 STACK_TOKEN_KERNELS = {
-    "gate": "gemm_stream_lds_kernel<3, 2, true, 32, -1,",
+    "gate": "gemm_stream_lds_kernel<3, 1, true, 32, -1,",
     "out_proj": "gemm_stream_lds_kernel<1, 2, false, 32, 0, 0>",
 }
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read, 1 GiB written

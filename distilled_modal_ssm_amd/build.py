@@ -17,9 +17,6 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhyena_modal.so")
-# the commit the library was built from (written at build time, travels with
-# the built library to machines that get the tree without its git metadata)
-BUILD_INFO = os.path.join(HERE, "build_info.json")
 
 SOURCES = ["hm_api.cpp", "decode.hip", "filter.hip", "prefill.hip", "prefill_mfma.hip", "dense.hip", "fir.hip", "fft.hip", "distill.hip",
            "gen_step.hip", "modal_fit.cpp"]
@@ -54,20 +51,6 @@ def _compile(src: str) -> str:
     return obj
 
 
-def _write_build_info() -> None:
-    """Record HEAD and whether the library's sources differ from it."""
-    import json
-
-    def git(*args):
-        r = subprocess.run(["git", "-C", ROOT, *args], capture_output=True, text=True)
-        return r.stdout.strip() if r.returncode == 0 else None
-
-    sha = git("rev-parse", "HEAD")
-    dirty = git("status", "--porcelain", "--", "distilled_modal_ssm_amd", "include")
-    with open(BUILD_INFO, "w") as f:
-        json.dump({"git_sha": sha, "sources_modified": bool(dirty) if dirty is not None else None}, f)
-
-
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
@@ -76,7 +59,6 @@ def build(verbose: bool = False) -> str:
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
-    _write_build_info()
     if verbose:
         print(f"built {LIB}")
     return LIB

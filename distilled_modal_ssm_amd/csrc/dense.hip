@@ -1064,13 +1064,18 @@ hipError_t launch_layer_step(const GemmArgs &g, int d, hipStream_t stream) {
 
 hipError_t launch_layer_gate(const GemmArgs &g, hipStream_t stream) {
     if (g.M == 0) return hipSuccess;
+    // Weights one chunk ahead (SW = 1), not two: measured on MI355X in the
+    // 24-layer stack at batch 64, 0.5134 -> 0.5063 ms per token; the state
+    // stream of the ride-along prepare gains more than the product loses.
+    // Two and more chunks of weights ahead, or the layer input one chunk
+    // ahead instead of two, or temporal weight loads, measured slower.
     const int64_t tiles = g.N / 48;
     const dim3 grid((unsigned)(((tiles + 7) / 8) * 16));
     switch (g.prep.B > 0 ? g.prep.d : 0) {
-        case 0: gemm_stream_lds_kernel<3, 2, true, 32, -1, 0><<<grid, dim3(256), 0, stream>>>(g); break;
-        case 8: gemm_stream_lds_kernel<3, 2, true, 32, -1, 8><<<grid, dim3(512), 0, stream>>>(g); break;
-        case 16: gemm_stream_lds_kernel<3, 2, true, 32, -1, 16><<<grid, dim3(512), 0, stream>>>(g); break;
-        case 32: gemm_stream_lds_kernel<3, 2, true, 32, -1, 32><<<grid, dim3(512), 0, stream>>>(g); break;
+        case 0: gemm_stream_lds_kernel<3, 1, true, 32, -1, 0><<<grid, dim3(256), 0, stream>>>(g); break;
+        case 8: gemm_stream_lds_kernel<3, 1, true, 32, -1, 8><<<grid, dim3(512), 0, stream>>>(g); break;
+        case 16: gemm_stream_lds_kernel<3, 1, true, 32, -1, 16><<<grid, dim3(512), 0, stream>>>(g); break;
+        case 32: gemm_stream_lds_kernel<3, 1, true, 32, -1, 32><<<grid, dim3(512), 0, stream>>>(g); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

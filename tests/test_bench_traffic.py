@@ -43,7 +43,7 @@ def test_stack_token_traffic_sums_every_layer(tmp_path, monkeypatch):
     copy, and other kernels in the run (the start-of-generation prepare) do not
     count."""
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
-    gate = "void hm::(anonymous namespace)::gemm_stream_lds_kernel<3, 2, true, 32, -1, 16>(hm::GemmArgs)"
+    gate = "void hm::(anonymous namespace)::gemm_stream_lds_kernel<3, 1, true, 32, -1, 16>(hm::GemmArgs)"
     outp = "void hm::(anonymous namespace)::gemm_stream_lds_kernel<1, 2, false, 32, 0, 0>(hm::GemmArgs)"
     prep = "void hm::(anonymous namespace)::prepare_kernel<16>(hm::PrepArgs)"
     copy = "void at::native::elementwise_kernel<direct_copy_kernel_cuda>"
