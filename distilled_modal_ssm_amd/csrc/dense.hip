@@ -343,18 +343,17 @@ __global__ __launch_bounds__(512) void gemm_dl8_kernel(GemmArgs g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // The row scales of the lane's 16 output rows, loaded during the last
-    // stage's products, before any output store: the vector memory counter
-    // counts stores and loads in order, so a scale loaded between the stores
-    // would wait for every store issued before it (16 store round trips per
-    // wave, one per row group).
-    float rsc[4][4];
+    // The products are taken with the W fragment as the first operand, so the
+    // C tiles are held transposed: lane l holds row 16 i + l % 16 of the wave's
+    // tile, columns 16 j + 4 (l / 16) .. + 3, four adjacent outputs that leave
+    // as one 8-byte piece.  The row scales of the lane's 4 rows are loaded
+    // during the last stage's products, before any output store (the vector
+    // memory counter counts stores and loads in order: a scale loaded between
+    // the stores would wait for every store issued before it).
+    float rsc[4];
     auto load_scales = [&]() {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                rsc[i][r] = g.row_scale ? g.row_scale[m0 + 64 * wm + 16 * i + 4 * (lane / 16) + r] : 1.0f;
+        for (int i = 0; i < 4; ++i) rsc[i] = g.row_scale ? g.row_scale[m0 + 64 * wm + 16 * i + lane % 16] : 1.0f;
     };
 
     // The stage barrier: this wave's wait (an s_waitcnt immediate: vmcnt in
@@ -404,27 +403,42 @@ __global__ __launch_bounds__(512) void gemm_dl8_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(af[st % 2][i], bf[j], acc[i][j]);
+            for (int i = 0; i < 4; ++i) acc[i][j] = mfma16(bf[j], af[st % 2][i], acc[i][j]);
             if constexpr (st + 1 < NK) bf[j] = frag(nws, 128 * wn + 16 * j);
         }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
     });
-    // epilogue: C-tile lane l holds rows 4 (l / 16) .. + 3, column l % 16
-    uint16_t *C = static_cast<uint16_t *>(g.C);
+    // Epilogue through LDS: each wave writes its 64 x 128 bf16 tile (16 KB)
+    // into one of the eight stage arrays as 8-byte pieces, then reads it back
+    // as whole 16-byte chunks, so each store instruction writes four complete
+    // 256-byte row segments of C (2-byte stores of the MFMA layout wrote four
+    // 32-byte pieces per instruction).  A row of the staged tile is 256 bytes,
+    // sixteen 16-byte chunks, with chunk c stored at c ^ (row % 16): the
+    // sixteen rows one piece-write instruction touches then fall on distinct
+    // banks.  Each wave reads only what it wrote (its LDS operations complete
+    // in order), so one barrier -- every wave done with the stage buffers --
+    // is all the epilogue needs.
+    __syncthreads();
+    uint16_t *ob = w == 0 ? A0 : w == 1 ? A1 : w == 2 ? A2 : w == 3 ? A3 : w == 4 ? W0 : w == 5 ? W1 : w == 6 ? W2 : W3;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        const int row = 16 * i + lane % 16;
+        const float sc = rsc[i];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int lrow = 64 * wm + 16 * i + 4 * (lane / 16) + r;
-            const int64_t row = m0 + lrow;
-            const float sc = rsc[i][r];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int64_t col = n0 + 128 * wn + 16 * j + lane % 16;
-                C[row * g.ldc + col] = (uint16_t)f32_to_bf16(acc[i][j][r] * sc);
-            }
+        for (int j = 0; j < 8; ++j) {
+            const int chunk = 2 * j + (lane / 16) / 2;  // 16-byte chunk of the row holding the piece
+            const uint2 piece = make_uint2(pack_bf16x2(acc[i][j][0] * sc, acc[i][j][1] * sc),
+                                           pack_bf16x2(acc[i][j][2] * sc, acc[i][j][3] * sc));
+            *reinterpret_cast<uint2 *>(&ob[row * 128 + 8 * (chunk ^ (row % 16)) + 4 * ((lane / 16) % 2)]) = piece;
         }
+    }
+    uint16_t *C = static_cast<uint16_t *>(g.C) + (m0 + 64 * wm) * g.ldc + n0 + 128 * wn;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const int row = 4 * t + lane / 16, chunk = lane % 16;
+        const uint4 v = *reinterpret_cast<const uint4 *>(&ob[row * 128 + 8 * (chunk ^ (row % 16))]);
+        *reinterpret_cast<uint4 *>(C + (int64_t)row * g.ldc + 8 * chunk) = v;
     }
 }
 
@@ -1015,7 +1029,7 @@ hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
     // out_proj N = 2048) 2.87 and 1.00 ms against 3.27 and 1.10 ms for the
     // tiled kernel below.
     if (!RMS && g.M % 256 == 0 && g.N % 256 == 0 && g.K == 2048 && g.lda % 8 == 0 && g.ldw % 8 == 0 &&
-        g.lda < (1 << 20) && g.ldw < (1 << 20)) {
+        g.ldc % 8 == 0 && reinterpret_cast<uintptr_t>(g.C) % 16 == 0 && g.lda < (1 << 20) && g.ldw < (1 << 20)) {
         gemm_dl8_kernel<64><<<dim3((unsigned)((g.M / 256) * (g.N / 256))), dim3(512), 0, stream>>>(g);
         return hipGetLastError();
     }

@@ -255,7 +255,8 @@ hm_status hyena_row_rms(const void *x, int64_t M, int64_t D, int64_t ld, float e
  * Requirements: K a positive multiple of 64; lda, ldw multiples of 8; A and W
  * 16-byte aligned (else HM_ERR_UNSUPPORTED).  M <= 64 takes a weight-streaming
  * path (the generation step), larger M an LDS-tiled path (M and N multiples of
- * 256 with K = 2048: K staged by direct global-to-LDS loads, the prompt
+ * 256 with K = 2048, ldc a multiple of 8 and C 16-byte aligned: K staged by
+ * direct global-to-LDS loads and C written as whole row segments, the prompt
  * projections of the 1.3B-width stack).
  */
 hm_status hyena_dense_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda,
