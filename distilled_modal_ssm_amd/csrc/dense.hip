@@ -835,16 +835,29 @@ __global__ __launch_bounds__(PDD > 0 ? 512 : 256) void gemm_stream_lds_kernel(Ge
         return;
     }
     uint16_t *C = static_cast<uint16_t *>(g.C);
-    for (int e = tid; e < MR * BN && tid < 256; e += 256) {
-        const int lr = e / BN, c = e % BN;
+    // each thread two adjacent columns of a row, one 4-byte store where C's
+    // layout allows (ldc even, C 4-byte aligned; wave-uniform)
+    const bool pairs = g.ldc % 2 == 0 && reinterpret_cast<uintptr_t>(g.C) % 4 == 0;
+    for (int e = tid; e < MR * BN / 2 && tid < 256; e += 256) {
+        const int lr = e / (BN / 2), c = 2 * (e % (BN / 2));
         const int64_t row = m0 + lr, col = n0 + c;
         if (row >= g.M || col >= g.N) continue;
-        const float sum = red[(0 * MR + lr) * BN + c] + red[(1 * MR + lr) * BN + c] +
-                          red[(2 * MR + lr) * BN + c] + red[(3 * MR + lr) * BN + c];
+        float2 sum = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float2 part = *reinterpret_cast<const float2 *>(&red[(q * MR + lr) * BN + c]);
+            sum.x += part.x;
+            sum.y += part.y;
+        }
         float sc = g.row_scale ? g.row_scale[row] : 1.0f;
         if constexpr (RMS)
             sc *= rms_scale(red_ss[lr] + red_ss[MR + lr] + red_ss[2 * MR + lr] + red_ss[3 * MR + lr], g.K, g.rms_eps);
-        C[row * g.ldc + col] = (uint16_t)f32_to_bf16(sum * sc);
+        if (pairs && col + 1 < g.N) {
+            *reinterpret_cast<uint32_t *>(&C[row * g.ldc + col]) = pack_bf16x2(sum.x * sc, sum.y * sc);
+        } else {
+            C[row * g.ldc + col] = (uint16_t)f32_to_bf16(sum.x * sc);
+            if (col + 1 < g.N) C[row * g.ldc + col + 1] = (uint16_t)f32_to_bf16(sum.y * sc);
+        }
     }
 }
 
