@@ -197,14 +197,17 @@ struct PrepArgs {
 
 // Prepare of one unit: batch row b, channels c and c + 1 (c even, one head;
 // D / H even), unit = b D/2 + c/2.  16-byte state accesses, non-temporal (the
-// state is streamed once per token).  The modes go in two halves, each loaded
-// whole, then updated and stored, so the state's stores start after half of
-// its loads (measured on MI355X riding in the 24-layer stack's gate at batch
-// 64, d = 16: 16.6 -> 16.4 us per layer; quarters 16.7 us).
+// state is streamed once per token).  The modes go in four quarters, each
+// loaded whole, then updated and stored, so the state's stores start after a
+// quarter of its loads.  Measured on MI355X riding in the 24-layer stack's
+// gate at batch 64, d = 16, with the gate's weights one chunk ahead: 0.495 ms
+// per token against 0.503 ms for halves, 0.514 ms for eighths and 0.533 ms for
+// one mode at a time (with the weights two chunks ahead, halves had measured
+// ahead of quarters).
 template <int DD>
 __device__ __forceinline__ void prepare_unit(const PrepArgs &p, int64_t unit) {
     typedef float f4 __attribute__((ext_vector_type(4)));
-    constexpr int HB = DD / 2;
+    constexpr int HB = DD / 4;
     const int64_t half = p.D / 2, b = unit / half, c = 2 * (unit - b * half), g = c / p.P;
     f4 *st = reinterpret_cast<f4 *>(p.state + ((b * p.H + g) * DD) * p.P + (c - g * p.P));
     const float2 up = *reinterpret_cast<const float2 *>(p.u_prev + b * p.D + c);
