@@ -71,7 +71,7 @@ KERNEL_SOURCES = {
 # the profiler prints them, matched by prefix).
 STACK_TOKEN_KERNELS = {
     "gate": "gemm_stream_lds_kernel<3, 1, true, 32, -1,",
-    "out_proj": "gemm_stream_lds_kernel<1, 2, false, 32, 0, 0>",
+    "out_proj": "gemm_stream_dl_kernel<6>",
 }
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read, 1 GiB written
 

@@ -23,6 +23,9 @@
 //     W slabs through double-buffered LDS.  Both sum their K parts through
 //     LDS.  Every workgroup re-reads its rows of A, so these are bound by
 //     L1->L2 request throughput as much as by the W stream.
+//   * gemm_stream_dl (the generation step's out_proj: M in (32, 64], no fused
+//     RMS): the 32-row, 16-column workgroups of gemm_stream_lds with K staged
+//     by direct global -> LDS loads into wave-private chunk buffers.
 //   * the fused generation step of a layer: gemm_stream_lds on in_proj
 //     weights packed so a 48-column tile is q, k, v of 16 channels, whose
 //     epilogue runs the modal decode step for them instead of storing C.
@@ -861,6 +864,131 @@ __global__ __launch_bounds__(PDD > 0 ? 512 : 256) void gemm_stream_lds_kernel(Ge
     }
 }
 
+// out_proj-shaped streaming GEMM: M in (32, 64], K = 2048, no fused RMS; a
+// workgroup owns 16 columns and one 32-row half (the two halves of a column
+// tile on one XCD, as in gemm_stream_lds), wave w K quarter w in 8 chunks of
+// 64.  K is staged by direct global -> LDS loads into NB wave-private chunk
+// buffers, NB - 1 chunks ahead: no staging registers and no LDS stores.  A
+// buffer row is 128 bytes (64 bf16), eight 16-byte pieces; piece p of row r
+// sits in slot p ^ (r % 8), so the 16 rows of a fragment read spread over
+// the banks.  A load instruction covers 8 rows (8 lanes per row, each lane
+// the piece that belongs in its slot), and each buffer is its own array, so
+// every wait names exactly the loads it needs.  The four K quarters are
+// summed through LDS as in gemm_stream_lds.
+template <int NB>
+__global__ __launch_bounds__(256) void gemm_stream_dl_kernel(GemmArgs g) {
+    constexpr int MR = 32, BN = 16, NCH = 8, LPC = MR / 8 + BN / 8;  // load instructions per chunk
+    static_assert(NB >= 3 && NB <= 6, "chunk buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t A0[4][MR * 64], A1[4][MR * 64], A2[4][MR * 64],
+        A3[NB > 3 ? 4 : 1][MR * 64], A4[NB > 4 ? 4 : 1][MR * 64], A5[NB > 5 ? 4 : 1][MR * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t W0[4][BN * 64], W1[4][BN * 64], W2[4][BN * 64],
+        W3[NB > 3 ? 4 : 1][BN * 64], W4[NB > 4 ? 4 : 1][BN * 64], W5[NB > 5 ? 4 : 1][BN * 64];
+    static_assert(4 * MR * BN * sizeof(float) <= sizeof(A0), "the K-part sums reuse the first A buffer");
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int64_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const int64_t m0 = 32 * (slot % 2), tile = (slot / 2) * 8 + xcd;
+    if (tile * BN >= g.N || m0 >= g.M) return;  // the whole workgroup
+    const int64_t n0 = tile * BN, kbeg = (int64_t)w * NCH * 64;
+    const uint16_t *A = static_cast<const uint16_t *>(g.A);
+    const uint16_t *W = static_cast<const uint16_t *>(g.W);
+    // lane l loads row 8 i + l / 8 of instruction i, the piece for slot l % 8
+    const int lrow = lane / 8, lpiece = (lane % 8) ^ (lane / 8);
+    const uint16_t *arow[MR / 8], *wrow[BN / 8];
+#pragma unroll
+    for (int i = 0; i < MR / 8; ++i) {
+        const int64_t r = m0 + 8 * i + lrow;
+        arow[i] = A + (r < g.M ? r : 0) * g.lda + kbeg + 8 * lpiece;  // clamped rows are masked at the end
+    }
+#pragma unroll
+    for (int i = 0; i < BN / 8; ++i) {
+        const int64_t c = n0 + 8 * i + lrow;
+        wrow[i] = W + (c < g.N ? c : 0) * g.ldw + kbeg + 8 * lpiece;  // clamped columns are masked at the end
+    }
+    auto bufs = [&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+        uint16_t *a = b == 0 ? A0[w] : b == 1 ? A1[w] : b == 2 ? A2[w] : b == 3 ? A3[NB > 3 ? w : 0]
+                    : b == 4 ? A4[NB > 4 ? w : 0] : A5[NB > 5 ? w : 0];
+        uint16_t *ww = b == 0 ? W0[w] : b == 1 ? W1[w] : b == 2 ? W2[w] : b == 3 ? W3[NB > 3 ? w : 0]
+                     : b == 4 ? W4[NB > 4 ? w : 0] : W5[NB > 5 ? w : 0];
+        return std::make_pair(a, ww);
+    };
+    auto issue = [&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        const auto [ab, wb] = bufs(std::integral_constant<int, c % NB>{});
+#pragma unroll
+        for (int i = 0; i < MR / 8; ++i)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(arow[i] + 64 * c), &ab[8 * i * 64], 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < BN / 8; ++i)
+            __builtin_amdgcn_global_load_lds(reinterpret_cast<const void *>(wrow[i] + 64 * c), &wb[8 * i * 64], 16, 0, 0);
+    };
+    auto frag = [&](const uint16_t *buf, int r, int q) {
+        return *reinterpret_cast<const uint4 *>(&buf[r * 64 + 8 * (q ^ (r % 8))]);
+    };
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    static_for<0, NB>([&](auto cc) { issue(cc); });
+    static_for<0, NCH>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        // chunks issued so far: 0 .. min(c + NB - 1, NCH - 1); wait for chunk c
+        // (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8 = 0)
+        constexpr int later = ((c + NB - 1 < NCH - 1) ? c + NB - 1 : NCH - 1) - c;
+        constexpr int vm = LPC * later;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt((vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4));
+        __builtin_amdgcn_sched_barrier(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const auto [ab, wb] = bufs(std::integral_constant<int, c % NB>{});
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint4 b = frag(wb, lane % 16, 4 * h + lane / 16);
+#pragma unroll
+            for (int m = 0; m < 2; ++m) acc[m] = mfma16(frag(ab, 16 * m + lane % 16, 4 * h + lane / 16), b, acc[m]);
+        }
+        if constexpr (c + NB < NCH) {
+            // this chunk's fragment reads are done (the products above used
+            // them) before its buffer takes chunk c + NB
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+            __builtin_amdgcn_sched_barrier(0);
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            issue(std::integral_constant<int, c + NB>{});
+        }
+    });
+    __syncthreads();  // every wave is done with its buffers; the sums reuse A0
+    float *red = reinterpret_cast<float *>(&A0[0][0]);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[(w * MR + m * 16 + 4 * (lane / 16) + r) * BN + lane % 16] = acc[m][r];
+    __syncthreads();
+    uint16_t *C = static_cast<uint16_t *>(g.C);
+    const bool pairs = g.ldc % 2 == 0 && reinterpret_cast<uintptr_t>(g.C) % 4 == 0;
+    {
+        const int e = tid;  // MR * BN / 2 = 256 pairs, one per thread
+        const int lr = e / (BN / 2), c = 2 * (e % (BN / 2));
+        const int64_t row = m0 + lr, col = n0 + c;
+        if (row < g.M && col < g.N) {
+            float2 sum = make_float2(0.f, 0.f);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float2 part = *reinterpret_cast<const float2 *>(&red[(q * MR + lr) * BN + c]);
+                sum.x += part.x;
+                sum.y += part.y;
+            }
+            const float sc = g.row_scale ? g.row_scale[row] : 1.0f;
+            if (pairs && col + 1 < g.N) {
+                *reinterpret_cast<uint32_t *>(&C[row * g.ldc + col]) = pack_bf16x2(sum.x * sc, sum.y * sc);
+            } else {
+                C[row * g.ldc + col] = (uint16_t)f32_to_bf16(sum.x * sc);
+                if (col + 1 < g.N) C[row * g.ldc + col + 1] = (uint16_t)f32_to_bf16(sum.y * sc);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ split-K GEMM (M <= 64)
 
 // Pass 1.  Workgroup = (64-column tile nt, 256-wide K slice sl), 4 waves; wave
@@ -1027,7 +1155,15 @@ hipError_t launch_gemm_t(const GemmArgs &g, hipStream_t stream) {
                 gemm_stream_lds_kernel<3, 2, RMS, 32><<<dim3((unsigned)(((tiles + 7) / 8) * 16)), dim3(256), 0, stream>>>(g);
             } else {
                 const int64_t tiles = (g.N + 15) / 16;
-                gemm_stream_lds_kernel<1, 2, RMS, 32><<<dim3((unsigned)(((tiles + 7) / 8) * 16)), dim3(256), 0, stream>>>(g);
+                const dim3 grid((unsigned)(((tiles + 7) / 8) * 16));
+                // out_proj (no fused RMS) stages K by direct loads, five chunks
+                // ahead (measured on MI355X in the 24-layer stack at batch 64,
+                // token 0.4956 ms with the register-staged kernel, 0.4940 /
+                // 0.4920 / 0.4899 ms with 3 / 4 / 6 chunk buffers)
+                if constexpr (!RMS)
+                    gemm_stream_dl_kernel<6><<<grid, dim3(256), 0, stream>>>(g);
+                else
+                    gemm_stream_lds_kernel<1, 2, RMS, 32><<<grid, dim3(256), 0, stream>>>(g);
             }
         } else if (g.N >= 4096)
             gemm_stream_lds_kernel<2, 2, RMS, 64><<<dim3((unsigned)((g.N + 31) / 32)), dim3(256), 0, stream>>>(g);

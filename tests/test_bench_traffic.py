@@ -44,7 +44,7 @@ def test_stack_token_traffic_sums_every_layer(tmp_path, monkeypatch):
     count."""
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
     gate = "void hm::(anonymous namespace)::gemm_stream_lds_kernel<3, 1, true, 32, -1, 16>(hm::GemmArgs)"
-    outp = "void hm::(anonymous namespace)::gemm_stream_lds_kernel<1, 2, false, 32, 0, 0>(hm::GemmArgs)"
+    outp = "void hm::(anonymous namespace)::gemm_stream_dl_kernel<6>(hm::GemmArgs)"
     prep = "void hm::(anonymous namespace)::prepare_kernel<16>(hm::PrepArgs)"
     copy = "void at::native::elementwise_kernel<direct_copy_kernel_cuda>"
     _csv(tmp_path / "f", "FETCH_SIZE", [(copy, 524288.0), (prep, 9999.0), (gate, 100.0), (outp, 10.0), (gate, 300.0),
