@@ -30,6 +30,8 @@ def _bits(rng, shape, std=1.0):
     (37, 4100, 2048),     # weight streaming path, ragged rows and columns
     (64, 2048, 2048),     # generation-step out_proj (streaming, 16 columns per workgroup)
     (45, 2000, 2048),     # streaming, two 32-row halves, 16 columns, ragged rows and columns
+    (33, 17, 2048),       # direct-load streaming: one row in the second half, a 1-column tile, odd ldc
+    (64, 4095, 2048),     # direct-load streaming: widest N it takes, a 15-column tile, odd ldc
     (21, 1000, 2048),     # streaming, one 64-row workgroup per 16 columns, ragged
     (37, 96, 1024),       # ragged rows and columns, skinny path
     (300, 200, 128),      # tiled path, ragged M and N
