@@ -18,7 +18,8 @@ way (filter taps, prefill, S decode steps as one graph replay):
   long64k-f32 (the 64k-token prefill).
 ``--config N`` runs a single workload (1-5) instead.  Counter runs use
 ``--decode-mode eager --calibrate-copy`` (operator workloads) or
-``--token-counters N`` (the stack's generated token), and ``--traffic-from``
+``--token-counters N`` (the stack's generated token) or ``--prefill-counters``
+(the stack's prompt GEMMs), and ``--traffic-from``
 turns their output into the committed traffic summaries.
 
 Inputs are resident in HBM before any timed region.  Every time comes from
@@ -66,6 +67,8 @@ KERNEL_SOURCES = {
     # the projected stack's generated token: the gate (with the next layer's
     # prepare riding along) and out_proj, both streaming GEMMs of dense.hip
     "stack_token": ["dense.hip", "hm_internal.hpp"],
+    # the stack's prompt GEMMs (in_proj with the row scale, out_proj), both gemm_dl8_kernel
+    "stack_prompt_gemm": ["dense.hip", "hm_internal.hpp"],
 }
 # Dispatches that make up one generated token of the stack, per layer (names as
 # the profiler prints them, matched by prefix).
@@ -73,6 +76,8 @@ STACK_TOKEN_KERNELS = {
     "gate": "gemm_stream_lds_kernel<3, 1, true, 32, -1,",
     "out_proj": "gemm_stream_dl_kernel<6>",
 }
+# Prompt GEMM dispatches of one layer's prefill: in_proj and out_proj, one each
+STACK_PROMPT_GEMM_KERNELS = {"in_proj + out_proj": ("gemm_dl8_kernel", 2)}
 COPY_BYTES = 1 << 30  # the calibration copy: 1 GiB read, 1 GiB written
 
 
@@ -195,8 +200,12 @@ def write_traffic(args):
     fetch_dir, write_dir = args.traffic_from
     # kernel name patterns and launches per unit: one dispatch of the kernel,
     # or for the stack's token every layer's gate and out_proj
-    parts = ({k: (v, cfg.layers) for k, v in STACK_TOKEN_KERNELS.items()} if kernel == "stack_token"
-             else {kernel: (kernel, 1)})
+    if kernel == "stack_token":
+        parts = {k: (v, cfg.layers) for k, v in STACK_TOKEN_KERNELS.items()}
+    elif kernel == "stack_prompt_gemm":
+        parts = dict(STACK_PROMPT_GEMM_KERNELS)  # per layer: the mean dispatch x 2
+    else:
+        parts = {kernel: (kernel, 1)}
     out = {}
     per_part = []
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
@@ -218,6 +227,8 @@ def write_traffic(args):
     sb = cfg.act_bytes
     if kernel == "stack_token":
         alg = stack_token_bytes(cfg)
+    elif kernel == "stack_prompt_gemm":
+        alg = stack_prompt_gemm_bytes(cfg)
     elif kernel.startswith("decode"):
         alg = cfg.B * cfg.D * (16 * cfg.d + 4 * sb)
     else:
@@ -316,7 +327,10 @@ def parse():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="no GPU: write the traffic summary of --traffic-kernel from two rocprofv3 --pmc runs")
     ap.add_argument("--traffic-kernel", default="decode_step_fixed",
-                    help="decode_step_fixed, chunk_mfma_kernel, chunk_scan_kernel or stack_token")
+                    help="decode_step_fixed, chunk_mfma_kernel, chunk_scan_kernel, stack_token or stack_prompt_gemm")
+    ap.add_argument("--prefill-counters", action="store_true",
+                    help="for counter runs of the stack's prompt GEMMs: the calibration copy, then one "
+                         "eager prefill of the prompt through all layers")
     ap.add_argument("--token-counters", type=int, default=None, metavar="N",
                     help="for counter runs of the stack's generated token: the calibration copy, then N "
                          "generated tokens launched eagerly from a synthetic state (no prompt, no graphs)")
@@ -634,6 +648,15 @@ def run_operator(args, cfg, dev) -> dict:
 # ------------------------------------------------------------------ projected stack
 
 
+def stack_prompt_gemm_bytes(cfg) -> int:
+    """HBM bytes one layer's two prompt GEMMs must move: in_proj reads the
+    layer input [B L][D] and W_in [3D][D] and writes q, k, v [B L][3D]; out_proj
+    reads the operator output [B L][D] and W_out [D][D] and writes [B L][D]
+    (bf16 throughout; the row scales, 4 bytes a row, are left out)."""
+    M, D = cfg.B * cfg.L, cfg.D
+    return 2 * (M * D + 3 * D * D + 3 * M * D) + 2 * (M * D + D * D + M * D)
+
+
 def stack_token_bytes(cfg) -> int:
     """HBM bytes a generated token of the projected stack must move: per layer the
     bf16 weights (W_in 3D x D, W_out D x D), the modal state read and written
@@ -751,7 +774,14 @@ def run_stack(args, cfg, dev) -> dict:
                           f"prepare, out_proj)",
                 "launch_ms": round(ms_tok, 5), "algorithmic_bytes_per_launch": token_bytes}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = read_traffic("stack_token", cfg.name) if roof["bound"] == "hbm" else None
+    # counter-measured HBM bytes of the dominant phase's kernels: the token's
+    # gates and out_projs, or the prompt GEMMs (summary per layer; the mfma
+    # roofline counts the prompt through all layers)
+    if roof["bound"] == "hbm":
+        roof["traffic"] = read_traffic("stack_token", cfg.name)
+    else:
+        t = read_traffic("stack_prompt_gemm", cfg.name)
+        roof["traffic"] = t * cfg.layers if t is not None else None
 
     # outside the timed region: the generation kernels alone, each captured
     # 24 times over the layers (cache-cold weights, as in the stack) and
@@ -821,6 +851,31 @@ def token_counter_run(cfg, dev, n_tokens: int) -> None:
         st.decode_step()
         torch.cuda.synchronize()
     print(json.dumps({"token_counter_run": cfg.name, "tokens": n_tokens, "layers": cfg.layers}), flush=True)
+
+
+def prefill_counter_run(cfg, dev) -> None:
+    """Counter collection for the stack's prompt GEMMs: the 1 GiB calibration
+    copy, then one prefill of the prompt through all layers (eager), whose
+    in_proj and out_proj are the kernels and shapes of the timed prefill."""
+    import torch
+    from distilled_modal_ssm_amd.stack import HyenaStack
+    from workloads import dense_weights, modal_params, stack_prompt
+
+    if not cfg.layers:
+        raise SystemExit("--prefill-counters needs the stack workload (--config 5)")
+    log(f"[bench] workload {cfg.index}: weights and prompt for the prefill counter run")
+    with ThreadPoolExecutor(8) as ex:
+        ws = list(ex.map(lambda l: dense_weights(cfg, l), range(cfg.layers)))
+    layers = [(modal_params(cfg, l), *ws[l]) for l in range(cfg.layers)]
+    del ws
+    st = HyenaStack(layers, cfg.B, cfg.L, device=dev)
+    X = torch.from_numpy(stack_prompt(cfg).view(np.int16)).view(torch.bfloat16).to(dev)
+    torch.cuda.synchronize()
+    calibration_copy()
+    log("[bench] prefill")
+    st.prefill(X)
+    torch.cuda.synchronize()
+    print(json.dumps({"prefill_counter_run": cfg.name, "layers": cfg.layers}), flush=True)
 
 
 def stack_record(cfg, st, X, rows, nl):
@@ -1090,6 +1145,8 @@ def main():
     cfg = get_config(args.config)
     if args.token_counters is not None:
         return token_counter_run(cfg, dev, args.token_counters)
+    if args.prefill_counters:
+        return prefill_counter_run(cfg, dev)
     subs = args.sub if args.sub is not None else ("3,4" if cfg.layers else "")
     subs = [int(s) for s in subs.split(",") if s.strip()]
     t_wall = time.perf_counter()

@@ -59,6 +59,30 @@ def test_stack_token_traffic_sums_every_layer(tmp_path, monkeypatch):
     assert "algorithmic_bytes_per_launch: 1635778560" in text
 
 
+def test_stack_prompt_gemm_traffic_is_per_layer(tmp_path, monkeypatch):
+    """A layer's prompt GEMMs are two gemm_dl8_kernel dispatches (in_proj and
+    out_proj): the summary is 2 x the mean dispatch per counter, scaled by the
+    copy, against the two GEMMs' algorithmic bytes; the row pass and the
+    operator's kernels in the same run do not count."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    dl8 = "void hm::(anonymous namespace)::gemm_dl8_kernel<64>(hm::GemmArgs)"
+    rms = "hm::(anonymous namespace)::row_rms_kernel(hm::RmsArgs)"
+    op = "void hm::(anonymous namespace)::chunk_mfma_kernel<16, 128, 1, false, false>(hm::OpArgs)"
+    copy = "void at::native::elementwise_kernel<direct_copy_kernel_cuda>"
+    _csv(tmp_path / "f", "FETCH_SIZE", [(copy, 524288.0), (rms, 777.0), (dl8, 3000.0), (op, 555.0), (dl8, 1000.0)])
+    _csv(tmp_path / "w", "WRITE_SIZE", [(copy, 1048576.0), (rms, 1.0), (dl8, 600.0), (op, 5.0), (dl8, 200.0)])
+    args = argparse.Namespace(config=5, traffic_kernel="stack_prompt_gemm",
+                              traffic_from=(str(tmp_path / "f"), str(tmp_path / "w")), traffic_cmd="a ;; b")
+    bench.write_traffic(args)
+    got = bench.read_traffic("stack_prompt_gemm", "stack24-bf16")
+    assert got == round(2 * (2000.0 * 2 + 400.0) * 1024)
+    M, D = 64 * 2048, 2048
+    alg = 2 * (M * D + 3 * D * D + 3 * M * D) + 2 * (M * D + D * D + M * D)
+    assert bench.stack_prompt_gemm_bytes(__import__("workloads").get_config(5)) == alg == 3254779904
+    text = (tmp_path / "profiles" / "stack_prompt_gemm.stack24-bf16.traffic.txt").read_text()
+    assert f"algorithmic_bytes_per_launch: {alg}" in text
+
+
 def test_trace_summary_from_kernel_stats(tmp_path):
     """rocprofv3 --stats rows of two processes are merged per kernel, sorted by
     total time, with calls, mean/min/max per dispatch and the command."""
